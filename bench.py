@@ -1,0 +1,407 @@
+"""Benchmark of the fused TP-reduce + mHC + RMSNorm sublayer boundary on one
+MI355X.
+
+Headline step: one delayed-mHC boundary call (TP partial sum, post-mix,
+collapse, RMSNorm) on the DSV4.1-shaped workload, hidden 5120, tp 8, M = 128
+decode tokens, all inputs resident in HBM.  Buffers rotate over > 3x the
+256 MB Infinity Cache so every call streams from HBM; the K timed calls are
+replayed from a captured HIP graph and bracketed by synchronizations.
+
+One JSON line on stdout: the metric, value (achieved HBM GB/s of algorithmic
+bytes), ms_per_step, the roofline of the boundary kernel, the oracle's CPU
+baseline, the M sweep (us/call at M = 1 and 64), and the other workloads
+(MoE finalize, GLM, MXFP8 at M = 8192, mailbox-fed).
+
+  python bench.py [--steps K] [--warmup W] [--quick] [--only headline|...]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import glob
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused reduce+mHC+RMSNorm: achieved HBM GB/s, tokens/s; µs/call at M=1,64"
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "boundary_dsv41_M128_traffic.txt")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# Algorithmic bytes (each tensor counted once; weights once per call)
+# ---------------------------------------------------------------------------
+
+def bytes_delayed(M, H, tp, mxfp8=False):
+    per_token = (tp + 9) * 2 * H + 96
+    if mxfp8:
+        per_token += H + H // 32
+    pad = ((M + 127) // 128 * 128 - M) * (H // 32) if mxfp8 else 0
+    return M * per_token + 2 * H + pad
+
+
+def bytes_mailbox_extra(M, H, tp):
+    # producer reads the partials and writes the slots; the consumer resets them
+    return M * 3 * tp * 2 * H
+
+
+def bytes_finalize(M, H, tp, top_k):
+    return M * (tp * (top_k + 1) * 2 * H + top_k * 8 + 9 * 2 * H + 96) + 2 * H
+
+
+def bytes_glm(M, H, tp):
+    return M * (tp * 2 * H + 9 * 2 * H + 80 + 96) + 24 * 4 * H * 2 + 2 * H + 27 * 4
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "tp_reduce_mhc_amd", "csrc", "*"))):
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch of the headline kernel from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    fields = {}
+    for line in open(TRAFFIC_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("source_hash") != source_hash():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ---------------------------------------------------------------------------
+# GPU timing
+# ---------------------------------------------------------------------------
+
+class Timed:
+    """Times `steps` calls of fn(i) (i = rotation index), captured in a HIP
+    graph when possible, with HIP events on the launching stream."""
+
+    def __init__(self, torch, fn, steps, warmup, use_graph=True):
+        self.torch = torch
+        self.fn, self.steps, self.warmup = fn, steps, warmup
+        self.graph = None
+        self.use_graph = use_graph
+
+    def run(self):
+        torch = self.torch
+        for i in range(self.warmup):
+            self.fn(i)
+        torch.cuda.synchronize()
+        if self.use_graph:
+            try:
+                s = torch.cuda.Stream()
+                s.wait_stream(torch.cuda.current_stream())
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=s):
+                    for i in range(self.steps):
+                        self.fn(i)
+                torch.cuda.synchronize()
+                g.replay()               # untimed replay
+                torch.cuda.synchronize()
+                self.graph = g
+            except Exception as e:  # capture unsupported: time eagerly
+                log(f"graph capture failed ({e}); timing eager launches")
+                self.graph = None
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record()
+        if self.graph is not None:
+            self.graph.replay()
+        else:
+            for i in range(self.steps):
+                self.fn(i)
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / self.steps  # ms per call
+
+
+def rotations(per_set_bytes, minimum=4):
+    return max(minimum, int(np.ceil(3.2 * MALL_BYTES / max(per_set_bytes, 1))))
+
+
+def make_sets(torch, tensors, count):
+    """`count` copies of the input tensors in distinct HBM."""
+    sets = [tensors]
+    for _ in range(count - 1):
+        sets.append({k: v.clone() for k, v in tensors.items()})
+    torch.cuda.synchronize()
+    return sets
+
+
+# ---------------------------------------------------------------------------
+# Workloads
+# ---------------------------------------------------------------------------
+
+def dev(torch, a):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16).copy()).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a).copy()).cuda()
+
+
+def delayed_sets(torch, b, count):
+    t = dict(partials=dev(torch, b.partials), residual=dev(torch, b.residual),
+             post=dev(torch, b.post), comb=dev(torch, b.comb), pre=dev(torch, b.pre),
+             gamma=dev(torch, b.gamma))
+    sets = make_sets(torch, t, count)
+    for s in sets:
+        s["residual_out"] = torch.empty((b.M, 4, b.H), dtype=torch.bfloat16, device="cuda")
+        s["layer_input"] = torch.empty((b.M, b.H), dtype=torch.bfloat16, device="cuda")
+    return sets
+
+
+def bench_delayed(torch, mhc, b, steps, warmup, mxfp8=False, check=False):
+    per_set = bytes_delayed(b.M, b.H, b.tp, mxfp8)
+    sets = delayed_sets(torch, b, rotations(per_set))
+    if mxfp8:
+        for s in sets:
+            s["values"] = torch.empty((b.M, b.H), dtype=torch.uint8, device="cuda")
+            s["scales"] = torch.empty(mhc.mhcb_mxfp8_scale_bytes(b.M, b.H), dtype=torch.uint8,
+                                      device="cuda")
+
+    def call(i):
+        s = sets[i % len(sets)]
+        mhc.mhcb_boundary(s["partials"], b.M * b.H, None, s["residual"], s["post"], s["comb"],
+                          s["pre"], s["gamma"], s["residual_out"], s["layer_input"],
+                          s.get("values"), s.get("scales"), b.M, b.H, 4, b.tp, b.norm_eps)
+
+    ms = Timed(torch, call, steps, warmup).run()
+    if check:
+        # Every rotation set's output of the graph replay equals an eager call.
+        for s in sets[:3]:
+            ro, li = s["residual_out"].clone(), s["layer_input"].clone()
+            mhc.mhcb_boundary(s["partials"], b.M * b.H, None, s["residual"], s["post"], s["comb"],
+                              s["pre"], s["gamma"], s["residual_out"], s["layer_input"],
+                              s.get("values"), s.get("scales"), b.M, b.H, 4, b.tp, b.norm_eps)
+            torch.cuda.synchronize()
+            assert torch.equal(ro.view(torch.int16), s["residual_out"].view(torch.int16))
+            assert torch.equal(li.view(torch.int16), s["layer_input"].view(torch.int16))
+    return ms, per_set, len(sets)
+
+
+def bench_mailbox(torch, mhc, b, steps, warmup):
+    """Producer (publish of all tp partials) + mailbox-fed consumer with the
+    MXFP8 epilogue, per step."""
+    mb = mhc.Mailbox(b.tp, b.M, b.H, "cuda")
+    mb.init()
+    sets = delayed_sets(torch, b, 2)
+    for s in sets:
+        s["values"] = torch.empty((b.M, b.H), dtype=torch.uint8, device="cuda")
+        s["scales"] = torch.empty(mhc.mhcb_mxfp8_scale_bytes(b.M, b.H), dtype=torch.uint8, device="cuda")
+
+    def call(i):
+        s = sets[i % len(sets)]
+        mhc.mhcb_publish(mb, s["partials"], b.M * b.H, 0, b.tp, b.M)
+        mhc.mhcb_boundary(None, 0, mb, s["residual"], s["post"], s["comb"], s["pre"], s["gamma"],
+                          s["residual_out"], s["layer_input"], s["values"], s["scales"], b.M, b.H,
+                          4, b.tp, b.norm_eps)
+
+    ms = Timed(torch, call, steps, warmup).run()
+    assert mb.status_ok()
+    return ms, bytes_delayed(b.M, b.H, b.tp, True) + bytes_mailbox_extra(b.M, b.H, b.tp)
+
+
+def bench_finalize(torch, mhc, f, steps, warmup, two_shot=False):
+    per_set = bytes_finalize(f.M, f.H, f.tp, f.top_k)
+    t = dict(gemm2=dev(torch, f.gemm2), weights=dev(torch, f.weights), idx=dev(torch, f.idx),
+             shared=dev(torch, f.shared), residual=dev(torch, f.residual), post=dev(torch, f.post),
+             comb=dev(torch, f.comb), pre=dev(torch, f.pre), gamma=dev(torch, f.gamma))
+    sets = make_sets(torch, t, rotations(per_set, minimum=2))
+    rows = f.gemm2.shape[1]
+    ws = None
+    if two_shot:
+        ws = torch.empty(mhc.mhcb_finalize_workspace_bytes(f.M, f.H, f.tp, 1), dtype=torch.uint8,
+                         device="cuda")
+    for s in sets:
+        s["residual_out"] = torch.empty((f.M, 4, f.H), dtype=torch.bfloat16, device="cuda")
+        s["layer_input"] = torch.empty((f.M, f.H), dtype=torch.bfloat16, device="cuda")
+
+    def call(i):
+        s = sets[i % len(sets)]
+        mhc.mhcb_finalize(s["gemm2"], rows * f.H, rows, s["weights"], 0, s["idx"], 0, s["shared"],
+                          f.M * f.H, s["residual"], s["post"], s["comb"], s["pre"], s["gamma"],
+                          s["residual_out"], s["layer_input"], None, None, int(two_shot), ws,
+                          ws.numel() if ws is not None else 0, f.M, f.H, 4, f.tp, f.top_k,
+                          f.norm_eps)
+
+    ms = Timed(torch, call, steps, warmup).run()
+    extra = f.M * (2 * f.tp * 2 * f.H + 2 * 2 * f.H) if two_shot else 0
+    return ms, per_set + extra
+
+
+def bench_glm(torch, mhc, g, steps, warmup):
+    per_set = bytes_glm(g.M, g.H, g.tp)
+    t = dict(partials=dev(torch, g.partials), residual=dev(torch, g.residual),
+             post=dev(torch, g.post), comb=dev(torch, g.comb))
+    sets = make_sets(torch, t, rotations(per_set))
+    fn, scale, base, gamma = (dev(torch, g.fn), dev(torch, g.scale), dev(torch, g.base),
+                              dev(torch, g.gamma))
+    for s in sets:
+        s["residual_out"] = torch.empty((g.M, 4, g.H), dtype=torch.bfloat16, device="cuda")
+        s["layer_input"] = torch.empty((g.M, g.H), dtype=torch.bfloat16, device="cuda")
+        s["mixes"] = torch.empty((g.M, 24), dtype=torch.float32, device="cuda")
+
+    def call(i):
+        s = sets[i % len(sets)]
+        mhc.mhcb_boundary_glm(s["partials"], g.M * g.H, s["residual"], s["post"], s["comb"], fn,
+                              scale, base, gamma, s["residual_out"], s["mixes"], s["layer_input"],
+                              g.M, g.H, 4, g.tp, g.rms_eps, g.hc_eps, g.norm_eps, 0)
+
+    ms = Timed(torch, call, steps, warmup).run()
+    return ms, per_set
+
+
+def entry(ms, nbytes, M):
+    return {"us_per_call": round(ms * 1e3, 3), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "tokens_per_s": round(M / (ms * 1e-3), 1), "algorithmic_bytes": int(nbytes)}
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample of the headline workload
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(b, budget_s=1.5):
+    import oracle
+    threads = oracle.default_threads()
+    oracle.boundary(b.partials[:, :2], b.residual[:2], b.post[:2], b.comb[:2], b.pre[:2], b.gamma,
+                    b.norm_eps, threads=1)  # load + warm
+    reps, times = 0, []
+    t_end = time.perf_counter() + budget_s
+    while reps < 3 or time.perf_counter() < t_end:
+        t0 = time.perf_counter()
+        oracle.boundary(b.partials, b.residual, b.post, b.comb, b.pre, b.gamma, b.norm_eps,
+                        threads=threads)
+        times.append(time.perf_counter() - t0)
+        reps += 1
+        if reps >= 50:
+            break
+    sec = float(np.median(times))
+    nbytes = bytes_delayed(b.M, b.H, b.tp)
+    return {"value": round(nbytes / sec / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "tokens_per_s": round(b.M / sec, 1),
+            "us_per_call": round(sec * 1e6, 1),
+            "sample": f"{reps} calls of the same workload ({b.name}), median wall time, "
+                      f"{threads} threads, about {sum(times) * threads:.0f} s of CPU work"}
+
+
+# ---------------------------------------------------------------------------
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--quick", action="store_true", help="headline only, no extra workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default="",
+                    help="run one workload only (headline, sweep, finalize, glm, mxfp8, mailbox) "
+                         "for profiling; prints no JSON")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this build has no "
+              "multi-GPU path; the boundary would shard over tokens, see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import tp_reduce_mhc_amd as mhc
+    torch.cuda.set_device(0)
+    K, W = args.steps, args.warmup
+    result = {}
+
+    if args.only in ("", "headline"):
+        b = synth.dsv41_delayed(128)
+        log(f"headline {b.name}: {K} steps, {W} warmup")
+        ms, nbytes, nsets = bench_delayed(torch, mhc, b, K, W, check=True)
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        traffic = measured_traffic()
+        result.update({
+            "metric": METRIC, "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
+            "warmup": W, "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f32", "storage": "bf16", "data": "synthetic",
+            "config": {"workload": b.name, "hidden_size": b.H, "tp": b.tp, "hc_mult": 4, "M": b.M,
+                       "rotating_input_sets": nsets, "timing": "HIP graph of K calls, HIP events"},
+            "tokens_per_s": round(b.M / (ms * 1e-3), 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBS, 4),
+                         "traffic": traffic, "kernel": "boundary_kernel (delayed mHC, tp 8)",
+                         "algorithmic_bytes_per_launch": int(nbytes)},
+        })
+        if not args.no_cpu_baseline and not args.only:
+            log("cpu baseline (oracle)")
+            result["cpu_baseline"] = cpu_baseline(b)
+        if args.only:
+            log(f"headline: {ms * 1e3:.2f} us/call, {gbps:.0f} GB/s")
+
+    if args.only in ("", "sweep") and not args.quick:
+        sweep = {}
+        for M in (1, 8, 32, 64, 128):
+            b = synth.dsv41_delayed(M)
+            ms, nbytes, _ = bench_delayed(torch, mhc, b, min(K, 200), W)
+            sweep[f"M{M}"] = entry(ms, nbytes, M)
+            log(f"sweep M={M}: {sweep[f'M{M}']}")
+        result["sweep_dsv41_delayed"] = sweep
+        result["us_per_call"] = {"M1": sweep["M1"]["us_per_call"], "M64": sweep["M64"]["us_per_call"]}
+
+    extra = {}
+    if args.only in ("", "finalize") and not args.quick:
+        for M in (64, 512, 4096):
+            f = synth.moe_finalize(M)
+            steps = max(10, min(K, 100 if M <= 512 else 20))
+            ms, nbytes = bench_finalize(torch, mhc, f, steps, min(W, 5))
+            extra[f"moe_finalize_M{M}"] = entry(ms, nbytes, M)
+            log(f"finalize M={M}: {extra[f'moe_finalize_M{M}']}")
+            if M == 512:
+                ms, nbytes = bench_finalize(torch, mhc, f, steps, min(W, 5), two_shot=True)
+                extra[f"moe_finalize_two_shot_M{M}"] = entry(ms, nbytes, M)
+            del f
+    if args.only in ("", "glm") and not args.quick:
+        for M in (1, 64, 512):
+            g = synth.glm(M)
+            ms, nbytes = bench_glm(torch, mhc, g, min(K, 100), min(W, 5))
+            extra[f"glm_M{M}"] = entry(ms, nbytes, M)
+            log(f"glm M={M}: {extra[f'glm_M{M}']}")
+    if args.only in ("", "mxfp8") and not args.quick:
+        b = synth.large_m_delayed(8192)
+        ms, nbytes, _ = bench_delayed(torch, mhc, b, 20, 3, mxfp8=True)
+        extra["mxfp8_M8192"] = entry(ms, nbytes, 8192)
+        log(f"mxfp8 M=8192: {extra['mxfp8_M8192']}")
+        if args.only in ("", "mailbox"):
+            ms, nbytes = bench_mailbox(torch, mhc, b, 10, 2)
+            extra["mailbox_mxfp8_M8192"] = entry(ms, nbytes, 8192)
+            log(f"mailbox M=8192: {extra['mailbox_mxfp8_M8192']}")
+    elif args.only == "mailbox":
+        b = synth.large_m_delayed(8192)
+        ms, nbytes = bench_mailbox(torch, mhc, b, 10, 2)
+        log(f"mailbox M=8192: {entry(ms, nbytes, 8192)}")
+    if extra:
+        result["other_workloads"] = extra
+
+    if not args.only:
+        print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

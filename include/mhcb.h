@@ -1,0 +1,189 @@
+/*
+ * mhcb.h -- C ABI of libmhcb: the fused TP-reduce + mHC + RMSNorm sublayer
+ * boundary on AMD Instinct MI355X (gfx950).
+ *
+ * The operations are those of two web pages, cited by title and section:
+ *   [DSV41] vllm.models.deepseek_v41.nvidia.ops.cute_dsl.all_reduce_mhc
+ *           (AllReduceMHC.__call__ / .finalize / ._check / ._consumer,
+ *            _LamportMHCDeviceKernel, _QuadFinalizePublishDeviceKernel,
+ *            _OwnerReduceMulticastDeviceKernel, _SharedOnlyPublishDeviceKernel)
+ *   [GLM]   vllm.models.glm5next.nvidia.specialized_decode.all_reduce_mhc
+ *           (AllReduceMhcBoundary.__call__ / .join, _BoundaryDeviceKernel,
+ *            _GroupBoundaryDeviceKernel, _MixesDeviceKernel, _PublishDeviceKernel)
+ *
+ * Conventions for every entry point
+ *  - Pointers are DEVICE pointers owned by the caller unless stated; the
+ *    library never allocates, frees or retains them.
+ *  - BF16 tensors are uint16_t bit patterns, 16-byte aligned; FP32 tensors
+ *    4-byte aligned; rank strides (in elements) keep 16-byte alignment.
+ *  - Every call validates all arguments before any launch or any write to a
+ *    mailbox or stage word ([DSV41] AllReduceMHC._consumer: a bad argument
+ *    leaves the state untouched), then enqueues its kernels on `stream`
+ *    (0 = the null stream) and returns without synchronizing.
+ *  - Outputs must not alias inputs.
+ *  - Return value: MHCB_OK or an error code; mhcb_last_error() gives the
+ *    calling thread's message for the last failure.
+ *  - hc_mult must be 4 ([GLM] ties the kernel to four streams); hidden_size
+ *    a multiple of 8 (16-byte fragments of 8 BF16 values) and at most 16384.
+ */
+#ifndef MHCB_H
+#define MHCB_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum mhcb_status {
+  MHCB_OK = 0,
+  MHCB_EINVAL = 1,       /* bad size, shape, null pointer or combination     */
+  MHCB_EALIGN = 2,       /* pointer or stride breaks the alignment rules     */
+  MHCB_EUNSUPPORTED = 3, /* valid per the pages but outside this build       */
+  MHCB_ELAUNCH = 4,      /* the HIP runtime rejected a launch                */
+  MHCB_ETIMEOUT = 5      /* a mailbox poll gave up (see mhcb_mailbox_status) */
+};
+
+/* Message of the calling thread's last failed call ("" if none). */
+const char *mhcb_last_error(void);
+
+/* Library version as "major.minor.patch". */
+const char *mhcb_version(void);
+
+/* Bytes of the swizzled 128x4 UE8M0 scale array for an [M, hidden_size]
+ * MXFP8 output: rows padded to a multiple of 128, hidden_size / 32 columns
+ * ([DSV41] AllReduceMHC.__call__, mxfp8_scale_bytes).  Host-only. */
+int64_t mhcb_mxfp8_scale_bytes(int64_t M, int64_t hidden_size);
+
+/* Workspace bytes mhcb_finalize needs: 0 for the one-shot path; for the
+ * two-shot emulation the owner mailboxes [tp][tp][ceil(M/tp)][hidden] plus
+ * the reduced sums [M][hidden], BF16.  Host-only; -1 on bad sizes. */
+int64_t mhcb_finalize_workspace_bytes(int M, int hidden_size, int tp, int two_shot);
+
+/* Three-generation Lamport mailbox ([GLM] AllReduceMhcBoundary.__init__,
+ * [DSV41] module text): slots[generation][rank][token][hidden] BF16, every
+ * empty slot holding the sentinel 0x8000 (BF16 -0); stage_state = {ACTIVE,
+ * NEXT}; status counts consumer polls that gave up.  All three pointers are
+ * caller-owned device memory; the struct itself is read on the host only. */
+typedef struct mhcb_mailbox {
+  uint16_t *slots;       /* [generations][tp][capacity][hidden_size]       */
+  int32_t *stage_state;  /* [2]: ACTIVE, NEXT                              */
+  int32_t *status;       /* [1]: poll time-outs since mhcb_mailbox_init    */
+  int generations;       /* must be 3                                      */
+  int tp;                /* ranks                                          */
+  int capacity;          /* max tokens per call                            */
+  int hidden_size;
+  int64_t spin_limit;    /* re-reads per fragment before giving up; <= 0:  */
+                         /* the default (about a second of polling)        */
+} mhcb_mailbox;
+
+/* Delayed-mHC boundary ([DSV41] AllReduceMHC.__call__ with
+ * _LamportMHCDeviceKernel), per token t and column c:
+ *   xr      = bf16( ((0 + x_0) + x_1) + ... + x_{tp-1} )       (FP32 adds)
+ *   y_j     = bf16( xr*post_j (+) sum_s residual_s * comb[s][j] )   (FMAs)
+ *   p       = bf16( 0 (+) y_0*pre_0 (+) ... (+) y_3*pre_3 )          (FMAs)
+ *   out     = bf16( (p * inv) * norm_weight ),
+ *             inv = 1/sqrt(sum_c p^2 / hidden + norm_eps)
+ * Inputs: partials = tp BF16 [M, hidden] arrays rank_stride elements apart
+ * (NULL iff mailbox is given: then the ACTIVE generation is polled until no
+ * element is the sentinel, NEXT is advanced and the slots are reset);
+ * residual [M, 4, hidden] BF16; post, pre [M, 4] FP32; comb [M, 4, 4] FP32
+ * indexed [source][target]; norm_weight [hidden] BF16.
+ * Outputs: residual_out [M, 4, hidden] = y; layer_input [M, hidden] = out;
+ * optionally mxfp8_values [M, hidden] E4M3 codes and mxfp8_scales
+ * (mhcb_mxfp8_scale_bytes) UE8M0 scales of out, per 32 columns, in the
+ * swizzled 128x4 layout, padding rows zeroed (hidden % 128 == 0 required).
+ * pre == norm_weight == layer_input == NULL selects the residual-only
+ * variant.  Errors: M < 1 or M > mailbox capacity, tp < 1 or tp > 64,
+ * pre/norm_weight given alone, MXFP8 on a residual-only call -> EINVAL;
+ * hidden % 8, hc_mult != 4, MXFP8 with hidden % 128 -> EUNSUPPORTED. */
+int mhcb_boundary(const uint16_t *partials, int64_t rank_stride, const mhcb_mailbox *mailbox,
+                  const uint16_t *residual, const float *post, const float *comb,
+                  const float *pre, const uint16_t *norm_weight, uint16_t *residual_out,
+                  uint16_t *layer_input, uint8_t *mxfp8_values, uint8_t *mxfp8_scales, int M,
+                  int hidden_size, int hc_mult, int tp, float norm_eps, hipStream_t stream);
+
+/* GLM boundary ([GLM] AllReduceMhcBoundary.__call__ with
+ * _BoundaryDeviceKernel / _GroupBoundaryDeviceKernel): xr and y as in
+ * mhcb_boundary, then from the new streams
+ *   g_k   = sum_{j,c} hc_fn[k][j*hidden + c] * y_j[c]   (k < 24)
+ *   rstd  = 1/sqrt(sum_{j,c} y_j[c]^2 / (4*hidden) + rms_eps)
+ *   mixes_out[t][k] = g_k * rstd                  (raw, for mhcb_mixes)
+ *   pre_j = sigmoid(mixes_j * scale[0] + base[j]) + hc_eps
+ *   p     = bf16((y_0*pre_0 + y_1*pre_1) + (y_2*pre_2 + y_3*pre_3))
+ *   out   = bf16((p * inv) * norm_weight) as above.
+ * hc_fn [24, 4*hidden] BF16; scale [3], base [24] FP32; mixes_out [M, 24]
+ * FP32.  tokens_per_wg (1, 2, 4; 0 = by M) tokens share one workgroup and
+ * one read of hc_fn; outputs do not depend on it.  hidden <= 8192. */
+int mhcb_boundary_glm(const uint16_t *partials, int64_t rank_stride, const uint16_t *residual,
+                      const float *post, const float *comb, const uint16_t *hc_fn,
+                      const float *scale, const float *base, const uint16_t *norm_weight,
+                      uint16_t *residual_out, float *mixes_out, uint16_t *layer_input, int M,
+                      int hidden_size, int hc_mult, int tp, float rms_eps, float hc_eps,
+                      float norm_eps, int tokens_per_wg, hipStream_t stream);
+
+/* Side-stream mixes for the next boundary ([GLM] _MixesDeviceKernel):
+ *   post_out[t][j] = sigmoid(mixes[t][4+j] * scale[1] + base[4+j]) * post_mult
+ *   comb_out[t]    = Sinkhorn(mixes[t][8+i] * scale[2] + base[8+i]), 4x4
+ *                    row-major, eps = hc_eps, sinkhorn_repeat rounds.
+ * mixes [M, 24]; post_out [M, 4]; comb_out [M, 4, 4] (FP32).  Meant for a
+ * second stream that the caller joins before the next boundary reads it. */
+int mhcb_mixes(const float *mixes, const float *scale, const float *base, float *post_out,
+               float *comb_out, int M, int hc_mult, float hc_eps, float post_mult,
+               int sinkhorn_repeat, hipStream_t stream);
+
+/* MoE finalize boundary ([DSV41] AllReduceMHC.finalize with
+ * _QuadFinalizePublishDeviceKernel): rank r's contribution to token t is
+ *   c_r = bf16( (sum_k fma over k ascending of gemm2_r[idx_r[t][k]] * w_r[t][k])
+ *               + shared_r[t] ), negative zero -> +0,
+ * a route whose row index is -1 (expert not held by rank r) or outside
+ * [0, rows) being skipped; then the boundary of mhcb_boundary on the c_r.
+ * gemm2_permuted: per rank [rows, hidden] BF16, gemm2_rank_stride apart;
+ * expert_weights [M, top_k] FP32 and permuted_idx [M, top_k] int32 per rank
+ * (rank strides 0 = replicated); shared_output per rank [M, hidden] BF16.
+ * two_shot = 1 runs the two-shot emulation instead: contributions stored
+ * to owner t % tp, slot t / tp of owner mailboxes in `workspace`
+ * (mhcb_finalize_workspace_bytes, 16-byte aligned, caller-owned), the
+ * owners' FP32 rank-ordered sums, then the boundary reads one reduced value
+ * per token; the results are bit-identical to two_shot = 0.
+ * Errors as mhcb_boundary, plus top_k < 1, tp * top_k > 1024, a workspace
+ * that is missing or too small -> EINVAL. */
+int mhcb_finalize(const uint16_t *gemm2_permuted, int64_t gemm2_rank_stride, int64_t rows,
+                  const float *expert_weights, int64_t weights_rank_stride,
+                  const int32_t *permuted_idx, int64_t idx_rank_stride,
+                  const uint16_t *shared_output, int64_t shared_rank_stride,
+                  const uint16_t *residual, const float *post, const float *comb,
+                  const float *pre, const uint16_t *norm_weight, uint16_t *residual_out,
+                  uint16_t *layer_input, uint8_t *mxfp8_values, uint8_t *mxfp8_scales,
+                  int two_shot, void *workspace, int64_t workspace_bytes, int M, int hidden_size,
+                  int hc_mult, int tp, int top_k, float norm_eps, hipStream_t stream);
+
+/* Standalone MXFP8 of a BF16 [M, hidden] array: the encoding of the
+ * boundary's epilogue ([DSV41] _LamportMHCDeviceKernel, quantize): per 32
+ * columns e = the smallest UE8M0 exponent with 2^(e-127) >= amax * fl(1/448),
+ * codes = E4M3 round-to-nearest-even (saturating) of x * 2^(127-e); values
+ * [M, hidden] bytes, scales mhcb_mxfp8_scale_bytes bytes. */
+int mhcb_quant_mxfp8(const uint16_t *x, uint8_t *values, uint8_t *scales, int M, int hidden_size,
+                     hipStream_t stream);
+
+/* Fills every slot with the sentinel, zeroes stage_state and status. */
+int mhcb_mailbox_init(const mhcb_mailbox *mailbox, hipStream_t stream);
+
+/* Producer ([GLM] _PublishDeviceKernel, [DSV41]
+ * _SharedOnlyPublishDeviceKernel): reads NEXT, stores ranks
+ * [rank_begin, rank_begin + rank_count) of tokens [0, M) -- their partials
+ * rank_stride elements apart -- with negative zero replaced by +0 into
+ * generation NEXT, then sets ACTIVE = NEXT. */
+int mhcb_publish(const mhcb_mailbox *mailbox, const uint16_t *partials, int64_t rank_stride,
+                 int rank_begin, int rank_count, int M, hipStream_t stream);
+
+/* Synchronizes `stream`, then returns MHCB_ETIMEOUT if any consumer poll of
+ * this mailbox gave up since mhcb_mailbox_init, else MHCB_OK. */
+int mhcb_mailbox_status(const mhcb_mailbox *mailbox, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MHCB_H */

@@ -1,0 +1,144 @@
+"""The C ABI without a GPU: libmhcb.so loads, exports every entry point that
+include/*.h declares, and rejects bad arguments before touching the device
+(no compute call is made here)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    names = set()
+    for header in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(header).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"\b(mhcb_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
+
+
+def test_header_declares_the_entry_points():
+    names = declared_symbols()
+    for want in ("mhcb_boundary", "mhcb_boundary_glm", "mhcb_finalize", "mhcb_mixes",
+                 "mhcb_quant_mxfp8", "mhcb_mailbox_init", "mhcb_publish", "mhcb_last_error"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    import tp_reduce_mhc_amd as mhc
+    lib = ctypes.CDLL(mhc.LIBRARY_PATH)
+    for name in declared_symbols():
+        assert hasattr(lib, name), f"{name} declared in include/ but not exported"
+    assert set(mhc.EXPORTED) == set(declared_symbols())
+
+
+def test_host_only_helpers():
+    import tp_reduce_mhc_amd as mhc
+    assert mhc.mhcb_mxfp8_scale_bytes(8192, 5120) == 8192 * 160
+    assert mhc.mhcb_mxfp8_scale_bytes(100, 5120) == 128 * 160
+    assert mhc.mhcb_mxfp8_scale_bytes(1, 128) == 128 * 4
+    assert mhc.mhcb_finalize_workspace_bytes(10, 512, 4, 0) == 0
+    assert mhc.mhcb_finalize_workspace_bytes(10, 512, 4, 1) == (4 * 4 * 3 + 10) * 512 * 2
+    assert mhc.mhcb_finalize_workspace_bytes(10, 512, 0, 1) == -1
+    assert mhc.mhcb_version().count(".") == 2
+
+
+FAKE = 0x10000  # an aligned non-null address; validation fails before any use of it
+
+
+def _boundary(**kw):
+    import tp_reduce_mhc_amd as mhc
+    args = dict(partials=FAKE, rank_stride=4 * 512, mailbox=None, residual=FAKE, post=FAKE,
+                comb=FAKE, pre=FAKE, norm_weight=FAKE, residual_out=FAKE, layer_input=FAKE,
+                mxfp8_values=None, mxfp8_scales=None, M=4, hidden_size=512, hc_mult=4, tp=2,
+                norm_eps=1e-6, stream=0)
+    args.update(kw)
+    return mhc.mhcb_boundary(**args)
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(M=0), 1, "M=0"),
+    (dict(hc_mult=2), 3, "hc_mult"),
+    (dict(hidden_size=100), 3, "multiple of 8"),
+    (dict(hidden_size=32768, rank_stride=4 * 32768), 3, "exceeds"),
+    (dict(tp=0), 1, "tp=0"),
+    (dict(tp=65), 1, "tp=65"),
+    (dict(pre=None), 1, "pre and norm_weight"),
+    (dict(mxfp8_values=FAKE), 1, "both given"),
+    (dict(pre=None, norm_weight=None, layer_input=None, mxfp8_values=FAKE, mxfp8_scales=FAKE), 1,
+     "residual-only"),
+    (dict(mxfp8_values=FAKE, mxfp8_scales=FAKE, hidden_size=520, rank_stride=4 * 520), 3, "% 128"),
+    (dict(residual=FAKE + 2), 2, "aligned"),
+    (dict(partials=None), 1, "exactly one"),
+    (dict(rank_stride=100), 1, "overlaps"),
+    (dict(rank_stride=4 * 512 + 4), 2, "rank_stride"),
+    (dict(residual_out=None), 1, "required"),
+])
+def test_boundary_validation(kw, code, text):
+    import tp_reduce_mhc_amd as mhc
+    with pytest.raises(mhc.MhcbError) as e:
+        _boundary(**kw)
+    assert e.value.code == code
+    assert text in str(e.value)
+
+
+def test_mailbox_validation():
+    import tp_reduce_mhc_amd as mhc
+    mb = mhc.mhcb_mailbox(FAKE, FAKE, FAKE, 3, 2, 8, 512, 0)
+    with pytest.raises(mhc.MhcbError, match="outside"):
+        _boundary(partials=None, mailbox=mb, M=9)
+    with pytest.raises(mhc.MhcbError, match="tp=2 but tp=4"):
+        _boundary(partials=None, mailbox=mb, tp=4)
+    bad = mhc.mhcb_mailbox(FAKE, FAKE, FAKE, 2, 2, 8, 512, 0)
+    with pytest.raises(mhc.MhcbError, match="generations"):
+        _boundary(partials=None, mailbox=bad)
+    with pytest.raises(mhc.MhcbError, match="exactly one"):
+        _boundary(mailbox=mb)
+    with pytest.raises(mhc.MhcbError, match="ranks"):
+        mhc.mhcb_publish(mb, FAKE, 4 * 512, 1, 2, 4, 0)
+    with pytest.raises(mhc.MhcbError, match="M=0"):
+        mhc.mhcb_publish(mb, FAKE, 4 * 512, 0, 2, 0, 0)
+
+
+def test_glm_mixes_finalize_quant_validation():
+    import tp_reduce_mhc_amd as mhc
+    glm = dict(partials=FAKE, rank_stride=4 * 512, residual=FAKE, post=FAKE, comb=FAKE, hc_fn=FAKE,
+               scale=FAKE, base=FAKE, norm_weight=FAKE, residual_out=FAKE, mixes_out=FAKE,
+               layer_input=FAKE, M=4, hidden_size=512, hc_mult=4, tp=2, rms_eps=1e-6, hc_eps=1e-6,
+               norm_eps=1e-6, stream=0)
+    for kw, text in ((dict(tokens_per_wg=3), "tokens_per_wg"), (dict(hc_fn=None), "required"),
+                     (dict(hidden_size=8200, rank_stride=4 * 8200), "exceeds"),
+                     (dict(tokens_per_wg=4, hidden_size=8192, rank_stride=4 * 8192), "tokens_per_wg=4")):
+        with pytest.raises(mhc.MhcbError, match=text):
+            mhc.mhcb_boundary_glm(**{**glm, **kw})
+    with pytest.raises(mhc.MhcbError, match="sinkhorn_repeat"):
+        mhc.mhcb_mixes(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 1e-6, 2.0, -1, 0)
+    with pytest.raises(mhc.MhcbError, match="hc_mult"):
+        mhc.mhcb_mixes(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 3, 1e-6, 2.0, 20, 0)
+    fin = dict(gemm2_permuted=FAKE, gemm2_rank_stride=32 * 512, rows=32, expert_weights=FAKE,
+               weights_rank_stride=0, permuted_idx=FAKE, idx_rank_stride=0, shared_output=FAKE,
+               shared_rank_stride=4 * 512, residual=FAKE, post=FAKE, comb=FAKE, pre=FAKE,
+               norm_weight=FAKE, residual_out=FAKE, layer_input=FAKE, mxfp8_values=None,
+               mxfp8_scales=None, two_shot=0, workspace=None, workspace_bytes=0, M=4,
+               hidden_size=512, hc_mult=4, tp=2, top_k=8, norm_eps=1e-6, stream=0)
+    for kw, text in ((dict(top_k=0), "top_k"), (dict(tp=64, top_k=32), "exceeds"),
+                     (dict(two_shot=1), "workspace"), (dict(rows=-1), "rows"),
+                     (dict(two_shot=1, workspace=FAKE + 8, workspace_bytes=1 << 20), "aligned")):
+        with pytest.raises(mhc.MhcbError, match=text):
+            mhc.mhcb_finalize(**{**fin, **kw})
+    with pytest.raises(mhc.MhcbError, match="multiple of 128"):
+        mhc.mhcb_quant_mxfp8(FAKE, FAKE, FAKE, 4, 520, 0)
+
+
+def test_product_path_does_not_touch_the_oracle():
+    """The binding and the HIP sources never import, load or name the
+    oracle's library or module."""
+    pkg = os.path.join(ROOT, "tp_reduce_mhc_amd")
+    for path in glob.glob(os.path.join(pkg, "**", "*"), recursive=True):
+        if os.path.isfile(path) and path.endswith((".py", ".hip", ".h", ".cpp")):
+            text = open(path).read()
+            assert "import oracle" not in text and "from oracle" not in text, path
+            assert "liboracle" not in text and "oracle_" not in text, path

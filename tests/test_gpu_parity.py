@@ -1,0 +1,398 @@
+"""Parity of the HIP path (through the C ABI) with the oracle, on seeded
+workloads of the pages' shapes.  Needs an MI355X: marked gpu.
+
+Bars: the BF16 rank sum and the MXFP8 codes/scales bit-exact; post-mixed
+streams and the delayed layer input within 1 BF16 ulp (they come out
+bit-exact here); GLM layer input within 1 ulp except tie-aware 2; raw GLM
+mixes |d| <= 1e-5 (|ref| + 1); side mixes |d| <= 1e-5 |ref| + 1e-7.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.gpu_util import (assert_bits_equal, assert_within_ulp, dev, glm_layer_input_check,
+                            glm_pre, host, u16)
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import tp_reduce_mhc_amd as mhc
+
+
+def run_boundary(b, mxfp8=False, pre=True):
+    out = mhc.boundary(dev(b.partials), dev(b.residual), dev(b.post), dev(b.comb),
+                       dev(b.pre) if pre else None, dev(b.gamma) if pre else None, b.norm_eps,
+                       mxfp8=mxfp8)
+    torch.cuda.synchronize()
+    ro, li, mx = out
+    return u16(ro), (u16(li) if li is not None else None), (
+        (host(mx[0]), host(mx[1])) if mx else None)
+
+
+def check_boundary(b, mxfp8=False, threads=8):
+    print(f"[gpu] {b.name} mxfp8={mxfp8}", flush=True)
+    ro, li, mx = run_boundary(b, mxfp8)
+    ro_ref, li_ref, mx_ref = oracle.boundary(b.partials, b.residual, b.post, b.comb, b.pre, b.gamma,
+                                             b.norm_eps, mxfp8=mxfp8, threads=threads)
+    assert_bits_equal(ro, ro_ref, "residual_out")
+    assert_within_ulp(li, li_ref, 1, "layer_input")
+    if mxfp8:
+        v_q, s_q = oracle.quant_mxfp8(li)          # the oracle quantizes the GPU's BF16 output
+        assert_bits_equal(mx[0], v_q, "mxfp8 values")
+        assert_bits_equal(mx[1], s_q, "mxfp8 scales")
+    return ro, li, mx
+
+
+# ---------------------------------------------------------------------------
+# Delayed-mHC boundary
+# ---------------------------------------------------------------------------
+
+def test_tiny_delayed_boundary():
+    check_boundary(synth.tiny_delayed(), mxfp8=True)
+
+
+@pytest.mark.parametrize("M", [1, 8, 32, 64, 128])
+def test_dsv41_delayed_boundary_sweep(M):
+    check_boundary(synth.dsv41_delayed(M))
+
+
+def test_bf16_sum_is_bit_exact_through_the_probe():
+    """post = 1, comb = 0 expose the BF16 rank sum in every output stream."""
+    b = synth.dsv41_delayed(32)
+    b.post = np.ones_like(b.post)
+    b.comb = np.zeros_like(b.comb)
+    ro, _, _ = run_boundary(b)
+    xr = np.array([[oracle.rank_sum_element(b.partials[:, t:t + 1], c) for c in range(0, b.H, 37)]
+                   for t in range(b.M)], np.uint16)
+    for j in range(4):
+        assert_bits_equal(ro[:, j, ::37], xr, f"stream {j}")
+
+
+def test_rank_order_designed_case():
+    """Ranks (1, 2^-8, 2^-24, 2^-24): only the in-order FP32 sum gives 1.0."""
+    b = synth.boundary(11, 2, 512, 4, 0.5)
+    b.partials[:, :, 5] = np.array([0x3F80, 0x3B80, 0x3380, 0x3380], np.uint16)[:, None]
+    b.post = np.ones_like(b.post)
+    b.comb = np.zeros_like(b.comb)
+    ro, _, _ = run_boundary(b)
+    assert (ro[:, :, 5] == 0x3F80).all()
+
+
+@pytest.mark.parametrize("tp", [1, 2, 3, 5, 8, 9, 16])
+def test_tp_variants(tp):
+    check_boundary(synth.boundary(12, 5, 1024, tp, 0.5, f"tp{tp}"))
+
+
+@pytest.mark.parametrize("H", [8, 520, 1032, 4104, 6144, 8200, 16384])
+def test_ragged_and_wide_hidden(H):
+    """Fragments not a multiple of the workgroup (ragged last trip), one
+    fragment, and the 1/2/4 fragments-per-thread geometries."""
+    check_boundary(synth.boundary(13, 3, H, 2, 0.5, f"H{H}"))
+
+
+def test_residual_only_variant():
+    b = synth.dsv41_delayed(8)
+    ro, li, _ = run_boundary(b, pre=False)
+    ro_ref, _, _ = oracle.boundary(b.partials, b.residual, b.post, b.comb, None, None, 1e-6)
+    assert li is None
+    assert_bits_equal(ro, ro_ref, "residual_out")
+
+
+def test_negative_zero_and_rounding_edges():
+    """Partials that are -0, subnormal, exact BF16 ties of the FP32 sum and
+    sums that cancel to zero."""
+    b = synth.boundary(14, 4, 256, 2, 0.5)
+    p = b.partials
+    p[0, :, 0:8] = 0x8000                                   # -0 + x
+    p[1, :, 8:16] = 0x8000
+    p[:, :, 16:24] = 0x8000                                 # -0 + -0
+    p[0, :, 24:32], p[1, :, 24:32] = 0x0001, 0x0002        # subnormal sums
+    p[0, :, 32:40], p[1, :, 32:40] = 0x3F80, 0x3B80        # 1 + 2^-8: BF16 tie
+    p[0, :, 40:48], p[1, :, 40:48] = 0x3F81, 0x3B80        # 1+2^-7 + 2^-8: tie to even up
+    p[0, :, 48:56] = 0x4000
+    p[1, :, 48:56] = 0xC000                                 # cancellation
+    b.residual[:, :, 60:64] = 0x0003                        # subnormal residuals
+    check_boundary(b)
+
+
+def test_mxfp8_epilogue_with_padding_rows():
+    for M in (100, 128, 129, 256):
+        b = synth.boundary(4, M, 5120, 8, 0.5, f"mxfp8-M{M}")
+        check_boundary(b, mxfp8=True)
+
+
+def test_standalone_quant_matches_oracle():
+    for M, H in ((1, 128), (3, 512), (130, 5120)):
+        x = synth.bf16_matrix(M, H, 2.0)
+        x[0, :32] = 0                                        # zero block
+        values, scales = mhc.quant_mxfp8(dev(x))
+        torch.cuda.synchronize()
+        v_ref, s_ref = oracle.quant_mxfp8(x)
+        assert_bits_equal(host(values), v_ref, "values")
+        assert_bits_equal(host(scales), s_ref, "scales")
+
+
+def test_large_m_sampled_tokens():
+    """M = 8192 (H=5120, tp=8) with the MXFP8 epilogue in the benchmark's
+    launch configuration: sampled tokens against the oracle run on just
+    those tokens (tokens are independent), MXFP8 scales read at their
+    swizzled offsets."""
+    b = synth.large_m_delayed(8192)
+    ro, li, (vals, scales) = run_boundary(b, mxfp8=True)
+    rng = np.random.default_rng(0)
+    toks = np.sort(rng.choice(8192, 48, replace=False))
+    toks[0], toks[-1] = 0, 8191
+    ro_ref, li_ref, (v_ref, s_ref) = oracle.boundary(
+        b.partials[:, toks], b.residual[toks], b.post[toks], b.comb[toks], b.pre[toks], b.gamma,
+        b.norm_eps, mxfp8=True, threads=8)
+    assert_bits_equal(ro[toks], ro_ref, "residual_out (sampled)")
+    assert_within_ulp(li[toks], li_ref, 1, "layer_input (sampled)")
+    v_q, _ = oracle.quant_mxfp8(li[toks])
+    assert_bits_equal(vals[toks], v_q, "mxfp8 values (sampled)")
+    K = 5120 // 32
+    for i, t in enumerate(toks):
+        got = np.array([scales[oracle.sf_index(int(t), k, K)] for k in range(K)])
+        want = np.array([s_ref[oracle.sf_index(i, k, K)] for k in range(K)])
+        if i < 128:  # the sampled run's own rows are < 128
+            assert_bits_equal(got, want, f"scales of token {t}")
+
+
+def test_cross_token_independence_and_determinism():
+    b = synth.dsv41_delayed(128)
+    ro1, li1, _ = run_boundary(b)
+    ro2, li2, _ = run_boundary(b)
+    assert_bits_equal(ro1, ro2, "run-to-run residual_out")
+    assert_bits_equal(li1, li2, "run-to-run layer_input")
+    s = synth.dsv41_delayed(128)
+    s.M = 8
+    s.partials, s.residual, s.post, s.comb, s.pre = (b.partials[:, :8], b.residual[:8], b.post[:8],
+                                                    b.comb[:8], b.pre[:8])
+    ro3, li3, _ = run_boundary(s)
+    assert_bits_equal(ro3, ro1[:8], "prefix residual_out")
+    assert_bits_equal(li3, li1[:8], "prefix layer_input")
+
+
+# ---------------------------------------------------------------------------
+# MoE finalize and the two-shot emulation
+# ---------------------------------------------------------------------------
+
+def run_finalize(f, two_shot=False, mxfp8=False):
+    out = mhc.finalize(dev(f.gemm2), dev(f.weights), dev(f.idx), dev(f.shared), dev(f.residual),
+                       dev(f.post), dev(f.comb), dev(f.pre), dev(f.gamma), f.norm_eps,
+                       two_shot=two_shot, mxfp8=mxfp8)
+    torch.cuda.synchronize()
+    ro, li, mx = out
+    return u16(ro), u16(li), ((host(mx[0]), host(mx[1])) if mx else None)
+
+
+@pytest.mark.parametrize("M", [64, 512])
+def test_moe_finalize_matches_oracle_and_two_shot(M):
+    f = synth.moe_finalize(M)
+    print(f"[gpu] {f.name}", flush=True)
+    ro, li, mx = run_finalize(f, mxfp8=True)
+    ro_ref, li_ref, _ = oracle.finalize(f.gemm2, f.weights, f.idx, f.shared, f.residual, f.post,
+                                        f.comb, f.pre, f.gamma, f.norm_eps, threads=8)
+    assert_bits_equal(ro, ro_ref, "residual_out")
+    assert_within_ulp(li, li_ref, 1, "layer_input")
+    ro2, li2, mx2 = run_finalize(f, two_shot=True, mxfp8=True)
+    assert_bits_equal(ro2, ro, "two-shot residual_out")
+    assert_bits_equal(li2, li, "two-shot layer_input")
+    assert_bits_equal(mx2[0], mx[0], "two-shot mxfp8 values")
+    assert_bits_equal(mx2[1], mx[1], "two-shot mxfp8 scales")
+
+
+def test_moe_finalize_per_rank_routing_with_dropped_experts():
+    f = synth.moe_finalize(37, H=1024, tp=4, top_k=8, replicated_routing=False, drop_fraction=0.15)
+    ro, li, _ = run_finalize(f)
+    ro_ref, li_ref, _ = oracle.finalize(f.gemm2, f.weights, f.idx, f.shared, f.residual, f.post,
+                                        f.comb, f.pre, f.gamma, f.norm_eps,
+                                        replicated_routing=False, threads=8)
+    assert_bits_equal(ro, ro_ref, "residual_out")
+    assert_within_ulp(li, li_ref, 1, "layer_input")
+    ro2, li2, _ = run_finalize(f, two_shot=True)
+    assert_bits_equal(ro2, ro, "two-shot residual_out")
+    assert_bits_equal(li2, li, "two-shot layer_input")
+
+
+def test_moe_finalize_large_m_sampled():
+    """M = 4096 (H=5120, tp=4, top_k=8): sampled tokens; two-shot equal."""
+    f = synth.moe_finalize(4096)
+    ro, li, _ = run_finalize(f)
+    ro2, li2, _ = run_finalize(f, two_shot=True)
+    assert_bits_equal(ro2, ro, "two-shot residual_out")
+    assert_bits_equal(li2, li, "two-shot layer_input")
+    toks = np.sort(np.random.default_rng(1).choice(4096, 24, replace=False))
+    contrib = oracle.finalize_contributions(f.gemm2, f.weights[toks], f.idx[toks], f.shared[:, toks],
+                                            threads=8)
+    ro_ref, li_ref, _ = oracle.boundary(contrib, f.residual[toks], f.post[toks], f.comb[toks],
+                                        f.pre[toks], f.gamma, f.norm_eps, threads=8)
+    assert_bits_equal(ro[toks], ro_ref, "residual_out (sampled)")
+    assert_within_ulp(li[toks], li_ref, 1, "layer_input (sampled)")
+
+
+# ---------------------------------------------------------------------------
+# GLM boundary and side mixes
+# ---------------------------------------------------------------------------
+
+def run_glm(g, G):
+    ro, mixes, li = mhc.boundary_glm(dev(g.partials), dev(g.residual), dev(g.post), dev(g.comb),
+                                     dev(g.fn), dev(g.scale), dev(g.base), dev(g.gamma), g.rms_eps,
+                                     g.hc_eps, g.norm_eps, tokens_per_wg=G)
+    torch.cuda.synchronize()
+    return u16(ro), host(mixes), u16(li)
+
+
+@pytest.mark.parametrize("M", [1, 16, 64, 7])
+def test_glm_boundary_matches_oracle(M):
+    g = synth.glm(M)
+    print(f"[gpu] {g.name}", flush=True)
+    ro_ref, mix_ref, li_ref, pre_ref = oracle.boundary_glm(
+        g.partials, g.residual, g.post, g.comb, g.fn, g.scale, g.base, g.gamma, g.rms_eps,
+        g.hc_eps, g.norm_eps, threads=8)
+    first = None
+    for G in (1, 2, 4):
+        ro, mixes, li = run_glm(g, G)
+        assert_bits_equal(ro, ro_ref, f"residual_out G={G}")
+        err = np.abs(mixes - mix_ref)
+        assert (err <= 1e-5 * (np.abs(mix_ref) + 1)).all(), f"mixes G={G}: max err {err.max()}"
+        pre_got = glm_pre(mixes, g.scale, g.base, g.hc_eps)
+        one, two = glm_layer_input_check(li, li_ref, ro_ref, pre_ref.astype(np.float64), pre_got)
+        print(f"[gpu]   G={G}: layer_input 1-ulp {one}, tie 2-ulp {two}", flush=True)
+        if first is None:
+            first = (ro, mixes, li)
+        else:   # outputs do not depend on the tokens per workgroup
+            assert_bits_equal(ro, first[0], f"G={G} residual_out vs G=1")
+            assert np.array_equal(mixes, first[1]), f"G={G} mixes vs G=1"
+            assert_bits_equal(li, first[2], f"G={G} layer_input vs G=1")
+
+
+def test_glm_large_m_sampled():
+    """M = 512 (H=6144, tp=8), the auto tokens-per-workgroup choice."""
+    g = synth.glm(512)
+    ro, mixes, li = run_glm(g, 0)
+    toks = np.array([0, 1, 63, 64, 200, 255, 256, 300, 510, 511])
+    ro_ref, mix_ref, li_ref, pre_ref = oracle.boundary_glm(
+        g.partials[:, toks], g.residual[toks], g.post[toks], g.comb[toks], g.fn, g.scale, g.base,
+        g.gamma, g.rms_eps, g.hc_eps, g.norm_eps, threads=8)
+    assert_bits_equal(ro[toks], ro_ref, "residual_out (sampled)")
+    err = np.abs(mixes[toks] - mix_ref)
+    assert (err <= 1e-5 * (np.abs(mix_ref) + 1)).all()
+    glm_layer_input_check(li[toks], li_ref, ro_ref, pre_ref.astype(np.float64),
+                          glm_pre(mixes[toks], g.scale, g.base, g.hc_eps))
+
+
+@pytest.mark.parametrize("M", [1, 64, 513])
+def test_side_mixes_match_oracle(M):
+    raw, scale, base = synth.raw_mixes(M)
+    post, comb = mhc.mixes(dev(raw), dev(scale), dev(base), 1e-6, 2.0, 20)
+    torch.cuda.synchronize()
+    p_ref, c_ref = oracle.side_mixes(raw, scale, base, 1e-6, 2.0, 20)
+    post, comb = host(post).reshape(M, 4), host(comb)
+    assert (np.abs(post - p_ref) <= 1e-5 * np.abs(p_ref) + 1e-7).all()
+    assert (np.abs(comb - c_ref) <= 1e-5 * np.abs(c_ref) + 1e-7).all()
+    print(f"[gpu] side mixes M={M}: bit-exact post {np.array_equal(post, p_ref)}, "
+          f"comb {np.array_equal(comb, c_ref)}", flush=True)
+
+
+def test_glm_boundary_object_side_stream_and_join():
+    g = synth.glm(16)
+    gb = mhc.GlmBoundary(rms_eps=g.rms_eps, hc_eps=g.hc_eps, post_mult=g.post_mult,
+                         sinkhorn_repeat=g.sinkhorn_repeat, norm_eps=g.norm_eps, device="cuda")
+    for _ in range(3):
+        ro, post_n, comb_n, li, raw = gb(dev(g.partials), dev(g.residual), dev(g.post),
+                                         dev(g.comb), dev(g.fn), dev(g.scale), dev(g.base),
+                                         dev(g.gamma))
+        gb.join()
+        torch.cuda.synchronize()
+        p_ref, c_ref = oracle.side_mixes(host(raw), g.scale, g.base, g.hc_eps, g.post_mult,
+                                         g.sinkhorn_repeat)
+        assert (np.abs(host(post_n).reshape(-1, 4) - p_ref) <= 1e-5 * np.abs(p_ref) + 1e-7).all()
+        assert (np.abs(host(comb_n) - c_ref) <= 1e-5 * np.abs(c_ref) + 1e-7).all()
+
+
+# ---------------------------------------------------------------------------
+# Mailbox stand-in
+# ---------------------------------------------------------------------------
+
+def test_mailbox_generations_cycle_and_match_direct():
+    from oracle.mailbox_model import MailboxModel
+    cap, H, tp = 64, 1024, 4
+    mb = mhc.Mailbox(tp, cap, H, "cuda")
+    mb.init()
+    model = MailboxModel(tp, cap, H)
+    for call, M in enumerate((5, 64, 17, 1, 33)):
+        b = synth.boundary(20 + call, M, H, tp, 0.5, f"mailbox-call{call}")
+        b.partials[0, 0, :8] = 0x8000                       # a -0 payload must not stall
+        print(f"[gpu] mailbox call {call} M={M}", flush=True)
+        mb.publish(dev(b.partials))
+        ro, li, _ = mb.boundary(M, dev(b.residual), dev(b.post), dev(b.comb), dev(b.pre),
+                                dev(b.gamma), b.norm_eps)
+        torch.cuda.synchronize()
+        model.publish(b.partials)
+        model.consume(M)
+        assert mb.status_ok()
+        assert_bits_equal(u16(mb.slots), model.slots, "mailbox slots after consume")
+        assert np.array_equal(host(mb.stage_state), model.stage), "stage_state"
+        ro_ref, li_ref, _ = oracle.boundary(b.partials, b.residual, b.post, b.comb, b.pre, b.gamma,
+                                            b.norm_eps)
+        assert_bits_equal(u16(ro), ro_ref, "residual_out")
+        assert_within_ulp(u16(li), li_ref, 1, "layer_input")
+
+
+def test_mailbox_large_m_with_mxfp8():
+    """Mailbox-fed boundary at M = 8192 with the MXFP8 epilogue, three calls
+    cycling the generations; equal to the direct path."""
+    b = synth.large_m_delayed(8192)
+    mb = mhc.Mailbox(8, 8192, 5120, "cuda")
+    mb.init()
+    ro_d, li_d, mx_d = run_boundary(b, mxfp8=True)
+    parts, res, post, comb, pre, gam = (dev(b.partials), dev(b.residual), dev(b.post),
+                                        dev(b.comb), dev(b.pre), dev(b.gamma))
+    for call in range(3):
+        mb.publish(parts)
+        ro, li, mx = mb.boundary(8192, res, post, comb, pre, gam, b.norm_eps, mxfp8=True)
+        torch.cuda.synchronize()
+        assert mb.status_ok()
+        assert host(mb.stage_state).tolist() == [call, (call + 1) % 3]
+        assert_bits_equal(u16(ro), ro_d, "mailbox residual_out")
+        assert_bits_equal(u16(li), li_d, "mailbox layer_input")
+        assert_bits_equal(host(mx[0]), mx_d[0], "mailbox mxfp8 values")
+        assert_bits_equal(host(mx[1]), mx_d[1], "mailbox mxfp8 scales")
+    assert (u16(mb.slots) == 0x8000).all()
+
+
+def test_mailbox_poll_gives_up_with_a_bounded_spin():
+    """A consumer whose producer never publishes: a tiny spin limit makes
+    every poll give up (all kernels exit normally) and the status reports
+    ETIMEOUT."""
+    mb = mhc.Mailbox(2, 4, 256, "cuda", spin_limit=4)
+    mb.init()
+    b = synth.boundary(30, 2, 256, 2, 0.5)
+    mb.boundary(2, dev(b.residual), dev(b.post), dev(b.comb), dev(b.pre), dev(b.gamma), 1e-6)
+    with pytest.raises(mhc.MhcbError) as e:
+        mb.status_ok()
+    assert e.value.code == mhc.MHCB_ETIMEOUT
+
+
+# ---------------------------------------------------------------------------
+# Errors leave state untouched
+# ---------------------------------------------------------------------------
+
+def test_bad_arguments_leave_mailbox_untouched():
+    mb = mhc.Mailbox(2, 8, 256, "cuda")
+    mb.init()
+    b = synth.boundary(31, 4, 256, 2, 0.5)
+    mb.publish(dev(b.partials))
+    torch.cuda.synchronize()
+    before_slots, before_stage = u16(mb.slots).copy(), host(mb.stage_state).copy()
+    with pytest.raises(mhc.MhcbError):
+        mb.boundary(9, dev(np.zeros((9, 4, 256), np.uint16)), dev(np.zeros((9, 4), np.float32)),
+                    dev(np.zeros((9, 4, 4), np.float32)), dev(np.zeros((9, 4), np.float32)),
+                    dev(b.gamma), 1e-6)                     # M > capacity
+    with pytest.raises(mhc.MhcbError):
+        mb.boundary(4, dev(b.residual), dev(b.post), dev(b.comb), dev(b.pre), None, 1e-6)
+    torch.cuda.synchronize()
+    assert_bits_equal(u16(mb.slots), before_slots, "slots")
+    assert np.array_equal(host(mb.stage_state), before_stage)

@@ -1,0 +1,320 @@
+// The C ABI of libmhcb: argument validation (before any launch or state
+// write, as AllReduceMHC._consumer on the DSV4.1 page requires) and dispatch
+// to the gfx950 kernels.  Host code only.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/mhcb.h"
+#include "device.h"
+#include "kernels.h"
+
+using namespace mhcb;
+
+namespace {
+
+thread_local char g_error[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_error, sizeof g_error, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_error[0] = '\0';
+  return MHCB_OK;
+}
+
+int launched(hipError_t e, const char *what) {
+  if (e != hipSuccess) return fail(MHCB_ELAUNCH, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+constexpr int kMaxHidden = 16384;
+constexpr int kMaxHiddenGlm = 8192;
+constexpr int kMaxTp = 64;
+constexpr int kMaxRoutes = 1024;
+constexpr int64_t kDefaultSpin = 1 << 20;
+
+// Checks shared by the boundary variants ([DSV41] AllReduceMHC._check and
+// _consumer, _LamportMHCDeviceKernel.__init__).
+int check_common(const char *fn, const uint16_t *residual, const float *post, const float *comb,
+                 const float *pre, const uint16_t *norm_weight, const uint16_t *residual_out,
+                 const uint16_t *layer_input, const uint8_t *mx_values, const uint8_t *mx_scales,
+                 int M, int H, int hc, int tp) {
+  if (M < 1) return fail(MHCB_EINVAL, "%s: M=%d is outside [1, capacity]", fn, M);
+  if (hc != kStreams) return fail(MHCB_EUNSUPPORTED, "%s: hc_mult=%d (only 4)", fn, hc);
+  if (H <= 0 || H % kFrag) return fail(MHCB_EUNSUPPORTED, "%s: hidden_size=%d must be a positive multiple of 8", fn, H);
+  if (H > kMaxHidden) return fail(MHCB_EUNSUPPORTED, "%s: hidden_size=%d exceeds %d", fn, H, kMaxHidden);
+  if (tp < 1 || tp > kMaxTp) return fail(MHCB_EINVAL, "%s: tp=%d is outside [1, %d]", fn, tp, kMaxTp);
+  if (!residual || !post || !comb || !residual_out)
+    return fail(MHCB_EINVAL, "%s: residual, post, comb and residual_out are required", fn);
+  if ((pre == nullptr) != (norm_weight == nullptr))
+    return fail(MHCB_EINVAL, "%s: pre and norm_weight are both given or both NULL", fn);
+  if ((pre == nullptr) != (layer_input == nullptr))
+    return fail(MHCB_EINVAL, "%s: layer_input is required exactly when pre is given", fn);
+  if ((mx_values == nullptr) != (mx_scales == nullptr))
+    return fail(MHCB_EINVAL, "%s: mxfp8_values and mxfp8_scales are both given or both NULL", fn);
+  if (mx_values && !pre) return fail(MHCB_EINVAL, "%s: a residual-only boundary has no layer input", fn);
+  if (mx_values && H % 128)
+    return fail(MHCB_EUNSUPPORTED, "%s: MXFP8 output needs hidden_size %% 128 == 0 (got %d)", fn, H);
+  if (!aligned(residual, 16) || !aligned(residual_out, 16) || (norm_weight && !aligned(norm_weight, 16)) ||
+      (layer_input && !aligned(layer_input, 16)) || (mx_values && !aligned(mx_values, 8)) ||
+      (mx_scales && !aligned(mx_scales, 4)) || !aligned(post, 4) || !aligned(comb, 4) ||
+      (pre && !aligned(pre, 4)))
+    return fail(MHCB_EALIGN, "%s: BF16 tensors must be 16-byte aligned, FP32 4-byte", fn);
+  return MHCB_OK;
+}
+
+int check_mailbox(const char *fn, const mhcb_mailbox *mb, int H, int tp, int M) {
+  if (!mb->slots || !mb->stage_state || !mb->status)
+    return fail(MHCB_EINVAL, "%s: mailbox slots, stage_state and status are required", fn);
+  if (mb->generations != 3) return fail(MHCB_EINVAL, "%s: mailbox generations=%d (must be 3)", fn, mb->generations);
+  if (mb->tp != tp) return fail(MHCB_EINVAL, "%s: mailbox tp=%d but tp=%d", fn, mb->tp, tp);
+  if (mb->hidden_size != H) return fail(MHCB_EINVAL, "%s: mailbox hidden_size=%d but hidden_size=%d", fn, mb->hidden_size, H);
+  if (mb->capacity < 1) return fail(MHCB_EINVAL, "%s: mailbox capacity=%d", fn, mb->capacity);
+  if (M > mb->capacity) return fail(MHCB_EINVAL, "%s: M=%d is outside [1, %d]", fn, M, mb->capacity);
+  if (!aligned(mb->slots, 16) || !aligned(mb->stage_state, 4) || !aligned(mb->status, 4))
+    return fail(MHCB_EALIGN, "%s: mailbox slots must be 16-byte aligned", fn);
+  return MHCB_OK;
+}
+
+MailboxView view_of(const mhcb_mailbox *mb) {
+  MailboxView v;
+  v.slots = mb->slots;
+  v.stage_state = mb->stage_state;
+  v.status = mb->status;
+  v.capacity = mb->capacity;
+  v.spin_limit = mb->spin_limit > 0 ? mb->spin_limit : kDefaultSpin;
+  return v;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *mhcb_last_error(void) { return g_error; }
+
+const char *mhcb_version(void) { return "0.1.0"; }
+
+int64_t mhcb_mxfp8_scale_bytes(int64_t M, int64_t hidden_size) {
+  if (M < 0 || hidden_size < 0) return -1;
+  return (M + 127) / 128 * 128 * (hidden_size / 32);
+}
+
+int64_t mhcb_finalize_workspace_bytes(int M, int hidden_size, int tp, int two_shot) {
+  if (M < 0 || hidden_size < 0 || tp < 1) return -1;
+  if (!two_shot) return 0;
+  const int64_t slots = ((int64_t)M + tp - 1) / tp;
+  return ((int64_t)tp * tp * slots + M) * hidden_size * 2;
+}
+
+int mhcb_boundary(const uint16_t *partials, int64_t rank_stride, const mhcb_mailbox *mailbox,
+                  const uint16_t *residual, const float *post, const float *comb, const float *pre,
+                  const uint16_t *norm_weight, uint16_t *residual_out, uint16_t *layer_input,
+                  uint8_t *mxfp8_values, uint8_t *mxfp8_scales, int M, int hidden_size, int hc_mult,
+                  int tp, float norm_eps, hipStream_t stream) {
+  const char *fn = "mhcb_boundary";
+  int rc = check_common(fn, residual, post, comb, pre, norm_weight, residual_out, layer_input,
+                        mxfp8_values, mxfp8_scales, M, hidden_size, hc_mult, tp);
+  if (rc) return rc;
+  if ((partials == nullptr) == (mailbox == nullptr))
+    return fail(MHCB_EINVAL, "%s: give exactly one of partials and mailbox", fn);
+  BoundaryArgs a = {};
+  if (mailbox) {
+    if ((rc = check_mailbox(fn, mailbox, hidden_size, tp, M))) return rc;
+    a.source = Source::kMailbox;
+    a.mailbox = view_of(mailbox);
+  } else {
+    if (tp > 1 && (rank_stride < (int64_t)M * hidden_size && rank_stride != 0))
+      return fail(MHCB_EINVAL, "%s: rank_stride=%lld overlaps a rank's [M, hidden] block", fn,
+                  (long long)rank_stride);
+    if (!aligned(partials, 16) || rank_stride % kFrag)
+      return fail(MHCB_EALIGN, "%s: partials must be 16-byte aligned with rank_stride %% 8 == 0", fn);
+    a.source = Source::kPartials;
+    a.partials = partials;
+    a.rank_stride = rank_stride;
+  }
+  a.tp = tp;
+  a.residual = residual;
+  a.post = post;
+  a.comb = comb;
+  a.pre = pre;
+  a.gamma = norm_weight;
+  a.residual_out = residual_out;
+  a.layer_input = layer_input;
+  a.mx_values = mxfp8_values;
+  a.mx_scales = mxfp8_scales;
+  a.M = M;
+  a.H = hidden_size;
+  a.norm_eps = norm_eps;
+  return launched(launch_boundary(a, stream), fn);
+}
+
+int mhcb_boundary_glm(const uint16_t *partials, int64_t rank_stride, const uint16_t *residual,
+                      const float *post, const float *comb, const uint16_t *hc_fn, const float *scale,
+                      const float *base, const uint16_t *norm_weight, uint16_t *residual_out,
+                      float *mixes_out, uint16_t *layer_input, int M, int hidden_size, int hc_mult,
+                      int tp, float rms_eps, float hc_eps, float norm_eps, int tokens_per_wg,
+                      hipStream_t stream) {
+  const char *fn = "mhcb_boundary_glm";
+  if (!partials || !hc_fn || !scale || !base || !norm_weight || !mixes_out || !layer_input)
+    return fail(MHCB_EINVAL, "%s: partials, hc_fn, scale, base, norm_weight, mixes_out and layer_input are required", fn);
+  // The GLM pre-mix is derived in-kernel from scale/base: check the normalized path.
+  int rc = check_common(fn, residual, post, comb, scale, norm_weight, residual_out, layer_input,
+                        nullptr, nullptr, M, hidden_size, hc_mult, tp);
+  if (rc) return rc;
+  if (hidden_size > kMaxHiddenGlm)
+    return fail(MHCB_EUNSUPPORTED, "%s: hidden_size=%d exceeds %d", fn, hidden_size, kMaxHiddenGlm);
+  if (tp > 1 && rank_stride < (int64_t)M * hidden_size && rank_stride != 0)
+    return fail(MHCB_EINVAL, "%s: rank_stride=%lld overlaps a rank's [M, hidden] block", fn, (long long)rank_stride);
+  if (!aligned(partials, 16) || rank_stride % kFrag || !aligned(hc_fn, 16) || !aligned(base, 4) ||
+      !aligned(mixes_out, 4))
+    return fail(MHCB_EALIGN, "%s: partials/hc_fn must be 16-byte aligned, rank_stride %% 8 == 0", fn);
+  int G = tokens_per_wg;
+  if (G == 0) G = M <= 64 ? 1 : (M <= 256 || hidden_size > 6144 ? 2 : 4);
+  if (G != 1 && G != 2 && G != 4)
+    return fail(MHCB_EINVAL, "%s: tokens_per_wg=%d (0, 1, 2 or 4)", fn, tokens_per_wg);
+  if (G == 4 && hidden_size > 6144)
+    return fail(MHCB_EUNSUPPORTED, "%s: tokens_per_wg=4 needs hidden_size <= 6144", fn);
+  GlmArgs a = {partials, rank_stride, tp, residual, post, comb, hc_fn, scale, base, norm_weight,
+               residual_out, mixes_out, layer_input, M, hidden_size, rms_eps, hc_eps, norm_eps, G};
+  return launched(launch_boundary_glm(a, stream), fn);
+}
+
+int mhcb_mixes(const float *mixes, const float *scale, const float *base, float *post_out,
+               float *comb_out, int M, int hc_mult, float hc_eps, float post_mult,
+               int sinkhorn_repeat, hipStream_t stream) {
+  const char *fn = "mhcb_mixes";
+  if (M < 1) return fail(MHCB_EINVAL, "%s: M=%d < 1", fn, M);
+  if (hc_mult != kStreams) return fail(MHCB_EUNSUPPORTED, "%s: hc_mult=%d (only 4)", fn, hc_mult);
+  if (sinkhorn_repeat < 0) return fail(MHCB_EINVAL, "%s: sinkhorn_repeat=%d < 0", fn, sinkhorn_repeat);
+  if (!mixes || !scale || !base || !post_out || !comb_out)
+    return fail(MHCB_EINVAL, "%s: every pointer is required", fn);
+  if (!aligned(mixes, 4) || !aligned(scale, 4) || !aligned(base, 4) || !aligned(post_out, 4) ||
+      !aligned(comb_out, 4))
+    return fail(MHCB_EALIGN, "%s: FP32 tensors must be 4-byte aligned", fn);
+  return launched(launch_mixes(mixes, scale, base, post_out, comb_out, M, hc_eps, post_mult,
+                               sinkhorn_repeat, stream), fn);
+}
+
+int mhcb_finalize(const uint16_t *gemm2_permuted, int64_t gemm2_rank_stride, int64_t rows,
+                  const float *expert_weights, int64_t weights_rank_stride,
+                  const int32_t *permuted_idx, int64_t idx_rank_stride,
+                  const uint16_t *shared_output, int64_t shared_rank_stride,
+                  const uint16_t *residual, const float *post, const float *comb, const float *pre,
+                  const uint16_t *norm_weight, uint16_t *residual_out, uint16_t *layer_input,
+                  uint8_t *mxfp8_values, uint8_t *mxfp8_scales, int two_shot, void *workspace,
+                  int64_t workspace_bytes, int M, int hidden_size, int hc_mult, int tp, int top_k,
+                  float norm_eps, hipStream_t stream) {
+  const char *fn = "mhcb_finalize";
+  int rc = check_common(fn, residual, post, comb, pre, norm_weight, residual_out, layer_input,
+                        mxfp8_values, mxfp8_scales, M, hidden_size, hc_mult, tp);
+  if (rc) return rc;
+  if (top_k < 1) return fail(MHCB_EINVAL, "%s: top_k=%d < 1", fn, top_k);
+  if ((int64_t)tp * top_k > kMaxRoutes)
+    return fail(MHCB_EINVAL, "%s: tp * top_k = %d exceeds %d", fn, tp * top_k, kMaxRoutes);
+  if (rows < 0) return fail(MHCB_EINVAL, "%s: rows=%lld < 0", fn, (long long)rows);
+  if (!gemm2_permuted || !expert_weights || !permuted_idx || !shared_output)
+    return fail(MHCB_EINVAL, "%s: gemm2_permuted, expert_weights, permuted_idx and shared_output are required", fn);
+  if (gemm2_rank_stride < 0 || weights_rank_stride < 0 || idx_rank_stride < 0 || shared_rank_stride < 0)
+    return fail(MHCB_EINVAL, "%s: negative rank stride", fn);
+  if (!aligned(gemm2_permuted, 16) || !aligned(shared_output, 16) || gemm2_rank_stride % kFrag ||
+      shared_rank_stride % kFrag || !aligned(expert_weights, 4) || !aligned(permuted_idx, 4))
+    return fail(MHCB_EALIGN, "%s: BF16 inputs must be 16-byte aligned with rank strides %% 8 == 0", fn);
+  FinalizeView f = {gemm2_permuted, gemm2_rank_stride, rows, expert_weights, weights_rank_stride,
+                    permuted_idx, idx_rank_stride, shared_output, shared_rank_stride, top_k};
+  BoundaryArgs a = {};
+  a.tp = tp;
+  a.residual = residual;
+  a.post = post;
+  a.comb = comb;
+  a.pre = pre;
+  a.gamma = norm_weight;
+  a.residual_out = residual_out;
+  a.layer_input = layer_input;
+  a.mx_values = mxfp8_values;
+  a.mx_scales = mxfp8_scales;
+  a.M = M;
+  a.H = hidden_size;
+  a.norm_eps = norm_eps;
+  if (!two_shot) {
+    a.source = Source::kFinalize;
+    a.fin = f;
+    return launched(launch_boundary(a, stream), fn);
+  }
+  const int64_t need = mhcb_finalize_workspace_bytes(M, hidden_size, tp, 1);
+  if (!workspace || workspace_bytes < need)
+    return fail(MHCB_EINVAL, "%s: the two-shot emulation needs a %lld-byte workspace", fn, (long long)need);
+  if (!aligned(workspace, 16)) return fail(MHCB_EALIGN, "%s: workspace must be 16-byte aligned", fn);
+  uint16_t *own = static_cast<uint16_t *>(workspace);
+  const int64_t slots = ((int64_t)M + tp - 1) / tp;
+  uint16_t *reduced = own + (int64_t)tp * tp * slots * hidden_size;
+  hipError_t e = launch_finalize_to_owners(f, tp, M, hidden_size, own, stream);
+  if (e == hipSuccess) e = launch_owner_reduce(own, tp, M, hidden_size, reduced, stream);
+  if (e != hipSuccess) return launched(e, fn);
+  a.source = Source::kPartials;
+  a.partials = reduced;
+  a.rank_stride = 0;
+  a.tp = 1;
+  return launched(launch_boundary(a, stream), fn);
+}
+
+int mhcb_quant_mxfp8(const uint16_t *x, uint8_t *values, uint8_t *scales, int M, int hidden_size,
+                     hipStream_t stream) {
+  const char *fn = "mhcb_quant_mxfp8";
+  if (M < 1) return fail(MHCB_EINVAL, "%s: M=%d < 1", fn, M);
+  if (hidden_size <= 0 || hidden_size % 128 || hidden_size > kMaxHidden)
+    return fail(MHCB_EUNSUPPORTED, "%s: hidden_size=%d must be a positive multiple of 128 up to %d", fn, hidden_size, kMaxHidden);
+  if (!x || !values || !scales) return fail(MHCB_EINVAL, "%s: every pointer is required", fn);
+  if (!aligned(x, 16) || !aligned(values, 8) || !aligned(scales, 4))
+    return fail(MHCB_EALIGN, "%s: x must be 16-byte aligned", fn);
+  return launched(launch_quant_mxfp8(x, values, scales, M, hidden_size, stream), fn);
+}
+
+int mhcb_mailbox_init(const mhcb_mailbox *mailbox, hipStream_t stream) {
+  const char *fn = "mhcb_mailbox_init";
+  if (!mailbox) return fail(MHCB_EINVAL, "%s: mailbox is required", fn);
+  if (mailbox->tp < 1 || mailbox->tp > kMaxTp) return fail(MHCB_EINVAL, "%s: tp=%d", fn, mailbox->tp);
+  const int H = mailbox->hidden_size;
+  if (H <= 0 || H % kFrag) return fail(MHCB_EUNSUPPORTED, "%s: hidden_size=%d", fn, H);
+  int rc = check_mailbox(fn, mailbox, H, mailbox->tp, 1);
+  if (rc) return rc;
+  return launched(launch_mailbox_init(view_of(mailbox), mailbox->tp, H, stream), fn);
+}
+
+int mhcb_publish(const mhcb_mailbox *mailbox, const uint16_t *partials, int64_t rank_stride,
+                 int rank_begin, int rank_count, int M, hipStream_t stream) {
+  const char *fn = "mhcb_publish";
+  if (!mailbox || !partials) return fail(MHCB_EINVAL, "%s: mailbox and partials are required", fn);
+  const int H = mailbox->hidden_size;
+  if (H <= 0 || H % kFrag) return fail(MHCB_EUNSUPPORTED, "%s: hidden_size=%d", fn, H);
+  if (M < 1) return fail(MHCB_EINVAL, "%s: M=%d < 1", fn, M);
+  int rc = check_mailbox(fn, mailbox, H, mailbox->tp, M);
+  if (rc) return rc;
+  if (rank_begin < 0 || rank_count < 1 || rank_begin + rank_count > mailbox->tp)
+    return fail(MHCB_EINVAL, "%s: ranks [%d, %d) outside [0, %d)", fn, rank_begin, rank_begin + rank_count, mailbox->tp);
+  if (rank_count > 1 && rank_stride < (int64_t)M * H)
+    return fail(MHCB_EINVAL, "%s: rank_stride=%lld overlaps a rank's [M, hidden] block", fn, (long long)rank_stride);
+  if (!aligned(partials, 16) || rank_stride % kFrag)
+    return fail(MHCB_EALIGN, "%s: partials must be 16-byte aligned with rank_stride %% 8 == 0", fn);
+  return launched(launch_publish(view_of(mailbox), mailbox->tp, H, partials, rank_stride, rank_begin,
+                                 rank_count, M, stream), fn);
+}
+
+int mhcb_mailbox_status(const mhcb_mailbox *mailbox, hipStream_t stream) {
+  const char *fn = "mhcb_mailbox_status";
+  if (!mailbox || !mailbox->status) return fail(MHCB_EINVAL, "%s: mailbox status word is required", fn);
+  hipError_t e = hipStreamSynchronize(stream);
+  int32_t status = 0;
+  if (e == hipSuccess) e = hipMemcpy(&status, mailbox->status, sizeof status, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(MHCB_ELAUNCH, "%s: %s", fn, hipGetErrorString(e));
+  if (status != 0) return fail(MHCB_ETIMEOUT, "%s: %d mailbox poll(s) gave up", fn, status);
+  return ok();
+}
+
+}  // extern "C"

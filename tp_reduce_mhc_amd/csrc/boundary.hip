@@ -1,0 +1,537 @@
+// Per-token sublayer-boundary kernels for gfx950: TP partial sum, mHC
+// post-mix, pre-mix collapse, RMSNorm and the optional MXFP8 epilogue, fed
+// from resident partials, from a Lamport mailbox, or from an unfinalized MoE
+// output.  Also the mailbox producer / initializer, the two-shot owner
+// reduce and the standalone MXFP8 quantizer.
+//
+// Arithmetic follows the pages
+//   vllm.models.deepseek_v41.nvidia.ops.cute_dsl.all_reduce_mhc
+//     (_LamportMHCDeviceKernel.kernel, _QuadFinalizePublishDeviceKernel.kernel,
+//      _OwnerReduceMulticastDeviceKernel.kernel, _SharedOnlyPublishDeviceKernel.kernel)
+//   vllm.models.glm5next.nvidia.specialized_decode.all_reduce_mhc
+//     (AllReduceMhcBoundary.__init__, _PublishDeviceKernel.kernel)
+// step for step: the rank sum starts at 0 and adds ranks in order; the
+// post-mix is x*post_j followed by four FMAs over the source streams; the
+// collapse is an FMA chain from 0 over the targets; RMSNorm multiplies
+// (p * inv) * gamma.  The design is gfx950's own: one workgroup per token,
+// 16-byte coalesced loads of consecutive fragments per lane, wave64
+// butterflies plus an LDS step for the sum of squares (no clusters), every
+// load of a token issued before its first use.
+#include "device.h"
+#include "kernels.h"
+
+namespace mhcb {
+
+// Fragments of a token split over at most kTokenThreads threads: 1, 2 or 4
+// fragments per thread (hidden <= 16384).
+Geometry token_geometry(int H) {
+  const int F = H / kFrag;
+  Geometry g;
+  g.trips = F <= kTokenThreads ? 1 : (F <= 2 * kTokenThreads ? 2 : 4);
+  const int per = (F + g.trips - 1) / g.trips;
+  g.threads = (per + kWave - 1) / kWave * kWave;
+  return g;
+}
+
+namespace {
+
+constexpr int kMaxRoutes = 1024;  // tp * top_k staged per workgroup
+
+struct Mixes {
+  float post[kStreams], comb[kStreams * kStreams], pre[kStreams];
+};
+
+__device__ __forceinline__ void load_mixes(const BoundaryArgs &a, int t, Mixes &m) {
+#pragma unroll
+  for (int j = 0; j < kStreams; ++j) m.post[j] = a.post[t * kStreams + j];
+#pragma unroll
+  for (int i = 0; i < kStreams * kStreams; ++i) m.comb[i] = a.comb[t * kStreams * kStreams + i];
+#pragma unroll
+  for (int j = 0; j < kStreams; ++j) m.pre[j] = a.pre ? a.pre[t * kStreams + j] : 0.0f;
+}
+
+// Adds one rank's fragment to the running FP32 sum (rank order).
+__device__ __forceinline__ void accumulate(float (&s)[8], u32x4 w) {
+  float v[8];
+  unpack8(w, v);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s[e] = s[e] + v[e];
+}
+
+// Waits until no element of a mailbox fragment is the sentinel, with a
+// bounded number of re-reads; a time-out is counted in `status` and the
+// fragment is used as read.
+__device__ __forceinline__ u32x4 poll(const uint16_t *p, u32x4 w, const MailboxView &mb) {
+  int64_t spins = 0;
+  while ((has_sentinel(w[0]) || has_sentinel(w[1]) || has_sentinel(w[2]) || has_sentinel(w[3]))) {
+    if (++spins > mb.spin_limit) {
+      atomicAdd(mb.status, 1);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+    w = load_agent(p);
+  }
+  return w;
+}
+
+// One rank's MoE finalize contribution to a fragment
+// (_QuadFinalizePublishDeviceKernel.kernel): acc = 0; for k ascending, a
+// route with a valid row adds fma(row[k], w[k], acc); then + shared; BF16;
+// negative zero -> +0.  Rows outside [0, rows) (e.g. -1: expert not held by
+// this rank) are skipped.
+__device__ __forceinline__ u32x4 finalize_fragment(const FinalizeView &f, const int32_t *srow,
+                                                   const float *sw, int r, int t, int H,
+                                                   int64_t col) {
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+  const uint16_t *g = f.gemm2 + r * f.g_stride + col;
+  u32x4 sh = load_stream(f.shared + r * f.s_stride + (int64_t)t * H + col);
+  for (int k0 = 0; k0 < f.top_k; k0 += 8) {
+    u32x4 rows[8];
+    bool ok[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int k = k0 + i;
+      const int32_t row = k < f.top_k ? srow[k] : -1;
+      ok[i] = row >= 0 && row < f.rows;
+      rows[i] = ok[i] ? load_stream(g + (int64_t)row * H) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (!ok[i]) continue;
+      const float w = sw[k0 + i];
+      float v[8];
+      unpack8(rows[i], v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(v[e], w, acc[e]);
+    }
+  }
+  float s[8];
+  unpack8(sh, s);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = acc[e] + s[e];
+  return sanitize4(pack8(acc));
+}
+
+// Stages every rank's (row, weight) routes of token t in LDS; a route whose
+// row is -1 gets weight 0 as on the page (it is skipped anyway).
+__device__ __forceinline__ void stage_routes(const FinalizeView &f, int tp, int t, int32_t *srow,
+                                             float *sw) {
+  const int n = tp * f.top_k;
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int r = i / f.top_k, k = i % f.top_k;
+    const int64_t e = (int64_t)t * f.top_k + k;
+    const int32_t row = f.idx[r * f.i_stride + e];
+    srow[i] = row;
+    sw[i] = row == -1 ? 0.0f : f.weights[r * f.w_stride + e];
+  }
+  __syncthreads();
+}
+
+// The fused boundary for one token per workgroup.  TP > 0 fixes the rank
+// count at compile time (all rank loads of all trips issued up front);
+// TP == 0 reads it from the arguments.
+template <int TRIPS, int TP, Source SRC>
+__global__ void __launch_bounds__(kTokenThreads)
+boundary_kernel(const BoundaryArgs a) {
+  __shared__ double red[kTokenThreads / kWave];
+  __shared__ int32_t srow[SRC == Source::kFinalize ? kMaxRoutes : 1];
+  __shared__ float sw[SRC == Source::kFinalize ? kMaxRoutes : 1];
+
+  const int t = blockIdx.x, H = a.H, F = H / kFrag, nt = blockDim.x, tid = threadIdx.x;
+  const int tp = TP > 0 ? TP : a.tp;
+  const bool norm = a.pre != nullptr;
+
+  Mixes m;
+  load_mixes(a, t, m);
+
+  // Sources of the contributions.
+  const uint16_t *src = nullptr;
+  int64_t rs = 0;
+  uint32_t gen = 0;
+  if constexpr (SRC == Source::kPartials) {
+    src = a.partials + (int64_t)t * H;
+    rs = a.rank_stride;
+  } else if constexpr (SRC == Source::kMailbox) {
+    gen = (uint32_t)__hip_atomic_load(a.mailbox.stage_state, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT) % 3u;  // stays inside the slots
+    rs = (int64_t)a.mailbox.capacity * H;
+    src = a.mailbox.slots + (int64_t)gen * tp * rs + (int64_t)t * H;
+  } else {
+    stage_routes(a.fin, tp, t, srow, sw);
+  }
+
+  int64_t col[TRIPS];
+  bool valid[TRIPS];
+#pragma unroll
+  for (int i = 0; i < TRIPS; ++i) {
+    const int f = tid + i * nt;
+    valid[i] = f < F;
+    col[i] = valid[i] ? (int64_t)f * kFrag : 0;
+  }
+
+  // Issue the loads: residual streams, gamma, and (fixed tp) the partials.
+  u32x4 res[TRIPS][kStreams], gam[TRIPS];
+  constexpr int kHeld = TP > 0 ? TP : 1;
+  u32x4 part[TRIPS][kHeld];
+#pragma unroll
+  for (int i = 0; i < TRIPS; ++i) {
+    if constexpr (TP > 0 && SRC != Source::kFinalize) {
+#pragma unroll
+      for (int r = 0; r < TP; ++r) {
+        const uint16_t *p = src + r * rs + col[i];
+        part[i][r] = SRC == Source::kMailbox ? load_agent(p) : load_stream(p);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < kStreams; ++s)
+      res[i][s] = load_stream(a.residual + ((int64_t)t * kStreams + s) * H + col[i]);
+    gam[i] = norm ? load_cached(a.gamma + col[i]) : u32x4{0, 0, 0, 0};
+  }
+
+  u32x4 pfrag[TRIPS];
+  double ss = 0.0;
+#pragma unroll
+  for (int i = 0; i < TRIPS; ++i) {
+    // a1: s = ((0 + c_0) + c_1) + ... ; xr = bf16(s).
+    float s[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s[e] = 0.0f;
+    if (valid[i]) {
+      if constexpr (SRC == Source::kFinalize) {
+        for (int r = 0; r < tp; ++r)
+          accumulate(s, finalize_fragment(a.fin, srow + r * a.fin.top_k, sw + r * a.fin.top_k, r,
+                                          t, H, col[i]));
+      } else if constexpr (TP > 0) {
+#pragma unroll
+        for (int r = 0; r < TP; ++r) {
+          u32x4 w = part[i][r];
+          if constexpr (SRC == Source::kMailbox) w = poll(src + r * rs + col[i], w, a.mailbox);
+          accumulate(s, w);
+        }
+      } else {
+        for (int r = 0; r < tp; ++r) {
+          const uint16_t *p = src + r * rs + col[i];
+          u32x4 w;
+          if constexpr (SRC == Source::kMailbox) w = poll(p, load_agent(p), a.mailbox);
+          else w = load_stream(p);
+          accumulate(s, w);
+        }
+      }
+    }
+    float x[8];
+    unpack8(pack8(s), x);
+
+    // a2: y_j = bf16(x * post_j (+) sum_s res_s * comb[s][j]), s ascending.
+    float r4[kStreams][8];
+#pragma unroll
+    for (int q = 0; q < kStreams; ++q) unpack8(res[i][q], r4[q]);
+    float y[kStreams][8];
+#pragma unroll
+    for (int j = 0; j < kStreams; ++j) {
+      float acc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float v = x[e] * m.post[j];
+#pragma unroll
+        for (int q = 0; q < kStreams; ++q) v = __builtin_fmaf(r4[q][e], m.comb[q * kStreams + j], v);
+        acc[e] = v;
+      }
+      const u32x4 packed = pack8(acc);
+      if (valid[i]) store_stream(a.residual_out + ((int64_t)t * kStreams + j) * H + col[i], packed);
+      unpack8(packed, y[j]);
+    }
+
+    // a4 (first half): p = bf16(0 (+) y_0*pre_0 (+) ... (+) y_3*pre_3).
+    float z[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kStreams; ++j) v = __builtin_fmaf(y[j][e], m.pre[j], v);
+      z[e] = v;
+    }
+    pfrag[i] = pack8(z);
+    if (valid[i] && norm) {
+      float p[8];
+      unpack8(pfrag[i], p);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += (double)p[e] * (double)p[e];
+    }
+  }
+
+  // Mailbox: advance the generation and return the consumed slots to the
+  // sentinel (the next publish of this generation is two calls away).
+  if constexpr (SRC == Source::kMailbox) {
+    if (t == 0 && tid == 0) a.mailbox.stage_state[1] = (int32_t)((gen + 1) % 3);
+    const u32x4 empty = {0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+#pragma unroll
+    for (int i = 0; i < TRIPS; ++i)
+      if (valid[i])
+        for (int r = 0; r < tp; ++r) store_stream(const_cast<uint16_t *>(src) + r * rs + col[i], empty);
+  }
+
+  if (!norm) return;  // residual-only variant: uniform over the workgroup
+
+  // a4 (second half): inv = 1/sqrt(sum p^2 / H + eps); out = bf16((p*inv)*gamma).
+  double tot[1] = {ss};
+  block_sum<double, 1>(tot, red);
+  const float inv = (float)(1.0 / __builtin_sqrt((double)(float)tot[0] / (double)H + (double)a.norm_eps));
+
+#pragma unroll
+  for (int i = 0; i < TRIPS; ++i) {
+    float p[8], g[8], o[8];
+    unpack8(pfrag[i], p);
+    unpack8(gam[i], g);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (p[e] * inv) * g[e];
+    const u32x4 out = pack8(o);
+    if (valid[i]) store_stream(a.layer_input + (int64_t)t * H + col[i], out);
+
+    if (a.mx_values) {
+      // a8: the block of 32 columns is the fragments of lanes 4q .. 4q+3.
+      float ov[8];
+      unpack8(out, ov);
+      float amax = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(ov[e]));
+      amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1, kWave));
+      amax = __builtin_fmaxf(amax, __shfl_xor(amax, 2, kWave));
+      const uint32_t e8 = ue8m0_round_up(amax * (1.0f / 448.0f));
+      const float sc = ue8m0_inverse(e8);
+      u32x2 codes = {0, 0};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) codes[e >> 2] |= e4m3_rne_sat(ov[e] * sc) << (8 * (e & 3));
+      if (valid[i]) {
+        store8(a.mx_values + (int64_t)t * H + col[i], codes);
+        const int f = tid + i * nt;
+        if ((f & 3) == 0) a.mx_scales[sf_offset(t, f >> 2, H / 32)] = (uint8_t)e8;
+      }
+    }
+  }
+
+  if (a.mx_values) {
+    // Zero the scales of the padding rows M .. ceil(M/128)*128 - 1, one
+    // 4-column word per store, spread over the grid.
+    const int K = H / 32, words_per_row = K / 4;
+    const int64_t padded = ((int64_t)a.M + 127) / 128 * 128;
+    const int64_t words = (padded - a.M) * words_per_row;
+    for (int64_t w = (int64_t)t * nt + tid; w < words; w += (int64_t)a.M * nt) {
+      const int64_t row = a.M + w / words_per_row;
+      const int k = (int)(w % words_per_row) * 4;
+      *reinterpret_cast<uint32_t *>(a.mx_scales + sf_offset(row, k, K)) = 0u;
+    }
+  }
+}
+
+template <int TRIPS, Source SRC>
+hipError_t launch_tp(const BoundaryArgs &a, int threads, hipStream_t stream) {
+  dim3 grid(a.M), block(threads);
+  if (SRC == Source::kFinalize) {
+    hipLaunchKernelGGL((boundary_kernel<TRIPS, 0, SRC>), grid, block, 0, stream, a);
+    return hipGetLastError();
+  }
+  switch (a.tp) {
+    case 1: hipLaunchKernelGGL((boundary_kernel<TRIPS, 1, SRC>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((boundary_kernel<TRIPS, 2, SRC>), grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((boundary_kernel<TRIPS, 4, SRC>), grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL((boundary_kernel<TRIPS, 8, SRC>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((boundary_kernel<TRIPS, 0, SRC>), grid, block, 0, stream, a); break;
+  }
+  return hipGetLastError();
+}
+
+template <Source SRC>
+hipError_t launch_src(const BoundaryArgs &a, hipStream_t stream) {
+  const Geometry g = token_geometry(a.H);
+  switch (g.trips) {
+    case 1: return launch_tp<1, SRC>(a, g.threads, stream);
+    case 2: return launch_tp<2, SRC>(a, g.threads, stream);
+    default: return launch_tp<4, SRC>(a, g.threads, stream);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Two-shot emulation
+// ---------------------------------------------------------------------------
+
+// Every rank's contribution of token t (blockIdx.x) into owner t % tp,
+// slot t / tp: own[owner][rank][slot][H]
+// (_QuadFinalizePublishDeviceKernel.kernel, two-shot branch).
+__global__ void __launch_bounds__(kTokenThreads)
+finalize_to_owners_kernel(const FinalizeView f, int tp, int M, int H, uint16_t *own) {
+  __shared__ int32_t srow[kMaxRoutes];
+  __shared__ float sw[kMaxRoutes];
+  const int t = blockIdx.x, F = H / kFrag;
+  stage_routes(f, tp, t, srow, sw);
+  const int64_t slots = (M + tp - 1) / tp;
+  const int owner = t % tp;
+  const int64_t slot = t / tp;
+  for (int fr = threadIdx.x; fr < F; fr += blockDim.x) {
+    const int64_t col = (int64_t)fr * kFrag;
+    for (int r = 0; r < tp; ++r) {
+      const u32x4 c = finalize_fragment(f, srow + r * f.top_k, sw + r * f.top_k, r, t, H, col);
+      store_stream(own + (((int64_t)owner * tp + r) * slots + slot) * H + col, c);
+    }
+  }
+}
+
+// The owners' reduce (_OwnerReduceMulticastDeviceKernel.kernel): token t's
+// tp contributions summed in FP32 from rank 0, BF16, negative zero -> +0.
+__global__ void __launch_bounds__(256)
+owner_reduce_kernel(const uint16_t *own, int tp, int M, int H, uint16_t *reduced) {
+  const int F = H / kFrag;
+  const int64_t slots = (M + tp - 1) / tp;
+  const int64_t n = (int64_t)M * F;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int t = (int)(i / F);
+    const int64_t col = (i % F) * kFrag;
+    const int owner = t % tp;
+    const int64_t slot = t / tp;
+    float s[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s[e] = 0.0f;
+    for (int r = 0; r < tp; ++r)
+      accumulate(s, load_stream(own + (((int64_t)owner * tp + r) * slots + slot) * H + col));
+    store_stream(reduced + (int64_t)t * H + col, sanitize4(pack8(s)));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Mailbox producer and initializer
+// ---------------------------------------------------------------------------
+
+// Fills every slot with the sentinel and zeroes the stage state and status
+// (AllReduceMhcBoundary.__init__).
+__global__ void __launch_bounds__(256)
+mailbox_init_kernel(MailboxView mb, int64_t frags) {
+  const u32x4 empty = {0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < frags;
+       i += (int64_t)gridDim.x * blockDim.x)
+    store_stream(mb.slots + i * kFrag, empty);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    mb.stage_state[0] = 0;
+    mb.stage_state[1] = 0;
+    *mb.status = 0;
+  }
+}
+
+// Publishes ranks [rank_begin, rank_begin + rank_count) of token t
+// (blockIdx.y) into generation NEXT: sanitized fragments stored at device
+// scope, then ACTIVE = NEXT (_PublishDeviceKernel.kernel).
+__global__ void __launch_bounds__(256)
+publish_kernel(MailboxView mb, int tp, int H, const uint16_t *partials, int64_t rank_stride,
+               int rank_begin, int rank_count) {
+  const int t = blockIdx.y, F = H / kFrag;
+  const int fr = blockIdx.x * blockDim.x + threadIdx.x;
+  const uint32_t gen = (uint32_t)__hip_atomic_load(mb.stage_state + 1, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT) % 3u;
+  if (fr < F) {
+    const int64_t col = (int64_t)fr * kFrag;
+    for (int q = 0; q < rank_count; ++q) {
+      const int r = rank_begin + q;
+      const u32x4 w = sanitize4(load_stream(partials + q * rank_stride + (int64_t)t * H + col));
+      store_agent(mb.slots + (((int64_t)gen * tp + r) * mb.capacity + t) * H + col, w);
+    }
+  }
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
+    __hip_atomic_store(mb.stage_state, (int32_t)gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
+// Standalone MXFP8 quantizer (same encoding as the fused epilogue)
+// ---------------------------------------------------------------------------
+
+__global__ void __launch_bounds__(kTokenThreads)
+quant_kernel(const uint16_t *x, uint8_t *values, uint8_t *scales, int M, int H) {
+  const int t = blockIdx.x, F = H / kFrag, K = H / 32;
+  for (int f0 = 0; f0 < F; f0 += blockDim.x) {
+    const int f = f0 + threadIdx.x;
+    const bool valid = f < F;
+    const int64_t col = valid ? (int64_t)f * kFrag : 0;
+    float v[8];
+    unpack8(load_stream(x + (int64_t)t * H + col), v);
+    float amax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[e]));
+    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1, kWave));
+    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 2, kWave));
+    const uint32_t e8 = ue8m0_round_up(amax * (1.0f / 448.0f));
+    const float sc = ue8m0_inverse(e8);
+    u32x2 codes = {0, 0};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) codes[e >> 2] |= e4m3_rne_sat(v[e] * sc) << (8 * (e & 3));
+    if (valid) {
+      store8(values + (int64_t)t * H + col, codes);
+      if ((f & 3) == 0) scales[sf_offset(t, f >> 2, K)] = (uint8_t)e8;
+    }
+  }
+  const int words_per_row = K / 4;
+  const int64_t padded = ((int64_t)M + 127) / 128 * 128;
+  const int64_t words = (padded - M) * words_per_row;
+  for (int64_t w = (int64_t)t * blockDim.x + threadIdx.x; w < words; w += (int64_t)M * blockDim.x) {
+    const int64_t row = M + w / words_per_row;
+    *reinterpret_cast<uint32_t *>(scales + sf_offset(row, (int)(w % words_per_row) * 4, K)) = 0u;
+  }
+}
+
+int grid_for(int64_t items, int block) {
+  int64_t g = (items + block - 1) / block;
+  if (g > 65536) g = 65536;
+  return (int)(g < 1 ? 1 : g);
+}
+
+}  // namespace
+
+hipError_t launch_boundary(const BoundaryArgs &a, hipStream_t stream) {
+  switch (a.source) {
+    case Source::kPartials: return launch_src<Source::kPartials>(a, stream);
+    case Source::kMailbox: return launch_src<Source::kMailbox>(a, stream);
+    case Source::kFinalize: return launch_src<Source::kFinalize>(a, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_finalize_to_owners(const FinalizeView &fin, int tp, int M, int H, uint16_t *own,
+                                     hipStream_t stream) {
+  const Geometry g = token_geometry(H);
+  hipLaunchKernelGGL(finalize_to_owners_kernel, dim3(M), dim3(g.threads), 0, stream, fin, tp, M, H,
+                     own);
+  return hipGetLastError();
+}
+
+hipError_t launch_owner_reduce(const uint16_t *own, int tp, int M, int H, uint16_t *reduced,
+                               hipStream_t stream) {
+  const int64_t items = (int64_t)M * (H / kFrag);
+  hipLaunchKernelGGL(owner_reduce_kernel, dim3(grid_for(items, 256)), dim3(256), 0, stream, own, tp,
+                     M, H, reduced);
+  return hipGetLastError();
+}
+
+hipError_t launch_mailbox_init(const MailboxView &mb, int tp, int H, hipStream_t stream) {
+  const int64_t frags = 3LL * tp * mb.capacity * (H / kFrag);
+  hipLaunchKernelGGL(mailbox_init_kernel, dim3(grid_for(frags, 256)), dim3(256), 0, stream, mb,
+                     frags);
+  return hipGetLastError();
+}
+
+hipError_t launch_publish(const MailboxView &mb, int tp, int H, const uint16_t *partials,
+                          int64_t rank_stride, int rank_begin, int rank_count, int M,
+                          hipStream_t stream) {
+  const int F = H / kFrag;
+  dim3 grid((F + 255) / 256, M);
+  hipLaunchKernelGGL(publish_kernel, grid, dim3(256), 0, stream, mb, tp, H, partials, rank_stride,
+                     rank_begin, rank_count);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_mxfp8(const uint16_t *x, uint8_t *values, uint8_t *scales, int M, int H,
+                              hipStream_t stream) {
+  const Geometry g = token_geometry(H);
+  hipLaunchKernelGGL(quant_kernel, dim3(M), dim3(g.threads), 0, stream, x, values, scales, M, H);
+  return hipGetLastError();
+}
+
+}  // namespace mhcb

@@ -1,0 +1,330 @@
+// GLM-style boundary for gfx950: the pre-mix is derived in-kernel from the
+// new residual through the 24-row prenorm GEMV, and a small side-stream
+// kernel finishes the post-mix and the Sinkhorn residual mix for the next
+// boundary.
+//
+// Arithmetic follows the page
+//   vllm.models.glm5next.nvidia.specialized_decode.all_reduce_mhc
+//     (_BoundaryDeviceKernel.kernel, _GroupBoundaryDeviceKernel.kernel,
+//      _MixesDeviceKernel.kernel, _MixesDeviceKernel._sinkhorn)
+// with the rank sum taken from rank 0 in order as the DSV4.1 page does (the
+// GLM page's lane butterfly assumes tp = 4).
+//
+// gfx950 design: one workgroup takes G tokens (1, 2 or 4) with one 16-byte
+// fragment per thread; each hc_fn fragment is read once per workgroup and
+// applied to all G tokens with v_dot2c_f32_bf16 (BF16 products are exact in
+// FP32); the 24 x G partial dot products are reduce-scattered across the
+// wave (each lane ends with one total) and the waves are added through LDS
+// in fixed order, in place of the page's cluster-wide DSMEM reduction.
+#include "device.h"
+#include "kernels.h"
+
+namespace mhcb {
+namespace {
+
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+constexpr int kGlmWideThreads = 768;  // G = 4 workgroups: hidden <= 6144
+
+// Each word is copied to a scalar before the bit cast: a bit cast applied
+// directly to an ext_vector element (a[i]) was compiled to read element 0
+// for every i by this toolchain.
+__device__ __forceinline__ float dot8(u32x4 a, u32x4 b, float acc) {
+  const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, aw[i]),
+                                          __builtin_bit_cast(bf16x2v, bw[i]), acc, false);
+  return acc;
+}
+
+// Wave64 reduce-scatter of N (32 or 64) values per lane: returns on every
+// lane the wave total of value index (N == 64 ? lane : lane / 2).  Each
+// halving step keeps the half selected by the lane bit and adds the
+// partner's copy of it; the steps are unrolled by template recursion so
+// every index is a compile-time constant (the values stay in VGPRs).
+template <int N, int O>
+struct HalvingStep {
+  static __device__ __forceinline__ void run(float *v, int lane) {
+    const bool upper = (lane & O) != 0;
+#pragma unroll
+    for (int i = 0; i < N / 2; ++i) {
+      const float send = upper ? v[i] : v[i + N / 2];
+      const float keep = upper ? v[i + N / 2] : v[i];
+      v[i] = keep + __shfl_xor(send, O, kWave);
+    }
+    HalvingStep<N / 2, O / 2>::run(v, lane);
+  }
+};
+template <int O>
+struct HalvingStep<1, O> {
+  static __device__ __forceinline__ void run(float *, int) {}
+};
+
+template <int N>
+__device__ __forceinline__ float reduce_scatter(float (&v)[N]) {
+  static_assert(N == 32 || N == 64, "32 or 64 values");
+  const int lane = threadIdx.x & (kWave - 1);
+  HalvingStep<N, kWave / 2>::run(v, lane);
+  float r = v[0];
+  if constexpr (N == 32) r += __shfl_xor(r, 1, kWave);
+  return r;
+}
+
+__device__ __forceinline__ float sigmoid(float x) {
+  return (float)(1.0 / (1.0 + exp(-(double)x)));
+}
+
+template <int G>
+struct GlmShared {
+  float part[kMaxThreads / kWave][64];  // per-wave reduce-scatter results
+  float mix[G][kMix];                   // GEMV totals of each token
+  float pre[G][kStreams];
+  double red[(kMaxThreads / kWave) * G];
+};
+
+// KB = hc_fn rows per pass (24 for G <= 2; 12 for G = 4 to bound registers);
+// MAXT = the workgroup size bound (768 for G = 4 leaves 168 VGPRs a lane).
+template <int G, int KB, int MAXT>
+__global__ void __launch_bounds__(MAXT)
+glm_kernel(const GlmArgs a) {
+  static_assert(kMix % KB == 0, "rows per pass must divide 24");
+  constexpr int V = G * KB;                  // values reduced per pass
+  constexpr int N = V <= 32 ? 32 : 64;
+  static_assert(V <= 64, "too many values per pass");
+  __shared__ GlmShared<G> sh;
+
+  const int H = a.H, F = H / kFrag, tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid / kWave, waves = blockDim.x / kWave;
+  const int t0 = blockIdx.x * G;
+  const bool valid = tid < F;
+  const int64_t col = valid ? (int64_t)tid * kFrag : 0;
+
+  // a1 + a2 for the G tokens: y[g][j] packed BF16, sum of y^2 per token.
+  u32x4 y[G][kStreams];
+  double ssy[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int t = t0 + g;
+    const bool live = valid && t < a.M;
+    const int tt = t < a.M ? t : a.M - 1;
+    u32x4 res[kStreams];
+#pragma unroll
+    for (int s = 0; s < kStreams; ++s)
+      res[s] = load_stream(a.residual + ((int64_t)tt * kStreams + s) * H + col);
+    float s8[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s8[e] = 0.0f;
+    const uint16_t *src = a.partials + (int64_t)tt * H + col;
+    for (int r0 = 0; r0 < a.tp; r0 += 8) {
+      u32x4 w[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        w[q] = r0 + q < a.tp ? load_stream(src + (r0 + q) * a.rank_stride) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (r0 + q >= a.tp) break;
+        float v[8];
+        unpack8(w[q], v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s8[e] = s8[e] + v[e];
+      }
+    }
+    float x[8];
+    unpack8(pack8(s8), x);
+    const float *post = a.post + tt * kStreams;
+    const float *comb = a.comb + tt * kStreams * kStreams;
+    float r4[kStreams][8];
+#pragma unroll
+    for (int q = 0; q < kStreams; ++q) unpack8(res[q], r4[q]);
+    ssy[g] = 0.0;
+#pragma unroll
+    for (int j = 0; j < kStreams; ++j) {
+      float acc[8];
+      const float pj = post[j];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float v = x[e] * pj;
+#pragma unroll
+        for (int q = 0; q < kStreams; ++q) v = __builtin_fmaf(r4[q][e], comb[q * kStreams + j], v);
+        acc[e] = v;
+      }
+      y[g][j] = pack8(acc);
+      if (live) {
+        store_stream(a.residual_out + ((int64_t)t * kStreams + j) * H + col, y[g][j]);
+        float yv[8];
+        unpack8(y[g][j], yv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ssy[g] += (double)yv[e] * (double)yv[e];
+      }
+    }
+    if (!valid) {
+#pragma unroll
+      for (int j = 0; j < kStreams; ++j) y[g][j] = u32x4{0, 0, 0, 0};
+    }
+  }
+
+  // a3: g_k = sum_{j,c} fn[k][j*H + c] * y_j[c], KB rows per pass.
+#pragma unroll
+  for (int pass = 0; pass < kMix / KB; ++pass) {
+    float acc[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) acc[i] = 0.0f;
+    if (valid) {
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk) {
+        const int k = pass * KB + kk;
+#pragma unroll
+        for (int j = 0; j < kStreams; ++j) {
+          const u32x4 w = load_cached(a.fn + (int64_t)k * kStreams * H + (int64_t)j * H + col);
+#pragma unroll
+          for (int g = 0; g < G; ++g) acc[g * KB + kk] = dot8(w, y[g][j], acc[g * KB + kk]);
+        }
+      }
+    }
+    const float total = reduce_scatter<N>(acc);
+    const int idx = N == 64 ? lane : lane >> 1;
+    if ((N == 64 || (lane & 1) == 0) && idx < V) sh.part[wave][idx] = total;
+    __syncthreads();
+    if (tid < V) {
+      float s = 0.0f;
+      for (int w = 0; w < waves; ++w) s += sh.part[w][tid];
+      sh.mix[tid / KB][pass * KB + tid % KB] = s;
+    }
+    __syncthreads();
+  }
+
+  // g_24 and rstd; raw mixes out; pre_j = sigmoid(mix_j * scale0 + base_j) + hc_eps.
+  block_sum<double, G>(ssy, sh.red);
+  if (tid < G * kMix) {
+    const int g = tid / kMix, k = tid % kMix, t = t0 + g;
+    const float rstd = (float)(1.0 / __builtin_sqrt((double)(float)ssy[g] / (4.0 * H) + (double)a.rms_eps));
+    const float mix = sh.mix[g][k] * rstd;
+    if (t < a.M) a.mixes_out[(int64_t)t * kMix + k] = mix;
+    if (k < kStreams) sh.pre[g][k] = sigmoid(__builtin_fmaf(mix, a.scale[0], a.base[k])) + a.hc_eps;
+  }
+  __syncthreads();
+
+  // a4: p = bf16((q0+q1)+(q2+q3)), q_j = y_j * pre_j; RMSNorm over H.
+  u32x4 p[G];
+  double pss[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float q[kStreams][8];
+#pragma unroll
+    for (int j = 0; j < kStreams; ++j) {
+      float yv[8];
+      unpack8(y[g][j], yv);
+      const float pj = sh.pre[g][j];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) q[j][e] = yv[e] * pj;
+    }
+    float z[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) z[e] = (q[0][e] + q[1][e]) + (q[2][e] + q[3][e]);
+    p[g] = pack8(z);
+    pss[g] = 0.0;
+    if (valid) {
+      float pv[8];
+      unpack8(p[g], pv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pss[g] += (double)pv[e] * (double)pv[e];
+    }
+  }
+  block_sum<double, G>(pss, sh.red);
+  float gam[8];
+  unpack8(load_cached(a.gamma + col), gam);
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int t = t0 + g;
+    const float inv = (float)(1.0 / __builtin_sqrt((double)(float)pss[g] / (double)H + (double)a.norm_eps));
+    float pv[8], o[8];
+    unpack8(p[g], pv);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (pv[e] * inv) * gam[e];
+    if (valid && t < a.M) store_stream(a.layer_input + (int64_t)t * H + col, pack8(o));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Side-stream mixes: one thread per token.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float rcp(float x) { return (float)(1.0 / (double)x); }
+__device__ __forceinline__ float expf_rounded(float x) { return (float)exp((double)x); }
+
+__global__ void __launch_bounds__(64)
+mixes_kernel(const float *mixes, const float *scale, const float *base, float *post_out,
+             float *comb_out, int M, float eps, float post_mult, int repeat) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= M) return;
+  const float *row = mixes + (int64_t)t * kMix;
+  const float s1 = scale[1], s2 = scale[2];
+#pragma unroll
+  for (int j = 0; j < kStreams; ++j)
+    post_out[(int64_t)t * kStreams + j] =
+        sigmoid(__builtin_fmaf(row[kStreams + j], s1, base[kStreams + j])) * post_mult;
+
+  // Sinkhorn on the 4x4 residual mix, row-major (source rows).
+  float c[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) c[i] = __builtin_fmaf(row[8 + i], s2, base[8 + i]);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    float *q = c + 4 * r;
+    const float peak = __builtin_fmaxf(__builtin_fmaxf(q[0], q[1]), __builtin_fmaxf(q[2], q[3]));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) q[k] = expf_rounded(q[k] - peak);
+    const float inv = rcp((q[0] + q[1]) + (q[2] + q[3]));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) q[k] = __builtin_fmaf(q[k], inv, eps);
+  }
+  for (int it = 0; it < repeat; ++it) {
+    if (it > 0) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float *q = c + 4 * r;
+        const float inv = rcp(((q[0] + q[1]) + (q[2] + q[3])) + eps);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) q[k] = q[k] * inv;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float inv = rcp(((c[k] + c[4 + k]) + (c[8 + k] + c[12 + k])) + eps);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) c[4 * r + k] = c[4 * r + k] * inv;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) comb_out[(int64_t)t * 16 + i] = c[i];
+}
+
+}  // namespace
+
+hipError_t launch_boundary_glm(const GlmArgs &a, hipStream_t stream) {
+  const int F = a.H / kFrag;
+  const int threads = (F + kWave - 1) / kWave * kWave;
+  const int G = a.tokens_per_wg;
+  dim3 grid((a.M + G - 1) / G), block(threads);
+  switch (G) {
+    case 1: hipLaunchKernelGGL((glm_kernel<1, 24, 1024>), grid, block, 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((glm_kernel<2, 24, 1024>), grid, block, 0, stream, a); break;
+    case 4:
+      if (threads > kGlmWideThreads) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((glm_kernel<4, 12, kGlmWideThreads>), grid, block, 0, stream, a);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_mixes(const float *mixes, const float *scale, const float *base, float *post_out,
+                        float *comb_out, int M, float hc_eps, float post_mult, int repeat,
+                        hipStream_t stream) {
+  hipLaunchKernelGGL(mixes_kernel, dim3((M + 63) / 64), dim3(64), 0, stream, mixes, scale, base,
+                     post_out, comb_out, M, hc_eps, post_mult, repeat);
+  return hipGetLastError();
+}
+
+}  // namespace mhcb

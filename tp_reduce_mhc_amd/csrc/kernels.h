@@ -1,0 +1,103 @@
+// Internal launch interface between the C-ABI layer (api.hip) and the
+// kernel translation units.  Arguments are validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mhcb {
+
+// Where a token's tp contributions come from.
+enum class Source : int {
+  kPartials = 0,   // tp BF16 [M, H] arrays, rank_stride elements apart
+  kMailbox = 1,    // the ACTIVE generation of a Lamport mailbox (polled)
+  kFinalize = 2,   // MoE finalize: top-k weighted expert rows + shared expert
+};
+
+struct MailboxView {
+  uint16_t *slots;       // [3][tp][capacity][H]
+  int32_t *stage_state;  // [ACTIVE, NEXT]
+  int32_t *status;       // poll time-outs
+  int capacity;
+  int64_t spin_limit;
+};
+
+struct FinalizeView {
+  const uint16_t *gemm2;  // per rank [rows, H], g_stride elements apart
+  int64_t g_stride, rows;
+  const float *weights;   // per rank [M, top_k], w_stride apart (0 = shared)
+  int64_t w_stride;
+  const int32_t *idx;     // per rank [M, top_k], i_stride apart (0 = shared)
+  int64_t i_stride;
+  const uint16_t *shared; // per rank [M, H], s_stride apart
+  int64_t s_stride;
+  int top_k;
+};
+
+struct BoundaryArgs {
+  Source source;
+  const uint16_t *partials;
+  int64_t rank_stride;
+  MailboxView mailbox;
+  FinalizeView fin;
+  int tp;
+  const uint16_t *residual;  // [M, 4, H]
+  const float *post;         // [M, 4]
+  const float *comb;         // [M, 4, 4] [source][target]
+  const float *pre;          // [M, 4] or null (residual only)
+  const uint16_t *gamma;     // [H] or null
+  uint16_t *residual_out;    // [M, 4, H]
+  uint16_t *layer_input;     // [M, H] or null
+  uint8_t *mx_values;        // [M, H] or null
+  uint8_t *mx_scales;        // swizzled scales or null
+  int M, H;
+  float norm_eps;
+};
+
+hipError_t launch_boundary(const BoundaryArgs &a, hipStream_t stream);
+
+// Two-shot emulation: every rank's finalize contribution into the owner
+// mailboxes own[t % tp][rank][t / tp][H], then the owners' reduced sums.
+hipError_t launch_finalize_to_owners(const FinalizeView &fin, int tp, int M, int H,
+                                     uint16_t *own, hipStream_t stream);
+hipError_t launch_owner_reduce(const uint16_t *own, int tp, int M, int H, uint16_t *reduced,
+                               hipStream_t stream);
+
+hipError_t launch_mailbox_init(const MailboxView &mb, int tp, int H, hipStream_t stream);
+hipError_t launch_publish(const MailboxView &mb, int tp, int H, const uint16_t *partials,
+                          int64_t rank_stride, int rank_begin, int rank_count, int M,
+                          hipStream_t stream);
+
+hipError_t launch_quant_mxfp8(const uint16_t *x, uint8_t *values, uint8_t *scales, int M, int H,
+                              hipStream_t stream);
+
+struct GlmArgs {
+  const uint16_t *partials;
+  int64_t rank_stride;
+  int tp;
+  const uint16_t *residual;
+  const float *post, *comb;
+  const uint16_t *fn;        // [24, 4H]
+  const float *scale, *base; // [3], [24]
+  const uint16_t *gamma;
+  uint16_t *residual_out;
+  float *mixes_out;          // [M, 24]
+  uint16_t *layer_input;
+  int M, H;
+  float rms_eps, hc_eps, norm_eps;
+  int tokens_per_wg;         // 1, 2 or 4
+};
+
+hipError_t launch_boundary_glm(const GlmArgs &a, hipStream_t stream);
+
+hipError_t launch_mixes(const float *mixes, const float *scale, const float *base, float *post_out,
+                        float *comb_out, int M, float hc_eps, float post_mult, int repeat,
+                        hipStream_t stream);
+
+// Launch geometry of the per-token kernels (fragments split in `trips`).
+struct Geometry {
+  int trips, threads;
+};
+Geometry token_geometry(int H);
+
+}  // namespace mhcb
