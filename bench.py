@@ -93,15 +93,18 @@ def measured_traffic():
 # GPU timing
 # ---------------------------------------------------------------------------
 
+USE_GRAPH = True
+
+
 class Timed:
     """Times `steps` calls of fn(i) (i = rotation index), captured in a HIP
     graph when possible, with HIP events on the launching stream."""
 
-    def __init__(self, torch, fn, steps, warmup, use_graph=True):
+    def __init__(self, torch, fn, steps, warmup, use_graph=None):
         self.torch = torch
         self.fn, self.steps, self.warmup = fn, steps, warmup
         self.graph = None
-        self.use_graph = use_graph
+        self.use_graph = USE_GRAPH if use_graph is None else use_graph
 
     def run(self):
         torch = self.torch
@@ -179,20 +182,25 @@ def bench_delayed(torch, mhc, b, steps, warmup, mxfp8=False, check=False):
             s["scales"] = torch.empty(mhc.mhcb_mxfp8_scale_bytes(b.M, b.H), dtype=torch.uint8,
                                       device="cuda")
 
+    ws = mhc.workspace(torch.device("cuda", torch.cuda.current_device()))
+
     def call(i):
         s = sets[i % len(sets)]
         mhc.mhcb_boundary(s["partials"], b.M * b.H, None, s["residual"], s["post"], s["comb"],
                           s["pre"], s["gamma"], s["residual_out"], s["layer_input"],
-                          s.get("values"), s.get("scales"), b.M, b.H, 4, b.tp, b.norm_eps)
+                          s.get("values"), s.get("scales"), ws, ws.numel(), b.M, b.H, 4, b.tp,
+                          b.norm_eps)
 
     ms = Timed(torch, call, steps, warmup).run()
+    mhc.mhcb_workspace_status(ws)
     if check:
         # Every rotation set's output of the graph replay equals an eager call.
         for s in sets[:3]:
             ro, li = s["residual_out"].clone(), s["layer_input"].clone()
             mhc.mhcb_boundary(s["partials"], b.M * b.H, None, s["residual"], s["post"], s["comb"],
                               s["pre"], s["gamma"], s["residual_out"], s["layer_input"],
-                              s.get("values"), s.get("scales"), b.M, b.H, 4, b.tp, b.norm_eps)
+                              s.get("values"), s.get("scales"), ws, ws.numel(), b.M, b.H, 4, b.tp,
+                              b.norm_eps)
             torch.cuda.synchronize()
             assert torch.equal(ro.view(torch.int16), s["residual_out"].view(torch.int16))
             assert torch.equal(li.view(torch.int16), s["layer_input"].view(torch.int16))
@@ -209,12 +217,14 @@ def bench_mailbox(torch, mhc, b, steps, warmup):
         s["values"] = torch.empty((b.M, b.H), dtype=torch.uint8, device="cuda")
         s["scales"] = torch.empty(mhc.mhcb_mxfp8_scale_bytes(b.M, b.H), dtype=torch.uint8, device="cuda")
 
+    ws = mhc.workspace(torch.device("cuda", torch.cuda.current_device()))
+
     def call(i):
         s = sets[i % len(sets)]
         mhc.mhcb_publish(mb, s["partials"], b.M * b.H, 0, b.tp, b.M)
         mhc.mhcb_boundary(None, 0, mb, s["residual"], s["post"], s["comb"], s["pre"], s["gamma"],
-                          s["residual_out"], s["layer_input"], s["values"], s["scales"], b.M, b.H,
-                          4, b.tp, b.norm_eps)
+                          s["residual_out"], s["layer_input"], s["values"], s["scales"], ws,
+                          ws.numel(), b.M, b.H, 4, b.tp, b.norm_eps)
 
     ms = Timed(torch, call, steps, warmup).run()
     assert mb.status_ok()
@@ -228,10 +238,7 @@ def bench_finalize(torch, mhc, f, steps, warmup, two_shot=False):
              comb=dev(torch, f.comb), pre=dev(torch, f.pre), gamma=dev(torch, f.gamma))
     sets = make_sets(torch, t, rotations(per_set, minimum=2))
     rows = f.gemm2.shape[1]
-    ws = None
-    if two_shot:
-        ws = torch.empty(mhc.mhcb_finalize_workspace_bytes(f.M, f.H, f.tp, 1), dtype=torch.uint8,
-                         device="cuda")
+    ws = mhc.new_workspace(mhc.mhcb_workspace_bytes(f.M, f.H, f.tp, int(two_shot)), "cuda")
     for s in sets:
         s["residual_out"] = torch.empty((f.M, 4, f.H), dtype=torch.bfloat16, device="cuda")
         s["layer_input"] = torch.empty((f.M, f.H), dtype=torch.bfloat16, device="cuda")
@@ -241,8 +248,7 @@ def bench_finalize(torch, mhc, f, steps, warmup, two_shot=False):
         mhc.mhcb_finalize(s["gemm2"], rows * f.H, rows, s["weights"], 0, s["idx"], 0, s["shared"],
                           f.M * f.H, s["residual"], s["post"], s["comb"], s["pre"], s["gamma"],
                           s["residual_out"], s["layer_input"], None, None, int(two_shot), ws,
-                          ws.numel() if ws is not None else 0, f.M, f.H, 4, f.tp, f.top_k,
-                          f.norm_eps)
+                          ws.numel(), f.M, f.H, 4, f.tp, f.top_k, f.norm_eps)
 
     ms = Timed(torch, call, steps, warmup).run()
     extra = f.M * (2 * f.tp * 2 * f.H + 2 * 2 * f.H) if two_shot else 0
@@ -261,11 +267,13 @@ def bench_glm(torch, mhc, g, steps, warmup):
         s["layer_input"] = torch.empty((g.M, g.H), dtype=torch.bfloat16, device="cuda")
         s["mixes"] = torch.empty((g.M, 24), dtype=torch.float32, device="cuda")
 
+    ws = mhc.workspace(torch.device("cuda", torch.cuda.current_device()))
+
     def call(i):
         s = sets[i % len(sets)]
         mhc.mhcb_boundary_glm(s["partials"], g.M * g.H, s["residual"], s["post"], s["comb"], fn,
                               scale, base, gamma, s["residual_out"], s["mixes"], s["layer_input"],
-                              g.M, g.H, 4, g.tp, g.rms_eps, g.hc_eps, g.norm_eps, 0)
+                              ws, ws.numel(), g.M, g.H, 4, g.tp, g.rms_eps, g.hc_eps, g.norm_eps, 0)
 
     ms = Timed(torch, call, steps, warmup).run()
     return ms, per_set
@@ -315,9 +323,19 @@ def main():
     ap.add_argument("--quick", action="store_true", help="headline only, no extra workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="",
-                    help="run one workload only (headline, sweep, finalize, glm, mxfp8, mailbox) "
-                         "for profiling; prints no JSON")
+                    help="comma-separated workloads to run alone for profiling (headline, sweep, "
+                         "finalize, glm, mxfp8, mailbox, copy); prints no JSON")
+    ap.add_argument("--slices", type=int, default=0,
+                    help="workgroups per token for small-M calls (0 = the library's choice)")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch the timed calls one by one instead of replaying a HIP graph")
     args = ap.parse_args()
+    global USE_GRAPH
+    USE_GRAPH = not args.eager
+    only = set(filter(None, args.only.split(",")))
+
+    def want(name):
+        return not only or name in only
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this build has no "
               "multi-GPU path; the boundary would shard over tokens, see the design notes)",
@@ -328,10 +346,11 @@ def main():
     import synth
     import tp_reduce_mhc_amd as mhc
     torch.cuda.set_device(0)
+    mhc.mhcb_set_token_slices(args.slices)
     K, W = args.steps, args.warmup
     result = {}
 
-    if args.only in ("", "headline"):
+    if want("headline"):
         b = synth.dsv41_delayed(128)
         log(f"headline {b.name}: {K} steps, {W} warmup")
         ms, nbytes, nsets = bench_delayed(torch, mhc, b, K, W, check=True)
@@ -349,13 +368,13 @@ def main():
                          "traffic": traffic, "kernel": "boundary_kernel (delayed mHC, tp 8)",
                          "algorithmic_bytes_per_launch": int(nbytes)},
         })
-        if not args.no_cpu_baseline and not args.only:
+        if not args.no_cpu_baseline and not only:
             log("cpu baseline (oracle)")
             result["cpu_baseline"] = cpu_baseline(b)
-        if args.only:
+        if only:
             log(f"headline: {ms * 1e3:.2f} us/call, {gbps:.0f} GB/s")
 
-    if args.only in ("", "sweep") and not args.quick:
+    if want("sweep") and not args.quick:
         sweep = {}
         for M in (1, 8, 32, 64, 128):
             b = synth.dsv41_delayed(M)
@@ -366,7 +385,7 @@ def main():
         result["us_per_call"] = {"M1": sweep["M1"]["us_per_call"], "M64": sweep["M64"]["us_per_call"]}
 
     extra = {}
-    if args.only in ("", "finalize") and not args.quick:
+    if want("finalize") and not args.quick:
         for M in (64, 512, 4096):
             f = synth.moe_finalize(M)
             steps = max(10, min(K, 100 if M <= 512 else 20))
@@ -377,29 +396,37 @@ def main():
                 ms, nbytes = bench_finalize(torch, mhc, f, steps, min(W, 5), two_shot=True)
                 extra[f"moe_finalize_two_shot_M{M}"] = entry(ms, nbytes, M)
             del f
-    if args.only in ("", "glm") and not args.quick:
+    if want("glm") and not args.quick:
         for M in (1, 64, 512):
             g = synth.glm(M)
             ms, nbytes = bench_glm(torch, mhc, g, min(K, 100), min(W, 5))
             extra[f"glm_M{M}"] = entry(ms, nbytes, M)
             log(f"glm M={M}: {extra[f'glm_M{M}']}")
-    if args.only in ("", "mxfp8") and not args.quick:
+    if (want("mxfp8") or want("mailbox")) and not args.quick:
         b = synth.large_m_delayed(8192)
-        ms, nbytes, _ = bench_delayed(torch, mhc, b, 20, 3, mxfp8=True)
-        extra["mxfp8_M8192"] = entry(ms, nbytes, 8192)
-        log(f"mxfp8 M=8192: {extra['mxfp8_M8192']}")
-        if args.only in ("", "mailbox"):
+        if want("mxfp8"):
+            ms, nbytes, _ = bench_delayed(torch, mhc, b, 20, 3, mxfp8=True)
+            extra["mxfp8_M8192"] = entry(ms, nbytes, 8192)
+            log(f"mxfp8 M=8192: {extra['mxfp8_M8192']}")
+        if want("mailbox"):
             ms, nbytes = bench_mailbox(torch, mhc, b, 10, 2)
             extra["mailbox_mxfp8_M8192"] = entry(ms, nbytes, 8192)
             log(f"mailbox M=8192: {extra['mailbox_mxfp8_M8192']}")
-    elif args.only == "mailbox":
-        b = synth.large_m_delayed(8192)
-        ms, nbytes = bench_mailbox(torch, mhc, b, 10, 2)
-        log(f"mailbox M=8192: {entry(ms, nbytes, 8192)}")
+    if "copy" in only:
+        # Calibration for the HBM byte counters: a plain device copy of a
+        # known size (read n bytes, write n bytes), launched `steps` times.
+        n = 512 << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy: {args.steps} copies of {n} bytes")
     if extra:
         result["other_workloads"] = extra
 
-    if not args.only:
+    if not only:
         print(json.dumps(result), flush=True)
 
 

@@ -56,10 +56,30 @@ const char *mhcb_version(void);
  * ([DSV41] AllReduceMHC.__call__, mxfp8_scale_bytes).  Host-only. */
 int64_t mhcb_mxfp8_scale_bytes(int64_t M, int64_t hidden_size);
 
-/* Workspace bytes mhcb_finalize needs: 0 for the one-shot path; for the
- * two-shot emulation the owner mailboxes [tp][tp][ceil(M/tp)][hidden] plus
- * the reduced sums [M][hidden], BF16.  Host-only; -1 on bad sizes. */
-int64_t mhcb_finalize_workspace_bytes(int M, int hidden_size, int tp, int two_shot);
+/* Workspace.  The boundary entry points take an optional caller-owned
+ * device workspace (256-byte aligned).  Its first part holds the state of
+ * the cross-workgroup reduction that lets small-M calls spread each token
+ * over several workgroups (with NULL every token takes one workgroup); it
+ * must be zero-filled once (mhcb_workspace_init) before its first use, and
+ * every call leaves it ready for the next one.  Calls that may run
+ * concurrently (on different streams) must not share a workspace.
+ * mhcb_workspace_bytes gives the size for a call: the sync state, plus for
+ * the two-shot emulation (mhcb_finalize, two_shot = 1) the owner mailboxes
+ * [tp][tp][ceil(M/tp)][hidden] and the reduced sums [M][hidden] (BF16).
+ * Host-only; -1 on bad sizes. */
+int64_t mhcb_workspace_bytes(int M, int hidden_size, int tp, int two_shot);
+
+/* Zero-fills the workspace's sync state (a kernel on `stream`). */
+int mhcb_workspace_init(void *workspace, int64_t workspace_bytes, hipStream_t stream);
+
+/* Synchronizes `stream`; MHCB_ETIMEOUT if a cross-workgroup wait of a call
+ * that used this workspace gave up (bounded spin), else MHCB_OK. */
+int mhcb_workspace_status(const void *workspace, hipStream_t stream);
+
+/* Tuning: workgroups per token for calls with a workspace (1..16; 0 =
+ * automatic, about two workgroups per compute unit).  Process-wide; returns
+ * the previous value.  Outputs do not depend on it. */
+int mhcb_set_token_slices(int slices);
 
 /* Three-generation Lamport mailbox ([GLM] AllReduceMhcBoundary.__init__,
  * [DSV41] module text): slots[generation][rank][token][hidden] BF16, every
@@ -95,14 +115,16 @@ typedef struct mhcb_mailbox {
  * (mhcb_mxfp8_scale_bytes) UE8M0 scales of out, per 32 columns, in the
  * swizzled 128x4 layout, padding rows zeroed (hidden % 128 == 0 required).
  * pre == norm_weight == layer_input == NULL selects the residual-only
- * variant.  Errors: M < 1 or M > mailbox capacity, tp < 1 or tp > 64,
+ * variant.  workspace: optional (see mhcb_workspace_bytes).
+ * Errors: M < 1 or M > mailbox capacity, tp < 1 or tp > 64,
  * pre/norm_weight given alone, MXFP8 on a residual-only call -> EINVAL;
  * hidden % 8, hc_mult != 4, MXFP8 with hidden % 128 -> EUNSUPPORTED. */
 int mhcb_boundary(const uint16_t *partials, int64_t rank_stride, const mhcb_mailbox *mailbox,
                   const uint16_t *residual, const float *post, const float *comb,
                   const float *pre, const uint16_t *norm_weight, uint16_t *residual_out,
-                  uint16_t *layer_input, uint8_t *mxfp8_values, uint8_t *mxfp8_scales, int M,
-                  int hidden_size, int hc_mult, int tp, float norm_eps, hipStream_t stream);
+                  uint16_t *layer_input, uint8_t *mxfp8_values, uint8_t *mxfp8_scales,
+                  void *workspace, int64_t workspace_bytes, int M, int hidden_size, int hc_mult,
+                  int tp, float norm_eps, hipStream_t stream);
 
 /* GLM boundary ([GLM] AllReduceMhcBoundary.__call__ with
  * _BoundaryDeviceKernel / _GroupBoundaryDeviceKernel): xr and y as in
@@ -115,13 +137,15 @@ int mhcb_boundary(const uint16_t *partials, int64_t rank_stride, const mhcb_mail
  *   out   = bf16((p * inv) * norm_weight) as above.
  * hc_fn [24, 4*hidden] BF16; scale [3], base [24] FP32; mixes_out [M, 24]
  * FP32.  tokens_per_wg (1, 2, 4; 0 = by M) tokens share one workgroup and
- * one read of hc_fn; outputs do not depend on it.  hidden <= 8192. */
+ * one read of hc_fn; outputs do not depend on it.  hidden <= 8192.
+ * workspace: optional (see mhcb_workspace_bytes). */
 int mhcb_boundary_glm(const uint16_t *partials, int64_t rank_stride, const uint16_t *residual,
                       const float *post, const float *comb, const uint16_t *hc_fn,
                       const float *scale, const float *base, const uint16_t *norm_weight,
-                      uint16_t *residual_out, float *mixes_out, uint16_t *layer_input, int M,
-                      int hidden_size, int hc_mult, int tp, float rms_eps, float hc_eps,
-                      float norm_eps, int tokens_per_wg, hipStream_t stream);
+                      uint16_t *residual_out, float *mixes_out, uint16_t *layer_input,
+                      void *workspace, int64_t workspace_bytes, int M, int hidden_size,
+                      int hc_mult, int tp, float rms_eps, float hc_eps, float norm_eps,
+                      int tokens_per_wg, hipStream_t stream);
 
 /* Side-stream mixes for the next boundary ([GLM] _MixesDeviceKernel):
  *   post_out[t][j] = sigmoid(mixes[t][4+j] * scale[1] + base[4+j]) * post_mult
@@ -144,9 +168,9 @@ int mhcb_mixes(const float *mixes, const float *scale, const float *base, float 
  * (rank strides 0 = replicated); shared_output per rank [M, hidden] BF16.
  * two_shot = 1 runs the two-shot emulation instead: contributions stored
  * to owner t % tp, slot t / tp of owner mailboxes in `workspace`
- * (mhcb_finalize_workspace_bytes, 16-byte aligned, caller-owned), the
- * owners' FP32 rank-ordered sums, then the boundary reads one reduced value
- * per token; the results are bit-identical to two_shot = 0.
+ * (required then; mhcb_workspace_bytes with two_shot = 1), the owners'
+ * FP32 rank-ordered sums, then the boundary reads one reduced value per
+ * token; the results are bit-identical to two_shot = 0.
  * Errors as mhcb_boundary, plus top_k < 1, tp * top_k > 1024, a workspace
  * that is missing or too small -> EINVAL. */
 int mhcb_finalize(const uint16_t *gemm2_permuted, int64_t gemm2_rank_stride, int64_t rows,

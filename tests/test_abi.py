@@ -40,9 +40,12 @@ def test_host_only_helpers():
     assert mhc.mhcb_mxfp8_scale_bytes(8192, 5120) == 8192 * 160
     assert mhc.mhcb_mxfp8_scale_bytes(100, 5120) == 128 * 160
     assert mhc.mhcb_mxfp8_scale_bytes(1, 128) == 128 * 4
-    assert mhc.mhcb_finalize_workspace_bytes(10, 512, 4, 0) == 0
-    assert mhc.mhcb_finalize_workspace_bytes(10, 512, 4, 1) == (4 * 4 * 3 + 10) * 512 * 2
-    assert mhc.mhcb_finalize_workspace_bytes(10, 512, 0, 1) == -1
+    sync = mhc.mhcb_workspace_bytes(10, 512, 4, 0)
+    assert sync > 0 and sync % 256 == 0
+    assert mhc.mhcb_workspace_bytes(10, 512, 4, 1) == sync + (4 * 4 * 3 + 10) * 512 * 2
+    assert mhc.mhcb_workspace_bytes(10, 512, 0, 1) == -1
+    prev = mhc.mhcb_set_token_slices(4)
+    assert mhc.mhcb_set_token_slices(prev) == 4
     assert mhc.mhcb_version().count(".") == 2
 
 
@@ -53,8 +56,8 @@ def _boundary(**kw):
     import tp_reduce_mhc_amd as mhc
     args = dict(partials=FAKE, rank_stride=4 * 512, mailbox=None, residual=FAKE, post=FAKE,
                 comb=FAKE, pre=FAKE, norm_weight=FAKE, residual_out=FAKE, layer_input=FAKE,
-                mxfp8_values=None, mxfp8_scales=None, M=4, hidden_size=512, hc_mult=4, tp=2,
-                norm_eps=1e-6, stream=0)
+                mxfp8_values=None, mxfp8_scales=None, workspace=None, workspace_bytes=0, M=4,
+                hidden_size=512, hc_mult=4, tp=2, norm_eps=1e-6, stream=0)
     args.update(kw)
     return mhc.mhcb_boundary(**args)
 
@@ -76,6 +79,8 @@ def _boundary(**kw):
     (dict(rank_stride=100), 1, "overlaps"),
     (dict(rank_stride=4 * 512 + 4), 2, "rank_stride"),
     (dict(residual_out=None), 1, "required"),
+    (dict(workspace=FAKE, workspace_bytes=100), 1, "workspace_bytes"),
+    (dict(workspace=FAKE + 16, workspace_bytes=1 << 20), 2, "256-byte"),
 ])
 def test_boundary_validation(kw, code, text):
     import tp_reduce_mhc_amd as mhc
@@ -107,8 +112,8 @@ def test_glm_mixes_finalize_quant_validation():
     import tp_reduce_mhc_amd as mhc
     glm = dict(partials=FAKE, rank_stride=4 * 512, residual=FAKE, post=FAKE, comb=FAKE, hc_fn=FAKE,
                scale=FAKE, base=FAKE, norm_weight=FAKE, residual_out=FAKE, mixes_out=FAKE,
-               layer_input=FAKE, M=4, hidden_size=512, hc_mult=4, tp=2, rms_eps=1e-6, hc_eps=1e-6,
-               norm_eps=1e-6, stream=0)
+               layer_input=FAKE, workspace=None, workspace_bytes=0, M=4, hidden_size=512, hc_mult=4,
+               tp=2, rms_eps=1e-6, hc_eps=1e-6, norm_eps=1e-6, stream=0)
     for kw, text in ((dict(tokens_per_wg=3), "tokens_per_wg"), (dict(hc_fn=None), "required"),
                      (dict(hidden_size=8200, rank_stride=4 * 8200), "exceeds"),
                      (dict(tokens_per_wg=4, hidden_size=8192, rank_stride=4 * 8192), "tokens_per_wg=4")):
@@ -126,11 +131,16 @@ def test_glm_mixes_finalize_quant_validation():
                hidden_size=512, hc_mult=4, tp=2, top_k=8, norm_eps=1e-6, stream=0)
     for kw, text in ((dict(top_k=0), "top_k"), (dict(tp=64, top_k=32), "exceeds"),
                      (dict(two_shot=1), "workspace"), (dict(rows=-1), "rows"),
-                     (dict(two_shot=1, workspace=FAKE + 8, workspace_bytes=1 << 20), "aligned")):
+                     (dict(two_shot=1, workspace=FAKE + 8, workspace_bytes=1 << 20), "aligned"),
+                     (dict(two_shot=1, workspace=FAKE, workspace_bytes=1 << 10), "workspace_bytes")):
         with pytest.raises(mhc.MhcbError, match=text):
             mhc.mhcb_finalize(**{**fin, **kw})
     with pytest.raises(mhc.MhcbError, match="multiple of 128"):
         mhc.mhcb_quant_mxfp8(FAKE, FAKE, FAKE, 4, 520, 0)
+    with pytest.raises(mhc.MhcbError, match="at least"):
+        mhc.mhcb_workspace_init(FAKE, 64, 0)
+    with pytest.raises(mhc.MhcbError, match="256-byte"):
+        mhc.mhcb_workspace_init(FAKE + 64, 1 << 20, 0)
 
 
 def test_product_path_does_not_touch_the_oracle():

@@ -159,6 +159,42 @@ def test_large_m_sampled_tokens():
             assert_bits_equal(got, want, f"scales of token {t}")
 
 
+@pytest.mark.parametrize("M", [1, 8, 64, 100])
+def test_token_split_gives_identical_bits(M):
+    """Every number of workgroups per token (1 = no split, no workspace)
+    gives the same bits: the partial sums of squares are exact in binary64.
+    The bounded cross-workgroup waits never gave up."""
+    b = synth.boundary(15, M, 5120, 8, 0.5, f"split-M{M}")
+    ref = run_boundary_split(b, None)
+    ws = mhc.new_workspace(mhc.mhcb_workspace_bytes(M, 5120, 8, 0), "cuda")
+    try:
+        for S in (0, 2, 3, 5, 8, 16):
+            mhc.mhcb_set_token_slices(S)
+            got = run_boundary_split(b, ws)
+            for g, r, what in zip(got, ref, ("residual_out", "layer_input", "values", "scales")):
+                assert_bits_equal(g, r, f"S={S} {what}")
+    finally:
+        mhc.mhcb_set_token_slices(0)
+    assert mhc.mhcb_workspace_status(ws) == mhc.MHCB_OK
+    ro_ref, li_ref, _ = oracle.boundary(b.partials, b.residual, b.post, b.comb, b.pre, b.gamma,
+                                        b.norm_eps, threads=8)
+    assert_bits_equal(ref[0], ro_ref, "residual_out")
+    assert_within_ulp(ref[1], li_ref, 1, "layer_input")
+
+
+def run_boundary_split(b, ws):
+    M, H = b.M, b.H
+    ro = torch.empty((M, 4, H), dtype=torch.bfloat16, device="cuda")
+    li = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+    vals = torch.empty((M, H), dtype=torch.uint8, device="cuda")
+    scales = torch.empty(mhc.mhcb_mxfp8_scale_bytes(M, H), dtype=torch.uint8, device="cuda")
+    mhc.mhcb_boundary(dev(b.partials), M * H, None, dev(b.residual), dev(b.post), dev(b.comb),
+                      dev(b.pre), dev(b.gamma), ro, li, vals, scales, ws,
+                      ws.numel() if ws is not None else 0, M, H, 4, b.tp, b.norm_eps)
+    torch.cuda.synchronize()
+    return u16(ro), u16(li), host(vals), host(scales)
+
+
 def test_cross_token_independence_and_determinism():
     b = synth.dsv41_delayed(128)
     ro1, li1, _ = run_boundary(b)
@@ -178,10 +214,10 @@ def test_cross_token_independence_and_determinism():
 # MoE finalize and the two-shot emulation
 # ---------------------------------------------------------------------------
 
-def run_finalize(f, two_shot=False, mxfp8=False):
+def run_finalize(f, two_shot=False, mxfp8=False, split=True):
     out = mhc.finalize(dev(f.gemm2), dev(f.weights), dev(f.idx), dev(f.shared), dev(f.residual),
                        dev(f.post), dev(f.comb), dev(f.pre), dev(f.gamma), f.norm_eps,
-                       two_shot=two_shot, mxfp8=mxfp8)
+                       two_shot=two_shot, mxfp8=mxfp8, split=split)
     torch.cuda.synchronize()
     ro, li, mx = out
     return u16(ro), u16(li), ((host(mx[0]), host(mx[1])) if mx else None)
@@ -201,6 +237,10 @@ def test_moe_finalize_matches_oracle_and_two_shot(M):
     assert_bits_equal(li2, li, "two-shot layer_input")
     assert_bits_equal(mx2[0], mx[0], "two-shot mxfp8 values")
     assert_bits_equal(mx2[1], mx[1], "two-shot mxfp8 scales")
+    ro3, li3, mx3 = run_finalize(f, mxfp8=True, split=False)
+    assert_bits_equal(ro3, ro, "one workgroup per token: residual_out")
+    assert_bits_equal(li3, li, "one workgroup per token: layer_input")
+    assert_bits_equal(mx3[1], mx[1], "one workgroup per token: mxfp8 scales")
 
 
 def test_moe_finalize_per_rank_routing_with_dropped_experts():

@@ -83,6 +83,67 @@ int check_mailbox(const char *fn, const mhcb_mailbox *mb, int H, int tp, int M) 
   return MHCB_OK;
 }
 
+int g_slices_override = 0;  // mhcb_set_token_slices (0 = automatic)
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Checks a workspace argument: NULL, or at least `need` bytes, 256-byte
+// aligned (its first kSyncBytes hold the cross-workgroup sync state).
+int check_workspace(const char *fn, const void *ws, int64_t bytes, int64_t need) {
+  if (!ws) return MHCB_OK;
+  if (bytes < need)
+    return fail(MHCB_EINVAL, "%s: workspace_bytes=%lld < %lld (mhcb_workspace_bytes)", fn,
+                (long long)bytes, (long long)need);
+  if (!aligned(ws, 256)) return fail(MHCB_EALIGN, "%s: workspace must be 256-byte aligned", fn);
+  return MHCB_OK;
+}
+
+SyncView sync_view(void *ws) {
+  char *b = static_cast<char *>(ws);
+  SyncView v;
+  v.status = reinterpret_cast<uint32_t *>(b);
+  v.slots = b + 256;
+  v.spin_limit = 1 << 20;
+  return v;
+}
+
+// Workgroups per token: with a workspace and few tokens, the token's
+// fragments are spread over up to `max_slices` workgroups (at least one
+// wave of fragments each; slices cover whole 32-column blocks) until there
+// are about `target` workgroups in flight.  Measured on MI355X (H=5120,
+// tp=8): 4 slices save 0.6-1.2 us per call for M <= 64; past that the
+// cross-workgroup exchange costs what the extra compute units gain.
+void choose_slices(BoundaryArgs &a, void *ws, int target, int max_slices) {
+  a.slices = 1;
+  a.slice_frags = a.H / kFrag;
+  if (!ws || a.M > kSyncTokens) return;
+  const int F = a.H / kFrag;
+  int S = g_slices_override > 0 ? g_slices_override : (a.M < 128 ? target / a.M : 1);
+  if (g_slices_override <= 0 && S > max_slices) S = max_slices;
+  const int cap = g_slices_override > 0 ? F / 4 : F / kWave;
+  S = S < 1 ? 1 : S;
+  S = S > kMaxSlices ? kMaxSlices : S;
+  S = S > cap ? cap : S;
+  if (S <= 1) return;
+  int frags = (F + S - 1) / S;
+  frags = (frags + 3) / 4 * 4;
+  a.slices = (F + frags - 1) / frags;
+  a.slice_frags = frags;
+  if (a.slices > 1) a.sync = sync_view(ws);
+}
+
 MailboxView view_of(const mhcb_mailbox *mb) {
   MailboxView v;
   v.slots = mb->slots;
@@ -106,22 +167,49 @@ int64_t mhcb_mxfp8_scale_bytes(int64_t M, int64_t hidden_size) {
   return (M + 127) / 128 * 128 * (hidden_size / 32);
 }
 
-int64_t mhcb_finalize_workspace_bytes(int M, int hidden_size, int tp, int two_shot) {
+int64_t mhcb_workspace_bytes(int M, int hidden_size, int tp, int two_shot) {
   if (M < 0 || hidden_size < 0 || tp < 1) return -1;
-  if (!two_shot) return 0;
+  if (!two_shot) return kSyncBytes;
   const int64_t slots = ((int64_t)M + tp - 1) / tp;
-  return ((int64_t)tp * tp * slots + M) * hidden_size * 2;
+  return kSyncBytes + ((int64_t)tp * tp * slots + M) * hidden_size * 2;
+}
+
+int mhcb_workspace_init(void *workspace, int64_t workspace_bytes, hipStream_t stream) {
+  const char *fn = "mhcb_workspace_init";
+  if (!workspace || workspace_bytes < kSyncBytes)
+    return fail(MHCB_EINVAL, "%s: a workspace of at least %lld bytes is required", fn, (long long)kSyncBytes);
+  if (!aligned(workspace, 256)) return fail(MHCB_EALIGN, "%s: workspace must be 256-byte aligned", fn);
+  return launched(launch_zero(workspace, kSyncBytes, stream), fn);
+}
+
+int mhcb_workspace_status(const void *workspace, hipStream_t stream) {
+  const char *fn = "mhcb_workspace_status";
+  if (!workspace) return fail(MHCB_EINVAL, "%s: workspace is required", fn);
+  hipError_t e = hipStreamSynchronize(stream);
+  uint32_t status = 0;
+  if (e == hipSuccess) e = hipMemcpy(&status, workspace, sizeof status, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(MHCB_ELAUNCH, "%s: %s", fn, hipGetErrorString(e));
+  if (status) return fail(MHCB_ETIMEOUT, "%s: %u cross-workgroup wait(s) gave up", fn, status);
+  return ok();
+}
+
+int mhcb_set_token_slices(int slices) {
+  const int previous = g_slices_override;
+  g_slices_override = slices < 0 ? 0 : (slices > kMaxSlices ? kMaxSlices : slices);
+  return previous;
 }
 
 int mhcb_boundary(const uint16_t *partials, int64_t rank_stride, const mhcb_mailbox *mailbox,
                   const uint16_t *residual, const float *post, const float *comb, const float *pre,
                   const uint16_t *norm_weight, uint16_t *residual_out, uint16_t *layer_input,
-                  uint8_t *mxfp8_values, uint8_t *mxfp8_scales, int M, int hidden_size, int hc_mult,
-                  int tp, float norm_eps, hipStream_t stream) {
+                  uint8_t *mxfp8_values, uint8_t *mxfp8_scales, void *workspace,
+                  int64_t workspace_bytes, int M, int hidden_size, int hc_mult, int tp,
+                  float norm_eps, hipStream_t stream) {
   const char *fn = "mhcb_boundary";
   int rc = check_common(fn, residual, post, comb, pre, norm_weight, residual_out, layer_input,
                         mxfp8_values, mxfp8_scales, M, hidden_size, hc_mult, tp);
   if (rc) return rc;
+  if ((rc = check_workspace(fn, workspace, workspace_bytes, kSyncBytes))) return rc;
   if ((partials == nullptr) == (mailbox == nullptr))
     return fail(MHCB_EINVAL, "%s: give exactly one of partials and mailbox", fn);
   BoundaryArgs a = {};
@@ -152,14 +240,16 @@ int mhcb_boundary(const uint16_t *partials, int64_t rank_stride, const mhcb_mail
   a.M = M;
   a.H = hidden_size;
   a.norm_eps = norm_eps;
+  choose_slices(a, workspace, device_cus(), 4);
   return launched(launch_boundary(a, stream), fn);
 }
 
 int mhcb_boundary_glm(const uint16_t *partials, int64_t rank_stride, const uint16_t *residual,
                       const float *post, const float *comb, const uint16_t *hc_fn, const float *scale,
                       const float *base, const uint16_t *norm_weight, uint16_t *residual_out,
-                      float *mixes_out, uint16_t *layer_input, int M, int hidden_size, int hc_mult,
-                      int tp, float rms_eps, float hc_eps, float norm_eps, int tokens_per_wg,
+                      float *mixes_out, uint16_t *layer_input, void *workspace,
+                      int64_t workspace_bytes, int M, int hidden_size, int hc_mult, int tp,
+                      float rms_eps, float hc_eps, float norm_eps, int tokens_per_wg,
                       hipStream_t stream) {
   const char *fn = "mhcb_boundary_glm";
   if (!partials || !hc_fn || !scale || !base || !norm_weight || !mixes_out || !layer_input)
@@ -168,6 +258,7 @@ int mhcb_boundary_glm(const uint16_t *partials, int64_t rank_stride, const uint1
   int rc = check_common(fn, residual, post, comb, scale, norm_weight, residual_out, layer_input,
                         nullptr, nullptr, M, hidden_size, hc_mult, tp);
   if (rc) return rc;
+  if ((rc = check_workspace(fn, workspace, workspace_bytes, kSyncBytes))) return rc;
   if (hidden_size > kMaxHiddenGlm)
     return fail(MHCB_EUNSUPPORTED, "%s: hidden_size=%d exceeds %d", fn, hidden_size, kMaxHiddenGlm);
   if (tp > 1 && rank_stride < (int64_t)M * hidden_size && rank_stride != 0)
@@ -243,15 +334,17 @@ int mhcb_finalize(const uint16_t *gemm2_permuted, int64_t gemm2_rank_stride, int
   a.H = hidden_size;
   a.norm_eps = norm_eps;
   if (!two_shot) {
+    if ((rc = check_workspace(fn, workspace, workspace_bytes, kSyncBytes))) return rc;
     a.source = Source::kFinalize;
     a.fin = f;
+    choose_slices(a, workspace, 2 * device_cus(), kMaxSlices);
     return launched(launch_boundary(a, stream), fn);
   }
-  const int64_t need = mhcb_finalize_workspace_bytes(M, hidden_size, tp, 1);
-  if (!workspace || workspace_bytes < need)
+  const int64_t need = mhcb_workspace_bytes(M, hidden_size, tp, 1);
+  if (!workspace)
     return fail(MHCB_EINVAL, "%s: the two-shot emulation needs a %lld-byte workspace", fn, (long long)need);
-  if (!aligned(workspace, 16)) return fail(MHCB_EALIGN, "%s: workspace must be 16-byte aligned", fn);
-  uint16_t *own = static_cast<uint16_t *>(workspace);
+  if ((rc = check_workspace(fn, workspace, workspace_bytes, need))) return rc;
+  uint16_t *own = reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) + kSyncBytes);
   const int64_t slots = ((int64_t)M + tp - 1) / tp;
   uint16_t *reduced = own + (int64_t)tp * tp * slots * hidden_size;
   hipError_t e = launch_finalize_to_owners(f, tp, M, hidden_size, own, stream);
@@ -261,6 +354,7 @@ int mhcb_finalize(const uint16_t *gemm2_permuted, int64_t gemm2_rank_stride, int
   a.partials = reduced;
   a.rank_stride = 0;
   a.tp = 1;
+  choose_slices(a, workspace, device_cus(), 4);
   return launched(launch_boundary(a, stream), fn);
 }
 

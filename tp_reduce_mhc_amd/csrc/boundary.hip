@@ -22,13 +22,12 @@
 
 namespace mhcb {
 
-// Fragments of a token split over at most kTokenThreads threads: 1, 2 or 4
-// fragments per thread (hidden <= 16384).
-Geometry token_geometry(int H) {
-  const int F = H / kFrag;
+// A workgroup covering `frags` fragments: 1, 2 or 4 fragments per thread,
+// at most kTokenThreads threads (frags <= 2048, i.e. hidden <= 16384).
+Geometry fragment_geometry(int frags) {
   Geometry g;
-  g.trips = F <= kTokenThreads ? 1 : (F <= 2 * kTokenThreads ? 2 : 4);
-  const int per = (F + g.trips - 1) / g.trips;
+  g.trips = frags <= kTokenThreads ? 1 : (frags <= 2 * kTokenThreads ? 2 : 4);
+  const int per = (frags + g.trips - 1) / g.trips;
   g.threads = (per + kWave - 1) / kWave * kWave;
   return g;
 }
@@ -129,22 +128,83 @@ __device__ __forceinline__ void stage_routes(const FinalizeView &f, int tp, int 
   __syncthreads();
 }
 
-// The fused boundary for one token per workgroup.  TP > 0 fixes the rank
-// count at compile time (all rank loads of all trips issued up front);
-// TP == 0 reads it from the arguments.
+// The token's sum of squares over all its slices.  Every slice publishes
+// its partial (binary64 bits), arrives on the token's counter, and waits
+// for the barrier generation to move (the last arrival resets the count and
+// bumps the generation: a sense-reversing barrier, reusable by the next
+// call).  All slices then add the partials in slice order, so they agree
+// bit for bit.
+//
+// Every shared word is accessed with device-scope atomics, which are
+// performed at the device's coherence point; ordering them only needs the
+// wave's earlier accesses to have completed (s_waitcnt vmcnt(0), which on
+// CDNA counts stores too), and the partials are read only after the
+// generation load that released the wait has returned.  Device-scope
+// release/acquire fences would instead write back / invalidate the whole L2
+// of the XCD at every arrival and every poll.
+//
+// The wait is bounded; a time-out is counted in the status word and the
+// kernel goes on (every wave always exits).
+__device__ double token_sum(const SyncView &sy, int t, int s, int slices, double local,
+                            double *shared) {
+  if (threadIdx.x == 0) {
+    char *slot = sy.slots + (int64_t)t * kSyncSlot;
+    uint32_t *count = reinterpret_cast<uint32_t *>(slot);
+    uint32_t *gen = count + 1;
+    uint64_t *part = reinterpret_cast<uint64_t *>(slot + 64);
+    __hip_atomic_store(part + s, __builtin_bit_cast(uint64_t, local), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t g = __hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    wait_vmem();  // the partial has landed at the coherence point
+    const uint32_t arrived =
+        __hip_atomic_fetch_add(count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (arrived == (uint32_t)slices - 1u) {
+      __hip_atomic_store(count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(gen, g + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      int64_t spins = 0;
+      while (__hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == g) {
+        if (++spins > sy.spin_limit) {
+          atomicAdd(sy.status, 1u);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    double total = 0.0;
+    for (int q = 0; q < slices; ++q)
+      total += __builtin_bit_cast(double, __hip_atomic_load(part + q, __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT));
+    *shared = total;
+  }
+  __syncthreads();
+  const double total = *shared;
+  __syncthreads();
+  return total;
+}
+
+// The fused boundary.  Workgroup (s, t) covers fragments
+// [s * slice_frags, (s + 1) * slice_frags) of token t (all of them when
+// slices == 1).  TP > 0 fixes the rank count at compile time so that every
+// rank load of every trip is issued up front; TP == 0 reads it from the
+// arguments.
 template <int TRIPS, int TP, Source SRC>
 __global__ void __launch_bounds__(kTokenThreads)
 boundary_kernel(const BoundaryArgs a) {
-  __shared__ double red[kTokenThreads / kWave];
+  __shared__ double red[kTokenThreads / kWave + 1];
   __shared__ int32_t srow[SRC == Source::kFinalize ? kMaxRoutes : 1];
   __shared__ float sw[SRC == Source::kFinalize ? kMaxRoutes : 1];
 
-  const int t = blockIdx.x, H = a.H, F = H / kFrag, nt = blockDim.x, tid = threadIdx.x;
+  // Split: grid (slices, M), a token's slices consecutive in dispatch order
+  // (so the workgroups a wait depends on are never queued behind it).
+  // Unsplit: grid (M).
+  const int s = a.slices > 1 ? blockIdx.x : 0, t = a.slices > 1 ? blockIdx.y : blockIdx.x;
+  const int H = a.H, F = H / kFrag, nt = blockDim.x;
+  const int tid = threadIdx.x;
   const int tp = TP > 0 ? TP : a.tp;
   const bool norm = a.pre != nullptr;
-
-  Mixes m;
-  load_mixes(a, t, m);
+  const int first = a.slices > 1 ? s * a.slice_frags : 0;
+  const int last = a.slices > 1 ? min(F, first + a.slice_frags) : F;
 
   // Sources of the contributions.
   const uint16_t *src = nullptr;
@@ -166,12 +226,13 @@ boundary_kernel(const BoundaryArgs a) {
   bool valid[TRIPS];
 #pragma unroll
   for (int i = 0; i < TRIPS; ++i) {
-    const int f = tid + i * nt;
-    valid[i] = f < F;
+    const int f = first + tid + i * nt;
+    valid[i] = f < last;
     col[i] = valid[i] ? (int64_t)f * kFrag : 0;
   }
 
-  // Issue the loads: residual streams, gamma, and (fixed tp) the partials.
+  // Issue the streamed loads first: residual streams, gamma, and (fixed tp)
+  // the partials, for every trip.
   u32x4 res[TRIPS][kStreams], gam[TRIPS];
   constexpr int kHeld = TP > 0 ? TP : 1;
   u32x4 part[TRIPS][kHeld];
@@ -185,30 +246,35 @@ boundary_kernel(const BoundaryArgs a) {
       }
     }
 #pragma unroll
-    for (int s = 0; s < kStreams; ++s)
-      res[i][s] = load_stream(a.residual + ((int64_t)t * kStreams + s) * H + col[i]);
+    for (int q = 0; q < kStreams; ++q)
+      res[i][q] = load_stream(a.residual + ((int64_t)t * kStreams + q) * H + col[i]);
     gam[i] = norm ? load_cached(a.gamma + col[i]) : u32x4{0, 0, 0, 0};
   }
+  // The token's mixes are scalar loads; keep them behind the vector loads so
+  // that waiting for them does not delay the stream.
+  __builtin_amdgcn_sched_barrier(0);
+  Mixes m;
+  load_mixes(a, t, m);
 
   u32x4 pfrag[TRIPS];
   double ss = 0.0;
 #pragma unroll
   for (int i = 0; i < TRIPS; ++i) {
     // a1: s = ((0 + c_0) + c_1) + ... ; xr = bf16(s).
-    float s[8];
+    float sum[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s[e] = 0.0f;
+    for (int e = 0; e < 8; ++e) sum[e] = 0.0f;
     if (valid[i]) {
       if constexpr (SRC == Source::kFinalize) {
         for (int r = 0; r < tp; ++r)
-          accumulate(s, finalize_fragment(a.fin, srow + r * a.fin.top_k, sw + r * a.fin.top_k, r,
-                                          t, H, col[i]));
+          accumulate(sum, finalize_fragment(a.fin, srow + r * a.fin.top_k, sw + r * a.fin.top_k, r,
+                                            t, H, col[i]));
       } else if constexpr (TP > 0) {
 #pragma unroll
         for (int r = 0; r < TP; ++r) {
           u32x4 w = part[i][r];
           if constexpr (SRC == Source::kMailbox) w = poll(src + r * rs + col[i], w, a.mailbox);
-          accumulate(s, w);
+          accumulate(sum, w);
         }
       } else {
         for (int r = 0; r < tp; ++r) {
@@ -216,12 +282,12 @@ boundary_kernel(const BoundaryArgs a) {
           u32x4 w;
           if constexpr (SRC == Source::kMailbox) w = poll(p, load_agent(p), a.mailbox);
           else w = load_stream(p);
-          accumulate(s, w);
+          accumulate(sum, w);
         }
       }
     }
     float x[8];
-    unpack8(pack8(s), x);
+    unpack8(pack8(sum), x);
 
     // a2: y_j = bf16(x * post_j (+) sum_s res_s * comb[s][j]), s ascending.
     float r4[kStreams][8];
@@ -264,7 +330,7 @@ boundary_kernel(const BoundaryArgs a) {
   // Mailbox: advance the generation and return the consumed slots to the
   // sentinel (the next publish of this generation is two calls away).
   if constexpr (SRC == Source::kMailbox) {
-    if (t == 0 && tid == 0) a.mailbox.stage_state[1] = (int32_t)((gen + 1) % 3);
+    if (t == 0 && s == 0 && tid == 0) a.mailbox.stage_state[1] = (int32_t)((gen + 1) % 3);
     const u32x4 empty = {0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
 #pragma unroll
     for (int i = 0; i < TRIPS; ++i)
@@ -272,11 +338,14 @@ boundary_kernel(const BoundaryArgs a) {
         for (int r = 0; r < tp; ++r) store_stream(const_cast<uint16_t *>(src) + r * rs + col[i], empty);
   }
 
-  if (!norm) return;  // residual-only variant: uniform over the workgroup
+  if (!norm) return;  // residual-only variant: uniform over the grid
 
   // a4 (second half): inv = 1/sqrt(sum p^2 / H + eps); out = bf16((p*inv)*gamma).
+  // The squares of BF16 values are exact in binary64 and so is their sum,
+  // whatever the order or the split.
   double tot[1] = {ss};
   block_sum<double, 1>(tot, red);
+  if (a.slices > 1) tot[0] = token_sum(a.sync, t, s, a.slices, tot[0], red + kTokenThreads / kWave);
   const float inv = (float)(1.0 / __builtin_sqrt((double)(float)tot[0] / (double)H + (double)a.norm_eps));
 
 #pragma unroll
@@ -305,7 +374,7 @@ boundary_kernel(const BoundaryArgs a) {
       for (int e = 0; e < 8; ++e) codes[e >> 2] |= e4m3_rne_sat(ov[e] * sc) << (8 * (e & 3));
       if (valid[i]) {
         store8(a.mx_values + (int64_t)t * H + col[i], codes);
-        const int f = tid + i * nt;
+        const int f = first + tid + i * nt;
         if ((f & 3) == 0) a.mx_scales[sf_offset(t, f >> 2, H / 32)] = (uint8_t)e8;
       }
     }
@@ -317,7 +386,8 @@ boundary_kernel(const BoundaryArgs a) {
     const int K = H / 32, words_per_row = K / 4;
     const int64_t padded = ((int64_t)a.M + 127) / 128 * 128;
     const int64_t words = (padded - a.M) * words_per_row;
-    for (int64_t w = (int64_t)t * nt + tid; w < words; w += (int64_t)a.M * nt) {
+    const int64_t wg = (int64_t)t * a.slices + s, wgs = (int64_t)a.M * a.slices;
+    for (int64_t w = wg * nt + tid; w < words; w += wgs * nt) {
       const int64_t row = a.M + w / words_per_row;
       const int k = (int)(w % words_per_row) * 4;
       *reinterpret_cast<uint32_t *>(a.mx_scales + sf_offset(row, k, K)) = 0u;
@@ -327,7 +397,7 @@ boundary_kernel(const BoundaryArgs a) {
 
 template <int TRIPS, Source SRC>
 hipError_t launch_tp(const BoundaryArgs &a, int threads, hipStream_t stream) {
-  dim3 grid(a.M), block(threads);
+  dim3 grid = a.slices > 1 ? dim3(a.slices, a.M) : dim3(a.M), block(threads);
   if (SRC == Source::kFinalize) {
     hipLaunchKernelGGL((boundary_kernel<TRIPS, 0, SRC>), grid, block, 0, stream, a);
     return hipGetLastError();
@@ -344,7 +414,7 @@ hipError_t launch_tp(const BoundaryArgs &a, int threads, hipStream_t stream) {
 
 template <Source SRC>
 hipError_t launch_src(const BoundaryArgs &a, hipStream_t stream) {
-  const Geometry g = token_geometry(a.H);
+  const Geometry g = fragment_geometry(a.slices > 1 ? a.slice_frags : a.H / kFrag);
   switch (g.trips) {
     case 1: return launch_tp<1, SRC>(a, g.threads, stream);
     case 2: return launch_tp<2, SRC>(a, g.threads, stream);
@@ -477,6 +547,12 @@ quant_kernel(const uint16_t *x, uint8_t *values, uint8_t *scales, int M, int H) 
   }
 }
 
+__global__ void __launch_bounds__(256) zero_kernel(uint32_t *p, int64_t words) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
 int grid_for(int64_t items, int block) {
   int64_t g = (items + block - 1) / block;
   if (g > 65536) g = 65536;
@@ -492,6 +568,13 @@ hipError_t launch_boundary(const BoundaryArgs &a, hipStream_t stream) {
     case Source::kFinalize: return launch_src<Source::kFinalize>(a, stream);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_zero(void *p, int64_t bytes, hipStream_t stream) {
+  const int64_t words = bytes / 4;
+  hipLaunchKernelGGL(zero_kernel, dim3(grid_for(words, 256)), dim3(256), 0, stream,
+                     static_cast<uint32_t *>(p), words);
+  return hipGetLastError();
 }
 
 hipError_t launch_finalize_to_owners(const FinalizeView &fin, int tp, int M, int H, uint16_t *own,

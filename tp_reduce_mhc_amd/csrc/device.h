@@ -108,6 +108,11 @@ __device__ __forceinline__ void store_agent(uint16_t *p, u32x4 w) {
                      __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Waits until every earlier vector-memory access of the wave, stores
+// included, has completed: s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at
+// their maxima, GFX9-family encoding).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // ---------------------------------------------------------------------------
 // Reductions.  Butterfly (xor) exchanges give every lane the same bits, and
 // the cross-wave step adds the waves in index order, so every sum is

@@ -34,8 +34,28 @@ struct FinalizeView {
   int top_k;
 };
 
+// Cross-workgroup state of the token-split kernels, at the start of the
+// caller's workspace: a 256-byte header (status word), then one 256-byte
+// slot per token -- arrival count (offset 0), barrier generation (4), the
+// slices' partial sums of squares as binary64 bits (64 + 8 s) -- so that
+// different tokens' atomics never share a cache line or memory channel.
+// Zero-filled once; every call leaves the counts at zero.
+constexpr int kSyncTokens = 1024;  // tokens a split call may have
+constexpr int kMaxSlices = 16;     // workgroups a token may be split over
+constexpr int kSyncSlot = 256;     // bytes per token
+constexpr int64_t kSyncBytes = 256 + (int64_t)kSyncSlot * kSyncTokens;
+
+struct SyncView {
+  uint32_t *status;   // barrier time-outs
+  char *slots;        // [kSyncTokens][kSyncSlot]
+  int64_t spin_limit;
+};
+
 struct BoundaryArgs {
   Source source;
+  int slices;        // workgroups per token (1 = no cross-workgroup sync)
+  int slice_frags;   // fragments per workgroup when slices > 1
+  SyncView sync;
   const uint16_t *partials;
   int64_t rank_stride;
   MailboxView mailbox;
@@ -94,10 +114,14 @@ hipError_t launch_mixes(const float *mixes, const float *scale, const float *bas
                         float *comb_out, int M, float hc_eps, float post_mult, int repeat,
                         hipStream_t stream);
 
-// Launch geometry of the per-token kernels (fragments split in `trips`).
+// Launch geometry of a workgroup covering `frags` 16-byte fragments
+// (1, 2 or 4 of them per thread, at most 512 threads).
 struct Geometry {
   int trips, threads;
 };
-Geometry token_geometry(int H);
+Geometry fragment_geometry(int frags);
+inline Geometry token_geometry(int H) { return fragment_geometry(H / 8); }
+
+hipError_t launch_zero(void *p, int64_t bytes, hipStream_t stream);
 
 }  // namespace mhcb

@@ -60,9 +60,13 @@ _SIGNATURES = {
     "mhcb_last_error": (ctypes.c_char_p, []),
     "mhcb_version": (ctypes.c_char_p, []),
     "mhcb_mxfp8_scale_bytes": (_I64, [_I64, _I64]),
-    "mhcb_finalize_workspace_bytes": (_I64, [_I, _I, _I, _I]),
-    "mhcb_boundary": (_I, [_P, _I64, _MB, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _P]),
-    "mhcb_boundary_glm": (_I, [_P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+    "mhcb_workspace_bytes": (_I64, [_I, _I, _I, _I]),
+    "mhcb_workspace_init": (_I, [_P, _I64, _P]),
+    "mhcb_workspace_status": (_I, [_P, _P]),
+    "mhcb_set_token_slices": (_I, [_I]),
+    "mhcb_boundary": (_I, [_P, _I64, _MB, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64,
+                           _I, _I, _I, _I, _F, _P]),
+    "mhcb_boundary_glm": (_I, [_P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64,
                                _I, _I, _I, _I, _F, _F, _F, _I, _P]),
     "mhcb_mixes": (_I, [_P, _P, _P, _P, _P, _I, _I, _F, _F, _I, _P]),
     "mhcb_finalize": (_I, [_P, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _P, _P, _P, _P, _P,
@@ -124,27 +128,43 @@ def mhcb_mxfp8_scale_bytes(M: int, hidden_size: int) -> int:
     return _lib.mhcb_mxfp8_scale_bytes(M, hidden_size)
 
 
-def mhcb_finalize_workspace_bytes(M: int, hidden_size: int, tp: int, two_shot: int) -> int:
-    return _lib.mhcb_finalize_workspace_bytes(M, hidden_size, tp, int(two_shot))
+def mhcb_workspace_bytes(M: int, hidden_size: int, tp: int, two_shot: int) -> int:
+    return _lib.mhcb_workspace_bytes(M, hidden_size, tp, int(two_shot))
+
+
+def mhcb_workspace_init(workspace, workspace_bytes, stream=None) -> None:
+    _check(_lib.mhcb_workspace_init(_ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def mhcb_workspace_status(workspace, stream=None) -> int:
+    rc = _lib.mhcb_workspace_status(_ptr(workspace), _stream(stream))
+    _check(rc)
+    return rc
+
+
+def mhcb_set_token_slices(slices: int) -> int:
+    return _lib.mhcb_set_token_slices(slices)
 
 
 def mhcb_boundary(partials, rank_stride, mailbox, residual, post, comb, pre, norm_weight,
-                  residual_out, layer_input, mxfp8_values, mxfp8_scales, M, hidden_size, hc_mult,
-                  tp, norm_eps, stream=None) -> None:
+                  residual_out, layer_input, mxfp8_values, mxfp8_scales, workspace, workspace_bytes,
+                  M, hidden_size, hc_mult, tp, norm_eps, stream=None) -> None:
     _check(_lib.mhcb_boundary(_ptr(partials), rank_stride, _mb(mailbox), _ptr(residual), _ptr(post),
                               _ptr(comb), _ptr(pre), _ptr(norm_weight), _ptr(residual_out),
-                              _ptr(layer_input), _ptr(mxfp8_values), _ptr(mxfp8_scales), M,
-                              hidden_size, hc_mult, tp, norm_eps, _stream(stream)))
+                              _ptr(layer_input), _ptr(mxfp8_values), _ptr(mxfp8_scales),
+                              _ptr(workspace), workspace_bytes, M, hidden_size, hc_mult, tp,
+                              norm_eps, _stream(stream)))
 
 
 def mhcb_boundary_glm(partials, rank_stride, residual, post, comb, hc_fn, scale, base, norm_weight,
-                      residual_out, mixes_out, layer_input, M, hidden_size, hc_mult, tp, rms_eps,
-                      hc_eps, norm_eps, tokens_per_wg=0, stream=None) -> None:
+                      residual_out, mixes_out, layer_input, workspace, workspace_bytes, M,
+                      hidden_size, hc_mult, tp, rms_eps, hc_eps, norm_eps, tokens_per_wg=0,
+                      stream=None) -> None:
     _check(_lib.mhcb_boundary_glm(_ptr(partials), rank_stride, _ptr(residual), _ptr(post), _ptr(comb),
                                   _ptr(hc_fn), _ptr(scale), _ptr(base), _ptr(norm_weight),
-                                  _ptr(residual_out), _ptr(mixes_out), _ptr(layer_input), M,
-                                  hidden_size, hc_mult, tp, rms_eps, hc_eps, norm_eps, tokens_per_wg,
-                                  _stream(stream)))
+                                  _ptr(residual_out), _ptr(mixes_out), _ptr(layer_input),
+                                  _ptr(workspace), workspace_bytes, M, hidden_size, hc_mult, tp,
+                                  rms_eps, hc_eps, norm_eps, tokens_per_wg, _stream(stream)))
 
 
 def mhcb_mixes(mixes, scale, base, post_out, comb_out, M, hc_mult, hc_eps, post_mult,
@@ -196,14 +216,43 @@ def _bf16_empty(shape, device):
     return torch.empty(shape, dtype=torch.bfloat16, device=device)
 
 
+_WORKSPACES = {}
+
+
+def workspace(device=None, *, M: int = 0, hidden_size: int = 0, tp: int = 1,
+              two_shot: bool = False) -> torch.Tensor:
+    """A zero-initialized workspace on `device`, cached per (device, size):
+    the sync state of the token-split calls, plus the two-shot scratch when
+    asked.  Calls on different streams need their own (fresh=True is not
+    offered: allocate with new_workspace)."""
+    device = torch.device(device if device is not None else "cuda")
+    if device.index is None:
+        device = torch.device("cuda", torch.cuda.current_device())
+    need = mhcb_workspace_bytes(M, hidden_size, tp, int(two_shot))
+    key = (device.index, need)
+    ws = _WORKSPACES.get(key)
+    if ws is None:
+        ws = new_workspace(need, device)
+        _WORKSPACES[key] = ws
+    return ws
+
+
+def new_workspace(nbytes: int, device) -> torch.Tensor:
+    """A fresh zero-filled workspace of `nbytes` (256-byte aligned by torch)."""
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+
 def boundary(partials: torch.Tensor, residual, post, comb, pre, norm_weight, norm_eps: float,
-             *, mxfp8: bool = False, stream=None):
-    """Delayed-mHC boundary on resident partials [tp, M, H] (BF16).
+             *, mxfp8: bool = False, split: bool = True, stream=None):
+    """Delayed-mHC boundary on resident partials [tp, M, H] (BF16).  With
+    split (default) the cached workspace lets small-M calls spread tokens
+    over several workgroups.
 
     Returns (residual_out [M,4,H], layer_input [M,H] or None,
     (values [M,H] u8, scales u8) or None)."""
     tp, M, H = partials.shape
     dev = partials.device
+    ws = workspace(dev) if split else None
     residual_out = _bf16_empty((M, 4, H), dev)
     layer_input = None if pre is None else _bf16_empty((M, H), dev)
     values = scales = None
@@ -211,7 +260,8 @@ def boundary(partials: torch.Tensor, residual, post, comb, pre, norm_weight, nor
         values = torch.empty((M, H), dtype=torch.uint8, device=dev)
         scales = torch.empty(mhcb_mxfp8_scale_bytes(M, H), dtype=torch.uint8, device=dev)
     mhcb_boundary(partials, M * H if tp > 1 else 0, None, residual, post, comb, pre, norm_weight,
-                  residual_out, layer_input, values, scales, M, H, 4, tp, norm_eps, stream)
+                  residual_out, layer_input, values, scales, ws, ws.numel() if ws is not None else 0,
+                  M, H, 4, tp, norm_eps, stream)
     return residual_out, layer_input, ((values, scales) if mxfp8 else None)
 
 
@@ -223,9 +273,10 @@ def boundary_glm(partials, residual, post, comb, hc_fn, scale, base, norm_weight
     residual_out = _bf16_empty((M, 4, H), dev)
     mixes = torch.empty((M, 24), dtype=torch.float32, device=dev)
     layer_input = _bf16_empty((M, H), dev)
+    ws = workspace(dev)
     mhcb_boundary_glm(partials, M * H if tp > 1 else 0, residual, post, comb, hc_fn, scale, base,
-                      norm_weight, residual_out, mixes, layer_input, M, H, 4, tp, rms_eps, hc_eps,
-                      norm_eps, tokens_per_wg, stream)
+                      norm_weight, residual_out, mixes, layer_input, ws, ws.numel(), M, H, 4, tp,
+                      rms_eps, hc_eps, norm_eps, tokens_per_wg, stream)
     return residual_out, mixes, layer_input
 
 
@@ -240,7 +291,7 @@ def mixes(raw_mixes, scale, base, hc_eps, post_mult, sinkhorn_repeat, *, stream=
 
 
 def finalize(gemm2, weights, idx, shared, residual, post, comb, pre, norm_weight, norm_eps, *,
-             two_shot: bool = False, mxfp8: bool = False, workspace=None, stream=None):
+             two_shot: bool = False, mxfp8: bool = False, split: bool = True, stream=None):
     """MoE finalize boundary.  gemm2 [tp, rows, H]; shared [tp, M, H];
     weights / idx [M, top_k] (replicated) or [tp, M, top_k]."""
     tp, rows, H = gemm2.shape
@@ -254,14 +305,11 @@ def finalize(gemm2, weights, idx, shared, residual, post, comb, pre, norm_weight
     if mxfp8:
         values = torch.empty((M, H), dtype=torch.uint8, device=dev)
         scales = torch.empty(mhcb_mxfp8_scale_bytes(M, H), dtype=torch.uint8, device=dev)
-    need = mhcb_finalize_workspace_bytes(M, H, tp, two_shot)
-    if two_shot and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws = workspace(dev, M=M, hidden_size=H, tp=tp, two_shot=True) if (two_shot or split) else None
     mhcb_finalize(gemm2, rows * H, rows, weights, M * top_k if per_rank else 0, idx,
                   M * top_k if per_rank else 0, shared, M * H, residual, post, comb, pre,
-                  norm_weight, residual_out, layer_input, values, scales, two_shot, workspace,
-                  workspace.numel() if workspace is not None else 0, M, H, 4, tp, top_k, norm_eps,
-                  stream)
+                  norm_weight, residual_out, layer_input, values, scales, two_shot, ws,
+                  ws.numel() if ws is not None else 0, M, H, 4, tp, top_k, norm_eps, stream)
     return residual_out, layer_input, ((values, scales) if mxfp8 else None)
 
 
@@ -304,8 +352,10 @@ class Mailbox:
         if mxfp8:
             values = torch.empty((M, H), dtype=torch.uint8, device=dev)
             scales = torch.empty(mhcb_mxfp8_scale_bytes(M, H), dtype=torch.uint8, device=dev)
+        ws = workspace(dev)
         mhcb_boundary(None, 0, self, residual, post, comb, pre, norm_weight, residual_out,
-                      layer_input, values, scales, M, H, 4, self.tp, norm_eps, stream)
+                      layer_input, values, scales, ws, ws.numel(), M, H, 4, self.tp, norm_eps,
+                      stream)
         return residual_out, layer_input, ((values, scales) if mxfp8 else None)
 
     def status_ok(self, stream=None) -> bool:
