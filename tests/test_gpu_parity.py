@@ -277,10 +277,18 @@ def test_moe_finalize_large_m_sampled():
 # ---------------------------------------------------------------------------
 
 def run_glm(g, G):
-    ro, mixes, li = mhc.boundary_glm(dev(g.partials), dev(g.residual), dev(g.post), dev(g.comb),
-                                     dev(g.fn), dev(g.scale), dev(g.base), dev(g.gamma), g.rms_eps,
-                                     g.hc_eps, g.norm_eps, tokens_per_wg=G)
+    """Outputs are pre-filled with NaN so that an element the kernel misses
+    cannot pass on a previous call's bits."""
+    M, H = g.M, g.H
+    ro = torch.full((M, 4, H), float("nan"), dtype=torch.bfloat16, device="cuda")
+    mixes = torch.full((M, 24), float("nan"), dtype=torch.float32, device="cuda")
+    li = torch.full((M, H), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ws = mhc.workspace("cuda")
+    mhc.mhcb_boundary_glm(dev(g.partials), M * H, dev(g.residual), dev(g.post), dev(g.comb),
+                          dev(g.fn), dev(g.scale), dev(g.base), dev(g.gamma), ro, mixes, li, ws,
+                          ws.numel(), M, H, 4, g.tp, g.rms_eps, g.hc_eps, g.norm_eps, G)
     torch.cuda.synchronize()
+    assert mhc.mhcb_workspace_status(ws) == mhc.MHCB_OK
     return u16(ro), host(mixes), u16(li)
 
 

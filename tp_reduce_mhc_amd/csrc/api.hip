@@ -272,8 +272,28 @@ int mhcb_boundary_glm(const uint16_t *partials, int64_t rank_stride, const uint1
     return fail(MHCB_EINVAL, "%s: tokens_per_wg=%d (0, 1, 2 or 4)", fn, tokens_per_wg);
   if (G == 4 && hidden_size > 6144)
     return fail(MHCB_EUNSUPPORTED, "%s: tokens_per_wg=4 needs hidden_size <= 6144", fn);
-  GlmArgs a = {partials, rank_stride, tp, residual, post, comb, hc_fn, scale, base, norm_weight,
-               residual_out, mixes_out, layer_input, M, hidden_size, rms_eps, hc_eps, norm_eps, G};
+  GlmArgs a = {1, hidden_size / kFrag, SyncView{}, partials, rank_stride, tp, residual, post, comb,
+               hc_fn, scale, base, norm_weight, residual_out, mixes_out, layer_input, M,
+               hidden_size, rms_eps, hc_eps, norm_eps, G};
+  // Slices per token group: measured on MI355X (H=6144, tp=8), 4 slices
+  // save about 3 us at M=1 and break even at M=64; larger M is faster
+  // unsplit.  The choice depends on M only (not on tokens_per_wg), so the
+  // results do not depend on tokens_per_wg.
+  if (workspace && M <= kSyncTokens) {
+    const int F = hidden_size / kFrag;
+    int S = g_slices_override > 0 ? g_slices_override : (M <= 64 ? 4 : 1);
+    const int cap = F / kWave;
+    S = S > kMaxSlices ? kMaxSlices : S;
+    S = S > cap ? cap : S;
+    if (S > 1) {
+      int frags = (F + S - 1) / S;
+      frags = (frags + 3) / 4 * 4;
+      a.slices = (F + frags - 1) / frags;
+      a.slice_frags = frags;
+      if (a.slices > 1) a.sync = sync_view(workspace);
+      else a.slice_frags = F;
+    }
+  }
   return launched(launch_boundary_glm(a, stream), fn);
 }
 

@@ -19,6 +19,7 @@
 // load of a token issued before its first use.
 #include "device.h"
 #include "kernels.h"
+#include "sync.h"
 
 namespace mhcb {
 
@@ -128,53 +129,18 @@ __device__ __forceinline__ void stage_routes(const FinalizeView &f, int tp, int 
   __syncthreads();
 }
 
-// The token's sum of squares over all its slices.  Every slice publishes
-// its partial (binary64 bits), arrives on the token's counter, and waits
-// for the barrier generation to move (the last arrival resets the count and
-// bumps the generation: a sense-reversing barrier, reusable by the next
-// call).  All slices then add the partials in slice order, so they agree
-// bit for bit.
-//
-// Every shared word is accessed with device-scope atomics, which are
-// performed at the device's coherence point; ordering them only needs the
-// wave's earlier accesses to have completed (s_waitcnt vmcnt(0), which on
-// CDNA counts stores too), and the partials are read only after the
-// generation load that released the wait has returned.  Device-scope
-// release/acquire fences would instead write back / invalidate the whole L2
-// of the XCD at every arrival and every poll.
-//
-// The wait is bounded; a time-out is counted in the status word and the
-// kernel goes on (every wave always exits).
+// The token's sum of squares over all its slices: every slice publishes
+// its binary64 partial and arrives at the token's barrier; all then add the
+// partials in slice order, so they agree bit for bit (and, the squares of
+// BF16 values being exact, with the unsplit sum).
 __device__ double token_sum(const SyncView &sy, int t, int s, int slices, double local,
                             double *shared) {
   if (threadIdx.x == 0) {
-    char *slot = sy.slots + (int64_t)t * kSyncSlot;
-    uint32_t *count = reinterpret_cast<uint32_t *>(slot);
-    uint32_t *gen = count + 1;
-    uint64_t *part = reinterpret_cast<uint64_t *>(slot + 64);
-    __hip_atomic_store(part + s, __builtin_bit_cast(uint64_t, local), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t g = __hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    wait_vmem();  // the partial has landed at the coherence point
-    const uint32_t arrived =
-        __hip_atomic_fetch_add(count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (arrived == (uint32_t)slices - 1u) {
-      __hip_atomic_store(count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(gen, g + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-      int64_t spins = 0;
-      while (__hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == g) {
-        if (++spins > sy.spin_limit) {
-          atomicAdd(sy.status, 1u);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(2);
-      }
-    }
+    char *slot = token_slot(sy, t);
+    slot_store64(slot, kSlotSum1 + 8 * s, local);
+    token_barrier(sy, t, slices);
     double total = 0.0;
-    for (int q = 0; q < slices; ++q)
-      total += __builtin_bit_cast(double, __hip_atomic_load(part + q, __ATOMIC_RELAXED,
-                                                            __HIP_MEMORY_SCOPE_AGENT));
+    for (int q = 0; q < slices; ++q) total += slot_load64(slot, kSlotSum1 + 8 * q);
     *shared = total;
   }
   __syncthreads();

@@ -18,6 +18,7 @@
 // in fixed order, in place of the page's cluster-wide DSMEM reduction.
 #include "device.h"
 #include "kernels.h"
+#include "sync.h"
 
 namespace mhcb {
 namespace {
@@ -80,11 +81,70 @@ struct GlmShared {
   float part[kMaxThreads / kWave][64];  // per-wave reduce-scatter results
   float mix[G][kMix];                   // GEMV totals of each token
   float pre[G][kStreams];
+  double tot[G];
   double red[(kMaxThreads / kWave) * G];
 };
 
+// Exchanges the per-slice partials of the G tokens of a split workgroup:
+// the GEMV rows sh.mix (FP32) and one binary64 sum per token (`sums`, slot
+// offset `offset`).  Afterwards every slice holds the slice-ordered totals.
+// Contains barriers: every thread of the workgroup calls it.
+template <int G>
+__device__ void exchange(const GlmArgs &a, GlmShared<G> &sh, int t0, int s, double (&sums)[G],
+                         int offset, bool rows) {
+  const int tid = threadIdx.x;
+  if (rows) {
+    for (int i = tid; i < G * kMix; i += blockDim.x) {
+      const int g = i / kMix, k = i % kMix;
+      if (t0 + g < a.M)
+        slot_store32(token_slot(a.sync, t0 + g), kSlotRows + 4 * (s * kMix + k), sh.mix[g][k]);
+    }
+  }
+  if (tid < G && t0 + tid < a.M) slot_store64(token_slot(a.sync, t0 + tid), offset + 8 * s, sums[tid]);
+  wait_vmem();
+  __syncthreads();
+  if (tid == 0) {  // one thread: every arrival of this slice before any wait
+    uint32_t seen[G];
+    bool done[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      done[g] = t0 + g >= a.M || barrier_arrive(a.sync, t0 + g, a.slices, &seen[g]);
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+      if (!done[g]) barrier_wait(a.sync, t0 + g, seen[g]);
+  }
+  __syncthreads();
+  if (rows) {
+    for (int i = tid; i < G * kMix; i += blockDim.x) {
+      const int g = i / kMix, k = i % kMix;
+      if (t0 + g < a.M) {
+        const char *slot = token_slot(a.sync, t0 + g);
+        float v = 0.0f;
+        for (int q = 0; q < a.slices; ++q) v += slot_load32(slot, kSlotRows + 4 * (q * kMix + k));
+        sh.mix[g][k] = v;
+      }
+    }
+  }
+  if (tid < G) {
+    double v = 0.0;
+    if (t0 + tid < a.M) {
+      const char *slot = token_slot(a.sync, t0 + tid);
+      for (int q = 0; q < a.slices; ++q) v += slot_load64(slot, offset + 8 * q);
+    }
+    sh.tot[tid] = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int g = 0; g < G; ++g) sums[g] = sh.tot[g];
+  __syncthreads();
+}
+
 // KB = hc_fn rows per pass (24 for G <= 2; 12 for G = 4 to bound registers);
 // MAXT = the workgroup size bound (768 for G = 4 leaves 168 VGPRs a lane).
+// Grid (slices, ceil(M/G)) when split, else (ceil(M/G)): workgroup (s, grp)
+// covers fragments [s * slice_frags, (s + 1) * slice_frags) of tokens
+// grp*G .. grp*G + G - 1; the slices exchange their partial GEMV rows and
+// sums of squares through the workspace.
 template <int G, int KB, int MAXT>
 __global__ void __launch_bounds__(MAXT)
 glm_kernel(const GlmArgs a) {
@@ -96,9 +156,13 @@ glm_kernel(const GlmArgs a) {
 
   const int H = a.H, F = H / kFrag, tid = threadIdx.x;
   const int lane = tid & (kWave - 1), wave = tid / kWave, waves = blockDim.x / kWave;
-  const int t0 = blockIdx.x * G;
-  const bool valid = tid < F;
-  const int64_t col = valid ? (int64_t)tid * kFrag : 0;
+  const int s = a.slices > 1 ? blockIdx.x : 0;
+  const int grp = a.slices > 1 ? blockIdx.y : blockIdx.x;
+  const int t0 = grp * G;
+  const int first = a.slices > 1 ? s * a.slice_frags : 0;
+  const int last = a.slices > 1 ? min(F, first + a.slice_frags) : F;
+  const bool valid = first + tid < last;
+  const int64_t col = valid ? (int64_t)(first + tid) * kFrag : 0;
 
   // a1 + a2 for the G tokens: y[g][j] packed BF16, sum of y^2 per token.
   u32x4 y[G][kStreams];
@@ -110,8 +174,8 @@ glm_kernel(const GlmArgs a) {
     const int tt = t < a.M ? t : a.M - 1;
     u32x4 res[kStreams];
 #pragma unroll
-    for (int s = 0; s < kStreams; ++s)
-      res[s] = load_stream(a.residual + ((int64_t)tt * kStreams + s) * H + col);
+    for (int q = 0; q < kStreams; ++q)
+      res[q] = load_stream(a.residual + ((int64_t)tt * kStreams + q) * H + col);
     float s8[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) s8[e] = 0.0f;
@@ -187,20 +251,24 @@ glm_kernel(const GlmArgs a) {
     if ((N == 64 || (lane & 1) == 0) && idx < V) sh.part[wave][idx] = total;
     __syncthreads();
     if (tid < V) {
-      float s = 0.0f;
-      for (int w = 0; w < waves; ++w) s += sh.part[w][tid];
-      sh.mix[tid / KB][pass * KB + tid % KB] = s;
+      float v = 0.0f;
+      for (int w = 0; w < waves; ++w) v += sh.part[w][tid];
+      sh.mix[tid / KB][pass * KB + tid % KB] = v;
     }
     __syncthreads();
   }
 
   // g_24 and rstd; raw mixes out; pre_j = sigmoid(mix_j * scale0 + base_j) + hc_eps.
   block_sum<double, G>(ssy, sh.red);
-  if (tid < G * kMix) {
-    const int g = tid / kMix, k = tid % kMix, t = t0 + g;
-    const float rstd = (float)(1.0 / __builtin_sqrt((double)(float)ssy[g] / (4.0 * H) + (double)a.rms_eps));
+  if (a.slices > 1) exchange<G>(a, sh, t0, s, ssy, kSlotSum1, true);
+  for (int i = tid; i < G * kMix; i += blockDim.x) {  // a workgroup may have fewer threads
+    const int g = i / kMix, k = i % kMix, t = t0 + g;
+    double total = 0.0;
+#pragma unroll
+    for (int q = 0; q < G; ++q) total = q == g ? ssy[q] : total;
+    const float rstd = (float)(1.0 / __builtin_sqrt((double)(float)total / (4.0 * H) + (double)a.rms_eps));
     const float mix = sh.mix[g][k] * rstd;
-    if (t < a.M) a.mixes_out[(int64_t)t * kMix + k] = mix;
+    if (t < a.M && s == 0) a.mixes_out[(int64_t)t * kMix + k] = mix;
     if (k < kStreams) sh.pre[g][k] = sigmoid(__builtin_fmaf(mix, a.scale[0], a.base[k])) + a.hc_eps;
   }
   __syncthreads();
@@ -232,6 +300,7 @@ glm_kernel(const GlmArgs a) {
     }
   }
   block_sum<double, G>(pss, sh.red);
+  if (a.slices > 1) exchange<G>(a, sh, t0, s, pss, kSlotSum2, false);
   float gam[8];
   unpack8(load_cached(a.gamma + col), gam);
 #pragma unroll
@@ -303,10 +372,11 @@ mixes_kernel(const float *mixes, const float *scale, const float *base, float *p
 }  // namespace
 
 hipError_t launch_boundary_glm(const GlmArgs &a, hipStream_t stream) {
-  const int F = a.H / kFrag;
+  const int F = a.slices > 1 ? a.slice_frags : a.H / kFrag;
   const int threads = (F + kWave - 1) / kWave * kWave;
   const int G = a.tokens_per_wg;
-  dim3 grid((a.M + G - 1) / G), block(threads);
+  const int groups = (a.M + G - 1) / G;
+  dim3 grid = a.slices > 1 ? dim3(a.slices, groups) : dim3(groups), block(threads);
   switch (G) {
     case 1: hipLaunchKernelGGL((glm_kernel<1, 24, 1024>), grid, block, 0, stream, a); break;
     case 2: hipLaunchKernelGGL((glm_kernel<2, 24, 1024>), grid, block, 0, stream, a); break;

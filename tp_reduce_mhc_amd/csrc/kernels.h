@@ -35,14 +35,17 @@ struct FinalizeView {
 };
 
 // Cross-workgroup state of the token-split kernels, at the start of the
-// caller's workspace: a 256-byte header (status word), then one 256-byte
-// slot per token -- arrival count (offset 0), barrier generation (4), the
-// slices' partial sums of squares as binary64 bits (64 + 8 s) -- so that
-// different tokens' atomics never share a cache line or memory channel.
+// caller's workspace: a 256-byte header (status word), then one slot per
+// token, so that different tokens' atomics never share a cache line:
+//   +0    arrival count          +4   barrier generation
+//   +64   [kMaxSlices] binary64  first partial sum per slice
+//   +192  [kMaxSlices] binary64  second partial sum per slice
+//   +320  [kMaxSlices][24] FP32  partial GEMV rows per slice (GLM)
 // Zero-filled once; every call leaves the counts at zero.
 constexpr int kSyncTokens = 1024;  // tokens a split call may have
 constexpr int kMaxSlices = 16;     // workgroups a token may be split over
-constexpr int kSyncSlot = 256;     // bytes per token
+constexpr int kSyncSlot = 2048;    // bytes per token
+constexpr int kSlotSum1 = 64, kSlotSum2 = 192, kSlotRows = 320;
 constexpr int64_t kSyncBytes = 256 + (int64_t)kSyncSlot * kSyncTokens;
 
 struct SyncView {
@@ -92,6 +95,9 @@ hipError_t launch_quant_mxfp8(const uint16_t *x, uint8_t *values, uint8_t *scale
                               hipStream_t stream);
 
 struct GlmArgs {
+  int slices;        // workgroups per token group (1 = no cross-workgroup sync)
+  int slice_frags;   // fragments per workgroup when slices > 1
+  SyncView sync;
   const uint16_t *partials;
   int64_t rank_stride;
   int tp;
