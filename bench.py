@@ -279,6 +279,25 @@ def bench_glm(torch, mhc, g, steps, warmup):
     return ms, per_set
 
 
+def copy_bandwidth(torch, nbytes=1 << 30, reps=20):
+    """Achieved GB/s (read + write bytes) of a plain device-to-device copy
+    of `nbytes`: the practical HBM ceiling next to the 8 TB/s peak."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / reps
+    del src, dst
+    return round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
+
+
 def entry(ms, nbytes, M):
     return {"us_per_call": round(ms * 1e3, 3), "GBps": round(nbytes / (ms * 1e-3) / 1e9, 1),
             "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -368,6 +387,9 @@ def main():
                          "traffic": traffic, "kernel": "boundary_kernel (delayed mHC, tp 8)",
                          "algorithmic_bytes_per_launch": int(nbytes)},
         })
+        if not only:
+            result["roofline"]["measured_copy_GBps"] = copy_bandwidth(torch)
+            log(f"device copy: {result['roofline']['measured_copy_GBps']} GB/s")
         if not args.no_cpu_baseline and not only:
             log("cpu baseline (oracle)")
             result["cpu_baseline"] = cpu_baseline(b)
