@@ -206,10 +206,10 @@ boundary_kernel(const BoundaryArgs a) {
   for (int i = 0; i < TRIPS; ++i) {
     if constexpr (TP > 0 && SRC != Source::kFinalize) {
 #pragma unroll
-      for (int r = 0; r < TP; ++r) {
-        const uint16_t *p = src + r * rs + col[i];
-        part[i][r] = SRC == Source::kMailbox ? load_agent(p) : load_stream(p);
-      }
+      // Mailbox: a plain streaming read first; a fragment still holding the
+      // sentinel is re-read at device scope by poll().  (In stream order the
+      // producer's kernel boundary has already made its stores visible.)
+      for (int r = 0; r < TP; ++r) part[i][r] = load_stream(src + r * rs + col[i]);
     }
 #pragma unroll
     for (int q = 0; q < kStreams; ++q)
@@ -236,18 +236,24 @@ boundary_kernel(const BoundaryArgs a) {
           accumulate(sum, finalize_fragment(a.fin, srow + r * a.fin.top_k, sw + r * a.fin.top_k, r,
                                             t, H, col[i]));
       } else if constexpr (TP > 0) {
+        if constexpr (SRC == Source::kMailbox) {
+          // Slow path only for fragments that are not all there yet.
+          bool dirty = false;
 #pragma unroll
-        for (int r = 0; r < TP; ++r) {
-          u32x4 w = part[i][r];
-          if constexpr (SRC == Source::kMailbox) w = poll(src + r * rs + col[i], w, a.mailbox);
-          accumulate(sum, w);
+          for (int r = 0; r < TP; ++r)
+            dirty |= has_sentinel(part[i][r][0]) | has_sentinel(part[i][r][1]) |
+                     has_sentinel(part[i][r][2]) | has_sentinel(part[i][r][3]);
+          if (dirty) {
+            for (int r = 0; r < TP; ++r) part[i][r] = poll(src + r * rs + col[i], part[i][r], a.mailbox);
+          }
         }
+#pragma unroll
+        for (int r = 0; r < TP; ++r) accumulate(sum, part[i][r]);
       } else {
         for (int r = 0; r < tp; ++r) {
           const uint16_t *p = src + r * rs + col[i];
-          u32x4 w;
-          if constexpr (SRC == Source::kMailbox) w = poll(p, load_agent(p), a.mailbox);
-          else w = load_stream(p);
+          u32x4 w = load_stream(p);
+          if constexpr (SRC == Source::kMailbox) w = poll(p, w, a.mailbox);
           accumulate(sum, w);
         }
       }
@@ -455,8 +461,10 @@ mailbox_init_kernel(MailboxView mb, int64_t frags) {
 }
 
 // Publishes ranks [rank_begin, rank_begin + rank_count) of token t
-// (blockIdx.y) into generation NEXT: sanitized fragments stored at device
-// scope, then ACTIVE = NEXT (_PublishDeviceKernel.kernel).
+// (blockIdx.y) into generation NEXT: sanitized fragments, then ACTIVE = NEXT
+// (_PublishDeviceKernel.kernel).  The rank loads of a fragment are issued
+// together; the 16-byte stores become visible device-wide at the latest when
+// the kernel ends, which a concurrent consumer's bounded poll waits out.
 __global__ void __launch_bounds__(256)
 publish_kernel(MailboxView mb, int tp, int H, const uint16_t *partials, int64_t rank_stride,
                int rank_begin, int rank_count) {
@@ -466,10 +474,18 @@ publish_kernel(MailboxView mb, int tp, int H, const uint16_t *partials, int64_t 
                                                    __HIP_MEMORY_SCOPE_AGENT) % 3u;
   if (fr < F) {
     const int64_t col = (int64_t)fr * kFrag;
-    for (int q = 0; q < rank_count; ++q) {
-      const int r = rank_begin + q;
-      const u32x4 w = sanitize4(load_stream(partials + q * rank_stride + (int64_t)t * H + col));
-      store_agent(mb.slots + (((int64_t)gen * tp + r) * mb.capacity + t) * H + col, w);
+    for (int q0 = 0; q0 < rank_count; q0 += 8) {
+      u32x4 w[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (q0 + i < rank_count)
+          w[i] = load_stream(partials + (q0 + i) * rank_stride + (int64_t)t * H + col);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (q0 + i >= rank_count) break;
+        const int r = rank_begin + q0 + i;
+        store_stream(mb.slots + (((int64_t)gen * tp + r) * mb.capacity + t) * H + col, sanitize4(w[i]));
+      }
     }
   }
   if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0)
