@@ -18,7 +18,6 @@ from __future__ import annotations
 
 import argparse
 import hashlib
-import glob
 import json
 import os
 import sys
@@ -64,10 +63,15 @@ def bytes_glm(M, H, tp):
     return M * (tp * 2 * H + 9 * 2 * H + 80 + 96) + 24 * 4 * H * 2 + 2 * H + 27 * 4
 
 
+# The files the headline kernel (boundary_kernel) is compiled from: a change
+# to any of them invalidates the committed counter summary.
+HEADLINE_SOURCES = ("boundary.hip", "device.h", "kernels.h", "sync.h")
+
+
 def source_hash():
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "tp_reduce_mhc_amd", "csrc", "*"))):
-        h.update(open(p, "rb").read())
+    for name in HEADLINE_SOURCES:
+        h.update(open(os.path.join(ROOT, "tp_reduce_mhc_amd", "csrc", name), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -308,21 +312,21 @@ def entry(ms, nbytes, M):
 # CPU baseline: the oracle on a bounded sample of the headline workload
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(b, budget_s=1.5):
+def cpu_baseline(b, cpu_seconds=12.0, wall_cap_s=20.0):
+    """The oracle on the host's cores, repeated on the headline workload until
+    about `cpu_seconds` of CPU work (wall time x threads) has been spent."""
     import oracle
     threads = oracle.default_threads()
     oracle.boundary(b.partials[:, :2], b.residual[:2], b.post[:2], b.comb[:2], b.pre[:2], b.gamma,
                     b.norm_eps, threads=1)  # load + warm
     reps, times = 0, []
-    t_end = time.perf_counter() + budget_s
-    while reps < 3 or time.perf_counter() < t_end:
+    start = time.perf_counter()
+    while reps < 3 or (sum(times) * threads < cpu_seconds and time.perf_counter() - start < wall_cap_s):
         t0 = time.perf_counter()
         oracle.boundary(b.partials, b.residual, b.post, b.comb, b.pre, b.gamma, b.norm_eps,
                         threads=threads)
         times.append(time.perf_counter() - t0)
         reps += 1
-        if reps >= 50:
-            break
     sec = float(np.median(times))
     nbytes = bytes_delayed(b.M, b.H, b.tp)
     return {"value": round(nbytes / sec / 1e9, 3), "unit": "GB/s", "cores": threads,
