@@ -357,7 +357,9 @@ int mhcb_finalize(const uint16_t *gemm2_permuted, int64_t gemm2_rank_stride, int
     if ((rc = check_workspace(fn, workspace, workspace_bytes, kSyncBytes))) return rc;
     a.source = Source::kFinalize;
     a.fin = f;
-    choose_slices(a, workspace, 2 * device_cus(), kMaxSlices);
+    // One workgroup per compute unit: measured on MI355X (H=5120, tp=4,
+    // top_k=8, M=64), 4 slices take 13.1 us, 2 take 14.1, 8 take 15.5.
+    choose_slices(a, workspace, device_cus(), kMaxSlices);
     return launched(launch_boundary(a, stream), fn);
   }
   const int64_t need = mhcb_workspace_bytes(M, hidden_size, tp, 1);

@@ -114,6 +114,48 @@ __device__ __forceinline__ u32x4 finalize_fragment(const FinalizeView &f, const 
   return sanitize4(pack8(acc));
 }
 
+// finalize_fragment for a compile-time rank count and top_k <= 8: every
+// expert row of every rank is loaded before the first multiply, so the
+// token waits for one round of gathers instead of one per rank.  `shared`
+// holds the ranks' shared-expert fragments, loaded earlier.
+template <int TP>
+__device__ __forceinline__ void finalize_fixed(const FinalizeView &f, const int32_t *srow,
+                                               const float *sw, const u32x4 (&shared)[TP], int H,
+                                               int64_t col, float (&sum)[8]) {
+  u32x4 rows[TP][8];
+  bool ok[TP][8];
+#pragma unroll
+  for (int r = 0; r < TP; ++r) {
+    const uint16_t *g = f.gemm2 + r * f.g_stride + col;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int32_t row = k < f.top_k ? srow[r * f.top_k + k] : -1;
+      ok[r][k] = row >= 0 && row < f.rows;
+      rows[r][k] = ok[r][k] ? load_stream(g + (int64_t)row * H) : u32x4{0, 0, 0, 0};
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < TP; ++r) {
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if (!ok[r][k]) continue;
+      const float w = sw[r * f.top_k + k];
+      float v[8];
+      unpack8(rows[r][k], v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(v[e], w, acc[e]);
+    }
+    float sh[8];
+    unpack8(shared[r], sh);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = acc[e] + sh[e];
+    accumulate(sum, sanitize4(pack8(acc)));
+  }
+}
+
 // Stages every rank's (row, weight) routes of token t in LDS; a route whose
 // row is -1 gets weight 0 as on the page (it is skipped anyway).
 __device__ __forceinline__ void stage_routes(const FinalizeView &f, int tp, int t, int32_t *srow,
@@ -123,8 +165,9 @@ __device__ __forceinline__ void stage_routes(const FinalizeView &f, int tp, int 
     const int r = i / f.top_k, k = i % f.top_k;
     const int64_t e = (int64_t)t * f.top_k + k;
     const int32_t row = f.idx[r * f.i_stride + e];
+    const float w = f.weights[r * f.w_stride + e];  // not behind the index load
     srow[i] = row;
-    sw[i] = row == -1 ? 0.0f : f.weights[r * f.w_stride + e];
+    sw[i] = row == -1 ? 0.0f : w;
   }
   __syncthreads();
 }
@@ -184,8 +227,6 @@ boundary_kernel(const BoundaryArgs a) {
                                       __HIP_MEMORY_SCOPE_AGENT) % 3u;  // stays inside the slots
     rs = (int64_t)a.mailbox.capacity * H;
     src = a.mailbox.slots + (int64_t)gen * tp * rs + (int64_t)t * H;
-  } else {
-    stage_routes(a.fin, tp, t, srow, sw);
   }
 
   int64_t col[TRIPS];
@@ -204,7 +245,11 @@ boundary_kernel(const BoundaryArgs a) {
   u32x4 part[TRIPS][kHeld];
 #pragma unroll
   for (int i = 0; i < TRIPS; ++i) {
-    if constexpr (TP > 0 && SRC != Source::kFinalize) {
+    if constexpr (TP > 0 && SRC == Source::kFinalize) {
+#pragma unroll
+      for (int r = 0; r < TP; ++r)
+        part[i][r] = load_stream(a.fin.shared + r * a.fin.s_stride + (int64_t)t * H + col[i]);
+    } else if constexpr (TP > 0) {
 #pragma unroll
       // Mailbox: a plain streaming read first; a fragment still holding the
       // sentinel is re-read at device scope by poll().  (In stream order the
@@ -216,6 +261,9 @@ boundary_kernel(const BoundaryArgs a) {
       res[i][q] = load_stream(a.residual + ((int64_t)t * kStreams + q) * H + col[i]);
     gam[i] = norm ? load_cached(a.gamma + col[i]) : u32x4{0, 0, 0, 0};
   }
+  // Finalize: the routes are staged while those loads are in flight (the
+  // workgroup barrier inside waits for LDS only).
+  if constexpr (SRC == Source::kFinalize) stage_routes(a.fin, tp, t, srow, sw);
   // The token's mixes are scalar loads; keep them behind the vector loads so
   // that waiting for them does not delay the stream.
   __builtin_amdgcn_sched_barrier(0);
@@ -231,7 +279,9 @@ boundary_kernel(const BoundaryArgs a) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) sum[e] = 0.0f;
     if (valid[i]) {
-      if constexpr (SRC == Source::kFinalize) {
+      if constexpr (SRC == Source::kFinalize && TP > 0) {
+        finalize_fixed<TP>(a.fin, srow, sw, part[i], H, col[i], sum);
+      } else if constexpr (SRC == Source::kFinalize) {
         for (int r = 0; r < tp; ++r)
           accumulate(sum, finalize_fragment(a.fin, srow + r * a.fin.top_k, sw + r * a.fin.top_k, r,
                                             t, H, col[i]));
@@ -370,16 +420,27 @@ boundary_kernel(const BoundaryArgs a) {
 template <int TRIPS, Source SRC>
 hipError_t launch_tp(const BoundaryArgs &a, int threads, hipStream_t stream) {
   dim3 grid = a.slices > 1 ? dim3(a.slices, a.M) : dim3(a.M), block(threads);
-  if (SRC == Source::kFinalize) {
-    hipLaunchKernelGGL((boundary_kernel<TRIPS, 0, SRC>), grid, block, 0, stream, a);
-    return hipGetLastError();
-  }
-  switch (a.tp) {
-    case 1: hipLaunchKernelGGL((boundary_kernel<TRIPS, 1, SRC>), grid, block, 0, stream, a); break;
-    case 2: hipLaunchKernelGGL((boundary_kernel<TRIPS, 2, SRC>), grid, block, 0, stream, a); break;
-    case 4: hipLaunchKernelGGL((boundary_kernel<TRIPS, 4, SRC>), grid, block, 0, stream, a); break;
-    case 8: hipLaunchKernelGGL((boundary_kernel<TRIPS, 8, SRC>), grid, block, 0, stream, a); break;
-    default: hipLaunchKernelGGL((boundary_kernel<TRIPS, 0, SRC>), grid, block, 0, stream, a); break;
+  if constexpr (SRC == Source::kFinalize) {
+    // All 36 gathers in flight at once need one fragment per thread.
+    if (TRIPS == 1 && a.tp == 4 && a.fin.top_k <= 8)
+      hipLaunchKernelGGL((boundary_kernel<1, 4, SRC>), grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL((boundary_kernel<TRIPS, 0, SRC>), grid, block, 0, stream, a);
+  } else {
+    switch (a.tp) {
+      case 1: hipLaunchKernelGGL((boundary_kernel<TRIPS, 1, SRC>), grid, block, 0, stream, a); break;
+      case 2: hipLaunchKernelGGL((boundary_kernel<TRIPS, 2, SRC>), grid, block, 0, stream, a); break;
+      case 4: hipLaunchKernelGGL((boundary_kernel<TRIPS, 4, SRC>), grid, block, 0, stream, a); break;
+      case 8:
+        // Four trips of eight held mailbox ranks would spill; that case takes
+        // the runtime-tp kernel.
+        if constexpr (TRIPS == 4 && SRC == Source::kMailbox)
+          hipLaunchKernelGGL((boundary_kernel<TRIPS, 0, SRC>), grid, block, 0, stream, a);
+        else
+          hipLaunchKernelGGL((boundary_kernel<TRIPS, 8, SRC>), grid, block, 0, stream, a);
+        break;
+      default: hipLaunchKernelGGL((boundary_kernel<TRIPS, 0, SRC>), grid, block, 0, stream, a); break;
+    }
   }
   return hipGetLastError();
 }
