@@ -316,6 +316,50 @@ def test_glm_boundary_matches_oracle(M):
             assert_bits_equal(li, first[2], f"G={G} layer_input vs G=1")
 
 
+def check_glm_against_oracle(g, ro, mixes, li, what):
+    ro_ref, mix_ref, li_ref, pre_ref = oracle.boundary_glm(
+        g.partials, g.residual, g.post, g.comb, g.fn, g.scale, g.base, g.gamma, g.rms_eps,
+        g.hc_eps, g.norm_eps, threads=8)
+    assert_bits_equal(ro, ro_ref, f"residual_out {what}")
+    err = np.abs(mixes - mix_ref)
+    assert (err <= 1e-5 * (np.abs(mix_ref) + 1)).all(), f"mixes {what}: max err {err.max()}"
+    one, two = glm_layer_input_check(li, li_ref, ro_ref, pre_ref.astype(np.float64),
+                                     glm_pre(mixes, g.scale, g.base, g.hc_eps))
+    print(f"[gpu]   {what}: layer_input 1-ulp {one}, tie 2-ulp {two}", flush=True)
+
+
+@pytest.mark.parametrize("M,H,tp", [(1, 6144, 8), (17, 6144, 8), (40, 2048, 3), (33, 512, 8),
+                                    (16, 8192, 8), (5, 1024, 1), (3, 64, 2)])
+def test_glm_tiles_match_oracle(M, H, tp):
+    """16-token matrix-core tiles (tokens_per_wg=16): ragged last tiles,
+    runtime and fixed rank counts, one to four steps per wave."""
+    g = synth.glm(M, H=H, tp=tp)
+    print(f"[gpu] {g.name} tiles", flush=True)
+    ro, mixes, li = run_glm(g, 16)
+    check_glm_against_oracle(g, ro, mixes, li, "tiles")
+
+
+@pytest.mark.parametrize("S", [1, 3, 16])
+def test_glm_tiles_any_slice_count(S):
+    g = synth.glm(20, H=2048, tp=8)
+    prev = mhc.mhcb_set_token_slices(S)
+    try:
+        print(f"[gpu] {g.name} tiles, slices {S}", flush=True)
+        ro, mixes, li = run_glm(g, 16)
+    finally:
+        mhc.mhcb_set_token_slices(prev)
+    check_glm_against_oracle(g, ro, mixes, li, f"tiles S={S}")
+
+
+def test_glm_tiles_more_tokens_than_one_launch():
+    """M above the per-launch token limit of the split kernels (1024): the
+    call is issued as several launches."""
+    g = synth.glm(1100, H=256, tp=2)
+    print(f"[gpu] {g.name} tiles", flush=True)
+    ro, mixes, li = run_glm(g, 16)
+    check_glm_against_oracle(g, ro, mixes, li, "tiles M=1100")
+
+
 def test_glm_large_m_sampled():
     """M = 512 (H=6144, tp=8), the auto tokens-per-workgroup choice."""
     g = synth.glm(512)

@@ -39,6 +39,7 @@ constexpr int kMaxHiddenGlm = 8192;
 constexpr int kMaxTp = 64;
 constexpr int kMaxRoutes = 1024;
 constexpr int64_t kDefaultSpin = 1 << 20;
+constexpr int kGlmTileMinM = 128;  // automatic matrix-core tiles from this M
 
 // Checks shared by the boundary variants ([DSV41] AllReduceMHC._check and
 // _consumer, _LamportMHCDeviceKernel.__init__).
@@ -267,14 +268,49 @@ int mhcb_boundary_glm(const uint16_t *partials, int64_t rank_stride, const uint1
       !aligned(mixes_out, 4))
     return fail(MHCB_EALIGN, "%s: partials/hc_fn must be 16-byte aligned, rank_stride %% 8 == 0", fn);
   int G = tokens_per_wg;
-  if (G == 0) G = M <= 64 ? 1 : (M <= 256 || hidden_size > 6144 ? 2 : 4);
-  if (G != 1 && G != 2 && G != 4)
-    return fail(MHCB_EINVAL, "%s: tokens_per_wg=%d (0, 1, 2 or 4)", fn, tokens_per_wg);
+  // Measured on MI355X (H=6144, tp=8): one token per workgroup is fastest up
+  // to M=256 (24.6 us vs 28.8 us with two), two beyond (M=512: 37.0 us vs
+  // 47.2 us with one and 48.5 us with four); with a workspace, 16-token
+  // matrix-core tiles from kGlmTileMinM tokens.
+  if (G == 0) G = workspace && M >= kGlmTileMinM ? kGlmTileTokens : (M <= 256 ? 1 : 2);
+  if (G != 1 && G != 2 && G != 4 && G != kGlmTileTokens)
+    return fail(MHCB_EINVAL, "%s: tokens_per_wg=%d (0, 1, 2, 4 or 16)", fn, tokens_per_wg);
   if (G == 4 && hidden_size > 6144)
     return fail(MHCB_EUNSUPPORTED, "%s: tokens_per_wg=4 needs hidden_size <= 6144", fn);
+  if (G == kGlmTileTokens && !workspace)
+    return fail(MHCB_EINVAL, "%s: tokens_per_wg=16 needs a workspace", fn);
   GlmArgs a = {1, hidden_size / kFrag, SyncView{}, partials, rank_stride, tp, residual, post, comb,
                hc_fn, scale, base, norm_weight, residual_out, mixes_out, layer_input, M,
                hidden_size, rms_eps, hc_eps, norm_eps, G};
+  if (G == kGlmTileTokens) {
+    // Slices of at most 64 fragments (four waves of four steps), 16 unless
+    // overridden; launches of at most kSyncTokens tokens.
+    const int F = hidden_size / kFrag;
+    int S = g_slices_override > 0 ? g_slices_override : kMaxSlices;
+    S = S > kMaxSlices ? kMaxSlices : S;
+    S = S > F / 4 ? F / 4 : S;
+    S = S < (F + 63) / 64 ? (F + 63) / 64 : S;
+    S = S < 1 ? 1 : S;
+    int frags = (F + S - 1) / S;
+    frags = (frags + 3) / 4 * 4;
+    a.slices = (F + frags - 1) / frags;
+    a.slice_frags = frags;
+    a.sync = sync_view(workspace);
+    const int64_t H = hidden_size;
+    for (int c = 0; c < M; c += kSyncTokens) {
+      GlmArgs b = a;
+      b.M = M - c < kSyncTokens ? M - c : kSyncTokens;
+      b.partials = partials + c * H;
+      b.residual = residual + c * kStreams * H;
+      b.post = post + (int64_t)c * kStreams;
+      b.comb = comb + (int64_t)c * kStreams * kStreams;
+      b.residual_out = residual_out + c * kStreams * H;
+      b.mixes_out = mixes_out + (int64_t)c * kMix;
+      b.layer_input = layer_input + c * H;
+      if ((rc = launched(launch_boundary_glm_tile(b, stream), fn))) return rc;
+    }
+    return ok();
+  }
   // Slices per token group: measured on MI355X (H=6144, tp=8), 4 slices
   // save about 3 us at M=1 and break even at M=64; larger M is faster
   // unsplit.  The choice depends on M only (not on tokens_per_wg), so the

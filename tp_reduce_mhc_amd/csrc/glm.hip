@@ -316,6 +316,375 @@ glm_kernel(const GlmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Token tiles: the prenorm GEMV of 16 tokens on the matrix cores.
+//
+// Workgroup (s, grp) takes tokens grp*16 .. grp*16+15 over the fragments
+// [s * sf, (s + 1) * sf) of their columns (sf = slice_frags).  The
+// streaming steps (rank sum, post-mix, residual_out, collapse, layer_input)
+// put consecutive threads on consecutive fragments of a token, so every
+// load and store is a contiguous run.  The post-mixed streams also go to
+// LDS, from where the GEMV reads them as the A operand of
+// v_mfma_f32_16x16x32_bf16: a wave step covers 16 tokens (rows) x 4
+// fragments (32 columns, K) of one stream, lane l taking token l % 16 at
+// fragment l / 16.  The B operand is hc_fn: lane l loads row l % 16 (and
+// 16 + l % 16 for the tile of rows 16..23) at the same fragment, so each
+// hc_fn fragment is read once per 16 tokens.  The 16 x 24 partial GEMV and
+// the sums of squares are added across waves in LDS and across slices
+// through the workspace, with one cross-workgroup barrier per tile (the
+// slot of its first token) for the mixes and one for the RMSNorm sum.
+// ---------------------------------------------------------------------------
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTile = 16;              // tokens per tile
+constexpr int kTileThreads = 256;      // at most; fewer for narrow slices
+constexpr int kTileWaves = kTileThreads / kWave;
+constexpr int kTileMaxFrags = 64;      // fragments per slice
+
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+struct TileShared {
+  float post[kTile][kStreams];
+  float comb[kTile][kStreams * kStreams];
+  float part[kTileWaves][kTile][kMix];  // per-wave GEMV partials
+  float mix[kTile][kMix];
+  float pre[kTile][kStreams];
+  double tot[kTile];
+};
+
+// Dynamic LDS of a tile workgroup: the post-mixed streams [tok][j*sf + f]
+// (token rows padded by 16 bytes so that the 16 rows of an MFMA read fall in
+// distinct banks), then the per-fragment sums of squares [tok][f].
+__host__ __device__ inline int tile_row_words(int sf) { return kStreams * sf + 1; }
+__host__ __device__ inline size_t tile_ys_bytes(int sf) {
+  return (size_t)kTile * tile_row_words(sf) * 16;
+}
+__host__ __device__ inline size_t tile_dyn_bytes(int sf) {
+  return tile_ys_bytes(sf) + (size_t)kTile * sf * 8;
+}
+
+__device__ __forceinline__ uint64_t slot_load_u64(const char *slot, int offset) {
+  return __hip_atomic_load(reinterpret_cast<const uint64_t *>(slot + offset), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void slot_store_u64(char *slot, int offset, uint64_t v) {
+  __hip_atomic_store(reinterpret_cast<uint64_t *>(slot + offset), v, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Publishes this slice's per-token sums sh.tot (and, with `rows`, the GEMV
+// partials in sh.mix), waits at the tile's barrier, and leaves the
+// slice-ordered totals in sh.tot (and sh.mix).  A thread fetches all the
+// slices' values of its (token, row) pairs with independent loads, then adds
+// them in slice order.  Every thread calls it.
+__device__ void tile_exchange(const GlmArgs &a, TileShared &sh, int t0, int s, int offset,
+                              bool rows) {
+  const int tid = threadIdx.x, nt = blockDim.x, S = a.slices;
+  const int valid = min(kTile, a.M - t0);
+  constexpr int kPairs = kMix / 2;  // a slice's 24 rows as 8-byte words
+  if (rows) {
+    for (int e = tid; e < valid * kPairs; e += nt) {
+      const int tok = e / kPairs, k = 2 * (e % kPairs);
+      const uint64_t w = (uint64_t)__builtin_bit_cast(uint32_t, sh.mix[tok][k]) |
+                         ((uint64_t)__builtin_bit_cast(uint32_t, sh.mix[tok][k + 1]) << 32);
+      slot_store_u64(token_slot(a.sync, t0 + tok), kSlotRows + 4 * (s * kMix + k), w);
+    }
+  }
+  if (tid < valid) slot_store64(token_slot(a.sync, t0 + tid), offset + 8 * s, sh.tot[tid]);
+  wait_vmem();
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t seen;
+    if (!barrier_arrive(a.sync, t0, S, &seen)) barrier_wait(a.sync, t0, seen);
+  }
+  __syncthreads();
+  // Work items: valid * 12 row pairs (with rows), then valid sums.
+  const int row_items = rows ? valid * kPairs : 0;
+  for (int e = tid; e < row_items + valid; e += nt) {
+    const bool is_row = e < row_items;
+    const int tok = is_row ? e / kPairs : e - row_items;
+    const int off = is_row ? kSlotRows + 8 * (e % kPairs) : offset;
+    const int step = is_row ? 4 * kMix : 8;  // bytes between slices
+    const char *slot = token_slot(a.sync, t0 + tok);
+    uint64_t w[kMaxSlices];
+#pragma unroll
+    for (int q = 0; q < kMaxSlices; ++q) w[q] = q < S ? slot_load_u64(slot, off + q * step) : 0;
+    if (is_row) {
+      float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+      for (int q = 0; q < kMaxSlices; ++q) {
+        if (q >= S) break;
+        lo += __builtin_bit_cast(float, (uint32_t)w[q]);
+        hi += __builtin_bit_cast(float, (uint32_t)(w[q] >> 32));
+      }
+      const int k = 2 * (e % kPairs);
+      sh.mix[tok][k] = lo;
+      sh.mix[tok][k + 1] = hi;
+    } else {
+      double v = 0.0;
+#pragma unroll
+      for (int q = 0; q < kMaxSlices; ++q) {
+        if (q >= S) break;
+        v += __builtin_bit_cast(double, w[q]);
+      }
+      sh.tot[tok] = v;
+    }
+  }
+  __syncthreads();
+}
+
+// sh.tot[tok] = sum over f < sf of item[tok][f], in fragment order.
+__device__ __forceinline__ void tile_item_sums(TileShared &sh, const double *item, int sf) {
+  __syncthreads();
+  if (threadIdx.x < kTile) {
+    double v = 0.0;
+    for (int f = 0; f < sf; ++f) v += item[threadIdx.x * sf + f];
+    sh.tot[threadIdx.x] = v;
+  }
+  __syncthreads();
+}
+
+// hc_fn B operands of one 4-fragment chunk for lane (i, q): rows i and
+// 16 + i (zero for rows past 24 or fragments past the slice) of each stream.
+struct FnChunk {
+  u32x4 b1[kStreams], b2[kStreams];
+};
+__device__ __forceinline__ void load_fn_chunk(const GlmArgs &a, int i, int f, bool ok, FnChunk &c) {
+  const int64_t H = a.H, col = ok ? (int64_t)f * kFrag : 0;
+#pragma unroll
+  for (int j = 0; j < kStreams; ++j) {
+    c.b1[j] = ok ? load_cached(a.fn + (int64_t)i * kStreams * H + j * H + col) : u32x4{0, 0, 0, 0};
+    c.b2[j] = ok && i < kMix - kTile
+                  ? load_cached(a.fn + (int64_t)(kTile + i) * kStreams * H + j * H + col)
+                  : u32x4{0, 0, 0, 0};
+  }
+}
+
+// U = (token, fragment) items per thread, and also 4-fragment GEMV chunks
+// per wave; TP = fixed rank count, or 0 for the runtime count.
+template <int U, int TP>
+__global__ void __launch_bounds__(kTileThreads, 2)
+glm_tile_kernel(const GlmArgs a) {
+  __shared__ TileShared sh;
+  extern __shared__ __align__(16) char dyn[];
+  const int H = a.H, F = H / kFrag, tid = threadIdx.x, nt = blockDim.x;
+  const int lane = tid & (kWave - 1), wave = tid / kWave, waves = nt / kWave;
+  const int s = blockIdx.x, t0 = blockIdx.y * kTile;
+  const int sf = a.slice_frags, first = s * sf, last = min(F, first + sf);
+  const int valid = min(kTile, a.M - t0);
+  const int tp = TP > 0 ? TP : a.tp;
+  const int rw = tile_row_words(sf);
+  u32x4 *ys = reinterpret_cast<u32x4 *>(dyn);
+  double *item = reinterpret_cast<double *>(dyn + tile_ys_bytes(sf));
+  const int mi = lane & (kTile - 1), mq = lane >> 4;  // MFMA row, K chunk
+
+  // The tile's post and comb (20 floats a token) and this wave's first
+  // hc_fn chunk, loaded before the streams.
+  constexpr int kMixVals = kTile * 20, kMixPerThread = kMixVals / kWave;
+  float mv[kMixPerThread];
+#pragma unroll
+  for (int u = 0; u < kMixPerThread; ++u) {
+    const int e = tid + u * nt, tok = e / 20, k = e % 20, tt = t0 + tok;
+    mv[u] = e < kMixVals && tok < valid
+                ? (k < kStreams ? a.post[(int64_t)tt * kStreams + k] : a.comb[(int64_t)tt * 16 + (k - kStreams)])
+                : 0.0f;
+  }
+  FnChunk fc[U];
+  load_fn_chunk(a, mi, first + 4 * wave + mq, 4 * wave < sf && first + 4 * wave + mq < last, fc[0]);
+
+  // Items: idx = tid + u * nt -> token idx / sf, fragment first + idx % sf.
+  int tok[U];
+  int64_t col[U];
+  bool live[U];
+  u32x4 part[U][TP > 0 ? TP : 1], res[U][kStreams], gam[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int idx = tid + u * nt;
+    tok[u] = idx / sf;
+    const int f = first + idx % sf;
+    live[u] = tok[u] < valid && f < last;
+    col[u] = live[u] ? (int64_t)f * kFrag : 0;
+    const int64_t t = t0 + (live[u] ? tok[u] : 0);
+#pragma unroll
+    for (int r = 0; r < kStreams; ++r)
+      res[u][r] = live[u] ? load_stream(a.residual + (t * kStreams + r) * H + col[u]) : u32x4{0, 0, 0, 0};
+    if constexpr (TP > 0) {
+#pragma unroll
+      for (int r = 0; r < TP; ++r)
+        part[u][r] = live[u] ? load_stream(a.partials + r * a.rank_stride + t * H + col[u]) : u32x4{0, 0, 0, 0};
+    }
+    gam[u] = live[u] ? load_cached(a.gamma + col[u]) : u32x4{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int u = 0; u < kMixPerThread; ++u) {
+    const int e = tid + u * nt, tk = e / 20, k = e % 20;
+    if (e < kMixVals) {
+      if (k < kStreams) sh.post[tk][k] = mv[u];
+      else sh.comb[tk][k - kStreams] = mv[u];
+    }
+  }
+  __syncthreads();
+
+  // a1 + a2 per item; y to LDS (the GEMV's A operand, and the collapse's).
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    float sum[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sum[e] = 0.0f;
+    const int64_t t = t0 + (live[u] ? tok[u] : 0);
+    if constexpr (TP > 0) {
+#pragma unroll
+      for (int r = 0; r < TP; ++r) {
+        float v[8];
+        unpack8(part[u][r], v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sum[e] = sum[e] + v[e];
+      }
+    } else {
+      const uint16_t *src = a.partials + t * H + col[u];
+      for (int r0 = 0; r0 < tp; r0 += 8) {
+        u32x4 w[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+          w[r] = live[u] && r0 + r < tp ? load_stream(src + (r0 + r) * a.rank_stride) : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          if (r0 + r >= tp) break;
+          float v[8];
+          unpack8(w[r], v);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sum[e] = sum[e] + v[e];
+        }
+      }
+    }
+    float x[8];
+    unpack8(pack8(sum), x);
+    float r4[kStreams][8];
+#pragma unroll
+    for (int r = 0; r < kStreams; ++r) unpack8(res[u][r], r4[r]);
+    const int tk = live[u] ? tok[u] : 0;
+    const int idx = tid + u * nt;
+    double ysq = 0.0;
+#pragma unroll
+    for (int j = 0; j < kStreams; ++j) {
+      const float pj = sh.post[tk][j];
+      float acc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float v = x[e] * pj;
+#pragma unroll
+        for (int r = 0; r < kStreams; ++r) v = __builtin_fmaf(r4[r][e], sh.comb[tk][r * kStreams + j], v);
+        acc[e] = v;
+      }
+      const u32x4 yj = live[u] ? pack8(acc) : u32x4{0, 0, 0, 0};
+      if (live[u]) {
+        store_stream(a.residual_out + (t * kStreams + j) * H + col[u], yj);
+        float yv[8];
+        unpack8(yj, yv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ysq += (double)yv[e] * (double)yv[e];
+      }
+      if (idx < kTile * sf) ys[(idx / sf) * rw + j * sf + idx % sf] = yj;
+    }
+    if (idx < kTile * sf) item[idx] = ysq;  // [tok][f]
+  }
+  // The wave's remaining hc_fn chunks, in flight across the barrier.
+#pragma unroll
+  for (int m = 1; m < U; ++m) {
+    const int c = wave + m * waves, f = first + 4 * c + mq;
+    load_fn_chunk(a, mi, f, 4 * c < sf && f < last, fc[m]);
+  }
+  __syncthreads();
+
+  // a3: the GEMV on the matrix cores, wave w taking 4-fragment chunks
+  // w, w + waves, ...
+  {
+    f32x4 c1 = {0.0f, 0.0f, 0.0f, 0.0f}, c2 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int m = 0; m < U; ++m) {
+      const int c = wave + m * waves;
+      if (4 * c >= sf) break;
+#pragma unroll
+      for (int j = 0; j < kStreams; ++j) {
+        const u32x4 av = ys[mi * rw + j * sf + 4 * c + mq];
+        c1 = mfma_bf16(av, fc[m].b1[j], c1);
+        c2 = mfma_bf16(av, fc[m].b2[j], c2);
+      }
+    }
+    // Lane l holds rows l % 16 and 16 + l % 16 of tokens 4*(l/16) .. +3.
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sh.part[wave][4 * mq + e][mi] = c1[e];
+      if (mi < kMix - kTile) sh.part[wave][4 * mq + e][kTile + mi] = c2[e];
+    }
+  }
+  tile_item_sums(sh, item, sf);  // (its first barrier also publishes sh.part)
+  for (int e = tid; e < kTile * kMix; e += nt) {
+    float v = 0.0f;
+    for (int w = 0; w < waves; ++w) v += sh.part[w][e / kMix][e % kMix];
+    sh.mix[e / kMix][e % kMix] = v;
+  }
+  __syncthreads();
+  tile_exchange(a, sh, t0, s, kSlotSum1, true);
+
+  // rstd over 4H; raw mixes out (slice 0); pre_j.
+  for (int e = tid; e < valid * kMix; e += nt) {
+    const int tk = e / kMix, k = e % kMix, tt = t0 + tk;
+    const float rstd = (float)(1.0 / __builtin_sqrt((double)(float)sh.tot[tk] / (4.0 * H) + (double)a.rms_eps));
+    const float mix = sh.mix[tk][k] * rstd;
+    if (s == 0) a.mixes_out[(int64_t)tt * kMix + k] = mix;
+    if (k < kStreams) sh.pre[tk][k] = sigmoid(__builtin_fmaf(mix, a.scale[0], a.base[k])) + a.hc_eps;
+  }
+  __syncthreads();
+
+  // a4: p = bf16((q0+q1)+(q2+q3)), q_j = y_j * pre_j; RMSNorm over H.
+  u32x4 p[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int idx = tid + u * nt;
+    const int tk = live[u] ? tok[u] : 0;
+    float qv[kStreams][8];
+#pragma unroll
+    for (int j = 0; j < kStreams; ++j) {
+      float yv[8];
+      unpack8(live[u] ? ys[tk * rw + j * sf + idx % sf] : u32x4{0, 0, 0, 0}, yv);
+      const float pj = sh.pre[tk][j];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[j][e] = yv[e] * pj;
+    }
+    float z[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) z[e] = (qv[0][e] + qv[1][e]) + (qv[2][e] + qv[3][e]);
+    p[u] = pack8(z);
+    double pss = 0.0;
+    if (live[u]) {
+      float pv[8];
+      unpack8(p[u], pv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pss += (double)pv[e] * (double)pv[e];
+    }
+    if (idx < kTile * sf) item[idx] = pss;
+  }
+  tile_item_sums(sh, item, sf);
+  tile_exchange(a, sh, t0, s, kSlotSum2, false);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (!live[u]) continue;
+    const float inv = (float)(1.0 / __builtin_sqrt((double)(float)sh.tot[tok[u]] / (double)H + (double)a.norm_eps));
+    float pv[8], g[8], o[8];
+    unpack8(p[u], pv);
+    unpack8(gam[u], g);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (pv[e] * inv) * g[e];
+    store_stream(a.layer_input + (int64_t)(t0 + tok[u]) * H + col[u], pack8(o));
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Side-stream mixes: one thread per token.
 // ---------------------------------------------------------------------------
 
@@ -386,6 +755,42 @@ hipError_t launch_boundary_glm(const GlmArgs &a, hipStream_t stream) {
       break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+// Tile geometry: 16 * slice_frags items over at most 256 threads (at most
+// four items each); dynamic LDS sized by the slice.
+hipError_t launch_boundary_glm_tile(const GlmArgs &a, hipStream_t stream) {
+  const int sf = a.slice_frags;
+  if (sf % 4 || sf > kTileMaxFrags || a.slices > kMaxSlices) return hipErrorInvalidValue;
+  const int items = kTile * sf;
+  const int threads = items >= kTileThreads ? kTileThreads : (items + kWave - 1) / kWave * kWave;
+  const int U = (items + threads - 1) / threads;
+  const dim3 grid(a.slices, (a.M + kTile - 1) / kTile), block(threads);
+  const size_t lds = tile_dyn_bytes(sf);
+  // Slices of more than 48 fragments take more than 64 KiB of LDS.
+#define MHCB_TILE_LAUNCH(UU, TPP)                                                            \
+  if (lds > 65536) {                                                                         \
+    const hipError_t e = hipFuncSetAttribute((const void *)glm_tile_kernel<UU, TPP>,          \
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,      \
+                                             (int)lds);                                      \
+    if (e != hipSuccess) return e;                                                           \
+  }                                                                                          \
+  hipLaunchKernelGGL((glm_tile_kernel<UU, TPP>), grid, block, lds, stream, a);
+#define MHCB_TILE(UU)                                                                        \
+  if (a.tp == 8) {                                                                           \
+    MHCB_TILE_LAUNCH(UU, 8)                                                                  \
+  } else {                                                                                   \
+    MHCB_TILE_LAUNCH(UU, 0)                                                                  \
+  }
+  switch (U) {
+    case 1: MHCB_TILE(1) break;
+    case 2: MHCB_TILE(2) break;
+    case 3: MHCB_TILE(3) break;
+    default: MHCB_TILE_LAUNCH(4, 0) break;  // four items of eight held ranks would spill
+  }
+#undef MHCB_TILE
+#undef MHCB_TILE_LAUNCH
   return hipGetLastError();
 }
 

@@ -37,7 +37,7 @@ struct FinalizeView {
 // Cross-workgroup state of the token-split kernels, at the start of the
 // caller's workspace: a 256-byte header (status word), then one slot per
 // token, so that different tokens' atomics never share a cache line:
-//   +0    arrival count          +4   barrier generation
+//   +0    arrival count          +4   barrier generation   (one 8-byte word)
 //   +64   [kMaxSlices] binary64  first partial sum per slice
 //   +192  [kMaxSlices] binary64  second partial sum per slice
 //   +320  [kMaxSlices][24] FP32  partial GEMV rows per slice (GLM)
@@ -115,6 +115,10 @@ struct GlmArgs {
 };
 
 hipError_t launch_boundary_glm(const GlmArgs &a, hipStream_t stream);
+// 16-token tiles on the matrix cores; always split (a.slices >= 1 with a
+// sync view), at most kSyncTokens tokens per launch.
+constexpr int kGlmTileTokens = 16;
+hipError_t launch_boundary_glm_tile(const GlmArgs &a, hipStream_t stream);
 
 hipError_t launch_mixes(const float *mixes, const float *scale, const float *base, float *post_out,
                         float *comb_out, int M, float hc_eps, float post_mult, int repeat,

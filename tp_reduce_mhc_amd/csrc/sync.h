@@ -5,7 +5,7 @@
 // performed at the device's coherence point; ordering them only needs the
 // wave's earlier accesses to have completed (wait_vmem: s_waitcnt vmcnt(0),
 // which on CDNA counts stores too), and values are read only after the
-// generation load that released the wait has returned.  Device-scope
+// atomic or generation load that released the wait has returned.  Device-scope
 // release/acquire fences would instead write back / invalidate the XCD's
 // whole L2 at every arrival and every poll.
 #pragma once
@@ -36,27 +36,28 @@ __device__ __forceinline__ float slot_load32(const char *slot, int offset) {
                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
 
-// Token t's barrier, in two halves so that one thread can take several
-// tokens' barriers without ever waiting while it still owes an arrival
-// (arrive at all of them, then wait at each).
+// Token t's barrier.  Word 0 of the slot (8 bytes) holds the arrivals of
+// the current generation in its low half and the generation in its high
+// half, so an arrival is one atomic add that also returns the generation,
+// and the last arrival starts the next generation (count back to zero,
+// generation + 1) with a second add.  It comes in two halves so that one
+// thread can take several tokens' barriers without ever waiting while it
+// still owes an arrival (arrive at all of them, then wait at each).
 //
-// barrier_arrive: one slice's arrival, after that slice's partials have been
-// stored and completed.  The last of `slices` arrivals resets the count and
-// moves the generation (returns true); otherwise returns false with the
-// generation to wait on in *gen_seen.
+// barrier_arrive: one slice's arrival.  The caller must have completed its
+// stores to the slot (wait_vmem) first; that same wait also covers this
+// thread's previous add on the word, so a last arrival's reset always lands
+// before the same thread arrives again.  Returns true for the last of
+// `slices` arrivals; otherwise false with the generation to wait on in
+// *gen_seen.
 __device__ __forceinline__ bool barrier_arrive(const SyncView &sy, int t, int slices,
                                                uint32_t *gen_seen) {
-  char *slot = token_slot(sy, t);
-  uint32_t *count = reinterpret_cast<uint32_t *>(slot);
-  uint32_t *gen = count + 1;
-  const uint32_t g = __hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  wait_vmem();  // the partials (and the generation read) have completed
-  const uint32_t arrived = __hip_atomic_fetch_add(count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  *gen_seen = g;
-  if (arrived != (uint32_t)slices - 1u) return false;
-  __hip_atomic_store(count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  wait_vmem();  // the reset lands before anyone can arrive at the next use
-  __hip_atomic_store(gen, g + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  uint64_t *word = reinterpret_cast<uint64_t *>(token_slot(sy, t));
+  const uint64_t old = __hip_atomic_fetch_add(word, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  *gen_seen = (uint32_t)(old >> 32);
+  if ((uint32_t)old != (uint32_t)slices - 1u) return false;
+  __hip_atomic_fetch_add(word, (1ull << 32) - (uint64_t)slices, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
   return true;
 }
 
@@ -75,9 +76,10 @@ __device__ __forceinline__ void barrier_wait(const SyncView &sy, int t, uint32_t
   }
 }
 
-// Both halves for a single token.  Reusable any number of times per call
-// and across calls.
+// Both halves for a single token, after this thread's slot stores.
+// Reusable any number of times per call and across calls.
 __device__ __forceinline__ void token_barrier(const SyncView &sy, int t, int slices) {
+  wait_vmem();
   uint32_t g;
   if (!barrier_arrive(sy, t, slices, &g)) barrier_wait(sy, t, g);
 }
