@@ -136,9 +136,15 @@ int mhcb_boundary(const uint16_t *partials, int64_t rank_stride, const mhcb_mail
  *   p     = bf16((y_0*pre_0 + y_1*pre_1) + (y_2*pre_2 + y_3*pre_3))
  *   out   = bf16((p * inv) * norm_weight) as above.
  * hc_fn [24, 4*hidden] BF16; scale [3], base [24] FP32; mixes_out [M, 24]
- * FP32.  tokens_per_wg (1, 2, 4; 0 = by M) tokens share one workgroup and
- * one read of hc_fn; outputs do not depend on it.  hidden <= 8192.
- * workspace: optional (see mhcb_workspace_bytes). */
+ * FP32.  tokens_per_wg = 1, 2 or 4: that many tokens share one workgroup
+ * and one read of hc_fn, and the outputs do not depend on the choice.
+ * tokens_per_wg = 16: tiles of 16 tokens whose GEMV runs on the matrix
+ * cores (needs a workspace); its FP32 sums are taken in another order, so
+ * mixes_out may differ from the 1/2/4 results in the last bits (both agree
+ * with the exact GEMV to about 1e-6 relative).  0 = chosen by M
+ * (16 above M = 256 when a workspace is given).  hidden <= 8192.
+ * workspace: optional for 1, 2, 4 (see mhcb_workspace_bytes); calls that
+ * share one must be ordered on one stream. */
 int mhcb_boundary_glm(const uint16_t *partials, int64_t rank_stride, const uint16_t *residual,
                       const float *post, const float *comb, const uint16_t *hc_fn,
                       const float *scale, const float *base, const uint16_t *norm_weight,

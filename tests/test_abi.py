@@ -115,6 +115,7 @@ def test_glm_mixes_finalize_quant_validation():
                layer_input=FAKE, workspace=None, workspace_bytes=0, M=4, hidden_size=512, hc_mult=4,
                tp=2, rms_eps=1e-6, hc_eps=1e-6, norm_eps=1e-6, stream=0)
     for kw, text in ((dict(tokens_per_wg=3), "tokens_per_wg"), (dict(hc_fn=None), "required"),
+                     (dict(tokens_per_wg=16), "needs a workspace"),
                      (dict(hidden_size=8200, rank_stride=4 * 8200), "exceeds"),
                      (dict(tokens_per_wg=4, hidden_size=8192, rank_stride=4 * 8192), "tokens_per_wg=4")):
         with pytest.raises(mhc.MhcbError, match=text):

@@ -39,7 +39,7 @@ constexpr int kMaxHiddenGlm = 8192;
 constexpr int kMaxTp = 64;
 constexpr int kMaxRoutes = 1024;
 constexpr int64_t kDefaultSpin = 1 << 20;
-constexpr int kGlmTileMinM = 128;  // automatic matrix-core tiles from this M
+constexpr int kGlmTileMinM = 257;  // automatic matrix-core tiles from this M
 
 // Checks shared by the boundary variants ([DSV41] AllReduceMHC._check and
 // _consumer, _LamportMHCDeviceKernel.__init__).
@@ -269,9 +269,9 @@ int mhcb_boundary_glm(const uint16_t *partials, int64_t rank_stride, const uint1
     return fail(MHCB_EALIGN, "%s: partials/hc_fn must be 16-byte aligned, rank_stride %% 8 == 0", fn);
   int G = tokens_per_wg;
   // Measured on MI355X (H=6144, tp=8): one token per workgroup is fastest up
-  // to M=256 (24.6 us vs 28.8 us with two), two beyond (M=512: 37.0 us vs
-  // 47.2 us with one and 48.5 us with four); with a workspace, 16-token
-  // matrix-core tiles from kGlmTileMinM tokens.
+  // to M=256 (25.7 us; two: 28.7, 16-token tiles: 25.8), 16-token tiles in 8
+  // slices beyond (M=512: 33.2 us; one token: 47.1, two: 36.5).  Without a
+  // workspace, two tokens per workgroup beyond M=256.
   if (G == 0) G = workspace && M >= kGlmTileMinM ? kGlmTileTokens : (M <= 256 ? 1 : 2);
   if (G != 1 && G != 2 && G != 4 && G != kGlmTileTokens)
     return fail(MHCB_EINVAL, "%s: tokens_per_wg=%d (0, 1, 2, 4 or 16)", fn, tokens_per_wg);
@@ -283,13 +283,17 @@ int mhcb_boundary_glm(const uint16_t *partials, int64_t rank_stride, const uint1
                hc_fn, scale, base, norm_weight, residual_out, mixes_out, layer_input, M,
                hidden_size, rms_eps, hc_eps, norm_eps, G};
   if (G == kGlmTileTokens) {
-    // Slices of at most 64 fragments (four waves of four steps), 16 unless
-    // overridden; launches of at most kSyncTokens tokens.
+    // Slices of at most 96 fragments; launches of at most kSyncTokens
+    // tokens.  16 slices while that gives at most one workgroup per compute
+    // unit (M <= 256 on 256 units), else 8: measured on MI355X at H=6144,
+    // M=256: 25.8 us (16) vs 28.8 us (8); M=512: 38.7 us (16) vs 33.2 us (8).
     const int F = hidden_size / kFrag;
-    int S = g_slices_override > 0 ? g_slices_override : kMaxSlices;
+    const int tiles = ((M < kSyncTokens ? M : kSyncTokens) + kGlmTileTokens - 1) / kGlmTileTokens;
+    int S = g_slices_override > 0 ? g_slices_override
+                                  : (tiles * kMaxSlices <= device_cus() ? kMaxSlices : 8);
     S = S > kMaxSlices ? kMaxSlices : S;
     S = S > F / 4 ? F / 4 : S;
-    S = S < (F + 63) / 64 ? (F + 63) / 64 : S;
+    S = S < (F + 95) / 96 ? (F + 95) / 96 : S;
     S = S < 1 ? 1 : S;
     int frags = (F + S - 1) / S;
     frags = (frags + 3) / 4 * 4;

@@ -338,9 +338,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = 16;              // tokens per tile
-constexpr int kTileThreads = 256;      // at most; fewer for narrow slices
+constexpr int kTileThreads = 512;      // at most
 constexpr int kTileWaves = kTileThreads / kWave;
-constexpr int kTileMaxFrags = 64;      // fragments per slice
+constexpr int kTileMaxFrags = 96;      // fragments per slice
 
 __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
@@ -467,7 +467,7 @@ __device__ __forceinline__ void load_fn_chunk(const GlmArgs &a, int i, int f, bo
 // U = (token, fragment) items per thread, and also 4-fragment GEMV chunks
 // per wave; TP = fixed rank count, or 0 for the runtime count.
 template <int U, int TP>
-__global__ void __launch_bounds__(kTileThreads, 2)
+__global__ void __launch_bounds__(kTileThreads, 1)
 glm_tile_kernel(const GlmArgs a) {
   __shared__ TileShared sh;
   extern __shared__ __align__(16) char dyn[];
@@ -583,10 +583,7 @@ glm_tile_kernel(const GlmArgs a) {
       const u32x4 yj = live[u] ? pack8(acc) : u32x4{0, 0, 0, 0};
       if (live[u]) {
         store_stream(a.residual_out + (t * kStreams + j) * H + col[u], yj);
-        float yv[8];
-        unpack8(yj, yv);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ysq += (double)yv[e] * (double)yv[e];
+        ysq += (double)dot8(yj, yj, 0.0f);  // FP32 within the fragment
       }
       if (idx < kTile * sf) ys[(idx / sf) * rw + j * sf + idx % sf] = yj;
     }
@@ -661,12 +658,7 @@ glm_tile_kernel(const GlmArgs a) {
     for (int e = 0; e < 8; ++e) z[e] = (qv[0][e] + qv[1][e]) + (qv[2][e] + qv[3][e]);
     p[u] = pack8(z);
     double pss = 0.0;
-    if (live[u]) {
-      float pv[8];
-      unpack8(p[u], pv);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pss += (double)pv[e] * (double)pv[e];
-    }
+    if (live[u]) pss = (double)dot8(p[u], p[u], 0.0f);
     if (idx < kTile * sf) item[idx] = pss;
   }
   tile_item_sums(sh, item, sf);
@@ -758,14 +750,16 @@ hipError_t launch_boundary_glm(const GlmArgs &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Tile geometry: 16 * slice_frags items over at most 256 threads (at most
-// four items each); dynamic LDS sized by the slice.
+// Tile geometry: 16 * slice_frags items, about three per thread (at most
+// 512 threads, four items); dynamic LDS sized by the slice.
 hipError_t launch_boundary_glm_tile(const GlmArgs &a, hipStream_t stream) {
   const int sf = a.slice_frags;
   if (sf % 4 || sf > kTileMaxFrags || a.slices > kMaxSlices) return hipErrorInvalidValue;
   const int items = kTile * sf;
-  const int threads = items >= kTileThreads ? kTileThreads : (items + kWave - 1) / kWave * kWave;
+  int threads = ((items + 2) / 3 + kWave - 1) / kWave * kWave;
+  threads = threads > kTileThreads ? kTileThreads : threads;
   const int U = (items + threads - 1) / threads;
+  if (U > 4) return hipErrorInvalidValue;
   const dim3 grid(a.slices, (a.M + kTile - 1) / kTile), block(threads);
   const size_t lds = tile_dyn_bytes(sf);
   // Slices of more than 48 fragments take more than 64 KiB of LDS.
