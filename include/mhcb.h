@@ -76,9 +76,12 @@ int mhcb_workspace_init(void *workspace, int64_t workspace_bytes, hipStream_t st
  * that used this workspace gave up (bounded spin), else MHCB_OK. */
 int mhcb_workspace_status(const void *workspace, hipStream_t stream);
 
-/* Tuning: workgroups per token for calls with a workspace (1..16; 0 =
- * automatic, about two workgroups per compute unit).  Process-wide; returns
- * the previous value.  Outputs do not depend on it. */
+/* Tuning: workgroups per token (or per GLM tile) for calls with a
+ * workspace (1..16; 0 = automatic, chosen by M from measurements).
+ * Process-wide; returns the previous value.  The BF16 sums, streams and the
+ * delayed / finalize layer inputs do not depend on it; the GLM GEMV is
+ * summed over the slices in FP32, so its raw mixes may change in the last
+ * bits. */
 int mhcb_set_token_slices(int slices);
 
 /* Three-generation Lamport mailbox ([GLM] AllReduceMhcBoundary.__init__,
