@@ -44,22 +44,32 @@ def glm_pre(mixes: np.ndarray, scale: np.ndarray, base: np.ndarray, hc_eps: floa
     return 1.0 / (1.0 + np.exp(-x)) + hc_eps
 
 
+def _ulp32(v: np.ndarray) -> np.ndarray:
+    return np.spacing(np.abs(v).astype(np.float32)).astype(np.float64)
+
+
 def glm_layer_input_check(got_li, ref_li, y, pre_ref, pre_got):
     """The GLM layer input within 1 BF16 ulp of the oracle, except <= 2 where
-    the oracle's unrounded collapse sum(y_j * pre_j) lies within the pre-mix
-    error band of a BF16 rounding midpoint (the pre-mix is derived in-kernel,
-    so an FP32-ulp difference there can flip the collapse's BF16 rounding).
-    Band = sum_j |y_j| |pre_got_j - pre_ref_j| + 4 FP32 ulps of the sum.
+    the oracle's FP32 collapse (q0+q1)+(q2+q3), q_j = y_j * pre_j, lies within
+    the pre-mix error band of a BF16 rounding midpoint (the pre-mix is derived
+    in-kernel, so an FP32-ulp difference there can flip the collapse's BF16
+    rounding).  The band bounds how far the GPU's FP32 collapse can be from
+    the oracle's: sum_j (|y_j| |pre_got_j - pre_ref_j| + ulp(q_j)) +
+    ulp(q0+q1) + ulp(q2+q3) + ulp(z) -- a changed pre can move every rounded
+    term by one ulp, which under cancellation is many ulps of z.
     Returns (elements off by 1, elements off by 2)."""
     d = bf16_ulp_distance(got_li, ref_li)
-    yv = bf16_value(y).astype(np.float64)                  # [M, 4, H]
-    z = np.einsum("tjc,tj->tc", yv, pre_ref)
-    band = np.einsum("tjc,tj->tc", np.abs(yv), np.abs(pre_got - pre_ref)) + 4 * np.spacing(
-        np.abs(z).astype(np.float32)).astype(np.float64)
+    yv = bf16_value(y).astype(np.float32)                          # [M, 4, H]
+    pre32 = pre_ref.astype(np.float32)[:, :, None]
+    q = yv * pre32                                                 # FP32 products
+    s01, s23 = q[:, 0] + q[:, 1], q[:, 2] + q[:, 3]
+    z = (s01 + s23).astype(np.float64)                             # the oracle's FP32 collapse
+    band = (np.abs(yv.astype(np.float64)) * np.abs(pre_got - pre_ref)[:, :, None]).sum(axis=1)
+    band += _ulp32(q).sum(axis=1) + _ulp32(s01) + _ulp32(s23) + _ulp32(z)
     # distance from z to the nearest BF16 rounding midpoint
     zb = np.abs(z).astype(np.float32)
     e = np.floor(np.log2(np.maximum(zb, 1e-38)))
-    step = np.exp2(e - 7)                                  # BF16 spacing at |z|
+    step = np.exp2(e - 7)                                          # BF16 spacing at |z|
     mid_dist = np.abs((np.abs(z) / step) % 1.0 - 0.5) * step
     near = mid_dist <= band
     if (d > 2).any() or ((d == 2) & ~near).any():

@@ -276,19 +276,21 @@ def test_moe_finalize_large_m_sampled():
 # GLM boundary and side mixes
 # ---------------------------------------------------------------------------
 
-def run_glm(g, G):
+def run_glm(g, G, workspace=True):
     """Outputs are pre-filled with NaN so that an element the kernel misses
     cannot pass on a previous call's bits."""
     M, H = g.M, g.H
     ro = torch.full((M, 4, H), float("nan"), dtype=torch.bfloat16, device="cuda")
     mixes = torch.full((M, 24), float("nan"), dtype=torch.float32, device="cuda")
     li = torch.full((M, H), float("nan"), dtype=torch.bfloat16, device="cuda")
-    ws = mhc.workspace("cuda")
+    ws = mhc.workspace("cuda") if workspace else None
     mhc.mhcb_boundary_glm(dev(g.partials), M * H, dev(g.residual), dev(g.post), dev(g.comb),
                           dev(g.fn), dev(g.scale), dev(g.base), dev(g.gamma), ro, mixes, li, ws,
-                          ws.numel(), M, H, 4, g.tp, g.rms_eps, g.hc_eps, g.norm_eps, G)
+                          ws.numel() if workspace else 0, M, H, 4, g.tp, g.rms_eps, g.hc_eps,
+                          g.norm_eps, G)
     torch.cuda.synchronize()
-    assert mhc.mhcb_workspace_status(ws) == mhc.MHCB_OK
+    if workspace:
+        assert mhc.mhcb_workspace_status(ws) == mhc.MHCB_OK
     return u16(ro), host(mixes), u16(li)
 
 
@@ -326,6 +328,17 @@ def check_glm_against_oracle(g, ro, mixes, li, what):
     one, two = glm_layer_input_check(li, li_ref, ro_ref, pre_ref.astype(np.float64),
                                      glm_pre(mixes, g.scale, g.base, g.hc_eps))
     print(f"[gpu]   {what}: layer_input 1-ulp {one}, tie 2-ulp {two}", flush=True)
+
+
+@pytest.mark.parametrize("M,H,G,workspace", [(100, 6144, 1, True), (100, 6144, 2, True),
+                                              (9, 6144, 2, False), (9, 1024, 4, False)])
+def test_glm_one_thread_per_fragment_and_no_workspace(M, H, G, workspace):
+    """Whole tokens in one workgroup: one thread per fragment (H=6144) or a
+    quad per fragment (H=1024); without a workspace nothing is split."""
+    g = synth.glm(M, H=H)
+    print(f"[gpu] {g.name} G={G} workspace={workspace}", flush=True)
+    ro, mixes, li = run_glm(g, G, workspace)
+    check_glm_against_oracle(g, ro, mixes, li, f"G={G}")
 
 
 @pytest.mark.parametrize("M,H,tp", [(1, 6144, 8), (17, 6144, 8), (40, 2048, 3), (33, 512, 8),
