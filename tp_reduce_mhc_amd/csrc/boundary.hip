@@ -24,9 +24,17 @@
 namespace mhcb {
 
 // A workgroup covering `frags` fragments: 1, 2 or 4 fragments per thread,
-// at most kTokenThreads threads (frags <= 2048, i.e. hidden <= 16384).
-Geometry fragment_geometry(int frags) {
+// at most kTokenThreads threads (frags <= 2048, i.e. hidden <= 16384); with
+// `wide`, one fragment per thread up to kTokenThreadsWide threads.  A token's
+// VALU work is then spread over more waves: at H=5120 ten one-fragment waves
+// put at most three fragments' work on a SIMD, five two-fragment waves four.
+Geometry fragment_geometry(int frags, bool wide) {
   Geometry g;
+  if (wide && frags <= kTokenThreadsWide) {
+    g.trips = 1;
+    g.threads = (frags + kWave - 1) / kWave * kWave;
+    return g;
+  }
   g.trips = frags <= kTokenThreads ? 1 : (frags <= 2 * kTokenThreads ? 2 : 4);
   const int per = (frags + g.trips - 1) / g.trips;
   g.threads = (per + kWave - 1) / kWave * kWave;
@@ -198,9 +206,10 @@ __device__ double token_sum(const SyncView &sy, int t, int s, int slices, double
 // rank load of every trip is issued up front; TP == 0 reads it from the
 // arguments.
 template <int TRIPS, int TP, Source SRC>
-__global__ void __launch_bounds__(kTokenThreads)
+__global__ void __launch_bounds__(TRIPS == 1 && SRC != Source::kFinalize ? kTokenThreadsWide
+                                                                         : kTokenThreads)
 boundary_kernel(const BoundaryArgs a) {
-  __shared__ double red[kTokenThreads / kWave + 1];
+  __shared__ double red[kTokenThreadsWide / kWave + 1];
   __shared__ int32_t srow[SRC == Source::kFinalize ? kMaxRoutes : 1];
   __shared__ float sw[SRC == Source::kFinalize ? kMaxRoutes : 1];
 
@@ -367,7 +376,7 @@ boundary_kernel(const BoundaryArgs a) {
   // whatever the order or the split.
   double tot[1] = {ss};
   block_sum<double, 1>(tot, red);
-  if (a.slices > 1) tot[0] = token_sum(a.sync, t, s, a.slices, tot[0], red + kTokenThreads / kWave);
+  if (a.slices > 1) tot[0] = token_sum(a.sync, t, s, a.slices, tot[0], red + kTokenThreadsWide / kWave);
   const float inv = (float)(1.0 / __builtin_sqrt((double)(float)tot[0] / (double)H + (double)a.norm_eps));
 
 #pragma unroll
@@ -447,7 +456,9 @@ hipError_t launch_tp(const BoundaryArgs &a, int threads, hipStream_t stream) {
 
 template <Source SRC>
 hipError_t launch_src(const BoundaryArgs &a, hipStream_t stream) {
-  const Geometry g = fragment_geometry(a.slices > 1 ? a.slice_frags : a.H / kFrag);
+  // Finalize keeps at most 512 threads: its gathers need the registers.
+  const Geometry g = fragment_geometry(a.slices > 1 ? a.slice_frags : a.H / kFrag,
+                                       SRC != Source::kFinalize);
   switch (g.trips) {
     case 1: return launch_tp<1, SRC>(a, g.threads, stream);
     case 2: return launch_tp<2, SRC>(a, g.threads, stream);

@@ -17,6 +17,7 @@ constexpr int kFrag = 8;           // BF16 values in one 16-byte fragment
 constexpr int kWave = 64;
 constexpr int kMaxThreads = 1024;
 constexpr int kTokenThreads = 512;  // workgroup size bound of the per-token kernels
+constexpr int kTokenThreadsWide = 1024;  // the same with one fragment per thread
 constexpr uint16_t kSentinel = 0x8000;  // BF16 negative zero marks an empty slot
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

@@ -125,11 +125,12 @@ hipError_t launch_mixes(const float *mixes, const float *scale, const float *bas
                         hipStream_t stream);
 
 // Launch geometry of a workgroup covering `frags` 16-byte fragments
-// (1, 2 or 4 of them per thread, at most 512 threads).
+// (1, 2 or 4 of them per thread, at most 512 threads; with `wide`, one per
+// thread up to 1024 threads).
 struct Geometry {
   int trips, threads;
 };
-Geometry fragment_geometry(int frags);
+Geometry fragment_geometry(int frags, bool wide = false);
 inline Geometry token_geometry(int H) { return fragment_geometry(H / 8); }
 
 hipError_t launch_zero(void *p, int64_t bytes, hipStream_t stream);
