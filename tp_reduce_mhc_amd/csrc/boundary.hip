@@ -206,8 +206,9 @@ __device__ double token_sum(const SyncView &sy, int t, int s, int slices, double
 // rank load of every trip is issued up front; TP == 0 reads it from the
 // arguments.
 template <int TRIPS, int TP, Source SRC>
-__global__ void __launch_bounds__(TRIPS == 1 && SRC != Source::kFinalize ? kTokenThreadsWide
-                                                                         : kTokenThreads)
+__global__ void __launch_bounds__(TRIPS == 1 && (SRC != Source::kFinalize || TP == 0)
+                                      ? kTokenThreadsWide
+                                      : kTokenThreads)
 boundary_kernel(const BoundaryArgs a) {
   __shared__ double red[kTokenThreadsWide / kWave + 1];
   __shared__ int32_t srow[SRC == Source::kFinalize ? kMaxRoutes : 1];
@@ -430,8 +431,9 @@ template <int TRIPS, Source SRC>
 hipError_t launch_tp(const BoundaryArgs &a, int threads, hipStream_t stream) {
   dim3 grid = a.slices > 1 ? dim3(a.slices, a.M) : dim3(a.M), block(threads);
   if constexpr (SRC == Source::kFinalize) {
-    // All 36 gathers in flight at once need one fragment per thread.
-    if (TRIPS == 1 && a.tp == 4 && a.fin.top_k <= 8)
+    // All 36 gathers in flight at once need one fragment per thread and at
+    // most 512 threads (their registers).
+    if (TRIPS == 1 && a.tp == 4 && a.fin.top_k <= 8 && threads <= kTokenThreads)
       hipLaunchKernelGGL((boundary_kernel<1, 4, SRC>), grid, block, 0, stream, a);
     else
       hipLaunchKernelGGL((boundary_kernel<TRIPS, 0, SRC>), grid, block, 0, stream, a);
@@ -456,9 +458,7 @@ hipError_t launch_tp(const BoundaryArgs &a, int threads, hipStream_t stream) {
 
 template <Source SRC>
 hipError_t launch_src(const BoundaryArgs &a, hipStream_t stream) {
-  // Finalize keeps at most 512 threads: its gathers need the registers.
-  const Geometry g = fragment_geometry(a.slices > 1 ? a.slice_frags : a.H / kFrag,
-                                       SRC != Source::kFinalize);
+  const Geometry g = fragment_geometry(a.slices > 1 ? a.slice_frags : a.H / kFrag, true);
   switch (g.trips) {
     case 1: return launch_tp<1, SRC>(a, g.threads, stream);
     case 2: return launch_tp<2, SRC>(a, g.threads, stream);
