@@ -195,6 +195,54 @@ def run_boundary_split(b, ws):
     return u16(ro), u16(li), host(vals), host(scales)
 
 
+def expected_sync_state():
+    """The sync state mhcb_workspace_init writes: the 256-byte header and each
+    2 KiB token slot's first 64 bytes (the counters) zero, every other 32-bit
+    word the empty marker 0x7FC0DEAD."""
+    slots = np.full((1024, 512), 0x7FC0DEAD, np.uint32)
+    slots[:, :16] = 0
+    return np.concatenate([np.zeros(64, np.uint32), slots.ravel()])
+
+
+def sync_state(ws):
+    torch.cuda.synchronize()
+    return ws[:4 * (64 + 1024 * 512)].cpu().numpy().view(np.uint32)
+
+
+def test_workspace_returns_to_its_initial_state():
+    """Every kind of split call leaves the sync state as mhcb_workspace_init
+    wrote it (counters back to zero, every exchanged value back to empty),
+    so the next call on the same workspace starts clean."""
+    want = expected_sync_state()
+    ws = mhc.new_workspace(mhc.mhcb_workspace_bytes(0, 0, 1, 0), "cuda")
+    assert np.array_equal(sync_state(ws), want), "after mhcb_workspace_init"
+    b = synth.boundary(16, 8, 5120, 8, 0.5, "state-delayed")
+    for S in (0, 3, 16):
+        mhc.mhcb_set_token_slices(S)
+        try:
+            run_boundary_split(b, ws)
+        finally:
+            mhc.mhcb_set_token_slices(0)
+        assert np.array_equal(sync_state(ws), want), f"after a delayed call, S={S}"
+    for g, G, S in ((synth.glm(7), 1, 0), (synth.glm(7), 2, 0), (synth.glm(7), 4, 0),
+                    (synth.glm(20, H=2048), 16, 3), (synth.glm(20, H=2048), 16, 0),
+                    (synth.glm(300), 16, 0)):
+        M, H = g.M, g.H
+        out = (torch.empty((M, 4, H), dtype=torch.bfloat16, device="cuda"),
+               torch.empty((M, 24), dtype=torch.float32, device="cuda"),
+               torch.empty((M, H), dtype=torch.bfloat16, device="cuda"))
+        mhc.mhcb_set_token_slices(S)
+        try:
+            mhc.mhcb_boundary_glm(dev(g.partials), M * H, dev(g.residual), dev(g.post),
+                                  dev(g.comb), dev(g.fn), dev(g.scale), dev(g.base),
+                                  dev(g.gamma), *out, ws, ws.numel(), M, H, 4, g.tp, g.rms_eps,
+                                  g.hc_eps, g.norm_eps, G)
+        finally:
+            mhc.mhcb_set_token_slices(0)
+        assert np.array_equal(sync_state(ws), want), f"after {g.name} G={G} S={S}"
+    assert mhc.mhcb_workspace_status(ws) == mhc.MHCB_OK
+
+
 def test_cross_token_independence_and_determinism():
     b = synth.dsv41_delayed(128)
     ro1, li1, _ = run_boundary(b)

@@ -180,7 +180,7 @@ int mhcb_workspace_init(void *workspace, int64_t workspace_bytes, hipStream_t st
   if (!workspace || workspace_bytes < kSyncBytes)
     return fail(MHCB_EINVAL, "%s: a workspace of at least %lld bytes is required", fn, (long long)kSyncBytes);
   if (!aligned(workspace, 256)) return fail(MHCB_EALIGN, "%s: workspace must be 256-byte aligned", fn);
-  return launched(launch_zero(workspace, kSyncBytes, stream), fn);
+  return launched(launch_sync_init(workspace, stream), fn);
 }
 
 int mhcb_workspace_status(const void *workspace, hipStream_t stream) {

@@ -181,23 +181,30 @@ __device__ __forceinline__ void stage_routes(const FinalizeView &f, int tp, int 
 }
 
 // The token's sum of squares over all its slices: every slice publishes
-// its binary64 partial and arrives at the token's barrier; all then add the
+// its binary64 partial and reads the others' as they land; all add the
 // partials in slice order, so they agree bit for bit (and, the squares of
-// BF16 values being exact, with the unsplit sum).
+// BF16 values being exact, with the unsplit sum).  The kernel counts the
+// slice on exchange 0 at its end (token_sum_done).
 __device__ double token_sum(const SyncView &sy, int t, int s, int slices, double local,
                             double *shared) {
   if (threadIdx.x == 0) {
     char *slot = token_slot(sy, t);
     slot_store64(slot, kSlotSum1 + 8 * s, local);
-    token_barrier(sy, t, slices);
-    double total = 0.0;
-    for (int q = 0; q < slices; ++q) total += slot_load64(slot, kSlotSum1 + 8 * q);
-    *shared = total;
+    *shared = gather_sum64(sy, slot, kSlotSum1, slices);
   }
   __syncthreads();
   const double total = *shared;
   __syncthreads();
   return total;
+}
+
+// After token_sum's value is used: the last slice to get here writes the
+// entries back to kSlotEmpty.
+__device__ __forceinline__ void token_sum_done(const SyncView &sy, int t, int slices) {
+  if (threadIdx.x == 0 && exchange_done(sy, t, 0, slices)) {
+    char *slot = token_slot(sy, t);
+    for (int q = 0; q < slices; ++q) slot_store_u64(slot, kSlotSum1 + 8 * q, kSlotEmpty64);
+  }
 }
 
 // The fused boundary.  Workgroup (s, t) covers fragments
@@ -425,6 +432,7 @@ boundary_kernel(const BoundaryArgs a) {
       *reinterpret_cast<uint32_t *>(a.mx_scales + sf_offset(row, k, K)) = 0u;
     }
   }
+  if (a.slices > 1) token_sum_done(a.sync, t, a.slices);
 }
 
 template <int TRIPS, Source SRC>
@@ -622,6 +630,23 @@ hipError_t launch_boundary(const BoundaryArgs &a, hipStream_t stream) {
     case Source::kFinalize: return launch_src<Source::kFinalize>(a, stream);
   }
   return hipErrorInvalidValue;
+}
+
+// The sync state's initial contents: header and each slot's first 64 bytes
+// (the counters) zero, every other word kSlotEmpty.
+__global__ void __launch_bounds__(256) sync_init_kernel(uint32_t *p, int64_t words) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t in_slot = (i - 64) % (kSyncSlot / 4);
+    p[i] = i < 64 || in_slot < 16 ? 0u : kSlotEmpty;
+  }
+}
+
+hipError_t launch_sync_init(void *workspace, hipStream_t stream) {
+  const int64_t words = kSyncBytes / 4;
+  hipLaunchKernelGGL(sync_init_kernel, dim3(grid_for(words, 256)), dim3(256), 0, stream,
+                     static_cast<uint32_t *>(workspace), words);
+  return hipGetLastError();
 }
 
 hipError_t launch_zero(void *p, int64_t bytes, hipStream_t stream) {

@@ -78,6 +78,7 @@ __device__ __forceinline__ float sigmoid(float x) {
 
 template <int G>
 struct GlmShared {
+  int last[2 * G];                      // this slice ends an exchange
   float part[kMaxThreads / kWave][64];  // per-wave reduce-scatter results
   float mix[G][kMix];                   // GEMV totals of each token
   float pre[G][kStreams];
@@ -86,9 +87,11 @@ struct GlmShared {
 };
 
 // Exchanges the per-slice partials of the G tokens of a split workgroup:
-// the GEMV rows sh.mix (FP32) and one binary64 sum per token (`sums`, slot
-// offset `offset`).  Afterwards every slice holds the slice-ordered totals.
-// Contains barriers: every thread of the workgroup calls it.
+// the GEMV rows sh.mix (FP32, with `rows`) and one binary64 sum per token
+// (`sums`, slot offset `offset`).  Afterwards every slice holds the
+// slice-ordered totals.  Exchange 0 is the rows and the first sums,
+// exchange 1 the second sums; glm_exchange_done counts them at the end of
+// the kernel.  Contains barriers: every thread of the workgroup calls it.
 template <int G>
 __device__ void exchange(const GlmArgs &a, GlmShared<G> &sh, int t0, int s, double (&sums)[G],
                          int offset, bool rows) {
@@ -101,42 +104,43 @@ __device__ void exchange(const GlmArgs &a, GlmShared<G> &sh, int t0, int s, doub
     }
   }
   if (tid < G && t0 + tid < a.M) slot_store64(token_slot(a.sync, t0 + tid), offset + 8 * s, sums[tid]);
-  wait_vmem();
-  __syncthreads();
-  if (tid == 0) {  // one thread: every arrival of this slice before any wait
-    uint32_t seen[G];
-    bool done[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-      done[g] = t0 + g >= a.M || barrier_arrive(a.sync, t0 + g, a.slices, &seen[g]);
-#pragma unroll
-    for (int g = 0; g < G; ++g)
-      if (!done[g]) barrier_wait(a.sync, t0 + g, seen[g]);
-  }
-  __syncthreads();
   if (rows) {
     for (int i = tid; i < G * kMix; i += blockDim.x) {
       const int g = i / kMix, k = i % kMix;
-      if (t0 + g < a.M) {
-        const char *slot = token_slot(a.sync, t0 + g);
-        float v = 0.0f;
-        for (int q = 0; q < a.slices; ++q) v += slot_load32(slot, kSlotRows + 4 * (q * kMix + k));
-        sh.mix[g][k] = v;
-      }
+      if (t0 + g < a.M)
+        sh.mix[g][k] = gather_sum32(a.sync, token_slot(a.sync, t0 + g), kSlotRows + 4 * k, 4 * kMix, a.slices);
     }
   }
-  if (tid < G) {
-    double v = 0.0;
-    if (t0 + tid < a.M) {
-      const char *slot = token_slot(a.sync, t0 + tid);
-      for (int q = 0; q < a.slices; ++q) v += slot_load64(slot, offset + 8 * q);
-    }
-    sh.tot[tid] = v;
-  }
+  if (tid < G)
+    sh.tot[tid] = t0 + tid < a.M ? gather_sum64(a.sync, token_slot(a.sync, t0 + tid), offset, a.slices) : 0.0;
   __syncthreads();
 #pragma unroll
   for (int g = 0; g < G; ++g) sums[g] = sh.tot[g];
   __syncthreads();
+}
+
+// End of a split GLM kernel: counts this slice on both exchanges of its
+// tokens; the last slice of each writes the entries back to kSlotEmpty.
+template <int G>
+__device__ void glm_exchange_done(const GlmArgs &a, int t0, int *last) {
+  const int tid = threadIdx.x;
+  if (tid < 2 * G) {
+    const int g = tid % G, e = tid / G;
+    last[tid] = t0 + g < a.M && exchange_done(a.sync, t0 + g, e, a.slices);
+  }
+  __syncthreads();
+  const int S = a.slices, per_tok = S * (kMix + 2);  // rows, then both sums
+  for (int i = tid; i < G * per_tok; i += blockDim.x) {
+    const int g = i / per_tok, r = i % per_tok;
+    char *slot = token_slot(a.sync, t0 + g);
+    if (r < S * kMix) {
+      if (last[g]) slot_store_u32(slot, kSlotRows + 4 * r, kSlotEmpty);
+    } else if (r < S * kMix + S) {
+      if (last[g]) slot_store_u64(slot, kSlotSum1 + 8 * (r - S * kMix), kSlotEmpty64);
+    } else {
+      if (last[G + g]) slot_store_u64(slot, kSlotSum2 + 8 * (r - S * kMix - S), kSlotEmpty64);
+    }
+  }
 }
 
 // KB = hc_fn rows per pass (24 for G <= 2; 12 for G = 4 to bound registers);
@@ -313,6 +317,7 @@ glm_kernel(const GlmArgs a) {
     for (int e = 0; e < 8; ++e) o[e] = (pv[e] * inv) * gam[e];
     if (valid && t < a.M) store_stream(a.layer_input + (int64_t)t * H + col, pack8(o));
   }
+  if (a.slices > 1) glm_exchange_done<G>(a, t0, sh.last);
 }
 
 // ---------------------------------------------------------------------------
@@ -348,6 +353,7 @@ __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
 }
 
 struct TileShared {
+  int last[2];                          // this slice ends an exchange
   float post[kTile][kStreams];
   float comb[kTile][kStreams * kStreams];
   float part[kTileWaves][kTile][kMix];  // per-wave GEMV partials
@@ -367,20 +373,12 @@ __host__ __device__ inline size_t tile_dyn_bytes(int sf) {
   return tile_ys_bytes(sf) + (size_t)kTile * sf * 8;
 }
 
-__device__ __forceinline__ uint64_t slot_load_u64(const char *slot, int offset) {
-  return __hip_atomic_load(reinterpret_cast<const uint64_t *>(slot + offset), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void slot_store_u64(char *slot, int offset, uint64_t v) {
-  __hip_atomic_store(reinterpret_cast<uint64_t *>(slot + offset), v, __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // Publishes this slice's per-token sums sh.tot (and, with `rows`, the GEMV
-// partials in sh.mix), waits at the tile's barrier, and leaves the
-// slice-ordered totals in sh.tot (and sh.mix).  A thread fetches all the
-// slices' values of its (token, row) pairs with independent loads, then adds
-// them in slice order.  Every thread calls it.
+// partials in sh.mix) on exchange e of the tile, and leaves the
+// slice-ordered totals in sh.tot (and sh.mix).  A thread reads all the
+// slices' values of its (token, row pair) as they land and adds them in
+// slice order.  tile_exchange_done counts the slice at the end of the
+// kernel.  Every thread calls it.
 __device__ void tile_exchange(const GlmArgs &a, TileShared &sh, int t0, int s, int offset,
                               bool rows) {
   const int tid = threadIdx.x, nt = blockDim.x, S = a.slices;
@@ -395,25 +393,16 @@ __device__ void tile_exchange(const GlmArgs &a, TileShared &sh, int t0, int s, i
     }
   }
   if (tid < valid) slot_store64(token_slot(a.sync, t0 + tid), offset + 8 * s, sh.tot[tid]);
-  wait_vmem();
-  __syncthreads();
-  if (tid == 0) {
-    uint32_t seen;
-    if (!barrier_arrive(a.sync, t0, S, &seen)) barrier_wait(a.sync, t0, seen);
-  }
-  __syncthreads();
+  __syncthreads();  // every thread has read its own sh values before they are replaced
   // Work items: valid * 12 row pairs (with rows), then valid sums.
   const int row_items = rows ? valid * kPairs : 0;
   for (int e = tid; e < row_items + valid; e += nt) {
     const bool is_row = e < row_items;
     const int tok = is_row ? e / kPairs : e - row_items;
-    const int off = is_row ? kSlotRows + 8 * (e % kPairs) : offset;
-    const int step = is_row ? 4 * kMix : 8;  // bytes between slices
     const char *slot = token_slot(a.sync, t0 + tok);
     uint64_t w[kMaxSlices];
-#pragma unroll
-    for (int q = 0; q < kMaxSlices; ++q) w[q] = q < S ? slot_load_u64(slot, off + q * step) : 0;
     if (is_row) {
+      gather64(a.sync, slot, kSlotRows + 8 * (e % kPairs), 4 * kMix, S, w);
       float lo = 0.0f, hi = 0.0f;
 #pragma unroll
       for (int q = 0; q < kMaxSlices; ++q) {
@@ -425,16 +414,33 @@ __device__ void tile_exchange(const GlmArgs &a, TileShared &sh, int t0, int s, i
       sh.mix[tok][k] = lo;
       sh.mix[tok][k + 1] = hi;
     } else {
-      double v = 0.0;
-#pragma unroll
-      for (int q = 0; q < kMaxSlices; ++q) {
-        if (q >= S) break;
-        v += __builtin_bit_cast(double, w[q]);
-      }
-      sh.tot[tok] = v;
+      sh.tot[tok] = gather_sum64(a.sync, slot, offset, S);
     }
   }
   __syncthreads();
+}
+
+// End of the tile kernel: counts this slice on both exchanges (counters in
+// the tile's first token's slot); the last slice of each writes the tile's
+// entries back to kSlotEmpty.
+__device__ void tile_exchange_done(const GlmArgs &a, int t0, int *last) {
+  const int tid = threadIdx.x, S = a.slices;
+  if (tid < 2) last[tid] = exchange_done(a.sync, t0, tid, S);
+  __syncthreads();
+  if (!last[0] && !last[1]) return;
+  const int valid = min(kTile, a.M - t0);
+  const int per_tok = S * (kMix / 2 + 2);  // row pairs, then both sums
+  for (int i = tid; i < valid * per_tok; i += blockDim.x) {
+    const int tok = i / per_tok, r = i % per_tok;
+    char *slot = token_slot(a.sync, t0 + tok);
+    if (r < S * kMix / 2) {
+      if (last[0]) slot_store_u64(slot, kSlotRows + 8 * r, kSlotEmpty64);
+    } else if (r < S * kMix / 2 + S) {
+      if (last[0]) slot_store_u64(slot, kSlotSum1 + 8 * (r - S * kMix / 2), kSlotEmpty64);
+    } else {
+      if (last[1]) slot_store_u64(slot, kSlotSum2 + 8 * (r - S * kMix / 2 - S), kSlotEmpty64);
+    }
+  }
 }
 
 // sh.tot[tok] = sum over f < sf of item[tok][f], in fragment order.
@@ -674,6 +680,7 @@ glm_tile_kernel(const GlmArgs a) {
     for (int e = 0; e < 8; ++e) o[e] = (pv[e] * inv) * g[e];
     store_stream(a.layer_input + (int64_t)(t0 + tok[u]) * H + col[u], pack8(o));
   }
+  tile_exchange_done(a, t0, sh.last);
 }
 
 // ---------------------------------------------------------------------------

@@ -37,11 +37,12 @@ struct FinalizeView {
 // Cross-workgroup state of the token-split kernels, at the start of the
 // caller's workspace: a 256-byte header (status word), then one slot per
 // token, so that different tokens' atomics never share a cache line:
-//   +0    arrival count          +4   barrier generation   (one 8-byte word)
-//   +64   [kMaxSlices] binary64  first partial sum per slice
-//   +192  [kMaxSlices] binary64  second partial sum per slice
-//   +320  [kMaxSlices][24] FP32  partial GEMV rows per slice (GLM)
-// Zero-filled once; every call leaves the counts at zero.
+//   +0    readers done, exchange 0   +4   readers done, exchange 1
+//   +64   [kMaxSlices] binary64  first partial sum per slice  (exchange 0)
+//   +192  [kMaxSlices] binary64  second partial sum per slice (exchange 1)
+//   +320  [kMaxSlices][24] FP32  partial GEMV rows per slice  (exchange 0)
+// Initialised once (launch_sync_init: counters 0, every other word
+// kSlotEmpty); every call leaves it that way (see sync.h).
 constexpr int kSyncTokens = 1024;  // tokens a split call may have
 constexpr int kMaxSlices = 16;     // workgroups a token may be split over
 constexpr int kSyncSlot = 2048;    // bytes per token
@@ -49,7 +50,7 @@ constexpr int kSlotSum1 = 64, kSlotSum2 = 192, kSlotRows = 320;
 constexpr int64_t kSyncBytes = 256 + (int64_t)kSyncSlot * kSyncTokens;
 
 struct SyncView {
-  uint32_t *status;   // barrier time-outs
+  uint32_t *status;   // cross-workgroup waits that gave up
   char *slots;        // [kSyncTokens][kSyncSlot]
   int64_t spin_limit;
 };
@@ -134,5 +135,6 @@ Geometry fragment_geometry(int frags, bool wide = false);
 inline Geometry token_geometry(int H) { return fragment_geometry(H / 8); }
 
 hipError_t launch_zero(void *p, int64_t bytes, hipStream_t stream);
+hipError_t launch_sync_init(void *workspace, hipStream_t stream);
 
 }  // namespace mhcb

@@ -1,13 +1,21 @@
-// Cross-workgroup exchange of the token-split kernels: a per-token
-// sense-reversing barrier in the caller's workspace (layout in kernels.h).
+// Cross-workgroup exchange of the token-split kernels, in the caller's
+// workspace (slot layout in kernels.h).
 //
-// Every shared word is accessed with device-scope atomics, which are
-// performed at the device's coherence point; ordering them only needs the
-// wave's earlier accesses to have completed (wait_vmem: s_waitcnt vmcnt(0),
-// which on CDNA counts stores too), and values are read only after the
-// atomic or generation load that released the wait has returned.  Device-scope
-// release/acquire fences would instead write back / invalidate the XCD's
-// whole L2 at every arrival and every poll.
+// Every value entry of a slot holds kSlotEmpty until a slice writes it.  A
+// slice stores its partials, then reads the other slices' entries, re-reading
+// (bounded) while any is still empty: a value that is no longer empty has
+// landed, so no barrier is needed and the wait costs about one device-scope
+// round trip after the slowest slice's store.  Once a workgroup has read
+// everything it needs (at the end of the kernel, off the critical path), it
+// counts itself on the exchange's counter; the last of the slices resets the
+// counter and writes kSlotEmpty back into the entries.  The next use of the
+// slot is a later kernel launch, which the kernel boundary orders after
+// those stores.
+//
+// Every shared word is accessed with device-scope (sc1) atomics, performed at
+// the device's coherence point, because the eight XCDs' L2 caches are not
+// coherent with one another.  No release/acquire fence is used: at device
+// scope they write back / invalidate the XCD's whole L2.
 #pragma once
 
 #include "device.h"
@@ -15,73 +23,110 @@
 
 namespace mhcb {
 
+// A NaN payload that no arithmetic here produces: BF16 data converted to
+// FP32 or FP64 carries zeros in those low mantissa bits, and the hardware's
+// own NaNs are canonical.
+constexpr uint32_t kSlotEmpty = 0x7FC0DEADu;
+constexpr uint64_t kSlotEmpty64 = ((uint64_t)kSlotEmpty << 32) | kSlotEmpty;
+
 __device__ __forceinline__ char *token_slot(const SyncView &sy, int t) {
   return sy.slots + (int64_t)t * kSyncSlot;
 }
 
-__device__ __forceinline__ void slot_store64(char *slot, int offset, double v) {
-  __hip_atomic_store(reinterpret_cast<uint64_t *>(slot + offset),
-                     __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ uint64_t slot_load_u64(const char *slot, int offset) {
+  return __hip_atomic_load(reinterpret_cast<const uint64_t *>(slot + offset), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ double slot_load64(const char *slot, int offset) {
-  return __builtin_bit_cast(double, __hip_atomic_load(reinterpret_cast<const uint64_t *>(slot + offset),
-                                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+__device__ __forceinline__ void slot_store_u64(char *slot, int offset, uint64_t v) {
+  __hip_atomic_store(reinterpret_cast<uint64_t *>(slot + offset), v, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t slot_load_u32(const char *slot, int offset) {
+  return __hip_atomic_load(reinterpret_cast<const uint32_t *>(slot + offset), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void slot_store_u32(char *slot, int offset, uint32_t v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t *>(slot + offset), v, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void slot_store64(char *slot, int offset, double v) {
+  slot_store_u64(slot, offset, __builtin_bit_cast(uint64_t, v));
 }
 __device__ __forceinline__ void slot_store32(char *slot, int offset, float v) {
-  __hip_atomic_store(reinterpret_cast<uint32_t *>(slot + offset), __builtin_bit_cast(uint32_t, v),
-                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float slot_load32(const char *slot, int offset) {
-  return __builtin_bit_cast(float, __hip_atomic_load(reinterpret_cast<const uint32_t *>(slot + offset),
-                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  slot_store_u32(slot, offset, __builtin_bit_cast(uint32_t, v));
 }
 
-// Token t's barrier.  Word 0 of the slot (8 bytes) holds the arrivals of
-// the current generation in its low half and the generation in its high
-// half, so an arrival is one atomic add that also returns the generation,
-// and the last arrival starts the next generation (count back to zero,
-// generation + 1) with a second add.  It comes in two halves so that one
-// thread can take several tokens' barriers without ever waiting while it
-// still owes an arrival (arrive at all of them, then wait at each).
-//
-// barrier_arrive: one slice's arrival.  The caller must have completed its
-// stores to the slot (wait_vmem) first; that same wait also covers this
-// thread's previous add on the word, so a last arrival's reset always lands
-// before the same thread arrives again.  Returns true for the last of
-// `slices` arrivals; otherwise false with the generation to wait on in
-// *gen_seen.
-__device__ __forceinline__ bool barrier_arrive(const SyncView &sy, int t, int slices,
-                                               uint32_t *gen_seen) {
-  uint64_t *word = reinterpret_cast<uint64_t *>(token_slot(sy, t));
-  const uint64_t old = __hip_atomic_fetch_add(word, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  *gen_seen = (uint32_t)(old >> 32);
-  if ((uint32_t)old != (uint32_t)slices - 1u) return false;
-  __hip_atomic_fetch_add(word, (1ull << 32) - (uint64_t)slices, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+// One more round of a bounded wait: false (and the time-out counted in the
+// status word) once `spin_limit` rounds have passed, so every wave exits.
+__device__ __forceinline__ bool spin_again(const SyncView &sy, int64_t &spins) {
+  if (++spins > sy.spin_limit) {
+    atomicAdd(sy.status, 1u);
+    return false;
+  }
+  __builtin_amdgcn_s_sleep(2);
   return true;
 }
 
-// barrier_wait: waits for token t's generation to move past `g`.  Bounded:
-// a time-out is counted in the status word and the caller goes on (every
-// wave always exits).
-__device__ __forceinline__ void barrier_wait(const SyncView &sy, int t, uint32_t g) {
-  const uint32_t *gen = reinterpret_cast<const uint32_t *>(token_slot(sy, t)) + 1;
+// The 8-byte entries at `offset + step * q` (q < slices <= kMaxSlices) of a
+// slot, once all are written: every load is issued before any is tested.
+__device__ __forceinline__ void gather64(const SyncView &sy, const char *slot, int offset, int step,
+                                         int slices, uint64_t (&w)[kMaxSlices]) {
   int64_t spins = 0;
-  while (__hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == g) {
-    if (++spins > sy.spin_limit) {
-      atomicAdd(sy.status, 1u);
-      return;
-    }
-    __builtin_amdgcn_s_sleep(2);
+  for (;;) {
+#pragma unroll
+    for (int q = 0; q < kMaxSlices; ++q) w[q] = q < slices ? slot_load_u64(slot, offset + step * q) : 0;
+    bool missing = false;
+#pragma unroll
+    for (int q = 0; q < kMaxSlices; ++q) missing |= q < slices && w[q] == kSlotEmpty64;
+    if (!missing || !spin_again(sy, spins)) return;
+  }
+}
+__device__ __forceinline__ void gather32(const SyncView &sy, const char *slot, int offset, int step,
+                                         int slices, uint32_t (&w)[kMaxSlices]) {
+  int64_t spins = 0;
+  for (;;) {
+#pragma unroll
+    for (int q = 0; q < kMaxSlices; ++q) w[q] = q < slices ? slot_load_u32(slot, offset + step * q) : 0;
+    bool missing = false;
+#pragma unroll
+    for (int q = 0; q < kMaxSlices; ++q) missing |= q < slices && w[q] == kSlotEmpty;
+    if (!missing || !spin_again(sy, spins)) return;
   }
 }
 
-// Both halves for a single token, after this thread's slot stores.
-// Reusable any number of times per call and across calls.
-__device__ __forceinline__ void token_barrier(const SyncView &sy, int t, int slices) {
-  wait_vmem();
-  uint32_t g;
-  if (!barrier_arrive(sy, t, slices, &g)) barrier_wait(sy, t, g);
+// Binary64 entries added in slice order.
+__device__ __forceinline__ double gather_sum64(const SyncView &sy, const char *slot, int offset,
+                                               int slices) {
+  uint64_t w[kMaxSlices];
+  gather64(sy, slot, offset, 8, slices, w);
+  double total = 0.0;
+#pragma unroll
+  for (int q = 0; q < kMaxSlices; ++q)
+    if (q < slices) total += __builtin_bit_cast(double, w[q]);
+  return total;
+}
+// FP32 entries `step` bytes apart, added in slice order.
+__device__ __forceinline__ float gather_sum32(const SyncView &sy, const char *slot, int offset,
+                                              int step, int slices) {
+  uint32_t w[kMaxSlices];
+  gather32(sy, slot, offset, step, slices, w);
+  float total = 0.0f;
+#pragma unroll
+  for (int q = 0; q < kMaxSlices; ++q)
+    if (q < slices) total += __builtin_bit_cast(float, w[q]);
+  return total;
+}
+
+// This workgroup has read everything it needs of exchange e (0 or 1) whose
+// counter is in token t's slot.  True for the last of `slices` workgroups,
+// which has reset the counter and must write kSlotEmpty back into the
+// exchange's entries.
+__device__ __forceinline__ bool exchange_done(const SyncView &sy, int t, int e, int slices) {
+  uint32_t *count = reinterpret_cast<uint32_t *>(token_slot(sy, t)) + e;
+  const uint32_t old = __hip_atomic_fetch_add(count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (old != (uint32_t)slices - 1u) return false;
+  __hip_atomic_store(count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
 }
 
 }  // namespace mhcb

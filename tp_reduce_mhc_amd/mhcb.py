@@ -221,7 +221,7 @@ _WORKSPACES = {}
 
 def workspace(device=None, *, M: int = 0, hidden_size: int = 0, tp: int = 1,
               two_shot: bool = False) -> torch.Tensor:
-    """A zero-initialized workspace on `device`, cached per (device, size):
+    """An initialized workspace on `device`, cached per (device, size):
     the sync state of the token-split calls, plus the two-shot scratch when
     asked.  Calls on different streams need their own (fresh=True is not
     offered: allocate with new_workspace)."""
@@ -237,9 +237,12 @@ def workspace(device=None, *, M: int = 0, hidden_size: int = 0, tp: int = 1,
     return ws
 
 
-def new_workspace(nbytes: int, device) -> torch.Tensor:
-    """A fresh zero-filled workspace of `nbytes` (256-byte aligned by torch)."""
-    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+def new_workspace(nbytes: int, device, stream=None) -> torch.Tensor:
+    """A fresh workspace of `nbytes` (256-byte aligned by torch), initialized
+    by mhcb_workspace_init on `stream` (the current stream by default)."""
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    mhcb_workspace_init(ws, nbytes, stream)
+    return ws
 
 
 def boundary(partials: torch.Tensor, residual, post, comb, pre, norm_weight, norm_eps: float,
