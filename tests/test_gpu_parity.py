@@ -243,6 +243,67 @@ def test_workspace_returns_to_its_initial_state():
     assert mhc.mhcb_workspace_status(ws) == mhc.MHCB_OK
 
 
+def test_graph_replays_match_eager_calls():
+    """Split calls captured in one HIP graph (delayed boundary with MXFP8,
+    MoE finalize, GLM tiles, all exchanging through one workspace) and
+    replayed three times, with eager calls on the same workspace in between,
+    give the eager results every time and leave the workspace clean."""
+    b = synth.boundary(17, 8, 1024, 8, 0.5, "graph-delayed")
+    f = synth.moe_finalize(8, H=1024)
+    g = synth.glm(40, H=2048)
+    ws = mhc.new_workspace(mhc.mhcb_workspace_bytes(0, 0, 1, 0), "cuda")
+    db = {k: dev(getattr(b, k)) for k in ("partials", "residual", "post", "comb", "pre", "gamma")}
+    df = {k: dev(getattr(f, k)) for k in ("gemm2", "weights", "idx", "shared", "residual", "post",
+                                          "comb", "pre", "gamma")}
+    dg = {k: dev(getattr(g, k)) for k in ("partials", "residual", "post", "comb", "fn", "scale",
+                                          "base", "gamma")}
+    outs = {
+        "b_ro": torch.empty((b.M, 4, b.H), dtype=torch.bfloat16, device="cuda"),
+        "b_li": torch.empty((b.M, b.H), dtype=torch.bfloat16, device="cuda"),
+        "b_v": torch.empty((b.M, b.H), dtype=torch.uint8, device="cuda"),
+        "b_s": torch.empty(mhc.mhcb_mxfp8_scale_bytes(b.M, b.H), dtype=torch.uint8, device="cuda"),
+        "f_ro": torch.empty((f.M, 4, f.H), dtype=torch.bfloat16, device="cuda"),
+        "f_li": torch.empty((f.M, f.H), dtype=torch.bfloat16, device="cuda"),
+        "g_ro": torch.empty((g.M, 4, g.H), dtype=torch.bfloat16, device="cuda"),
+        "g_mx": torch.empty((g.M, 24), dtype=torch.float32, device="cuda"),
+        "g_li": torch.empty((g.M, g.H), dtype=torch.bfloat16, device="cuda"),
+    }
+    rows = f.M * f.top_k
+
+    def calls():
+        mhc.mhcb_boundary(db["partials"], b.M * b.H, None, db["residual"], db["post"], db["comb"],
+                          db["pre"], db["gamma"], outs["b_ro"], outs["b_li"], outs["b_v"],
+                          outs["b_s"], ws, ws.numel(), b.M, b.H, 4, b.tp, b.norm_eps)
+        mhc.mhcb_finalize(df["gemm2"], rows * f.H, rows, df["weights"], 0, df["idx"], 0,
+                          df["shared"], f.M * f.H, df["residual"], df["post"], df["comb"],
+                          df["pre"], df["gamma"], outs["f_ro"], outs["f_li"], None, None, 0, ws,
+                          ws.numel(), f.M, f.H, 4, f.tp, f.top_k, f.norm_eps)
+        mhc.mhcb_boundary_glm(dg["partials"], g.M * g.H, dg["residual"], dg["post"], dg["comb"],
+                              dg["fn"], dg["scale"], dg["base"], dg["gamma"], outs["g_ro"],
+                              outs["g_mx"], outs["g_li"], ws, ws.numel(), g.M, g.H, 4, g.tp,
+                              g.rms_eps, g.hc_eps, g.norm_eps, 16)
+
+    calls()
+    torch.cuda.synchronize()
+    want = {k: v.clone() for k, v in outs.items()}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        calls()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for v in outs.values():
+            v.fill_(0x5A if v.dtype == torch.uint8 else float("nan"))
+        run_boundary_split(b, ws)                       # eager work on the same workspace
+        graph.replay()
+        torch.cuda.synchronize()
+        for k, v in outs.items():
+            assert torch.equal(v.view(torch.uint8), want[k].view(torch.uint8)), f"replay {rep}: {k}"
+    assert mhc.mhcb_workspace_status(ws) == mhc.MHCB_OK
+    assert np.array_equal(sync_state(ws), expected_sync_state())
+
+
 def test_cross_token_independence_and_determinism():
     b = synth.dsv41_delayed(128)
     ro1, li1, _ = run_boundary(b)
