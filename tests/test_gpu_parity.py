@@ -610,3 +610,65 @@ def test_bad_arguments_leave_mailbox_untouched():
     torch.cuda.synchronize()
     assert_bits_equal(u16(mb.slots), before_slots, "slots")
     assert np.array_equal(host(mb.stage_state), before_stage)
+
+
+# ---------------------------------------------------------------------------
+# Seeded random shapes
+# ---------------------------------------------------------------------------
+
+def _random_shapes(seed, count):
+    rng = np.random.default_rng([seed, 20260])
+    for i in range(count):
+        H = int(rng.choice([8, 24, 136, 512, 1000, 2048, 3072, 5120, 7168, 8192, 12288, 16384]))
+        M = int(rng.integers(1, 300))
+        tp = int(rng.choice([1, 2, 3, 4, 5, 8, 12, 16]))
+        slices = int(rng.choice([0, 1, 2, 3, 16]))
+        yield i, M, H, tp, slices
+
+
+@pytest.mark.parametrize("case", list(_random_shapes(1, 12)), ids=lambda c: f"M{c[1]}-H{c[2]}-tp{c[3]}-S{c[4]}")
+def test_delayed_random_shapes(case):
+    """Delayed boundary on seeded random (M, hidden, tp, slices): residual
+    streams bit-exact, layer input within 1 ulp (bit-exact in practice), and
+    the MXFP8 epilogue bit-exact wherever hidden % 128 == 0."""
+    i, M, H, tp, S = case
+    b = synth.boundary(40 + i, M, H, tp, 0.5, f"random-{i}")
+    mxfp8 = H % 128 == 0
+    ws = mhc.workspace("cuda")
+    prev = mhc.mhcb_set_token_slices(S)
+    try:
+        got = run_boundary_split(b, ws) if mxfp8 else None
+        if not mxfp8:
+            ro = torch.empty((M, 4, H), dtype=torch.bfloat16, device="cuda")
+            li = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+            mhc.mhcb_boundary(dev(b.partials), M * H, None, dev(b.residual), dev(b.post),
+                              dev(b.comb), dev(b.pre), dev(b.gamma), ro, li, None, None, ws,
+                              ws.numel(), M, H, 4, tp, b.norm_eps)
+            torch.cuda.synchronize()
+            got = (u16(ro), u16(li), None, None)
+    finally:
+        mhc.mhcb_set_token_slices(prev)
+    print(f"[gpu] {b.name} M={M} H={H} tp={tp} S={S} mxfp8={mxfp8}", flush=True)
+    ro_ref, li_ref, _ = oracle.boundary(b.partials, b.residual, b.post, b.comb, b.pre, b.gamma,
+                                        b.norm_eps, threads=8)
+    assert_bits_equal(got[0], ro_ref, "residual_out")
+    assert_within_ulp(got[1], li_ref, 1, "layer_input")
+    if mxfp8:
+        v_q, s_q = oracle.quant_mxfp8(got[1])
+        assert_bits_equal(got[2], v_q, "mxfp8 values")
+        assert_bits_equal(got[3], s_q, "mxfp8 scales")
+    assert mhc.mhcb_workspace_status(ws) == mhc.MHCB_OK
+
+
+@pytest.mark.parametrize("case", [(0, 5, 1024, 3, 1), (1, 33, 3072, 8, 2), (2, 2, 8192, 2, 4),
+                                  (3, 70, 512, 8, 16), (4, 300, 2048, 5, 0), (5, 17, 6144, 12, 16)],
+                         ids=lambda c: f"M{c[1]}-H{c[2]}-tp{c[3]}-G{c[4]}")
+def test_glm_random_shapes(case):
+    """GLM on mixed shapes, tokens per workgroup and tiles, against the oracle."""
+    i, M, H, tp, G = case
+    g = synth.glm(M, H=H, tp=tp, name=f"glm-random-{i}")
+    if G == 4 and H > 6144:
+        G = 2
+    print(f"[gpu] {g.name} M={M} H={H} tp={tp} G={G}", flush=True)
+    ro, mixes, li = run_glm(g, G)
+    check_glm_against_oracle(g, ro, mixes, li, f"G={G}")
