@@ -672,3 +672,24 @@ def test_glm_random_shapes(case):
     print(f"[gpu] {g.name} M={M} H={H} tp={tp} G={G}", flush=True)
     ro, mixes, li = run_glm(g, G)
     check_glm_against_oracle(g, ro, mixes, li, f"G={G}")
+
+
+@pytest.mark.parametrize("case", [(3, 1024, 1, 1, True, 0.0), (17, 2048, 2, 16, False, 0.3),
+                                  (64, 5120, 4, 6, True, 0.0), (40, 3072, 8, 2, False, 0.5),
+                                  (130, 512, 3, 8, True, 0.0)],
+                         ids=lambda c: f"M{c[0]}-H{c[1]}-tp{c[2]}-k{c[3]}")
+def test_finalize_random_shapes(case):
+    """MoE finalize on mixed (M, hidden, tp, top_k, routing): split and
+    unsplit, hoisted and runtime-rank gathers, dropped routes; one-shot and
+    two-shot give the same bits and match the oracle."""
+    M, H, tp, k, replicated, drop = case
+    f = synth.moe_finalize(M, H=H, tp=tp, top_k=k, replicated_routing=replicated,
+                           drop_fraction=drop)
+    print(f"[gpu] {f.name} M={M} H={H} tp={tp} top_k={k}", flush=True)
+    ro_ref, li_ref, _ = oracle.finalize(f.gemm2, f.weights, f.idx, f.shared, f.residual, f.post,
+                                        f.comb, f.pre, f.gamma, f.norm_eps,
+                                        replicated_routing=replicated, threads=8)
+    for two_shot, split in ((False, True), (False, False), (True, True)):
+        ro, li, _ = run_finalize(f, two_shot=two_shot, split=split)
+        assert_bits_equal(ro, ro_ref, f"residual_out two_shot={two_shot} split={split}")
+        assert_within_ulp(li, li_ref, 1, f"layer_input two_shot={two_shot} split={split}")
