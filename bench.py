@@ -360,8 +360,8 @@ def main():
     def want(name):
         return not only or name in only
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this build has no "
-              "multi-GPU path; the boundary would shard over tokens, see the design notes)",
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (libmhcb has no "
+              "multi-GPU path; the boundary would shard over tokens)",
               file=sys.stderr)
         sys.exit(2)
 

@@ -40,7 +40,7 @@ enum mhcb_status {
   MHCB_OK = 0,
   MHCB_EINVAL = 1,       /* bad size, shape, null pointer or combination     */
   MHCB_EALIGN = 2,       /* pointer or stride breaks the alignment rules     */
-  MHCB_EUNSUPPORTED = 3, /* valid per the pages but outside this build       */
+  MHCB_EUNSUPPORTED = 3, /* valid per the pages but not handled by libmhcb   */
   MHCB_ELAUNCH = 4,      /* the HIP runtime rejected a launch                */
   MHCB_ETIMEOUT = 5      /* a mailbox poll gave up (see mhcb_mailbox_status) */
 };

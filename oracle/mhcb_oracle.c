@@ -19,7 +19,7 @@
  * Where the pages leave an order to a hardware reduction tree (sums of
  * squares, the 24-row GEMV) the sum is accumulated in binary64 and rounded
  * to binary32 once.  exp, 1/x and 1/sqrt are evaluated in binary64 and
- * rounded once.  Every reading of an open point is listed in the design notes.
+ * rounded once.
  *
  * All arrays are row-major and dense unless a stride is passed.  BF16 values
  * are uint16_t bit patterns.  Work is split over tokens across `threads`
