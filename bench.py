@@ -259,7 +259,7 @@ def bench_finalize(torch, mhc, f, steps, warmup, two_shot=False):
     return ms, per_set + extra
 
 
-def bench_glm(torch, mhc, g, steps, warmup):
+def bench_glm(torch, mhc, g, steps, warmup, tokens_per_wg=0):
     per_set = bytes_glm(g.M, g.H, g.tp)
     t = dict(partials=dev(torch, g.partials), residual=dev(torch, g.residual),
              post=dev(torch, g.post), comb=dev(torch, g.comb))
@@ -277,7 +277,8 @@ def bench_glm(torch, mhc, g, steps, warmup):
         s = sets[i % len(sets)]
         mhc.mhcb_boundary_glm(s["partials"], g.M * g.H, s["residual"], s["post"], s["comb"], fn,
                               scale, base, gamma, s["residual_out"], s["mixes"], s["layer_input"],
-                              ws, ws.numel(), g.M, g.H, 4, g.tp, g.rms_eps, g.hc_eps, g.norm_eps, 0)
+                              ws, ws.numel(), g.M, g.H, 4, g.tp, g.rms_eps, g.hc_eps, g.norm_eps,
+                              tokens_per_wg)
 
     ms = Timed(torch, call, steps, warmup).run()
     return ms, per_set
@@ -423,11 +424,16 @@ def main():
                 extra[f"moe_finalize_two_shot_M{M}"] = entry(ms, nbytes, M)
             del f
     if want("glm") and not args.quick:
-        for M in (1, 64, 512):
+        for M in (1, 16, 64, 256, 512):
             g = synth.glm(M)
             ms, nbytes = bench_glm(torch, mhc, g, min(K, 100), min(W, 5))
             extra[f"glm_M{M}"] = entry(ms, nbytes, M)
             log(f"glm M={M}: {extra[f'glm_M{M}']}")
+            if M == 64:  # the tokens-per-workgroup choices at one size
+                for G in (1, 2, 4, 16):
+                    ms, nbytes = bench_glm(torch, mhc, g, min(K, 100), min(W, 5), G)
+                    extra[f"glm_M64_tokens_per_wg{G}"] = entry(ms, nbytes, M)
+                    log(f"glm M=64 tokens_per_wg={G}: {extra[f'glm_M64_tokens_per_wg{G}']}")
     if (want("mxfp8") or want("mailbox")) and not args.quick:
         b = synth.large_m_delayed(8192)
         if want("mxfp8"):
