@@ -180,25 +180,34 @@ __device__ __forceinline__ void stage_routes(const FinalizeView &f, int tp, int 
   __syncthreads();
 }
 
-// The token's sum of squares over all its slices: every slice publishes
-// its binary64 partial and reads the others' as they land; all add the
-// partials in slice order, so they agree bit for bit (and, the squares of
-// BF16 values being exact, with the unsplit sum).  The kernel counts the
-// slice on exchange 0 at its end (token_sum_done).
-__device__ double token_sum(const SyncView &sy, int t, int s, int slices, double local,
-                            double *shared) {
+// The token's RMSNorm factor inv = (float)(1/sqrt((double)(float)ss/H +
+// eps)) from each thread's binary64 sum of squares: wave xor sums, then one
+// thread adds the waves in index order (and, split, publishes its slice's
+// partial and adds the slices' in slice order: the squares of BF16 values
+// are exact in binary64, so the bits do not depend on the split), evaluates
+// inv once and shares it through LDS.  The kernel counts the slice on
+// exchange 0 at its end (token_sum_done).  Every thread calls it.
+__device__ float token_inv(const BoundaryArgs &a, int t, int s, double ss, double *red) {
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  ss = wave_sum(ss);
+  if (lane == 0) red[wave] = ss;
+  __syncthreads();
   if (threadIdx.x == 0) {
-    char *slot = token_slot(sy, t);
-    slot_store64(slot, kSlotSum1 + 8 * s, local);
-    *shared = gather_sum64(sy, slot, kSlotSum1, slices);
+    double total = 0.0;
+    for (int w = 0; w < (int)blockDim.x / kWave; ++w) total += red[w];
+    if (a.slices > 1) {
+      char *slot = token_slot(a.sync, t);
+      slot_store64(slot, kSlotSum1 + 8 * s, total);
+      total = gather_sum64(a.sync, slot, kSlotSum1, a.slices);
+    }
+    red[kTokenThreadsWide / kWave] =
+        (double)(float)(1.0 / __builtin_sqrt((double)(float)total / (double)a.H + (double)a.norm_eps));
   }
   __syncthreads();
-  const double total = *shared;
-  __syncthreads();
-  return total;
+  return (float)red[kTokenThreadsWide / kWave];
 }
 
-// After token_sum's value is used: the last slice to get here writes the
+// After token_inv's value is used: the last slice to get here writes the
 // entries back to kSlotEmpty.
 __device__ __forceinline__ void token_sum_done(const SyncView &sy, int t, int slices) {
   if (threadIdx.x == 0 && exchange_done(sy, t, 0, slices)) {
@@ -382,10 +391,7 @@ boundary_kernel(const BoundaryArgs a) {
   // a4 (second half): inv = 1/sqrt(sum p^2 / H + eps); out = bf16((p*inv)*gamma).
   // The squares of BF16 values are exact in binary64 and so is their sum,
   // whatever the order or the split.
-  double tot[1] = {ss};
-  block_sum<double, 1>(tot, red);
-  if (a.slices > 1) tot[0] = token_sum(a.sync, t, s, a.slices, tot[0], red + kTokenThreadsWide / kWave);
-  const float inv = (float)(1.0 / __builtin_sqrt((double)(float)tot[0] / (double)H + (double)a.norm_eps));
+  const float inv = token_inv(a, t, s, ss, red);
 
 #pragma unroll
   for (int i = 0; i < TRIPS; ++i) {
