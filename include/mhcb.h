@@ -147,7 +147,7 @@ int mhcb_boundary(const uint16_t *partials, int64_t rank_stride, const mhcb_mail
  * cores (needs a workspace); its FP32 sums are taken in another order, so
  * mixes_out may differ from the 1/2/4 results in the last bits (both agree
  * with the exact GEMV to about 1e-6 relative).  0 = chosen by M
- * (16 above M = 256 when a workspace is given).  hidden <= 8192.
+ * (16 from M = 256 when a workspace is given).  hidden <= 8192.
  * workspace: optional for 1, 2, 4 (see mhcb_workspace_bytes); calls that
  * share one must be ordered on one stream. */
 int mhcb_boundary_glm(const uint16_t *partials, int64_t rank_stride, const uint16_t *residual,

@@ -39,7 +39,7 @@ constexpr int kMaxHiddenGlm = 8192;
 constexpr int kMaxTp = 64;
 constexpr int kMaxRoutes = 1024;
 constexpr int64_t kDefaultSpin = 1 << 20;
-constexpr int kGlmTileMinM = 257;  // automatic matrix-core tiles from this M
+constexpr int kGlmTileMinM = 256;  // automatic matrix-core tiles from this M
 
 // Checks shared by the boundary variants ([DSV41] AllReduceMHC._check and
 // _consumer, _LamportMHCDeviceKernel.__init__).
@@ -268,10 +268,11 @@ int mhcb_boundary_glm(const uint16_t *partials, int64_t rank_stride, const uint1
       !aligned(mixes_out, 4))
     return fail(MHCB_EALIGN, "%s: partials/hc_fn must be 16-byte aligned, rank_stride %% 8 == 0", fn);
   int G = tokens_per_wg;
-  // Measured on MI355X (H=6144, tp=8): one token per workgroup is fastest up
-  // to M=256 (25.7 us; two: 28.7, 16-token tiles: 25.8), 16-token tiles in 8
-  // slices beyond (M=512: 33.2 us; one token: 47.1, two: 36.5).  Without a
-  // workspace, two tokens per workgroup beyond M=256.
+  // Measured on MI355X (H=6144, tp=8): one token per workgroup below M=256
+  // (M=128: 18.8 us; 16-token tiles: 22.3), 16-token tiles from M=256
+  // (24.8 us; one token: 25.7, two: 28.7) and beyond (M=512: 33.2 us; one
+  // token: 47.1, two: 36.5).  Without a workspace, two tokens per workgroup
+  // beyond M=256.
   if (G == 0) G = workspace && M >= kGlmTileMinM ? kGlmTileTokens : (M <= 256 ? 1 : 2);
   if (G != 1 && G != 2 && G != 4 && G != kGlmTileTokens)
     return fail(MHCB_EINVAL, "%s: tokens_per_wg=%d (0, 1, 2, 4 or 16)", fn, tokens_per_wg);

@@ -343,7 +343,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = 16;              // tokens per tile
-constexpr int kTileThreads = 768;      // at most
+constexpr int kTileThreads = 512;      // at most
 constexpr int kTileWaves = kTileThreads / kWave;
 constexpr int kTileMaxFrags = 96;      // fragments per slice
 
@@ -473,7 +473,7 @@ __device__ __forceinline__ void load_fn_chunk(const GlmArgs &a, int i, int f, bo
 // U = (token, fragment) items per thread, and also 4-fragment GEMV chunks
 // per wave; TP = fixed rank count, or 0 for the runtime count.
 template <int U, int TP>
-__global__ void __launch_bounds__(U <= 2 ? kTileThreads : 512, 1)
+__global__ void __launch_bounds__(kTileThreads, 1)
 glm_tile_kernel(const GlmArgs a) {
   __shared__ TileShared sh;
   extern __shared__ __align__(16) char dyn[];
@@ -757,13 +757,14 @@ hipError_t launch_boundary_glm(const GlmArgs &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Tile geometry: 16 * slice_frags items, about three per thread (at most
+// Tile geometry: 16 * slice_frags items, two or three per thread (at most
 // 512 threads, four items); dynamic LDS sized by the slice.
 hipError_t launch_boundary_glm_tile(const GlmArgs &a, hipStream_t stream) {
   const int sf = a.slice_frags;
   if (sf % 4 || sf > kTileMaxFrags || a.slices > kMaxSlices) return hipErrorInvalidValue;
   const int items = kTile * sf;
-  // Two items per thread (up to 768 threads); three beyond that.
+  // Two items per thread (up to 512 threads); three beyond that.  Every
+  // rank load of every item is then issued before the first use (tp = 8).
   int threads = ((items + 1) / 2 + kWave - 1) / kWave * kWave;
   if (threads > kTileThreads) threads = ((items + 2) / 3 + kWave - 1) / kWave * kWave;
   threads = threads > kTileThreads ? kTileThreads : threads;
@@ -788,7 +789,7 @@ hipError_t launch_boundary_glm_tile(const GlmArgs &a, hipStream_t stream) {
   }
   switch (U) {
     case 1: MHCB_TILE(1) break;
-    case 2: MHCB_TILE_LAUNCH(2, 0) break;  // eight held ranks would spill at 768 threads
+    case 2: MHCB_TILE(2) break;
     case 3: MHCB_TILE(3) break;
     default: MHCB_TILE_LAUNCH(4, 0) break;  // four items of eight held ranks would spill
   }
