@@ -60,18 +60,22 @@ int64_t mhcb_mxfp8_scale_bytes(int64_t M, int64_t hidden_size);
  * device workspace (256-byte aligned).  Its first part holds the state of
  * the cross-workgroup reduction that lets small-M calls spread each token
  * over several workgroups (with NULL every token takes one workgroup); it
- * must be initialized once (mhcb_workspace_init) before its first use, and
- * every call leaves it in that initial state for the next one.  Calls that may run
- * concurrently (on different streams) must not share a workspace.
+ * must be initialized once (mhcb_workspace_init) before its first use.  Each
+ * token slot has two copies of its exchange area, used by alternate calls;
+ * a call clears the copy the previous call used while it works, so the
+ * state is ready for the next call, with any slice count, with no reset at
+ * the end.  Calls that may run concurrently (on different streams) must not
+ * share a workspace.
  * mhcb_workspace_bytes gives the size for a call: the sync state, plus for
  * the two-shot emulation (mhcb_finalize, two_shot = 1) the owner mailboxes
  * [tp][tp][ceil(M/tp)][hidden] and the reduced sums [M][hidden] (BF16).
  * Host-only; -1 on bad sizes. */
 int64_t mhcb_workspace_bytes(int M, int hidden_size, int tp, int two_shot);
 
-/* Writes the workspace's sync state (a kernel on `stream`): counters zero,
- * every exchange entry the empty marker.  A timed-out call (see
- * mhcb_workspace_status) may leave it otherwise: initialize it again. */
+/* Writes the workspace's sync state (a kernel on `stream`): status word and
+ * epochs zero, every exchange word the empty marker.  After a timed-out call
+ * (see mhcb_workspace_status) the status stays set until the workspace is
+ * initialized again. */
 int mhcb_workspace_init(void *workspace, int64_t workspace_bytes, hipStream_t stream);
 
 /* Synchronizes `stream`; MHCB_ETIMEOUT if a cross-workgroup wait of a call

@@ -80,7 +80,7 @@ def _boundary(**kw):
     (dict(rank_stride=4 * 512 + 4), 2, "rank_stride"),
     (dict(residual_out=None), 1, "required"),
     (dict(workspace=FAKE, workspace_bytes=100), 1, "workspace_bytes"),
-    (dict(workspace=FAKE + 16, workspace_bytes=1 << 22), 2, "256-byte"),
+    (dict(workspace=FAKE + 16, workspace_bytes=1 << 23), 2, "256-byte"),
 ])
 def test_boundary_validation(kw, code, text):
     import tp_reduce_mhc_amd as mhc
@@ -132,7 +132,7 @@ def test_glm_mixes_finalize_quant_validation():
                hidden_size=512, hc_mult=4, tp=2, top_k=8, norm_eps=1e-6, stream=0)
     for kw, text in ((dict(top_k=0), "top_k"), (dict(tp=64, top_k=32), "exceeds"),
                      (dict(two_shot=1), "workspace"), (dict(rows=-1), "rows"),
-                     (dict(two_shot=1, workspace=FAKE + 8, workspace_bytes=1 << 22), "aligned"),
+                     (dict(two_shot=1, workspace=FAKE + 8, workspace_bytes=1 << 23), "aligned"),
                      (dict(two_shot=1, workspace=FAKE, workspace_bytes=1 << 10), "workspace_bytes")):
         with pytest.raises(mhc.MhcbError, match=text):
             mhc.mhcb_finalize(**{**fin, **kw})
@@ -141,7 +141,7 @@ def test_glm_mixes_finalize_quant_validation():
     with pytest.raises(mhc.MhcbError, match="at least"):
         mhc.mhcb_workspace_init(FAKE, 64, 0)
     with pytest.raises(mhc.MhcbError, match="256-byte"):
-        mhc.mhcb_workspace_init(FAKE + 64, 1 << 22, 0)
+        mhc.mhcb_workspace_init(FAKE + 64, 1 << 23, 0)
 
 
 def test_product_path_does_not_touch_the_oracle():

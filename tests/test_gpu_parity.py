@@ -195,59 +195,110 @@ def run_boundary_split(b, ws):
     return u16(ro), u16(li), host(vals), host(scales)
 
 
-def expected_sync_state():
-    """The sync state mhcb_workspace_init writes: the 256-byte header and each
-    2 KiB token slot's first 64 bytes (the counters) zero, every other 32-bit
-    word the empty marker 0x7FC0DEAD."""
-    slots = np.full((1024, 512), 0x7FC0DEAD, np.uint32)
-    slots[:, :16] = 0
-    return np.concatenate([np.zeros(64, np.uint32), slots.ravel()])
+# The sync state: a 256-byte header, then a 4 KiB slot per token holding the
+# epoch word (split calls on the slot, low 32 bits; the last one's slice
+# count, high 32 bits) at +0 and two 1792-byte copies of the exchange area at
+# +128 and +1920; a call uses copy epoch % 2.
+EMPTY = 0x7FC0DEAD
 
 
 def sync_state(ws):
+    """(epochs [1024], last slice counts [1024], copies [1024, 2, 448] as
+    32-bit words, status)."""
     torch.cuda.synchronize()
-    return ws[:4 * (64 + 1024 * 512)].cpu().numpy().view(np.uint32)
+    raw = ws[:256 + 4096 * 1024].cpu().numpy()
+    slots = raw[256:].reshape(1024, 4096)
+    epoch_word = slots[:, :8].copy().view(np.uint32)
+    copies = np.stack([slots[:, 128:1920].copy().view(np.uint32),
+                       slots[:, 1920:3712].copy().view(np.uint32)], axis=1)
+    return (epoch_word[:, 0].astype(np.int64), epoch_word[:, 1].astype(np.int64), copies,
+            int(raw[:4].view(np.uint32)[0]))
 
 
-def test_workspace_returns_to_its_initial_state():
-    """Every kind of split call leaves the sync state as mhcb_workspace_init
-    wrote it (counters back to zero, every exchanged value back to empty),
-    so the next call on the same workspace starts clean."""
-    want = expected_sync_state()
+def run_glm_on(g, G, ws):
+    M, H = g.M, g.H
+    out = (torch.empty((M, 4, H), dtype=torch.bfloat16, device="cuda"),
+           torch.empty((M, 24), dtype=torch.float32, device="cuda"),
+           torch.empty((M, H), dtype=torch.bfloat16, device="cuda"))
+    mhc.mhcb_boundary_glm(dev(g.partials), M * H, dev(g.residual), dev(g.post), dev(g.comb),
+                          dev(g.fn), dev(g.scale), dev(g.base), dev(g.gamma), *out, ws,
+                          ws.numel(), M, H, 4, g.tp, g.rms_eps, g.hc_eps, g.norm_eps, G)
+    torch.cuda.synchronize()
+    return u16(out[0]), host(out[1]), u16(out[2])
+
+
+def effective_slices(F, S):
+    """The library's slice count for a requested S over F fragments: slices
+    of ceil(F/S) fragments rounded up to a multiple of 4."""
+    frags = -(-F // S)
+    frags = -(-frags // 4) * 4
+    return -(-F // frags)
+
+
+def check_call_state(ws, want_epochs, want_slices, what):
+    """After a call: every slot's epoch counts its split calls and records the
+    last one's slice count, and the copy the next call on the slot will use
+    is entirely empty (so it starts clean whatever its slice count)."""
+    epochs, slices, copies, status = sync_state(ws)
+    assert status == 0, f"a wait gave up ({what})"
+    assert np.array_equal(epochs, want_epochs), f"epochs after {what}"
+    assert np.array_equal(slices, want_slices), f"last slice counts after {what}"
+    nxt = copies[np.arange(1024), epochs % 2]
+    assert (nxt == EMPTY).all(), f"the next call's copy is not empty after {what}"
+
+
+def test_workspace_epochs_and_clean_copies():
+    """mhcb_workspace_init writes the epochs 0 and every exchange word empty.
+    Every split call advances the epoch of its tokens' slots and leaves the
+    copy the next call will use empty, with no reset at its end: the slices
+    clear the previous call's entries while they work.  The slice count
+    changes from call to call (16, 3, 1, 16, 2, ...), every result still
+    matches (the delayed boundary bit for bit with the unsplit call) and no
+    wait gives up."""
     ws = mhc.new_workspace(mhc.mhcb_workspace_bytes(0, 0, 1, 0), "cuda")
-    assert np.array_equal(sync_state(ws), want), "after mhcb_workspace_init"
+    want = np.zeros(1024, np.int64)
+    want_s = np.zeros(1024, np.int64)
+    epochs, slices, copies, status = sync_state(ws)
+    assert status == 0 and not epochs.any() and not slices.any() and (copies == EMPTY).all()
+
     b = synth.boundary(16, 8, 5120, 8, 0.5, "state-delayed")
-    for S in (0, 3, 16):
+    ref = run_boundary_split(b, None)
+    for S in (16, 3, 1, 16, 2, 5, 16):
         mhc.mhcb_set_token_slices(S)
         try:
-            run_boundary_split(b, ws)
+            got = run_boundary_split(b, ws)
         finally:
             mhc.mhcb_set_token_slices(0)
-        assert np.array_equal(sync_state(ws), want), f"after a delayed call, S={S}"
-    for g, G, S in ((synth.glm(7), 1, 0), (synth.glm(7), 2, 0), (synth.glm(7), 4, 0),
-                    (synth.glm(20, H=2048), 16, 3), (synth.glm(20, H=2048), 16, 0),
-                    (synth.glm(300), 16, 0)):
-        M, H = g.M, g.H
-        out = (torch.empty((M, 4, H), dtype=torch.bfloat16, device="cuda"),
-               torch.empty((M, 24), dtype=torch.float32, device="cuda"),
-               torch.empty((M, H), dtype=torch.bfloat16, device="cuda"))
+        for x, y, what in zip(got, ref, ("residual_out", "layer_input", "values", "scales")):
+            assert_bits_equal(x, y, f"delayed S={S} {what}")
+        if S > 1:
+            want[:b.M] += 1
+            want_s[:b.M] = effective_slices(640, S)
+        check_call_state(ws, want, want_s, f"delayed S={S}")
+
+    # (GLM input, tokens per workgroup, slices); 16 = tiles.
+    for g, G, S in ((synth.glm(7), 1, 2), (synth.glm(7), 2, 16), (synth.glm(7), 4, 5),
+                    (synth.glm(20, H=2048), 16, 3), (synth.glm(20, H=2048), 16, 16),
+                    (synth.glm(20, H=2048), 16, 4), (synth.glm(300), 16, 8)):
+        print(f"[gpu] {g.name} G={G} S={S}", flush=True)
         mhc.mhcb_set_token_slices(S)
         try:
-            mhc.mhcb_boundary_glm(dev(g.partials), M * H, dev(g.residual), dev(g.post),
-                                  dev(g.comb), dev(g.fn), dev(g.scale), dev(g.base),
-                                  dev(g.gamma), *out, ws, ws.numel(), M, H, 4, g.tp, g.rms_eps,
-                                  g.hc_eps, g.norm_eps, G)
+            ro, mixes, li = run_glm_on(g, G, ws)
         finally:
             mhc.mhcb_set_token_slices(0)
-        assert np.array_equal(sync_state(ws), want), f"after {g.name} G={G} S={S}"
-    assert mhc.mhcb_workspace_status(ws) == mhc.MHCB_OK
+        check_glm_against_oracle(g, ro, mixes, li, f"G={G} S={S}")
+        F = g.H // 8
+        want[:g.M] += 1
+        want_s[:g.M] = effective_slices(F, S if G == 16 else min(S, F // 64))
+        check_call_state(ws, want, want_s, f"{g.name} G={G} S={S}")
 
 
 def test_graph_replays_match_eager_calls():
     """Split calls captured in one HIP graph (delayed boundary with MXFP8,
     MoE finalize, GLM tiles, all exchanging through one workspace) and
     replayed three times, with eager calls on the same workspace in between,
-    give the eager results every time and leave the workspace clean."""
+    give the eager results every time (the tags the exchanges wait for are
+    read from the workspace at each replay, not frozen into the graph)."""
     b = synth.boundary(17, 8, 1024, 8, 0.5, "graph-delayed")
     f = synth.moe_finalize(8, H=1024)
     g = synth.glm(40, H=2048)
@@ -301,7 +352,9 @@ def test_graph_replays_match_eager_calls():
         for k, v in outs.items():
             assert torch.equal(v.view(torch.uint8), want[k].view(torch.uint8)), f"replay {rep}: {k}"
     assert mhc.mhcb_workspace_status(ws) == mhc.MHCB_OK
-    assert np.array_equal(sync_state(ws), expected_sync_state())
+    epochs, _, copies, status = sync_state(ws)
+    assert status == 0 and epochs.max() > 0
+    assert (copies[np.arange(1024), epochs % 2] == EMPTY).all(), "the next call's copy is empty"
 
 
 def test_cross_token_independence_and_determinism():
@@ -417,8 +470,9 @@ def test_glm_boundary_matches_oracle(M):
         err = np.abs(mixes - mix_ref)
         assert (err <= 1e-5 * (np.abs(mix_ref) + 1)).all(), f"mixes G={G}: max err {err.max()}"
         pre_got = glm_pre(mixes, g.scale, g.base, g.hc_eps)
-        one, two = glm_layer_input_check(li, li_ref, ro_ref, pre_ref.astype(np.float64), pre_got)
-        print(f"[gpu]   G={G}: layer_input 1-ulp {one}, tie 2-ulp {two}", flush=True)
+        one, two = glm_layer_input_check(li, li_ref, ro_ref, pre_ref.astype(np.float64), pre_got,
+                                         g.gamma, g.norm_eps)
+        print(f"[gpu]   G={G}: layer_input 1-ulp {one}, 2+ ulp {two}", flush=True)
         if first is None:
             first = (ro, mixes, li)
         else:   # outputs do not depend on the tokens per workgroup
@@ -435,8 +489,8 @@ def check_glm_against_oracle(g, ro, mixes, li, what):
     err = np.abs(mixes - mix_ref)
     assert (err <= 1e-5 * (np.abs(mix_ref) + 1)).all(), f"mixes {what}: max err {err.max()}"
     one, two = glm_layer_input_check(li, li_ref, ro_ref, pre_ref.astype(np.float64),
-                                     glm_pre(mixes, g.scale, g.base, g.hc_eps))
-    print(f"[gpu]   {what}: layer_input 1-ulp {one}, tie 2-ulp {two}", flush=True)
+                                     glm_pre(mixes, g.scale, g.base, g.hc_eps), g.gamma, g.norm_eps)
+    print(f"[gpu]   {what}: layer_input 1-ulp {one}, 2+ ulp {two}", flush=True)
 
 
 @pytest.mark.parametrize("M,H,G,workspace", [(100, 6144, 1, True), (100, 6144, 2, True),
@@ -494,7 +548,7 @@ def test_glm_large_m_sampled():
     err = np.abs(mixes[toks] - mix_ref)
     assert (err <= 1e-5 * (np.abs(mix_ref) + 1)).all()
     glm_layer_input_check(li[toks], li_ref, ro_ref, pre_ref.astype(np.float64),
-                          glm_pre(mixes[toks], g.scale, g.base, g.hc_eps))
+                          glm_pre(mixes[toks], g.scale, g.base, g.hc_eps), g.gamma, g.norm_eps)
 
 
 @pytest.mark.parametrize("M", [1, 64, 513])

@@ -124,8 +124,8 @@ SyncView sync_view(void *ws) {
 // fragments are spread over up to `max_slices` workgroups (at least one
 // wave of fragments each; slices cover whole 32-column blocks) until there
 // are about `target` workgroups in flight.  Measured on MI355X (H=5120,
-// tp=8): 4 slices save 0.6-1.2 us per call for M <= 64; past that the
-// cross-workgroup exchange costs what the extra compute units gain.
+// tp=8): 4 slices save 0.5-0.8 us per call for M <= 64 (M=1: 4.9 vs 5.7 us,
+// M=64: 6.0 vs 6.5); at M=128, 2 slices cost 0.3 us more than none.
 void choose_slices(BoundaryArgs &a, void *ws, int target, int max_slices) {
   a.slices = 1;
   a.slice_frags = a.H / kFrag;

@@ -182,38 +182,34 @@ __device__ __forceinline__ void stage_routes(const FinalizeView &f, int tp, int 
 
 // The token's RMSNorm factor inv = (float)(1/sqrt((double)(float)ss/H +
 // eps)) from each thread's binary64 sum of squares: wave xor sums, then one
-// thread adds the waves in index order (and, split, publishes its slice's
-// partial and adds the slices' in slice order: the squares of BF16 values
-// are exact in binary64, so the bits do not depend on the split), evaluates
-// inv once and shares it through LDS.  The kernel counts the slice on
-// exchange 0 at its end (token_sum_done).  Every thread calls it.
-__device__ float token_inv(const BoundaryArgs &a, int t, int s, double ss, double *red) {
+// wave adds the waves in index order (and, split, publishes its slice's
+// partial, adds the slices' in slice order and advances the slot's epoch:
+// the squares of BF16 values are exact in binary64, so the bits do not
+// depend on the split), one thread evaluates inv and shares it through LDS.
+// `callw` is the slot's epoch word (wave 0's).  Every thread calls it.
+__device__ float token_inv(const BoundaryArgs &a, int t, int s, double ss, double *red,
+                           uint64_t callw) {
   const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
   ss = wave_sum(ss);
   if (lane == 0) red[wave] = ss;
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (wave == 0) {
     double total = 0.0;
     for (int w = 0; w < (int)blockDim.x / kWave; ++w) total += red[w];
     if (a.slices > 1) {
       char *slot = token_slot(a.sync, t);
-      slot_store64(slot, kSlotSum1 + 8 * s, total);
-      total = gather_sum64(a.sync, slot, kSlotSum1, a.slices);
+      const SlotCall c = unpack_call(callw);
+      char *area = slot + copy_offset(c.epoch);
+      if (lane == 0) slot_store64(area, kCopySum1 + 8 * s, total);
+      total = wave_gather_sum64(a.sync, area, kCopySum1, a.slices);
+      if (lane == 0) advance_epoch(slot, c, a.slices);  // after this slice's last read
     }
-    red[kTokenThreadsWide / kWave] =
-        (double)(float)(1.0 / __builtin_sqrt((double)(float)total / (double)a.H + (double)a.norm_eps));
+    if (lane == 0)
+      red[kTokenThreadsWide / kWave] =
+          (double)(float)(1.0 / __builtin_sqrt((double)(float)total / (double)a.H + (double)a.norm_eps));
   }
   __syncthreads();
   return (float)red[kTokenThreadsWide / kWave];
-}
-
-// After token_inv's value is used: the last slice to get here writes the
-// entries back to kSlotEmpty.
-__device__ __forceinline__ void token_sum_done(const SyncView &sy, int t, int slices) {
-  if (threadIdx.x == 0 && exchange_done(sy, t, 0, slices)) {
-    char *slot = token_slot(sy, t);
-    for (int q = 0; q < slices; ++q) slot_store_u64(slot, kSlotSum1 + 8 * q, kSlotEmpty64);
-  }
 }
 
 // The fused boundary.  Workgroup (s, t) covers fragments
@@ -295,6 +291,10 @@ boundary_kernel(const BoundaryArgs a) {
   __builtin_amdgcn_sched_barrier(0);
   Mixes m;
   load_mixes(a, t, m);
+  // Split: the token slot's epoch word, read by wave 0 (its latency hides
+  // behind the loads above).
+  uint64_t callw = 0;
+  if (a.slices > 1 && norm && tid < kWave) callw = slot_call_word(token_slot(a.sync, t));
 
   u32x4 pfrag[TRIPS];
   double ss = 0.0;
@@ -317,8 +317,8 @@ boundary_kernel(const BoundaryArgs a) {
           bool dirty = false;
 #pragma unroll
           for (int r = 0; r < TP; ++r)
-            dirty |= has_sentinel(part[i][r][0]) | has_sentinel(part[i][r][1]) |
-                     has_sentinel(part[i][r][2]) | has_sentinel(part[i][r][3]);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) dirty |= has_sentinel(part[i][r][k]);
           if (dirty) {
             for (int r = 0; r < TP; ++r) part[i][r] = poll(src + r * rs + col[i], part[i][r], a.mailbox);
           }
@@ -391,7 +391,10 @@ boundary_kernel(const BoundaryArgs a) {
   // a4 (second half): inv = 1/sqrt(sum p^2 / H + eps); out = bf16((p*inv)*gamma).
   // The squares of BF16 values are exact in binary64 and so is their sum,
   // whatever the order or the split.
-  const float inv = token_inv(a, t, s, ss, red);
+  const float inv = token_inv(a, t, s, ss, red, callw);
+  if (a.slices > 1 && tid < kWave)
+    for (int w = tid * a.slices + s; w < kClearWords; w += kWave * a.slices)
+      clear_previous_word(token_slot(a.sync, t), unpack_call(callw), w);
 
 #pragma unroll
   for (int i = 0; i < TRIPS; ++i) {
@@ -438,7 +441,6 @@ boundary_kernel(const BoundaryArgs a) {
       *reinterpret_cast<uint32_t *>(a.mx_scales + sf_offset(row, k, K)) = 0u;
     }
   }
-  if (a.slices > 1) token_sum_done(a.sync, t, a.slices);
 }
 
 template <int TRIPS, Source SRC>
@@ -638,13 +640,13 @@ hipError_t launch_boundary(const BoundaryArgs &a, hipStream_t stream) {
   return hipErrorInvalidValue;
 }
 
-// The sync state's initial contents: header and each slot's first 64 bytes
-// (the counters) zero, every other word kSlotEmpty.
+// The sync state's initial contents: the header and each slot's first 128
+// bytes (the epoch word) zero, every other word kSlotEmpty.
 __global__ void __launch_bounds__(256) sync_init_kernel(uint32_t *p, int64_t words) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words;
        i += (int64_t)gridDim.x * blockDim.x) {
     const int64_t in_slot = (i - 64) % (kSyncSlot / 4);
-    p[i] = i < 64 || in_slot < 16 ? 0u : kSlotEmpty;
+    p[i] = i < 64 || in_slot < kSlotCopy0 / 4 ? 0u : kSlotEmpty;
   }
 }
 

@@ -76,9 +76,52 @@ __device__ __forceinline__ float sigmoid(float x) {
   return (float)(1.0 / (1.0 + exp(-(double)x)));
 }
 
+// Offsets in a token's exchange area (kernels.h): the binary64 sums of
+// exchange 0 and 1, and the GEMV rows, stored two FP32 rows per 8-byte word.
+constexpr int kSum1 = kCopySum1, kSum2 = kCopySum2;
+constexpr int kPairs = kMix / 2;
+
+// The GEMV rows a workgroup of slice s (of S) needs after exchange 0: the
+// pre-mix rows 0..3, and the rows k >= 4 with k % S == s.  Row k's raw mix
+// is written by slice k % S, so each slice gathers a few rows instead of 24.
+// Row j of the list is needed_row(j); the list has `count` rows (at most
+// 24).  No integer division: the values are uniform and tiny, loops suffice.
+struct RowList {
+  int first, count;  // first own row >= 4; rows in the list
+};
+__device__ __forceinline__ RowList row_list(int S, int s) {
+  int m = s - kStreams;
+  while (m < 0) m += S;
+  RowList l = {kStreams + m, kStreams};
+  for (int k = l.first; k < kMix; k += S) ++l.count;
+  return l;
+}
+__device__ __forceinline__ int needed_row(const RowList &l, int S, int j) {
+  return j < kStreams ? j : l.first + (j - kStreams) * S;
+}
+// Whether row k (a row of the list) is this slice's to write: k % S == s.
+__device__ __forceinline__ bool own_row(int S, int s, int k) {
+  if (k >= kStreams) return true;  // rows >= 4 are in the list only if owned
+  const int d = k - s;             // k < 4: owned iff d is 0, S, 2S or 3S
+  return d == 0 || d == S || d == 2 * S || d == 3 * S;
+}
+// The 8-byte row pairs that hold the list's rows: pairs 0 and 1 (rows 0..3),
+// then the pair of each own row (distinct for S >= 2; all 12 for S = 1).
+__device__ __forceinline__ int pair_count(const RowList &l, int S) {
+  return S == 1 ? kPairs : 2 + (l.count - kStreams);
+}
+__device__ __forceinline__ int needed_pair(const RowList &l, int S, int j) {
+  return S == 1 || j < 2 ? j : needed_row(l, S, j + 2) >> 1;
+}
+
+// A token's exchange area for this call, from its slot's epoch word.
+__device__ __forceinline__ char *call_area(const GlmArgs &a, int t, uint64_t callw) {
+  return token_slot(a.sync, t) + copy_offset(unpack_call(callw).epoch);
+}
+
 template <int G>
 struct GlmShared {
-  int last[2 * G];                      // this slice ends an exchange
+  uint64_t callw[G];                    // split: each token slot's epoch word
   float part[kMaxThreads / kWave][64];  // per-wave reduce-scatter results
   float mix[G][kMix];                   // GEMV totals of each token
   float pre[G][kStreams];
@@ -88,58 +131,77 @@ struct GlmShared {
 
 // Exchanges the per-slice partials of the G tokens of a split workgroup:
 // the GEMV rows sh.mix (FP32, with `rows`) and one binary64 sum per token
-// (`sums`, slot offset `offset`).  Afterwards every slice holds the
-// slice-ordered totals.  Exchange 0 is the rows and the first sums,
-// exchange 1 the second sums; glm_exchange_done counts them at the end of
-// the kernel.  Contains barriers: every thread of the workgroup calls it.
+// (`sums`, at `sum` in the exchange area).  Afterwards every slice holds the
+// slice-ordered totals of the sums and of the rows in its row_list.
+// Exchange 0 is the rows and sum 1, exchange 1 is sum 2.  Contains
+// barriers: every thread of the workgroup calls it.
 template <int G>
 __device__ void exchange(const GlmArgs &a, GlmShared<G> &sh, int t0, int s, double (&sums)[G],
-                         int offset, bool rows) {
-  const int tid = threadIdx.x;
+                         int sum, bool rows) {
+  const int tid = threadIdx.x, S = a.slices;
   if (rows) {
-    for (int i = tid; i < G * kMix; i += blockDim.x) {
-      const int g = i / kMix, k = i % kMix;
-      if (t0 + g < a.M)
-        slot_store32(token_slot(a.sync, t0 + g), kSlotRows + 4 * (s * kMix + k), sh.mix[g][k]);
+    for (int i = tid; i < G * kPairs; i += blockDim.x) {
+      const int g = i / kPairs, p = i % kPairs;
+      if (t0 + g < a.M) {
+        const uint64_t w = (uint64_t)__builtin_bit_cast(uint32_t, sh.mix[g][2 * p]) |
+                           ((uint64_t)__builtin_bit_cast(uint32_t, sh.mix[g][2 * p + 1]) << 32);
+        slot_store_u64(call_area(a, t0 + g, sh.callw[g]), kCopyRows + kRowsEntry * s + 8 * p, w);
+      }
     }
   }
-  if (tid < G && t0 + tid < a.M) slot_store64(token_slot(a.sync, t0 + tid), offset + 8 * s, sums[tid]);
+  if (tid < G && t0 + tid < a.M) {
+    double v = 0.0;  // sums[tid], without indexing a register array at run time
+#pragma unroll
+    for (int g = 0; g < G; ++g) v = g == tid ? sums[g] : v;
+    slot_store64(call_area(a, t0 + tid, sh.callw[tid]), sum + 8 * s, v);
+  }
   if (rows) {
-    for (int i = tid; i < G * kMix; i += blockDim.x) {
-      const int g = i / kMix, k = i % kMix;
-      if (t0 + g < a.M)
-        sh.mix[g][k] = gather_sum32(a.sync, token_slot(a.sync, t0 + g), kSlotRows + 4 * k, 4 * kMix, a.slices);
+    const RowList l = row_list(S, s);
+    for (int i = tid; i < G * 32; i += blockDim.x) {
+      const int g = i >> 5, j = i & 31;
+      if (j >= pair_count(l, S) || t0 + g >= a.M) continue;
+      const int p = needed_pair(l, S, j);
+      uint64_t w[kMaxSlices];
+      gather64(a.sync, call_area(a, t0 + g, sh.callw[g]), kCopyRows + 8 * p, kRowsEntry, S, w);
+      float lo = 0.0f, hi = 0.0f;
+#pragma unroll
+      for (int q = 0; q < kMaxSlices; ++q) {
+        if (q >= S) break;
+        lo += __builtin_bit_cast(float, (uint32_t)w[q]);
+        hi += __builtin_bit_cast(float, (uint32_t)(w[q] >> 32));
+      }
+      sh.mix[g][2 * p] = lo;
+      sh.mix[g][2 * p + 1] = hi;
     }
   }
   if (tid < G)
-    sh.tot[tid] = t0 + tid < a.M ? gather_sum64(a.sync, token_slot(a.sync, t0 + tid), offset, a.slices) : 0.0;
+    sh.tot[tid] = t0 + tid < a.M ? gather_sum64(a.sync, call_area(a, t0 + tid, sh.callw[tid]), sum, S)
+                                 : 0.0;
   __syncthreads();
 #pragma unroll
   for (int g = 0; g < G; ++g) sums[g] = sh.tot[g];
   __syncthreads();
 }
 
-// End of a split GLM kernel: counts this slice on both exchanges of its
-// tokens; the last slice of each writes the entries back to kSlotEmpty.
-template <int G>
-__device__ void glm_exchange_done(const GlmArgs &a, int t0, int *last) {
-  const int tid = threadIdx.x;
-  if (tid < 2 * G) {
-    const int g = tid % G, e = tid / G;
-    last[tid] = t0 + g < a.M && exchange_done(a.sync, t0 + g, e, a.slices);
-  }
-  __syncthreads();
-  const int S = a.slices, per_tok = S * (kMix + 2);  // rows, then both sums
-  for (int i = tid; i < G * per_tok; i += blockDim.x) {
-    const int g = i / per_tok, r = i % per_tok;
-    char *slot = token_slot(a.sync, t0 + g);
-    if (r < S * kMix) {
-      if (last[g]) slot_store_u32(slot, kSlotRows + 4 * r, kSlotEmpty);
-    } else if (r < S * kMix + S) {
-      if (last[g]) slot_store_u64(slot, kSlotSum1 + 8 * (r - S * kMix), kSlotEmpty64);
-    } else {
-      if (last[G + g]) slot_store_u64(slot, kSlotSum2 + 8 * (r - S * kMix - S), kSlotEmpty64);
-    }
+// When the call exchanges (`exchanges`), thread i < tokens reads the epoch
+// word of token t0 + i's slot (0 for other threads and tokens past M).
+__device__ __forceinline__ uint64_t read_call_word(const GlmArgs &a, bool exchanges, int t0,
+                                                   int tokens, int i) {
+  if (!exchanges || i >= tokens || t0 + i >= a.M) return 0u;
+  return slot_call_word(token_slot(a.sync, t0 + i));
+}
+
+// After a slice's last read of the call's exchanges: thread i < tokens
+// advances token t0 + i's epoch, and the slices share the clearing of the
+// copies the previous calls used (sync.h), one (token, word) item per
+// worker (the worker index interleaves the slices).  Every thread calls it.
+__device__ void finish_exchanges(const GlmArgs &a, const uint64_t *callw, int t0, int tokens, int s) {
+  const int tid = threadIdx.x, nt = blockDim.x, S = a.slices;
+  if (tid < tokens && t0 + tid < a.M)
+    advance_epoch(token_slot(a.sync, t0 + tid), unpack_call(callw[tid]), S);
+  for (int f = tid * S + s; f < tokens * kClearWords; f += nt * S) {
+    const int g = f / kClearWords;
+    if (t0 + g < a.M) clear_previous_word(token_slot(a.sync, t0 + g), unpack_call(callw[g]), f % kClearWords);
   }
 }
 
@@ -167,6 +229,8 @@ glm_kernel(const GlmArgs a) {
   const int last = a.slices > 1 ? min(F, first + a.slice_frags) : F;
   const bool valid = first + tid < last;
   const int64_t col = valid ? (int64_t)(first + tid) * kFrag : 0;
+  // Split: each token slot's epoch word, in flight with the streams.
+  const uint64_t callw = read_call_word(a, a.slices > 1, t0, G, tid);
 
   // a1 + a2 for the G tokens: y[g][j] packed BF16, sum of y^2 per token.
   u32x4 y[G][kStreams];
@@ -263,16 +327,21 @@ glm_kernel(const GlmArgs a) {
   }
 
   // g_24 and rstd; raw mixes out; pre_j = sigmoid(mix_j * scale0 + base_j) + hc_eps.
+  if (a.slices > 1 && tid < G) sh.callw[tid] = callw;  // read after block_sum's barriers
   block_sum<double, G>(ssy, sh.red);
-  if (a.slices > 1) exchange<G>(a, sh, t0, s, ssy, kSlotSum1, true);
-  for (int i = tid; i < G * kMix; i += blockDim.x) {  // a workgroup may have fewer threads
-    const int g = i / kMix, k = i % kMix, t = t0 + g;
+  if (a.slices > 1) exchange<G>(a, sh, t0, s, ssy, kSum1, true);
+  // (Unsplit: S = 1, every row here.)
+  const int S = a.slices;
+  const RowList rl = row_list(S, s);
+  for (int i = tid; i < G * 32; i += blockDim.x) {  // a workgroup may have fewer threads
+    const int g = i >> 5, j = i & 31, k = needed_row(rl, S, j), t = t0 + g;
+    if (j >= rl.count) continue;
     double total = 0.0;
 #pragma unroll
     for (int q = 0; q < G; ++q) total = q == g ? ssy[q] : total;
     const float rstd = (float)(1.0 / __builtin_sqrt((double)(float)total / (4.0 * H) + (double)a.rms_eps));
     const float mix = sh.mix[g][k] * rstd;
-    if (t < a.M && s == 0) a.mixes_out[(int64_t)t * kMix + k] = mix;
+    if (t < a.M && own_row(S, s, k)) a.mixes_out[(int64_t)t * kMix + k] = mix;
     if (k < kStreams) sh.pre[g][k] = sigmoid(__builtin_fmaf(mix, a.scale[0], a.base[k])) + a.hc_eps;
   }
   __syncthreads();
@@ -304,7 +373,10 @@ glm_kernel(const GlmArgs a) {
     }
   }
   block_sum<double, G>(pss, sh.red);
-  if (a.slices > 1) exchange<G>(a, sh, t0, s, pss, kSlotSum2, false);
+  if (a.slices > 1) {
+    exchange<G>(a, sh, t0, s, pss, kSum2, false);
+    finish_exchanges(a, sh.callw, t0, G, s);
+  }
   float gam[8];
   unpack8(load_cached(a.gamma + col), gam);
 #pragma unroll
@@ -317,7 +389,6 @@ glm_kernel(const GlmArgs a) {
     for (int e = 0; e < 8; ++e) o[e] = (pv[e] * inv) * gam[e];
     if (valid && t < a.M) store_stream(a.layer_input + (int64_t)t * H + col, pack8(o));
   }
-  if (a.slices > 1) glm_exchange_done<G>(a, t0, sh.last);
 }
 
 // ---------------------------------------------------------------------------
@@ -353,7 +424,7 @@ __device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
 }
 
 struct TileShared {
-  int last[2];                          // this slice ends an exchange
+  uint64_t callw[kTile];                // each token slot's epoch word
   float post[kTile][kStreams];
   float comb[kTile][kStreams * kStreams];
   float part[kTileWaves][kTile][kMix];  // per-wave GEMV partials
@@ -373,36 +444,36 @@ __host__ __device__ inline size_t tile_dyn_bytes(int sf) {
   return tile_ys_bytes(sf) + (size_t)kTile * sf * 8;
 }
 
-// Publishes this slice's per-token sums sh.tot (and, with `rows`, the GEMV
-// partials in sh.mix) on exchange e of the tile, and leaves the
-// slice-ordered totals in sh.tot (and sh.mix).  A thread reads all the
-// slices' values of its (token, row pair) as they land and adds them in
-// slice order.  tile_exchange_done counts the slice at the end of the
-// kernel.  Every thread calls it.
-__device__ void tile_exchange(const GlmArgs &a, TileShared &sh, int t0, int s, int offset,
-                              bool rows) {
+// Publishes this slice's per-token sums sh.tot (at `sum` in the exchange
+// area; with `rows`, also the GEMV partials in sh.mix) and leaves the
+// slice-ordered totals in sh.tot (and, of the rows in its row_list, in
+// sh.mix).  A thread reads all the slices' values of its (token, row pair)
+// or token sum as they land and adds them in slice order.  Every thread
+// calls it.
+__device__ void tile_exchange(const GlmArgs &a, TileShared &sh, int t0, int s, int sum, bool rows) {
   const int tid = threadIdx.x, nt = blockDim.x, S = a.slices;
   const int valid = min(kTile, a.M - t0);
-  constexpr int kPairs = kMix / 2;  // a slice's 24 rows as 8-byte words
   if (rows) {
     for (int e = tid; e < valid * kPairs; e += nt) {
-      const int tok = e / kPairs, k = 2 * (e % kPairs);
-      const uint64_t w = (uint64_t)__builtin_bit_cast(uint32_t, sh.mix[tok][k]) |
-                         ((uint64_t)__builtin_bit_cast(uint32_t, sh.mix[tok][k + 1]) << 32);
-      slot_store_u64(token_slot(a.sync, t0 + tok), kSlotRows + 4 * (s * kMix + k), w);
+      const int tok = e / kPairs, p = e % kPairs;
+      const uint64_t w = (uint64_t)__builtin_bit_cast(uint32_t, sh.mix[tok][2 * p]) |
+                         ((uint64_t)__builtin_bit_cast(uint32_t, sh.mix[tok][2 * p + 1]) << 32);
+      slot_store_u64(call_area(a, t0 + tok, sh.callw[tok]), kCopyRows + kRowsEntry * s + 8 * p, w);
     }
   }
-  if (tid < valid) slot_store64(token_slot(a.sync, t0 + tid), offset + 8 * s, sh.tot[tid]);
+  if (tid < valid) slot_store64(call_area(a, t0 + tid, sh.callw[tid]), sum + 8 * s, sh.tot[tid]);
   __syncthreads();  // every thread has read its own sh values before they are replaced
-  // Work items: valid * 12 row pairs (with rows), then valid sums.
-  const int row_items = rows ? valid * kPairs : 0;
+  // Work items: the row pairs this slice needs of each token (with rows; a
+  // stride of 12 per token keeps them within one pass), then the sums.
+  const RowList l = row_list(S, s);
+  const int np = pair_count(l, S), row_items = rows ? valid * kPairs : 0;
   for (int e = tid; e < row_items + valid; e += nt) {
-    const bool is_row = e < row_items;
-    const int tok = is_row ? e / kPairs : e - row_items;
-    const char *slot = token_slot(a.sync, t0 + tok);
-    uint64_t w[kMaxSlices];
-    if (is_row) {
-      gather64(a.sync, slot, kSlotRows + 8 * (e % kPairs), 4 * kMix, S, w);
+    if (e < row_items) {
+      const int tok = e / kPairs, j = e % kPairs;
+      if (j >= np) continue;
+      const int p = needed_pair(l, S, j);
+      uint64_t w[kMaxSlices];
+      gather64(a.sync, call_area(a, t0 + tok, sh.callw[tok]), kCopyRows + 8 * p, kRowsEntry, S, w);
       float lo = 0.0f, hi = 0.0f;
 #pragma unroll
       for (int q = 0; q < kMaxSlices; ++q) {
@@ -410,37 +481,14 @@ __device__ void tile_exchange(const GlmArgs &a, TileShared &sh, int t0, int s, i
         lo += __builtin_bit_cast(float, (uint32_t)w[q]);
         hi += __builtin_bit_cast(float, (uint32_t)(w[q] >> 32));
       }
-      const int k = 2 * (e % kPairs);
-      sh.mix[tok][k] = lo;
-      sh.mix[tok][k + 1] = hi;
+      sh.mix[tok][2 * p] = lo;
+      sh.mix[tok][2 * p + 1] = hi;
     } else {
-      sh.tot[tok] = gather_sum64(a.sync, slot, offset, S);
+      const int tok = e - row_items;
+      sh.tot[tok] = gather_sum64(a.sync, call_area(a, t0 + tok, sh.callw[tok]), sum, S);
     }
   }
   __syncthreads();
-}
-
-// End of the tile kernel: counts this slice on both exchanges (counters in
-// the tile's first token's slot); the last slice of each writes the tile's
-// entries back to kSlotEmpty.
-__device__ void tile_exchange_done(const GlmArgs &a, int t0, int *last) {
-  const int tid = threadIdx.x, S = a.slices;
-  if (tid < 2) last[tid] = exchange_done(a.sync, t0, tid, S);
-  __syncthreads();
-  if (!last[0] && !last[1]) return;
-  const int valid = min(kTile, a.M - t0);
-  const int per_tok = S * (kMix / 2 + 2);  // row pairs, then both sums
-  for (int i = tid; i < valid * per_tok; i += blockDim.x) {
-    const int tok = i / per_tok, r = i % per_tok;
-    char *slot = token_slot(a.sync, t0 + tok);
-    if (r < S * kMix / 2) {
-      if (last[0]) slot_store_u64(slot, kSlotRows + 8 * r, kSlotEmpty64);
-    } else if (r < S * kMix / 2 + S) {
-      if (last[0]) slot_store_u64(slot, kSlotSum1 + 8 * (r - S * kMix / 2), kSlotEmpty64);
-    } else {
-      if (last[1]) slot_store_u64(slot, kSlotSum2 + 8 * (r - S * kMix / 2 - S), kSlotEmpty64);
-    }
-  }
 }
 
 // sh.tot[tok] = sum over f < sf of item[tok][f], in fragment order.
@@ -488,6 +536,9 @@ glm_tile_kernel(const GlmArgs a) {
   double *item = reinterpret_cast<double *>(dyn + tile_ys_bytes(sf));
   const int mi = lane & (kTile - 1), mq = lane >> 4;  // MFMA row, K chunk
 
+  // Each token slot's epoch word (thread i < 16: token t0 + i), first in the
+  // queue: loads return in order, and it is needed only at the exchanges.
+  const uint64_t callw = read_call_word(a, true, t0, kTile, tid);
   // The tile's post and comb (20 floats a token) and this wave's first
   // hc_fn chunk, loaded before the streams.
   constexpr int kMixVals = kTile * 20, kMixPerThread = kMixVals / kWave;
@@ -601,6 +652,7 @@ glm_tile_kernel(const GlmArgs a) {
     const int c = wave + m * waves, f = first + 4 * c + mq;
     load_fn_chunk(a, mi, f, 4 * c < sf && f < last, fc[m]);
   }
+  if (tid < kTile) sh.callw[tid] = callw;
   __syncthreads();
 
   // a3: the GEMV on the matrix cores, wave w taking 4-fragment chunks
@@ -632,14 +684,17 @@ glm_tile_kernel(const GlmArgs a) {
     sh.mix[e / kMix][e % kMix] = v;
   }
   __syncthreads();
-  tile_exchange(a, sh, t0, s, kSlotSum1, true);
+  tile_exchange(a, sh, t0, s, kSum1, true);
 
-  // rstd over 4H; raw mixes out (slice 0); pre_j.
-  for (int e = tid; e < valid * kMix; e += nt) {
-    const int tk = e / kMix, k = e % kMix, tt = t0 + tk;
+  // rstd over 4H; raw mixes out (row k by slice k % S); pre_j.
+  const int S = a.slices;
+  const RowList rl = row_list(S, s);
+  for (int e = tid; e < valid * 32; e += nt) {
+    const int tk = e >> 5, j = e & 31, k = needed_row(rl, S, j), tt = t0 + tk;
+    if (j >= rl.count) continue;
     const float rstd = (float)(1.0 / __builtin_sqrt((double)(float)sh.tot[tk] / (4.0 * H) + (double)a.rms_eps));
     const float mix = sh.mix[tk][k] * rstd;
-    if (s == 0) a.mixes_out[(int64_t)tt * kMix + k] = mix;
+    if (own_row(S, s, k)) a.mixes_out[(int64_t)tt * kMix + k] = mix;
     if (k < kStreams) sh.pre[tk][k] = sigmoid(__builtin_fmaf(mix, a.scale[0], a.base[k])) + a.hc_eps;
   }
   __syncthreads();
@@ -668,7 +723,8 @@ glm_tile_kernel(const GlmArgs a) {
     if (idx < kTile * sf) item[idx] = pss;
   }
   tile_item_sums(sh, item, sf);
-  tile_exchange(a, sh, t0, s, kSlotSum2, false);
+  tile_exchange(a, sh, t0, s, kSum2, false);
+  finish_exchanges(a, sh.callw, t0, kTile, s);
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     if (!live[u]) continue;
@@ -680,7 +736,6 @@ glm_tile_kernel(const GlmArgs a) {
     for (int e = 0; e < 8; ++e) o[e] = (pv[e] * inv) * g[e];
     store_stream(a.layer_input + (int64_t)(t0 + tok[u]) * H + col[u], pack8(o));
   }
-  tile_exchange_done(a, t0, sh.last);
 }
 
 // ---------------------------------------------------------------------------

@@ -35,18 +35,27 @@ struct FinalizeView {
 };
 
 // Cross-workgroup state of the token-split kernels, at the start of the
-// caller's workspace: a 256-byte header (status word), then one slot per
-// token, so that different tokens' atomics never share a cache line:
-//   +0    readers done, exchange 0   +4   readers done, exchange 1
-//   +64   [kMaxSlices] binary64  first partial sum per slice  (exchange 0)
-//   +192  [kMaxSlices] binary64  second partial sum per slice (exchange 1)
-//   +320  [kMaxSlices][24] FP32  partial GEMV rows per slice  (exchange 0)
-// Initialised once (launch_sync_init: counters 0, every other word
-// kSlotEmpty); every call leaves it that way (see sync.h).
+// caller's workspace: a 256-byte header (status word), then one 4 KiB slot
+// per token, so that different tokens' words never share a cache line.  A
+// slot holds (sync.h):
+//   +0     epoch word: split calls that used the slot (low 32 bits) and the
+//          slice count of the last of them (high 32 bits)
+//   +128   copy 0 of the exchange area, +1920 copy 1, each:
+//            +0    [kMaxSlices] binary64  first partial sum per slice
+//            +128  [kMaxSlices] binary64  second partial sum per slice
+//            +256  [kMaxSlices][24] FP32  partial GEMV rows per slice
+// mhcb_workspace_init writes the epoch words 0 and every other word of the
+// slots kSlotEmpty.
 constexpr int kSyncTokens = 1024;  // tokens a split call may have
 constexpr int kMaxSlices = 16;     // workgroups a token may be split over
-constexpr int kSyncSlot = 2048;    // bytes per token
-constexpr int kSlotSum1 = 64, kSlotSum2 = 192, kSlotRows = 320;
+constexpr int kSyncSlot = 4096;    // bytes per token
+constexpr int kSlotEpoch = 0, kSlotCopy0 = 128;
+constexpr int kCopySum1 = 0, kCopySum2 = 128, kCopyRows = 256;
+constexpr int kRowsEntry = 4 * 24;  // bytes per slice in the rows
+constexpr int kCopyBytes = kCopyRows + kMaxSlices * kRowsEntry;  // 1792, a multiple of 128
+static_assert(kCopySum2 == kCopySum1 + 8 * kMaxSlices && kCopyRows == kCopySum2 + 8 * kMaxSlices,
+              "copy layout");
+static_assert(kCopyBytes % 128 == 0 && kSlotCopy0 + 2 * kCopyBytes <= kSyncSlot, "slot layout");
 constexpr int64_t kSyncBytes = 256 + (int64_t)kSyncSlot * kSyncTokens;
 
 struct SyncView {
