@@ -186,18 +186,40 @@ def boundary(partials, residual, post, comb, pre, gamma, norm_eps, *, mxfp8=Fals
     return res_out, layer, (None if not mxfp8 else (values, scales))
 
 
-def finalize_contributions(gemm2, weights, idx, shared, *, replicated_routing=True, threads=1):
+def routing_weights(weights, routed_scaling_factor=1.0) -> np.ndarray:
+    """[DSV41] _QuadFinalizePublishDeviceKernel (the routing-weight load; the
+    module compiles one kernel per routing-weight dtype, AllReduceMHC.__init__):
+    each route's weight is read as FP32, or as BF16 widened to FP32; when the
+    routed scaling factor is not 1 it is then multiplied by that factor (an
+    FP32 product, one rounding).  A route whose row index is -1 is skipped by
+    the contribution itself.
+
+    weights: float32 values, or uint16 BF16 bit patterns.  Returns float32."""
+    w = np.asarray(weights)
+    if w.dtype == np.uint16:
+        w32 = bf16_to_f32(w)
+    elif w.dtype == np.float32:
+        w32 = w.copy()
+    else:
+        raise TypeError(f"routing weights must be float32 or BF16 bits (uint16), not {w.dtype}")
+    if float(routed_scaling_factor) != 1.0:
+        w32 = (w32 * np.float32(routed_scaling_factor)).astype(np.float32)
+    return w32
+
+
+def finalize_contributions(gemm2, weights, idx, shared, *, replicated_routing=True,
+                           routed_scaling_factor=1.0, threads=1):
     """a6 contributions of every rank.
 
-    gemm2 [tp, rows, H] u16; shared [tp, M, H] u16; weights [M, top_k] f32 and
-    idx [M, top_k] i32 when replicated_routing, else [tp, M, top_k].
-    Returns [tp, M, H] u16.
+    gemm2 [tp, rows, H] u16; shared [tp, M, H] u16; weights [M, top_k] (f32,
+    or u16 BF16 bits: routing_weights) and idx [M, top_k] i32 when
+    replicated_routing, else [tp, M, top_k].  Returns [tp, M, H] u16.
     """
     gemm2 = _c(gemm2, np.uint16)
     shared = _c(shared, np.uint16)
     tp, rows, H = gemm2.shape
     M = shared.shape[1]
-    weights = _c(weights, np.float32)
+    weights = np.ascontiguousarray(routing_weights(weights, routed_scaling_factor))
     idx = _c(idx, np.int32)
     top_k = weights.shape[-1]
     ws = 0 if replicated_routing else M * top_k
@@ -210,14 +232,15 @@ def finalize_contributions(gemm2, weights, idx, shared, *, replicated_routing=Tr
 
 
 def finalize(gemm2, weights, idx, shared, residual, post, comb, pre, gamma, norm_eps, *,
-             two_shot=False, replicated_routing=True, mxfp8=False, threads=1):
+             two_shot=False, replicated_routing=True, routed_scaling_factor=1.0, mxfp8=False,
+             threads=1):
     """MoE finalize boundary (a6 + a1/a7 + a2 + a4 [+ a8]); shapes as in
     finalize_contributions and boundary."""
     gemm2 = _c(gemm2, np.uint16)
     shared = _c(shared, np.uint16)
     tp, rows, H = gemm2.shape
     M = shared.shape[1]
-    weights = _c(weights, np.float32)
+    weights = np.ascontiguousarray(routing_weights(weights, routed_scaling_factor))
     idx = _c(idx, np.int32)
     top_k = weights.shape[-1]
     ws = 0 if replicated_routing else M * top_k

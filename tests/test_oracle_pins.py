@@ -583,6 +583,59 @@ def test_finalize_brute_force_exact_rationals():
                 assert c[r, t, col] == want
 
 
+def test_routing_weights_bf16_values_from_the_format():
+    """BF16 routing weights widen exactly: sign, 8-bit exponent, 7-bit
+    fraction (1.0, -3.0, 0.25, +-0, the smallest normal, 2^-133)."""
+    bits = np.array([0x3F80, 0xC040, 0x3E80, 0x0000, 0x8000, 0x0080, 0x0001], np.uint16)
+    got = oracle.routing_weights(bits)
+    want = np.array([1.0, -3.0, 0.25, 0.0, -0.0, 2.0 ** -126, 2.0 ** -133], np.float32)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_routing_weights_scale_is_one_fp32_product():
+    """A factor of 1 leaves the bits alone (-0 and subnormals included);
+    otherwise each weight is the correctly rounded FP32 product."""
+    rng = np.random.default_rng(40)
+    w = np.concatenate([rng.uniform(-2, 2, 64).astype(np.float32),
+                        np.array([-0.0, 1e-42, 1 + 2.0 ** -23], np.float32)])
+    assert np.array_equal(oracle.routing_weights(w, 1.0).view(np.uint32), w.view(np.uint32))
+    for scale in (2.5, 1 + 2.0 ** -23, 0.3):
+        got = oracle.routing_weights(w, scale)
+        s32 = float(np.float32(scale))
+        for g, x in zip(got, w):
+            assert g == np.float32(f32(exact(x) * exact(s32))), (x, scale)
+    # 1 + 2^-23 squared is 1 + 2^-22 + 2^-46: one rounding gives 1 + 2^-22.
+    assert oracle.routing_weights(np.array([1 + 2.0 ** -23], np.float32), 1 + 2.0 ** -23)[0] == \
+        np.float32(1 + 2.0 ** -22)
+
+
+def test_finalize_bf16_scaled_weights_brute_force():
+    """BF16 routing weights times a routed scale of 0.3, each route's weight
+    scaled before its FMA (not the sum afterwards): exact rationals."""
+    M, H, tp, k = 2, 8, 2, 3
+    rng = np.random.default_rng(41)
+    gemm2 = rand_bf16((tp, M * k, H), 0.5, rng)
+    shared = rand_bf16((tp, M, H), 0.5, rng)
+    idx = np.stack([rng.permutation(M * k).astype(np.int32).reshape(M, k) for _ in range(tp)])
+    idx[1, 0, 1] = -1
+    wb = rand_bf16((tp, M, k), 0.5, rng)
+    c = oracle.finalize_contributions(gemm2, wb, idx, shared, replicated_routing=False,
+                                      routed_scaling_factor=0.3)
+    s32 = float(np.float32(0.3))
+    for r in range(tp):
+        for t in range(M):
+            for col in range(H):
+                acc = 0.0
+                for kk in range(k):
+                    row = idx[r, t, kk]
+                    if row == -1:
+                        continue
+                    w = f32(exact(bf16_value(wb[r, t, kk])) * exact(s32))
+                    acc = f32(exact(bf16_value(gemm2[r, row, col])) * exact(w) + exact(acc))
+                want = bf16_bits_of(exact(f32(exact(acc) + exact(bf16_value(shared[r, t, col])))))
+                assert c[r, t, col] == want
+
+
 def test_two_shot_owner_layout_and_bit_equality():
     """Token t sits in owner t % tp, slot t // tp; the owner reduce gives the
     same bits as the direct sum (the pages' claim), here with -0 and
