@@ -55,8 +55,8 @@ def bytes_mailbox_extra(M, H, tp):
     return M * 3 * tp * 2 * H
 
 
-def bytes_finalize(M, H, tp, top_k):
-    return M * (tp * (top_k + 1) * 2 * H + top_k * 8 + 9 * 2 * H + 96) + 2 * H
+def bytes_finalize(M, H, tp, top_k, weight_bytes=4):
+    return M * (tp * (top_k + 1) * 2 * H + top_k * (4 + weight_bytes) + 9 * 2 * H + 96) + 2 * H
 
 
 def bytes_glm(M, H, tp):
@@ -235,9 +235,14 @@ def bench_mailbox(torch, mhc, b, steps, warmup):
     return ms, bytes_delayed(b.M, b.H, b.tp, True) + bytes_mailbox_extra(b.M, b.H, b.tp)
 
 
-def bench_finalize(torch, mhc, f, steps, warmup, two_shot=False):
-    per_set = bytes_finalize(f.M, f.H, f.tp, f.top_k)
-    t = dict(gemm2=dev(torch, f.gemm2), weights=dev(torch, f.weights), idx=dev(torch, f.idx),
+def bench_finalize(torch, mhc, f, steps, warmup, two_shot=False, bf16_weights=False, scale=1.0):
+    """MoE finalize; with bf16_weights the routing weights are BF16 (their
+    bit patterns from the generator's rounding) and `scale` is the routed
+    scaling factor (mhcb_finalize_ex)."""
+    import synth
+    weights = synth.to_bf16_bits(f.weights) if bf16_weights else f.weights
+    per_set = bytes_finalize(f.M, f.H, f.tp, f.top_k, 2 if bf16_weights else 4)
+    t = dict(gemm2=dev(torch, f.gemm2), weights=dev(torch, weights), idx=dev(torch, f.idx),
              shared=dev(torch, f.shared), residual=dev(torch, f.residual), post=dev(torch, f.post),
              comb=dev(torch, f.comb), pre=dev(torch, f.pre), gamma=dev(torch, f.gamma))
     sets = make_sets(torch, t, rotations(per_set, minimum=2))
@@ -249,10 +254,11 @@ def bench_finalize(torch, mhc, f, steps, warmup, two_shot=False):
 
     def call(i):
         s = sets[i % len(sets)]
-        mhc.mhcb_finalize(s["gemm2"], rows * f.H, rows, s["weights"], 0, s["idx"], 0, s["shared"],
-                          f.M * f.H, s["residual"], s["post"], s["comb"], s["pre"], s["gamma"],
-                          s["residual_out"], s["layer_input"], None, None, int(two_shot), ws,
-                          ws.numel(), f.M, f.H, 4, f.tp, f.top_k, f.norm_eps)
+        mhc.mhcb_finalize_ex(s["gemm2"], rows * f.H, rows, s["weights"], 0, int(bf16_weights),
+                             scale, s["idx"], 0, s["shared"], f.M * f.H, s["residual"], s["post"],
+                             s["comb"], s["pre"], s["gamma"], s["residual_out"], s["layer_input"],
+                             None, None, int(two_shot), ws, ws.numel(), f.M, f.H, 4, f.tp, f.top_k,
+                             f.norm_eps)
 
     ms = Timed(torch, call, steps, warmup).run()
     extra = f.M * (2 * f.tp * 2 * f.H + 2 * 2 * f.H) if two_shot else 0
@@ -422,6 +428,11 @@ def main():
             if M == 512:
                 ms, nbytes = bench_finalize(torch, mhc, f, steps, min(W, 5), two_shot=True)
                 extra[f"moe_finalize_two_shot_M{M}"] = entry(ms, nbytes, M)
+                ms, nbytes = bench_finalize(torch, mhc, f, steps, min(W, 5), bf16_weights=True,
+                                            scale=2.5)
+                extra[f"moe_finalize_bf16_weights_scale2.5_M{M}"] = entry(ms, nbytes, M)
+                log(f"finalize M={M} BF16 weights, scale 2.5: "
+                    f"{extra[f'moe_finalize_bf16_weights_scale2.5_M{M}']}")
             del f
     if want("glm") and not args.quick:
         for M in (1, 16, 64, 256, 512):

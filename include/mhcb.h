@@ -198,6 +198,27 @@ int mhcb_finalize(const uint16_t *gemm2_permuted, int64_t gemm2_rank_stride, int
                   int two_shot, void *workspace, int64_t workspace_bytes, int M, int hidden_size,
                   int hc_mult, int tp, int top_k, float norm_eps, hipStream_t stream);
 
+/* mhcb_finalize with the routing-weight options of the page
+ * ([DSV41] _QuadFinalizePublishDeviceKernel, whose module compiles one
+ * kernel per routing-weight dtype in AllReduceMHC.__init__): expert_weights
+ * holds FP32 values (weights_bf16 = 0, 4-byte aligned) or BF16 bit patterns
+ * (weights_bf16 = 1, 2-byte aligned), [M, top_k] per rank with
+ * weights_rank_stride in elements; each weight is widened to FP32 and, when
+ * routed_scaling_factor is not 1, multiplied by it in FP32 before its fused
+ * multiply-add.  mhcb_finalize is this call with FP32 weights and factor 1.
+ * Errors as mhcb_finalize, plus weights_bf16 not 0 or 1, or a factor that
+ * is not finite -> EINVAL. */
+int mhcb_finalize_ex(const uint16_t *gemm2_permuted, int64_t gemm2_rank_stride, int64_t rows,
+                     const void *expert_weights, int64_t weights_rank_stride, int weights_bf16,
+                     float routed_scaling_factor, const int32_t *permuted_idx,
+                     int64_t idx_rank_stride, const uint16_t *shared_output,
+                     int64_t shared_rank_stride, const uint16_t *residual, const float *post,
+                     const float *comb, const float *pre, const uint16_t *norm_weight,
+                     uint16_t *residual_out, uint16_t *layer_input, uint8_t *mxfp8_values,
+                     uint8_t *mxfp8_scales, int two_shot, void *workspace, int64_t workspace_bytes,
+                     int M, int hidden_size, int hc_mult, int tp, int top_k, float norm_eps,
+                     hipStream_t stream);
+
 /* Standalone MXFP8 of a BF16 [M, hidden] array: the encoding of the
  * boundary's epilogue ([DSV41] _LamportMHCDeviceKernel, quantize): per 32
  * columns e = the smallest UE8M0 exponent with 2^(e-127) >= amax * fl(1/448),

@@ -22,7 +22,7 @@ def declared_symbols():
 
 def test_header_declares_the_entry_points():
     names = declared_symbols()
-    for want in ("mhcb_boundary", "mhcb_boundary_glm", "mhcb_finalize", "mhcb_mixes",
+    for want in ("mhcb_boundary", "mhcb_boundary_glm", "mhcb_finalize", "mhcb_finalize_ex", "mhcb_mixes",
                  "mhcb_quant_mxfp8", "mhcb_mailbox_init", "mhcb_publish", "mhcb_last_error"):
         assert want in names
 
@@ -136,6 +136,15 @@ def test_glm_mixes_finalize_quant_validation():
                      (dict(two_shot=1, workspace=FAKE, workspace_bytes=1 << 10), "workspace_bytes")):
         with pytest.raises(mhc.MhcbError, match=text):
             mhc.mhcb_finalize(**{**fin, **kw})
+    fin_ex = {**fin, "weights_bf16": 1, "routed_scaling_factor": 2.5}
+    for kw, text in ((dict(weights_bf16=2), "weights_bf16"),
+                     (dict(routed_scaling_factor=float("inf")), "finite"),
+                     (dict(routed_scaling_factor=float("nan")), "finite"),
+                     (dict(expert_weights=FAKE + 1), "aligned"),
+                     (dict(weights_bf16=0, expert_weights=FAKE + 2), "aligned"),
+                     (dict(top_k=0), "top_k")):
+        with pytest.raises(mhc.MhcbError, match=text):
+            mhc.mhcb_finalize_ex(**{**fin_ex, **kw})
     with pytest.raises(mhc.MhcbError, match="multiple of 128"):
         mhc.mhcb_quant_mxfp8(FAKE, FAKE, FAKE, 4, 520, 0)
     with pytest.raises(mhc.MhcbError, match="at least"):

@@ -728,6 +728,28 @@ def test_glm_random_shapes(case):
     check_glm_against_oracle(g, ro, mixes, li, f"G={G}")
 
 
+@pytest.mark.parametrize("bf16_weights,scale", [(True, 1.0), (True, 0.3), (False, 2.5),
+                                                 (True, 2.5)])
+def test_finalize_routing_weight_options(bf16_weights, scale):
+    """mhcb_finalize_ex: BF16 or FP32 routing weights and a routed scaling
+    factor, per-rank routing with dropped routes; one-shot split and unsplit
+    and two-shot all match the oracle."""
+    f = synth.moe_finalize(40, H=1024, tp=4, top_k=8, replicated_routing=False,
+                           drop_fraction=0.1)
+    w = synth.to_bf16_bits(f.weights) if bf16_weights else f.weights
+    print(f"[gpu] {f.name} bf16_weights={bf16_weights} scale={scale}", flush=True)
+    ro_ref, li_ref, _ = oracle.finalize(f.gemm2, w, f.idx, f.shared, f.residual, f.post, f.comb,
+                                        f.pre, f.gamma, f.norm_eps, replicated_routing=False,
+                                        routed_scaling_factor=scale, threads=8)
+    for two_shot, split in ((False, True), (False, False), (True, True)):
+        out = mhc.finalize(dev(f.gemm2), dev(w), dev(f.idx), dev(f.shared), dev(f.residual),
+                           dev(f.post), dev(f.comb), dev(f.pre), dev(f.gamma), f.norm_eps,
+                           two_shot=two_shot, split=split, routed_scaling_factor=scale)
+        torch.cuda.synchronize()
+        assert_bits_equal(u16(out[0]), ro_ref, f"residual_out two_shot={two_shot} split={split}")
+        assert_within_ulp(u16(out[1]), li_ref, 1, f"layer_input two_shot={two_shot} split={split}")
+
+
 @pytest.mark.parametrize("case", [(3, 1024, 1, 1, True, 0.0), (17, 2048, 2, 16, False, 0.3),
                                   (64, 5120, 4, 6, True, 0.0), (40, 3072, 8, 2, False, 0.5),
                                   (130, 512, 3, 8, True, 0.0)],

@@ -4,6 +4,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <cmath>
+
 #include "../../include/mhcb.h"
 #include "device.h"
 #include "kernels.h"
@@ -356,20 +358,25 @@ int mhcb_mixes(const float *mixes, const float *scale, const float *base, float 
                                sinkhorn_repeat, stream), fn);
 }
 
-int mhcb_finalize(const uint16_t *gemm2_permuted, int64_t gemm2_rank_stride, int64_t rows,
-                  const float *expert_weights, int64_t weights_rank_stride,
-                  const int32_t *permuted_idx, int64_t idx_rank_stride,
-                  const uint16_t *shared_output, int64_t shared_rank_stride,
-                  const uint16_t *residual, const float *post, const float *comb, const float *pre,
-                  const uint16_t *norm_weight, uint16_t *residual_out, uint16_t *layer_input,
-                  uint8_t *mxfp8_values, uint8_t *mxfp8_scales, int two_shot, void *workspace,
-                  int64_t workspace_bytes, int M, int hidden_size, int hc_mult, int tp, int top_k,
-                  float norm_eps, hipStream_t stream) {
-  const char *fn = "mhcb_finalize";
+static int finalize_impl(const char *fn, const uint16_t *gemm2_permuted, int64_t gemm2_rank_stride,
+                         int64_t rows, const void *expert_weights, int64_t weights_rank_stride,
+                         int weights_bf16, float routed_scaling_factor,
+                         const int32_t *permuted_idx, int64_t idx_rank_stride,
+                         const uint16_t *shared_output, int64_t shared_rank_stride,
+                         const uint16_t *residual, const float *post, const float *comb,
+                         const float *pre, const uint16_t *norm_weight, uint16_t *residual_out,
+                         uint16_t *layer_input, uint8_t *mxfp8_values, uint8_t *mxfp8_scales,
+                         int two_shot, void *workspace, int64_t workspace_bytes, int M,
+                         int hidden_size, int hc_mult, int tp, int top_k, float norm_eps,
+                         hipStream_t stream) {
   int rc = check_common(fn, residual, post, comb, pre, norm_weight, residual_out, layer_input,
                         mxfp8_values, mxfp8_scales, M, hidden_size, hc_mult, tp);
   if (rc) return rc;
   if (top_k < 1) return fail(MHCB_EINVAL, "%s: top_k=%d < 1", fn, top_k);
+  if (weights_bf16 != 0 && weights_bf16 != 1)
+    return fail(MHCB_EINVAL, "%s: weights_bf16=%d (0 = FP32, 1 = BF16)", fn, weights_bf16);
+  if (!std::isfinite(routed_scaling_factor))
+    return fail(MHCB_EINVAL, "%s: routed_scaling_factor must be finite", fn);
   if ((int64_t)tp * top_k > kMaxRoutes)
     return fail(MHCB_EINVAL, "%s: tp * top_k = %d exceeds %d", fn, tp * top_k, kMaxRoutes);
   if (rows < 0) return fail(MHCB_EINVAL, "%s: rows=%lld < 0", fn, (long long)rows);
@@ -378,10 +385,13 @@ int mhcb_finalize(const uint16_t *gemm2_permuted, int64_t gemm2_rank_stride, int
   if (gemm2_rank_stride < 0 || weights_rank_stride < 0 || idx_rank_stride < 0 || shared_rank_stride < 0)
     return fail(MHCB_EINVAL, "%s: negative rank stride", fn);
   if (!aligned(gemm2_permuted, 16) || !aligned(shared_output, 16) || gemm2_rank_stride % kFrag ||
-      shared_rank_stride % kFrag || !aligned(expert_weights, 4) || !aligned(permuted_idx, 4))
+      shared_rank_stride % kFrag)
     return fail(MHCB_EALIGN, "%s: BF16 inputs must be 16-byte aligned with rank strides %% 8 == 0", fn);
+  if (!aligned(expert_weights, weights_bf16 ? 2 : 4) || !aligned(permuted_idx, 4))
+    return fail(MHCB_EALIGN, "%s: expert_weights must be aligned to its element (4 bytes FP32, 2 BF16), permuted_idx to 4", fn);
   FinalizeView f = {gemm2_permuted, gemm2_rank_stride, rows, expert_weights, weights_rank_stride,
-                    permuted_idx, idx_rank_stride, shared_output, shared_rank_stride, top_k};
+                    weights_bf16, routed_scaling_factor, permuted_idx, idx_rank_stride,
+                    shared_output, shared_rank_stride, top_k};
   BoundaryArgs a = {};
   a.tp = tp;
   a.residual = residual;
@@ -421,6 +431,40 @@ int mhcb_finalize(const uint16_t *gemm2_permuted, int64_t gemm2_rank_stride, int
   a.tp = 1;
   choose_slices(a, workspace, device_cus(), 4);
   return launched(launch_boundary(a, stream), fn);
+}
+
+int mhcb_finalize(const uint16_t *gemm2_permuted, int64_t gemm2_rank_stride, int64_t rows,
+                  const float *expert_weights, int64_t weights_rank_stride,
+                  const int32_t *permuted_idx, int64_t idx_rank_stride,
+                  const uint16_t *shared_output, int64_t shared_rank_stride,
+                  const uint16_t *residual, const float *post, const float *comb, const float *pre,
+                  const uint16_t *norm_weight, uint16_t *residual_out, uint16_t *layer_input,
+                  uint8_t *mxfp8_values, uint8_t *mxfp8_scales, int two_shot, void *workspace,
+                  int64_t workspace_bytes, int M, int hidden_size, int hc_mult, int tp, int top_k,
+                  float norm_eps, hipStream_t stream) {
+  return finalize_impl("mhcb_finalize", gemm2_permuted, gemm2_rank_stride, rows, expert_weights,
+                       weights_rank_stride, 0, 1.0f, permuted_idx, idx_rank_stride, shared_output,
+                       shared_rank_stride, residual, post, comb, pre, norm_weight, residual_out,
+                       layer_input, mxfp8_values, mxfp8_scales, two_shot, workspace,
+                       workspace_bytes, M, hidden_size, hc_mult, tp, top_k, norm_eps, stream);
+}
+
+int mhcb_finalize_ex(const uint16_t *gemm2_permuted, int64_t gemm2_rank_stride, int64_t rows,
+                     const void *expert_weights, int64_t weights_rank_stride, int weights_bf16,
+                     float routed_scaling_factor, const int32_t *permuted_idx,
+                     int64_t idx_rank_stride, const uint16_t *shared_output,
+                     int64_t shared_rank_stride, const uint16_t *residual, const float *post,
+                     const float *comb, const float *pre, const uint16_t *norm_weight,
+                     uint16_t *residual_out, uint16_t *layer_input, uint8_t *mxfp8_values,
+                     uint8_t *mxfp8_scales, int two_shot, void *workspace, int64_t workspace_bytes,
+                     int M, int hidden_size, int hc_mult, int tp, int top_k, float norm_eps,
+                     hipStream_t stream) {
+  return finalize_impl("mhcb_finalize_ex", gemm2_permuted, gemm2_rank_stride, rows,
+                       expert_weights, weights_rank_stride, weights_bf16, routed_scaling_factor,
+                       permuted_idx, idx_rank_stride, shared_output, shared_rank_stride, residual,
+                       post, comb, pre, norm_weight, residual_out, layer_input, mxfp8_values,
+                       mxfp8_scales, two_shot, workspace, workspace_bytes, M, hidden_size,
+                       hc_mult, tp, top_k, norm_eps, stream);
 }
 
 int mhcb_quant_mxfp8(const uint16_t *x, uint8_t *values, uint8_t *scales, int M, int hidden_size,

@@ -164,16 +164,21 @@ __device__ __forceinline__ void finalize_fixed(const FinalizeView &f, const int3
   }
 }
 
-// Stages every rank's (row, weight) routes of token t in LDS; a route whose
-// row is -1 gets weight 0 as on the page (it is skipped anyway).
+// Stages every rank's (row, weight) routes of token t in LDS
+// (_QuadFinalizePublishDeviceKernel.kernel): the weight is read as FP32 or
+// widened from BF16, multiplied by the routed scaling factor when that is
+// not 1, and a route whose row is -1 gets weight 0 (it is skipped anyway).
 __device__ __forceinline__ void stage_routes(const FinalizeView &f, int tp, int t, int32_t *srow,
                                              float *sw) {
   const int n = tp * f.top_k;
   for (int i = threadIdx.x; i < n; i += blockDim.x) {
     const int r = i / f.top_k, k = i % f.top_k;
-    const int64_t e = (int64_t)t * f.top_k + k;
-    const int32_t row = f.idx[r * f.i_stride + e];
-    const float w = f.weights[r * f.w_stride + e];  // not behind the index load
+    const int64_t e = r * f.w_stride + (int64_t)t * f.top_k + k;
+    const int32_t row = f.idx[r * f.i_stride + (int64_t)t * f.top_k + k];
+    // (not behind the index load)
+    float w = f.w_bf16 ? __uint_as_float((uint32_t)static_cast<const uint16_t *>(f.weights)[e] << 16)
+                       : static_cast<const float *>(f.weights)[e];
+    if (f.w_scale != 1.0f) w = w * f.w_scale;
     srow[i] = row;
     sw[i] = row == -1 ? 0.0f : w;
   }

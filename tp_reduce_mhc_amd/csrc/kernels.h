@@ -25,8 +25,10 @@ struct MailboxView {
 struct FinalizeView {
   const uint16_t *gemm2;  // per rank [rows, H], g_stride elements apart
   int64_t g_stride, rows;
-  const float *weights;   // per rank [M, top_k], w_stride apart (0 = shared)
-  int64_t w_stride;
+  const void *weights;    // per rank [M, top_k], w_stride apart (0 = shared):
+  int64_t w_stride;       //   FP32, or BF16 bit patterns when w_bf16
+  int w_bf16;
+  float w_scale;          // routed scaling factor (1 = none)
   const int32_t *idx;     // per rank [M, top_k], i_stride apart (0 = shared)
   int64_t i_stride;
   const uint16_t *shared; // per rank [M, H], s_stride apart

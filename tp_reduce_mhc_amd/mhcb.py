@@ -71,6 +71,8 @@ _SIGNATURES = {
     "mhcb_mixes": (_I, [_P, _P, _P, _P, _P, _I, _I, _F, _F, _I, _P]),
     "mhcb_finalize": (_I, [_P, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _P, _P, _P, _P, _P,
                            _P, _P, _P, _I, _P, _I64, _I, _I, _I, _I, _I, _F, _P]),
+    "mhcb_finalize_ex": (_I, [_P, _I64, _I64, _P, _I64, _I, _F, _P, _I64, _P, _I64, _P, _P, _P, _P,
+                              _P, _P, _P, _P, _P, _I, _P, _I64, _I, _I, _I, _I, _I, _F, _P]),
     "mhcb_quant_mxfp8": (_I, [_P, _P, _P, _I, _I, _P]),
     "mhcb_mailbox_init": (_I, [_MB, _P]),
     "mhcb_publish": (_I, [_MB, _P, _I64, _I, _I, _I, _P]),
@@ -186,6 +188,22 @@ def mhcb_finalize(gemm2_permuted, gemm2_rank_stride, rows, expert_weights, weigh
                               int(two_shot), _ptr(workspace), workspace_bytes, M, hidden_size,
                               hc_mult, tp, top_k, norm_eps, _stream(stream)))
 
+def mhcb_finalize_ex(gemm2_permuted, gemm2_rank_stride, rows, expert_weights, weights_rank_stride,
+                     weights_bf16, routed_scaling_factor, permuted_idx, idx_rank_stride,
+                     shared_output, shared_rank_stride, residual, post, comb, pre, norm_weight,
+                     residual_out, layer_input, mxfp8_values, mxfp8_scales, two_shot, workspace,
+                     workspace_bytes, M, hidden_size, hc_mult, tp, top_k, norm_eps,
+                     stream=None) -> None:
+    _check(_lib.mhcb_finalize_ex(_ptr(gemm2_permuted), gemm2_rank_stride, rows,
+                                 _ptr(expert_weights), weights_rank_stride, int(weights_bf16),
+                                 routed_scaling_factor, _ptr(permuted_idx), idx_rank_stride,
+                                 _ptr(shared_output), shared_rank_stride, _ptr(residual),
+                                 _ptr(post), _ptr(comb), _ptr(pre), _ptr(norm_weight),
+                                 _ptr(residual_out), _ptr(layer_input), _ptr(mxfp8_values),
+                                 _ptr(mxfp8_scales), int(two_shot), _ptr(workspace),
+                                 workspace_bytes, M, hidden_size, hc_mult, tp, top_k, norm_eps,
+                                 _stream(stream)))
+
 
 def mhcb_quant_mxfp8(x, values, scales, M, hidden_size, stream=None) -> None:
     _check(_lib.mhcb_quant_mxfp8(_ptr(x), _ptr(values), _ptr(scales), M, hidden_size,
@@ -294,9 +312,10 @@ def mixes(raw_mixes, scale, base, hc_eps, post_mult, sinkhorn_repeat, *, stream=
 
 
 def finalize(gemm2, weights, idx, shared, residual, post, comb, pre, norm_weight, norm_eps, *,
-             two_shot: bool = False, mxfp8: bool = False, split: bool = True, stream=None):
+             two_shot: bool = False, mxfp8: bool = False, split: bool = True,
+             routed_scaling_factor: float = 1.0, stream=None):
     """MoE finalize boundary.  gemm2 [tp, rows, H]; shared [tp, M, H];
-    weights / idx [M, top_k] (replicated) or [tp, M, top_k]."""
+    weights (FP32 or BF16) / idx [M, top_k] (replicated) or [tp, M, top_k]."""
     tp, rows, H = gemm2.shape
     M = shared.shape[1]
     top_k = weights.shape[-1]
@@ -309,10 +328,11 @@ def finalize(gemm2, weights, idx, shared, residual, post, comb, pre, norm_weight
         values = torch.empty((M, H), dtype=torch.uint8, device=dev)
         scales = torch.empty(mhcb_mxfp8_scale_bytes(M, H), dtype=torch.uint8, device=dev)
     ws = workspace(dev, M=M, hidden_size=H, tp=tp, two_shot=True) if (two_shot or split) else None
-    mhcb_finalize(gemm2, rows * H, rows, weights, M * top_k if per_rank else 0, idx,
-                  M * top_k if per_rank else 0, shared, M * H, residual, post, comb, pre,
-                  norm_weight, residual_out, layer_input, values, scales, two_shot, ws,
-                  ws.numel() if ws is not None else 0, M, H, 4, tp, top_k, norm_eps, stream)
+    mhcb_finalize_ex(gemm2, rows * H, rows, weights, M * top_k if per_rank else 0,
+                     weights.dtype == torch.bfloat16, routed_scaling_factor, idx,
+                     M * top_k if per_rank else 0, shared, M * H, residual, post, comb, pre,
+                     norm_weight, residual_out, layer_input, values, scales, two_shot, ws,
+                     ws.numel() if ws is not None else 0, M, H, 4, tp, top_k, norm_eps, stream)
     return residual_out, layer_input, ((values, scales) if mxfp8 else None)
 
 
