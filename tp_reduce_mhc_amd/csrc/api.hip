@@ -318,15 +318,16 @@ int mhcb_boundary_glm(const uint16_t *partials, int64_t rank_stride, const uint1
     }
     return ok();
   }
-  // Slices per token group: measured on MI355X (H=6144, tp=8), 4 slices
-  // save about 3 us at M=1 and break even at M=64; larger M is faster
-  // unsplit.  The choice depends on M only (not on tokens_per_wg), so the
-  // results do not depend on tokens_per_wg.
+  // Slices per token group: measured on MI355X (H=6144, tp=8), one-wave
+  // slices save about 3 us at M=1; at M=64 4 slices break even; larger M
+  // is faster unsplit.  The choice depends on M only (not on
+  // tokens_per_wg), so the results do not depend on tokens_per_wg.
   if (workspace && M <= kSyncTokens) {
     const int F = hidden_size / kFrag;
-    // (M=1: 8 slices 11.4 us, 4 slices 12.0 us; M=16 and 64: 4 or more
-    // equal or worse.)
-    int S = g_slices_override > 0 ? g_slices_override : (M <= 4 ? 8 : M <= 64 ? 4 : 1);
+    // (Requested 16, i.e. 12 slices of one wave at H=6144: M=1 11.6 us,
+    // M=16 12.5 us; 8 slices: 11.8 and 13.5; 4: 12.5 and 13.3.  M=64: 4
+    // slices 15.0 us, 16 requested 16.6.)
+    int S = g_slices_override > 0 ? g_slices_override : (M <= 16 ? 16 : M <= 64 ? 4 : 1);
     const int cap = F / kWave;
     S = S > kMaxSlices ? kMaxSlices : S;
     S = S > cap ? cap : S;
