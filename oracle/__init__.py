@@ -42,7 +42,7 @@ _SIGNATURES = {
     "oracle_ue8m0_round_up": (ctypes.c_uint8, [_F]),
     "oracle_sf_index": (_I64, [_I64, _I64, _I64]),
     "oracle_mxfp8_scale_bytes": (_I64, [_I64, _I64]),
-    "oracle_boundary": (_I, [_P, _I64, _I, _P, _P, _P, _P, _P, _F, _I, _I, _P, _P, _P, _P, _I]),
+    "oracle_boundary": (_I, [_P, _I64, _I, _P, _P, _P, _P, _P, _F, _I, _I, _I, _P, _P, _P, _P, _I]),
     "oracle_finalize_element": (ctypes.c_uint16, [_P, _I64, _P, _P, _P, _I, _I64, _I, _I]),
     "oracle_finalize_contributions": (
         _I, [_P, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _I, _I, _I, _I, _P, _I]),
@@ -50,7 +50,7 @@ _SIGNATURES = {
     "oracle_owner_reduce": (None, [_P, _I, _I, _I, _P]),
     "oracle_finalize": (
         _I, [_P, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _I, _I,
-             _P, _P, _P, _P, _P, _F, _I, _I, _I, _P, _P, _P, _P, _I]),
+             _P, _P, _P, _P, _P, _F, _I, _I, _I, _I, _P, _P, _P, _P, _I]),
     "oracle_glm_mixes_token": (None, [_P, _P, _P, _P, _I, _F, _F, _P, _P]),
     "oracle_boundary_glm": (
         _I, [_P, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _F, _F, _F, _I, _I, _P, _P, _P, _P, _I]),
@@ -161,27 +161,28 @@ def boundary(partials, residual, post, comb, pre, gamma, norm_eps, *, mxfp8=Fals
              threads=1):
     """Delayed-mHC boundary (a1, a2, a4, optional a8).
 
-    partials [tp, M, H] u16; residual [M, 4, H] u16; post, pre [M, 4] f32;
-    comb [M, 4, 4] f32 [source, target]; gamma [H] u16.  pre=None and
-    gamma=None select the residual-only variant.
+    partials [tp, M, H] u16; residual [M, hc, H] u16 (hc = 1..8, from its
+    shape); post, pre [M, hc] f32; comb [M, hc, hc] f32 [source, target];
+    gamma [H] u16.  pre=None and gamma=None select the residual-only variant.
     Returns (residual_out, layer_input or None, (values, scales) or None).
     """
     partials = _c(partials, np.uint16)
     tp, M, H = partials.shape
-    residual = _c(residual, np.uint16).reshape(M, 4, H)
-    post = _c(post, np.float32).reshape(M, 4)
-    comb = _c(comb, np.float32).reshape(M, 4, 4)
-    pre = None if pre is None else _c(pre, np.float32).reshape(M, 4)
+    residual = _c(residual, np.uint16).reshape(M, -1, H)
+    hc = residual.shape[1]
+    post = _c(post, np.float32).reshape(M, hc)
+    comb = _c(comb, np.float32).reshape(M, hc, hc)
+    pre = None if pre is None else _c(pre, np.float32).reshape(M, hc)
     gamma = None if gamma is None else _c(gamma, np.uint16).reshape(H)
-    res_out = np.empty((M, 4, H), np.uint16)
+    res_out = np.empty((M, hc, H), np.uint16)
     layer = None if pre is None else np.empty((M, H), np.uint16)
     values = scales = None
     if mxfp8:
         values = np.empty((M, H), np.uint8)
         scales = np.full(mxfp8_scale_bytes(M, H), 0xAA, np.uint8)
     rc = lib().oracle_boundary(_ptr(partials), M * H, tp, _ptr(residual), _ptr(post), _ptr(comb),
-                               _ptr(pre), _ptr(gamma), norm_eps, M, H, _ptr(res_out), _ptr(layer),
-                               _ptr(values), _ptr(scales), threads)
+                               _ptr(pre), _ptr(gamma), norm_eps, M, H, hc, _ptr(res_out),
+                               _ptr(layer), _ptr(values), _ptr(scales), threads)
     _check(rc, "boundary")
     return res_out, layer, (None if not mxfp8 else (values, scales))
 
@@ -244,12 +245,13 @@ def finalize(gemm2, weights, idx, shared, residual, post, comb, pre, gamma, norm
     idx = _c(idx, np.int32)
     top_k = weights.shape[-1]
     ws = 0 if replicated_routing else M * top_k
-    residual = _c(residual, np.uint16).reshape(M, 4, H)
-    post = _c(post, np.float32).reshape(M, 4)
-    comb = _c(comb, np.float32).reshape(M, 4, 4)
-    pre = None if pre is None else _c(pre, np.float32).reshape(M, 4)
+    residual = _c(residual, np.uint16).reshape(M, -1, H)
+    hc = residual.shape[1]
+    post = _c(post, np.float32).reshape(M, hc)
+    comb = _c(comb, np.float32).reshape(M, hc, hc)
+    pre = None if pre is None else _c(pre, np.float32).reshape(M, hc)
     gamma = None if gamma is None else _c(gamma, np.uint16).reshape(H)
-    res_out = np.empty((M, 4, H), np.uint16)
+    res_out = np.empty((M, hc, H), np.uint16)
     layer = None if pre is None else np.empty((M, H), np.uint16)
     values = scales = None
     if mxfp8:
@@ -257,7 +259,8 @@ def finalize(gemm2, weights, idx, shared, residual, post, comb, pre, gamma, norm
         scales = np.full(mxfp8_scale_bytes(M, H), 0xAA, np.uint8)
     rc = lib().oracle_finalize(_ptr(gemm2), rows * H, rows, _ptr(weights), ws, _ptr(idx), ws,
                                _ptr(shared), M * H, tp, top_k, _ptr(residual), _ptr(post),
-                               _ptr(comb), _ptr(pre), _ptr(gamma), norm_eps, M, H, int(two_shot),
+                               _ptr(comb), _ptr(pre), _ptr(gamma), norm_eps, M, H, hc,
+                               int(two_shot),
                                _ptr(res_out), _ptr(layer), _ptr(values), _ptr(scales), threads)
     _check(rc, "finalize")
     return res_out, layer, (None if not mxfp8 else (values, scales))

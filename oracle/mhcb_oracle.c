@@ -31,7 +31,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { NSTREAM = 4, NMIX = 24 };
+enum { NSTREAM = 4, MAXSTREAM = 8, NMIX = 24 };
 
 /* ------------------------------------------------------------------------ */
 /* BF16 <-> FP32                                                             */
@@ -101,13 +101,13 @@ uint16_t oracle_rank_sum(const uint16_t *partials, int64_t rank_stride, int tp,
 /* ------------------------------------------------------------------------ */
 
 /* [DSV41] _LamportMHCDeviceKernel.kernel (and [GLM] _BoundaryDeviceKernel
- * .kernel): new stream j = x * post_j, then the four old streams are added in
- * source order, each times comb[source][j]; the sum of a product is an FMA
- * (reading).  Rounded to BF16. */
-static uint16_t post_mix(float x, const uint16_t res[NSTREAM], const float *post,
-                         const float *comb, int j) {
+ * .kernel): new stream j = x * post_j, then the hc old streams (four for GLM)
+ * are added in source order, each times comb[source][j]; the sum of a
+ * product is an FMA (reading).  Rounded to BF16. */
+static uint16_t post_mix(float x, const uint16_t *res, const float *post, const float *comb,
+                         int j, int hc) {
   float a = x * post[j];
-  for (int s = 0; s < NSTREAM; ++s) a = fmaf(bf(res[s]), comb[s * NSTREAM + j], a);
+  for (int s = 0; s < hc; ++s) a = fmaf(bf(res[s]), comb[s * hc + j], a);
   return tobf(a);
 }
 
@@ -116,10 +116,10 @@ static uint16_t post_mix(float x, const uint16_t res[NSTREAM], const float *post
 /* ------------------------------------------------------------------------ */
 
 /* [DSV41] _LamportMHCDeviceKernel.kernel: the collapse starts at 0.0 and adds
- * y_j * pre_j in stream order (FMA reading). */
-static uint16_t collapse_delayed(const uint16_t y[NSTREAM], const float *pre) {
+ * y_j * pre_j over the hc streams in order (FMA reading). */
+static uint16_t collapse_delayed(const uint16_t *y, const float *pre, int hc) {
   float z = 0.0f;
-  for (int j = 0; j < NSTREAM; ++j) z = fmaf(bf(y[j]), pre[j], z);
+  for (int j = 0; j < hc; ++j) z = fmaf(bf(y[j]), pre[j], z);
   return tobf(z);
 }
 
@@ -291,7 +291,7 @@ typedef struct {
   const float *post, *comb, *pre;
   const uint16_t *gamma;
   float norm_eps;
-  int H;
+  int H, hc;
   uint16_t *residual_out, *layer_input;
   uint8_t *mx_values, *mx_scales;
 } boundary_ctx;
@@ -301,18 +301,19 @@ static void boundary_tokens(void *arg, int t0, int t1) {
   int H = a->H;
   uint16_t *p = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)H);
   uint16_t *out = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)H);
+  const int hc = a->hc;
   for (int t = t0; t < t1; ++t) {
-    const float *post = a->post + (int64_t)t * NSTREAM;
-    const float *comb = a->comb + (int64_t)t * NSTREAM * NSTREAM;
+    const float *post = a->post + (int64_t)t * hc;
+    const float *comb = a->comb + (int64_t)t * hc * hc;
     for (int c = 0; c < H; ++c) {
       float x = bf(oracle_rank_sum(a->partials, a->rank_stride, a->tp, (int64_t)t * H + c));
-      uint16_t res[NSTREAM], y[NSTREAM];
-      for (int s = 0; s < NSTREAM; ++s) res[s] = a->residual[((int64_t)t * NSTREAM + s) * H + c];
-      for (int j = 0; j < NSTREAM; ++j) {
-        y[j] = post_mix(x, res, post, comb, j);
-        a->residual_out[((int64_t)t * NSTREAM + j) * H + c] = y[j];
+      uint16_t res[MAXSTREAM], y[MAXSTREAM];
+      for (int s = 0; s < hc; ++s) res[s] = a->residual[((int64_t)t * hc + s) * H + c];
+      for (int j = 0; j < hc; ++j) {
+        y[j] = post_mix(x, res, post, comb, j, hc);
+        a->residual_out[((int64_t)t * hc + j) * H + c] = y[j];
       }
-      if (a->pre) p[c] = collapse_delayed(y, a->pre + (int64_t)t * NSTREAM);
+      if (a->pre) p[c] = collapse_delayed(y, a->pre + (int64_t)t * hc, hc);
     }
     if (!a->pre) continue; /* residual-only variant */
     rmsnorm_token(p, a->gamma, H, a->norm_eps, out);
@@ -323,21 +324,22 @@ static void boundary_tokens(void *arg, int t0, int t1) {
   free(out);
 }
 
-/* [DSV41] AllReduceMHC.__call__ with _LamportMHCDeviceKernel: partials are tp
- * BF16 [M, H] arrays `rank_stride` elements apart; residual [M, 4, H]; post,
- * pre [M, 4] FP32; comb [M, 4, 4] FP32 indexed [source][target]; gamma [H].
+/* [DSV41] AllReduceMHC.__call__ with _LamportMHCDeviceKernel (compiled for
+ * the module's hc_mult): partials are tp BF16 [M, H] arrays `rank_stride`
+ * elements apart; residual [M, hc, H]; post, pre [M, hc] FP32; comb
+ * [M, hc, hc] FP32 indexed [source][target]; gamma [H]; 1 <= hc <= 8.
  * pre == NULL selects the residual-only variant (layer_input, gamma and the
  * MXFP8 outputs unused).  mx_values [M, H] / mx_scales (scale_bytes) optional. */
 int oracle_boundary(const uint16_t *partials, int64_t rank_stride, int tp,
                     const uint16_t *residual, const float *post, const float *comb,
-                    const float *pre, const uint16_t *gamma, float norm_eps, int M, int H,
+                    const float *pre, const uint16_t *gamma, float norm_eps, int M, int H, int hc,
                     uint16_t *residual_out, uint16_t *layer_input, uint8_t *mx_values,
                     uint8_t *mx_scales, int threads) {
-  if (M < 0 || H <= 0 || tp < 1) return 1;
+  if (M < 0 || H <= 0 || tp < 1 || hc < 1 || hc > MAXSTREAM) return 1;
   if ((pre == NULL) != (gamma == NULL) || (pre == NULL && mx_values != NULL)) return 1;
   if (mx_values && H % 128) return 1;
   boundary_ctx a = {partials, rank_stride, tp, residual, post, comb, pre, gamma,
-                    norm_eps, H, residual_out, layer_input, mx_values, mx_scales};
+                    norm_eps, H, hc, residual_out, layer_input, mx_values, mx_scales};
   if (parallel_tokens(M, threads, boundary_tokens, &a)) return 2;
   if (mx_values) zero_padding_scales(M, H, mx_scales);
   return 0;
@@ -441,7 +443,7 @@ int oracle_finalize(const uint16_t *gemm2, int64_t g_stride, int64_t rows, const
                     const uint16_t *shared, int64_t s_stride, int tp, int top_k,
                     const uint16_t *residual, const float *post, const float *comb,
                     const float *pre, const uint16_t *gamma, float norm_eps, int M, int H,
-                    int two_shot, uint16_t *residual_out, uint16_t *layer_input,
+                    int hc, int two_shot, uint16_t *residual_out, uint16_t *layer_input,
                     uint8_t *mx_values, uint8_t *mx_scales, int threads) {
   if (M < 0 || H <= 0 || tp < 1 || top_k < 1) return 1;
   uint16_t *contrib = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)tp * (size_t)M * (size_t)H + 2);
@@ -450,7 +452,7 @@ int oracle_finalize(const uint16_t *gemm2, int64_t g_stride, int64_t rows, const
                                          shared, s_stride, tp, top_k, M, H, contrib, threads);
   if (rc == 0 && !two_shot) {
     rc = oracle_boundary(contrib, (int64_t)M * H, tp, residual, post, comb, pre, gamma,
-                         norm_eps, M, H, residual_out, layer_input, mx_values, mx_scales,
+                         norm_eps, M, H, hc, residual_out, layer_input, mx_values, mx_scales,
                          threads);
   } else if (rc == 0) {
     int64_t slots = (M + tp - 1) / tp;
@@ -461,7 +463,7 @@ int oracle_finalize(const uint16_t *gemm2, int64_t g_stride, int64_t rows, const
     } else {
       oracle_two_shot_publish(contrib, tp, M, H, own);
       oracle_owner_reduce(own, tp, M, H, reduced);
-      rc = oracle_boundary(reduced, 0, 1, residual, post, comb, pre, gamma, norm_eps, M, H,
+      rc = oracle_boundary(reduced, 0, 1, residual, post, comb, pre, gamma, norm_eps, M, H, hc,
                            residual_out, layer_input, mx_values, mx_scales, threads);
     }
     free(own);
@@ -530,7 +532,7 @@ static void glm_tokens(void *arg, int t0, int t1) {
       float x = bf(oracle_rank_sum(a->partials, a->rank_stride, a->tp, (int64_t)t * H + c));
       uint16_t res[NSTREAM];
       for (int s = 0; s < NSTREAM; ++s) res[s] = a->residual[((int64_t)t * NSTREAM + s) * H + c];
-      for (int j = 0; j < NSTREAM; ++j) y[(int64_t)j * H + c] = post_mix(x, res, post, comb, j);
+      for (int j = 0; j < NSTREAM; ++j) y[(int64_t)j * H + c] = post_mix(x, res, post, comb, j, NSTREAM);
     }
     memcpy(a->residual_out + (int64_t)t * NSTREAM * H, y, sizeof(uint16_t) * (size_t)NSTREAM * (size_t)H);
     float mixes[NMIX], pre[NSTREAM];

@@ -220,6 +220,88 @@ def test_post_mix_and_collapse_fma_chains_brute_force():
     assert bf16_ulp_distance(li, torch_bf16(ref)).max() <= 1
 
 
+# ---------------------------------------------------------------------------
+# General hc_mult (the DSV4.1 consumer is compiled for the module's hc)
+# ---------------------------------------------------------------------------
+
+def _hc_case(hc, M=3, H=16, tp=2, seed=50):
+    rng = np.random.default_rng(seed)
+    partials = rand_bf16((tp, M, H), 0.5, rng)
+    residual = rand_bf16((M, hc, H), 1.0, rng)
+    post = rng.uniform(0, 1, (M, hc)).astype(np.float32)
+    comb = rng.uniform(0, 0.5, (M, hc, hc)).astype(np.float32)
+    pre = rng.uniform(0, 1, (M, hc)).astype(np.float32)
+    gamma = torch_bf16(1 + 0.1 * rng.standard_normal(H))
+    return partials, residual, post, comb, pre, gamma
+
+
+@pytest.mark.parametrize("hc", [1, 2, 3, 8])
+def test_general_hc_identity_and_permutation(hc):
+    """comb = I with post = 0 leaves the hc streams unchanged; comb = the
+    cyclic permutation s -> s + 1 moves stream s to s + 1 (source-major
+    [s, j] indexing at every hc)."""
+    partials, residual, post, comb, pre, gamma = _hc_case(hc)
+    M = residual.shape[0]
+    eye = np.broadcast_to(np.eye(hc, dtype=np.float32), (M, hc, hc)).copy()
+    ro, _, _ = oracle.boundary(partials, residual, np.zeros_like(post), eye, pre, gamma, 1e-6)
+    assert np.array_equal(ro, residual)
+    P = np.zeros((hc, hc), np.float32)
+    for s_ in range(hc):
+        P[s_, (s_ + 1) % hc] = 1.0
+    ro, _, _ = oracle.boundary(partials, residual, np.zeros_like(post),
+                               np.broadcast_to(P, (M, hc, hc)).copy(), pre, gamma, 1e-6)
+    for s_ in range(hc):
+        assert np.array_equal(ro[:, (s_ + 1) % hc], residual[:, s_])
+
+
+@pytest.mark.parametrize("hc", [1, 2, 8])
+def test_general_hc_fma_chains_brute_force(hc):
+    """The post-mix FMA chain over hc sources and the collapse chain over hc
+    streams, checked with exact rationals (one rounding per fused step)."""
+    partials, residual, post, comb, pre, gamma = _hc_case(hc, M=2, H=8, seed=51 + hc)
+    ro, li, _ = oracle.boundary(partials, residual, post, comb, pre, gamma, 1e-6)
+    M, H = 2, 8
+    p_bits = np.zeros((M, H), np.uint16)
+    for t in range(M):
+        for c in range(H):
+            s_ = f32(exact(bf16_value(partials[0, t, c])))
+            s_ = f32(exact(s_) + exact(bf16_value(partials[1, t, c])))
+            x = exact(bf16_value(bf16_bits_of(exact(s_))))
+            ys = []
+            for j in range(hc):
+                a = f32(x * exact(post[t, j]))
+                for src_ in range(hc):
+                    a = f32(exact(bf16_value(residual[t, src_, c])) * exact(comb[t, src_, j]) + exact(a))
+                yb = bf16_bits_of(exact(a))
+                assert ro[t, j, c] == yb
+                ys.append(yb)
+            z = 0.0
+            for j in range(hc):
+                z = f32(exact(bf16_value(ys[j])) * exact(pre[t, j]) + exact(z))
+            p_bits[t, c] = bf16_bits_of(exact(z))
+    p = bf16_value(p_bits).astype(np.float64)
+    ref = p / np.sqrt((p ** 2).mean(axis=1, keepdims=True) + 1e-6) * bf16_value(gamma)
+    assert bf16_ulp_distance(li, torch_bf16(ref)).max() <= 1
+
+
+def test_general_hc_finalize_equals_boundary_on_contributions():
+    f = synth.moe_finalize(4, H=128, tp=2, top_k=3)
+    rng = np.random.default_rng(55)
+    for hc in (2, 8):
+        residual = rand_bf16((4, hc, 128), 1.0, rng)
+        post = rng.uniform(0, 1, (4, hc)).astype(np.float32)
+        comb = rng.uniform(0, 0.5, (4, hc, hc)).astype(np.float32)
+        pre = rng.uniform(0, 1, (4, hc)).astype(np.float32)
+        contrib = oracle.finalize_contributions(f.gemm2, f.weights, f.idx, f.shared)
+        a = oracle.finalize(f.gemm2, f.weights, f.idx, f.shared, residual, post, comb, pre,
+                            f.gamma, 1e-6)
+        b = oracle.boundary(contrib, residual, post, comb, pre, f.gamma, 1e-6)
+        c = oracle.finalize(f.gemm2, f.weights, f.idx, f.shared, residual, post, comb, pre,
+                            f.gamma, 1e-6, two_shot=True)
+        for x, y, z in ((a[0], b[0], c[0]), (a[1], b[1], c[1])):
+            assert np.array_equal(x, y) and np.array_equal(x, z)
+
+
 # 3.0 * C is 2^-8 + 2^-24 + (a little): 1 + 3*C rounds in one step to
 # 1 + 2^-8 + 2^-23 (BF16 then rounds up to 0x3F81), while rounding 3*C first
 # gives exactly the midpoint 1 + 2^-8 + 2^-24 -> 1 + 2^-8 -> BF16 tie -> 0x3F80.
