@@ -42,8 +42,9 @@ def log(msg):
 # Algorithmic bytes (each tensor counted once; weights once per call)
 # ---------------------------------------------------------------------------
 
-def bytes_delayed(M, H, tp, mxfp8=False):
-    per_token = (tp + 9) * 2 * H + 96
+def bytes_delayed(M, H, tp, mxfp8=False, hc=4):
+    # partials, hc residual streams in and out, the layer input; post, comb, pre
+    per_token = (tp + 2 * hc + 1) * 2 * H + 4 * (2 * hc + hc * hc)
     if mxfp8:
         per_token += H + H // 32
     pad = ((M + 127) // 128 * 128 - M) * (H // 32) if mxfp8 else 0
@@ -172,13 +173,14 @@ def delayed_sets(torch, b, count):
              gamma=dev(torch, b.gamma))
     sets = make_sets(torch, t, count)
     for s in sets:
-        s["residual_out"] = torch.empty((b.M, 4, b.H), dtype=torch.bfloat16, device="cuda")
+        s["residual_out"] = torch.empty(b.residual.shape, dtype=torch.bfloat16, device="cuda")
         s["layer_input"] = torch.empty((b.M, b.H), dtype=torch.bfloat16, device="cuda")
     return sets
 
 
 def bench_delayed(torch, mhc, b, steps, warmup, mxfp8=False, check=False):
-    per_set = bytes_delayed(b.M, b.H, b.tp, mxfp8)
+    hc = b.residual.shape[1]
+    per_set = bytes_delayed(b.M, b.H, b.tp, mxfp8, hc)
     sets = delayed_sets(torch, b, rotations(per_set))
     if mxfp8:
         for s in sets:
@@ -192,7 +194,7 @@ def bench_delayed(torch, mhc, b, steps, warmup, mxfp8=False, check=False):
         s = sets[i % len(sets)]
         mhc.mhcb_boundary(s["partials"], b.M * b.H, None, s["residual"], s["post"], s["comb"],
                           s["pre"], s["gamma"], s["residual_out"], s["layer_input"],
-                          s.get("values"), s.get("scales"), ws, ws.numel(), b.M, b.H, 4, b.tp,
+                          s.get("values"), s.get("scales"), ws, ws.numel(), b.M, b.H, hc, b.tp,
                           b.norm_eps)
 
     ms = Timed(torch, call, steps, warmup).run()
@@ -203,7 +205,7 @@ def bench_delayed(torch, mhc, b, steps, warmup, mxfp8=False, check=False):
             ro, li = s["residual_out"].clone(), s["layer_input"].clone()
             mhc.mhcb_boundary(s["partials"], b.M * b.H, None, s["residual"], s["post"], s["comb"],
                               s["pre"], s["gamma"], s["residual_out"], s["layer_input"],
-                              s.get("values"), s.get("scales"), ws, ws.numel(), b.M, b.H, 4, b.tp,
+                              s.get("values"), s.get("scales"), ws, ws.numel(), b.M, b.H, hc, b.tp,
                               b.norm_eps)
             torch.cuda.synchronize()
             assert torch.equal(ro.view(torch.int16), s["residual_out"].view(torch.int16))
@@ -416,6 +418,11 @@ def main():
             log(f"sweep M={M}: {sweep[f'M{M}']}")
         result["sweep_dsv41_delayed"] = sweep
         result["us_per_call"] = {"M1": sweep["M1"]["us_per_call"], "M64": sweep["M64"]["us_per_call"]}
+        for hc in (1, 2, 8):
+            b = synth.dsv41_delayed(128, hc)
+            ms, nbytes, _ = bench_delayed(torch, mhc, b, min(K, 200), W)
+            sweep[f"hc{hc}_M128"] = entry(ms, nbytes, 128)
+            log(f"sweep hc={hc} M=128: {sweep[f'hc{hc}_M128']}")
 
     extra = {}
     if want("finalize") and not args.quick:

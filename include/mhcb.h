@@ -23,7 +23,10 @@
  *  - Outputs must not alias inputs.
  *  - Return value: MHCB_OK or an error code; mhcb_last_error() gives the
  *    calling thread's message for the last failure.
- *  - hc_mult must be 4 ([GLM] ties the kernel to four streams); hidden_size
+ *  - hc_mult (residual streams): 1, 2, 4 or 8 for mhcb_boundary and the
+ *    finalize calls ([DSV41] compiles _LamportMHCDeviceKernel for the
+ *    module's hc_mult); exactly 4 for mhcb_boundary_glm and mhcb_mixes
+ *    ([GLM] ties those kernels to four streams and 24 mixes).  hidden_size
  *    a multiple of 8 (16-byte fragments of 8 BF16 values) and at most 16384.
  */
 #ifndef MHCB_H
@@ -111,15 +114,15 @@ typedef struct mhcb_mailbox {
  * _LamportMHCDeviceKernel), per token t and column c:
  *   xr      = bf16( ((0 + x_0) + x_1) + ... + x_{tp-1} )       (FP32 adds)
  *   y_j     = bf16( xr*post_j (+) sum_s residual_s * comb[s][j] )   (FMAs)
- *   p       = bf16( 0 (+) y_0*pre_0 (+) ... (+) y_3*pre_3 )          (FMAs)
+ *   p       = bf16( 0 (+) y_0*pre_0 (+) ... (+) y_{hc-1}*pre_{hc-1} )  (FMAs)
  *   out     = bf16( (p * inv) * norm_weight ),
  *             inv = 1/sqrt(sum_c p^2 / hidden + norm_eps)
  * Inputs: partials = tp BF16 [M, hidden] arrays rank_stride elements apart
  * (NULL iff mailbox is given: then the ACTIVE generation is polled until no
  * element is the sentinel, NEXT is advanced and the slots are reset);
- * residual [M, 4, hidden] BF16; post, pre [M, 4] FP32; comb [M, 4, 4] FP32
- * indexed [source][target]; norm_weight [hidden] BF16.
- * Outputs: residual_out [M, 4, hidden] = y; layer_input [M, hidden] = out;
+ * residual [M, hc, hidden] BF16; post, pre [M, hc] FP32; comb [M, hc, hc]
+ * FP32 indexed [source][target]; norm_weight [hidden] BF16 (hc = hc_mult).
+ * Outputs: residual_out [M, hc, hidden] = y; layer_input [M, hidden] = out;
  * optionally mxfp8_values [M, hidden] E4M3 codes and mxfp8_scales
  * (mhcb_mxfp8_scale_bytes) UE8M0 scales of out, per 32 columns, in the
  * swizzled 128x4 layout, padding rows zeroed (hidden % 128 == 0 required).
@@ -127,7 +130,8 @@ typedef struct mhcb_mailbox {
  * variant.  workspace: optional (see mhcb_workspace_bytes).
  * Errors: M < 1 or M > mailbox capacity, tp < 1 or tp > 64,
  * pre/norm_weight given alone, MXFP8 on a residual-only call -> EINVAL;
- * hidden % 8, hc_mult != 4, MXFP8 with hidden % 128 -> EUNSUPPORTED. */
+ * hidden % 8, hc_mult not 1, 2, 4 or 8, MXFP8 with hidden % 128
+ * -> EUNSUPPORTED. */
 int mhcb_boundary(const uint16_t *partials, int64_t rank_stride, const mhcb_mailbox *mailbox,
                   const uint16_t *residual, const float *post, const float *comb,
                   const float *pre, const uint16_t *norm_weight, uint16_t *residual_out,

@@ -40,9 +40,9 @@ def _normal_bf16(rng, shape, std):
     return to_bf16_bits(rng.standard_normal(shape, dtype=np.float32) * np.float32(std))
 
 
-def doubly_stochastic(rng, m: int, rounds: int = 20) -> np.ndarray:
-    """[m, 4, 4] float32: Sinkhorn-Knopp (textbook, float64) of exp(N(0,1))."""
-    a = np.exp(rng.standard_normal((m, HC, HC)))
+def doubly_stochastic(rng, m: int, rounds: int = 20, hc: int = HC) -> np.ndarray:
+    """[m, hc, hc] float32: Sinkhorn-Knopp (textbook, float64) of exp(N(0,1))."""
+    a = np.exp(rng.standard_normal((m, hc, hc)))
     for _ in range(rounds):
         a = a / a.sum(axis=2, keepdims=True)
         a = a / a.sum(axis=1, keepdims=True)
@@ -57,10 +57,10 @@ class Boundary:
     H: int
     tp: int
     partials: np.ndarray        # [tp, M, H] u16
-    residual: np.ndarray        # [M, 4, H] u16
-    post: np.ndarray            # [M, 4] f32
-    comb: np.ndarray            # [M, 4, 4] f32, [source, target]
-    pre: np.ndarray             # [M, 4] f32
+    residual: np.ndarray        # [M, hc, H] u16
+    post: np.ndarray            # [M, hc] f32
+    comb: np.ndarray            # [M, hc, hc] f32, [source, target]
+    pre: np.ndarray             # [M, hc] f32
     gamma: np.ndarray           # [H] u16
     norm_eps: float = 1e-6
 
@@ -108,10 +108,10 @@ class Finalize:
     replicated_routing: bool = True
 
 
-def _mixes(rng, m):
-    post = rng.uniform(0.0, 1.0, (m, HC)).astype(np.float32)
-    pre = rng.uniform(0.0, 1.0, (m, HC)).astype(np.float32)
-    comb = doubly_stochastic(rng, m)
+def _mixes(rng, m, hc=HC):
+    post = rng.uniform(0.0, 1.0, (m, hc)).astype(np.float32)
+    pre = rng.uniform(0.0, 1.0, (m, hc)).astype(np.float32)
+    comb = doubly_stochastic(rng, m, hc=hc)
     return post, comb, pre
 
 
@@ -120,11 +120,12 @@ def _gamma(rng, h):
 
 
 def boundary(workload: int, M: int, H: int, tp: int, partial_std: float,
-             name: str = "") -> Boundary:
+             name: str = "", hc: int = HC) -> Boundary:
+    """hc residual streams (4 unless given)."""
     rng = _rng(workload, M)
     partials = _normal_bf16(rng, (tp, M, H), partial_std)
-    residual = _normal_bf16(rng, (M, HC, H), 1.0)
-    post, comb, pre = _mixes(rng, M)
+    residual = _normal_bf16(rng, (M, hc, H), 1.0)
+    post, comb, pre = _mixes(rng, M, hc)
     gamma = _gamma(rng, H)
     return Boundary(name or f"boundary-H{H}-tp{tp}-M{M}", M, H, tp, partials, residual,
                     post, comb, pre, gamma)
@@ -135,9 +136,12 @@ def tiny_delayed() -> Boundary:
     return boundary(0, 4, 512, 2, 1.0, "tiny-delayed-H512-tp2-M4")
 
 
-def dsv41_delayed(M: int) -> Boundary:
-    """DSV4.1-shaped delayed boundary: H=5120, tp=8, partials N(0,0.5)."""
-    return boundary(1, M, 5120, 8, 0.5, f"dsv41-delayed-H5120-tp8-M{M}")
+def dsv41_delayed(M: int, hc: int = HC) -> Boundary:
+    """DSV4.1-shaped delayed boundary: H=5120, tp=8, partials N(0,0.5);
+    hc residual streams (4 unless given)."""
+    if hc == HC:
+        return boundary(1, M, 5120, 8, 0.5, f"dsv41-delayed-H5120-tp8-M{M}")
+    return boundary(1, M, 5120, 8, 0.5, f"dsv41-delayed-H5120-tp8-hc{hc}-M{M}", hc)
 
 
 def large_m_delayed(M: int = 8192) -> Boundary:

@@ -64,7 +64,8 @@ def _boundary(**kw):
 
 @pytest.mark.parametrize("kw,code,text", [
     (dict(M=0), 1, "M=0"),
-    (dict(hc_mult=2), 3, "hc_mult"),
+    (dict(hc_mult=3), 3, "hc_mult"),
+    (dict(hc_mult=16), 3, "1, 2, 4 or 8"),
     (dict(hidden_size=100), 3, "multiple of 8"),
     (dict(hidden_size=32768, rank_stride=4 * 32768), 3, "exceeds"),
     (dict(tp=0), 1, "tp=0"),
@@ -124,6 +125,8 @@ def test_glm_mixes_finalize_quant_validation():
         mhc.mhcb_mixes(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 4, 1e-6, 2.0, -1, 0)
     with pytest.raises(mhc.MhcbError, match="hc_mult"):
         mhc.mhcb_mixes(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 3, 1e-6, 2.0, 20, 0)
+    with pytest.raises(mhc.MhcbError, match="only 4"):
+        mhc.mhcb_boundary_glm(**{**glm, "hc_mult": 2})
     fin = dict(gemm2_permuted=FAKE, gemm2_rank_stride=32 * 512, rows=32, expert_weights=FAKE,
                weights_rank_stride=0, permuted_idx=FAKE, idx_rank_stride=0, shared_output=FAKE,
                shared_rank_stride=4 * 512, residual=FAKE, post=FAKE, comb=FAKE, pre=FAKE,

@@ -584,6 +584,58 @@ def test_glm_boundary_object_side_stream_and_join():
 # Mailbox stand-in
 # ---------------------------------------------------------------------------
 
+def _hc_inputs(hc, M, H, tp, seed):
+    """Seeded delayed-boundary inputs with hc residual streams."""
+    rng = np.random.default_rng(seed)
+    partials = synth.to_bf16_bits(rng.standard_normal((tp, M, H)).astype(np.float32) * 0.5)
+    residual = synth.to_bf16_bits(rng.standard_normal((M, hc, H)).astype(np.float32))
+    post = rng.uniform(0, 1, (M, hc)).astype(np.float32)
+    comb = (rng.uniform(0, 1, (M, hc, hc)) / hc).astype(np.float32)
+    pre = rng.uniform(0, 1, (M, hc)).astype(np.float32)
+    gamma = synth.to_bf16_bits((1 + 0.1 * rng.standard_normal(H)).astype(np.float32))
+    return partials, residual, post, comb, pre, gamma
+
+
+@pytest.mark.parametrize("hc", [1, 2, 8])
+def test_general_hc_delayed_finalize_and_mailbox(hc):
+    """hc_mult = 1, 2 and 8 streams: the delayed boundary (split and unsplit,
+    MXFP8 epilogue), the MoE finalize (one-shot split and unsplit, two-shot)
+    and the mailbox-fed consumer, against the oracle."""
+    M, H, tp = 37, 1024, 4
+    partials, residual, post, comb, pre, gamma = _hc_inputs(hc, M, H, tp, 70 + hc)
+    print(f"[gpu] general hc={hc} M={M} H={H}", flush=True)
+    ro_ref, li_ref, (v_ref, s_ref) = oracle.boundary(partials, residual, post, comb, pre, gamma,
+                                                     1e-6, mxfp8=True, threads=8)
+    d = [dev(x) for x in (partials, residual, post, comb, pre, gamma)]
+    for split in (True, False):
+        ro, li, (vals, scales) = mhc.boundary(*d, 1e-6, mxfp8=True, split=split)
+        torch.cuda.synchronize()
+        assert_bits_equal(u16(ro), ro_ref, f"residual_out split={split}")
+        assert_within_ulp(u16(li), li_ref, 1, f"layer_input split={split}")
+        v_q, s_q = oracle.quant_mxfp8(u16(li))
+        assert_bits_equal(host(vals), v_q, "mxfp8 values")
+        assert_bits_equal(host(scales), s_q, "mxfp8 scales")
+
+    f = synth.moe_finalize(M, H=H, tp=tp, top_k=4, replicated_routing=False, drop_fraction=0.1)
+    fro_ref, fli_ref, _ = oracle.finalize(f.gemm2, f.weights, f.idx, f.shared, residual, post, comb,
+                                          pre, gamma, 1e-6, replicated_routing=False, threads=8)
+    for two_shot, split in ((False, True), (False, False), (True, True)):
+        out = mhc.finalize(dev(f.gemm2), dev(f.weights), dev(f.idx), dev(f.shared), d[1], d[2],
+                           d[3], d[4], d[5], 1e-6, two_shot=two_shot, split=split)
+        torch.cuda.synchronize()
+        assert_bits_equal(u16(out[0]), fro_ref, f"finalize residual_out two_shot={two_shot} split={split}")
+        assert_within_ulp(u16(out[1]), fli_ref, 1, f"finalize layer_input two_shot={two_shot}")
+
+    mb = mhc.Mailbox(tp, 64, H, "cuda")
+    mb.init()
+    mb.publish(d[0])
+    ro, li, _ = mb.boundary(M, d[1], d[2], d[3], d[4], d[5], 1e-6)
+    torch.cuda.synchronize()
+    assert mb.status_ok()
+    assert_bits_equal(u16(ro), ro_ref, "mailbox residual_out")
+    assert_within_ulp(u16(li), li_ref, 1, "mailbox layer_input")
+
+
 def test_mailbox_generations_cycle_and_match_direct():
     from oracle.mailbox_model import MailboxModel
     cap, H, tp = 64, 1024, 4

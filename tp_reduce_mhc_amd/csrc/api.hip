@@ -48,9 +48,10 @@ constexpr int kGlmTileMinM = 256;  // automatic matrix-core tiles from this M
 int check_common(const char *fn, const uint16_t *residual, const float *post, const float *comb,
                  const float *pre, const uint16_t *norm_weight, const uint16_t *residual_out,
                  const uint16_t *layer_input, const uint8_t *mx_values, const uint8_t *mx_scales,
-                 int M, int H, int hc, int tp) {
+                 int M, int H, int hc, int tp, bool any_hc) {
   if (M < 1) return fail(MHCB_EINVAL, "%s: M=%d is outside [1, capacity]", fn, M);
-  if (hc != kStreams) return fail(MHCB_EUNSUPPORTED, "%s: hc_mult=%d (only 4)", fn, hc);
+  if (any_hc ? (hc != 1 && hc != 2 && hc != 4 && hc != 8) : hc != kStreams)
+    return fail(MHCB_EUNSUPPORTED, "%s: hc_mult=%d (%s)", fn, hc, any_hc ? "1, 2, 4 or 8" : "only 4");
   if (H <= 0 || H % kFrag) return fail(MHCB_EUNSUPPORTED, "%s: hidden_size=%d must be a positive multiple of 8", fn, H);
   if (H > kMaxHidden) return fail(MHCB_EUNSUPPORTED, "%s: hidden_size=%d exceeds %d", fn, H, kMaxHidden);
   if (tp < 1 || tp > kMaxTp) return fail(MHCB_EINVAL, "%s: tp=%d is outside [1, %d]", fn, tp, kMaxTp);
@@ -210,7 +211,7 @@ int mhcb_boundary(const uint16_t *partials, int64_t rank_stride, const mhcb_mail
                   float norm_eps, hipStream_t stream) {
   const char *fn = "mhcb_boundary";
   int rc = check_common(fn, residual, post, comb, pre, norm_weight, residual_out, layer_input,
-                        mxfp8_values, mxfp8_scales, M, hidden_size, hc_mult, tp);
+                        mxfp8_values, mxfp8_scales, M, hidden_size, hc_mult, tp, true);
   if (rc) return rc;
   if ((rc = check_workspace(fn, workspace, workspace_bytes, kSyncBytes))) return rc;
   if ((partials == nullptr) == (mailbox == nullptr))
@@ -231,6 +232,7 @@ int mhcb_boundary(const uint16_t *partials, int64_t rank_stride, const mhcb_mail
     a.rank_stride = rank_stride;
   }
   a.tp = tp;
+  a.hc = hc_mult;
   a.residual = residual;
   a.post = post;
   a.comb = comb;
@@ -259,7 +261,7 @@ int mhcb_boundary_glm(const uint16_t *partials, int64_t rank_stride, const uint1
     return fail(MHCB_EINVAL, "%s: partials, hc_fn, scale, base, norm_weight, mixes_out and layer_input are required", fn);
   // The GLM pre-mix is derived in-kernel from scale/base: check the normalized path.
   int rc = check_common(fn, residual, post, comb, scale, norm_weight, residual_out, layer_input,
-                        nullptr, nullptr, M, hidden_size, hc_mult, tp);
+                        nullptr, nullptr, M, hidden_size, hc_mult, tp, false);
   if (rc) return rc;
   if ((rc = check_workspace(fn, workspace, workspace_bytes, kSyncBytes))) return rc;
   if (hidden_size > kMaxHiddenGlm)
@@ -371,7 +373,7 @@ static int finalize_impl(const char *fn, const uint16_t *gemm2_permuted, int64_t
                          int hidden_size, int hc_mult, int tp, int top_k, float norm_eps,
                          hipStream_t stream) {
   int rc = check_common(fn, residual, post, comb, pre, norm_weight, residual_out, layer_input,
-                        mxfp8_values, mxfp8_scales, M, hidden_size, hc_mult, tp);
+                        mxfp8_values, mxfp8_scales, M, hidden_size, hc_mult, tp, true);
   if (rc) return rc;
   if (top_k < 1) return fail(MHCB_EINVAL, "%s: top_k=%d < 1", fn, top_k);
   if (weights_bf16 != 0 && weights_bf16 != 1)
@@ -395,6 +397,7 @@ static int finalize_impl(const char *fn, const uint16_t *gemm2_permuted, int64_t
                     shared_output, shared_rank_stride, top_k};
   BoundaryArgs a = {};
   a.tp = tp;
+  a.hc = hc_mult;
   a.residual = residual;
   a.post = post;
   a.comb = comb;

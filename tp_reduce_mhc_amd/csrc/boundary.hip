@@ -45,17 +45,21 @@ namespace {
 
 constexpr int kMaxRoutes = 1024;  // tp * top_k staged per workgroup
 
+// A token's mixes for HC streams (post [HC], comb [HC][HC] source-major,
+// pre [HC]).
+template <int HC>
 struct Mixes {
-  float post[kStreams], comb[kStreams * kStreams], pre[kStreams];
+  float post[HC], comb[HC * HC], pre[HC];
 };
 
-__device__ __forceinline__ void load_mixes(const BoundaryArgs &a, int t, Mixes &m) {
+template <int HC>
+__device__ __forceinline__ void load_mixes(const BoundaryArgs &a, int t, Mixes<HC> &m) {
 #pragma unroll
-  for (int j = 0; j < kStreams; ++j) m.post[j] = a.post[t * kStreams + j];
+  for (int j = 0; j < HC; ++j) m.post[j] = a.post[t * HC + j];
 #pragma unroll
-  for (int i = 0; i < kStreams * kStreams; ++i) m.comb[i] = a.comb[t * kStreams * kStreams + i];
+  for (int i = 0; i < HC * HC; ++i) m.comb[i] = a.comb[t * HC * HC + i];
 #pragma unroll
-  for (int j = 0; j < kStreams; ++j) m.pre[j] = a.pre ? a.pre[t * kStreams + j] : 0.0f;
+  for (int j = 0; j < HC; ++j) m.pre[j] = a.pre ? a.pre[t * HC + j] : 0.0f;
 }
 
 // Adds one rank's fragment to the running FP32 sum (rank order).
@@ -222,8 +226,8 @@ __device__ float token_inv(const BoundaryArgs &a, int t, int s, double ss, doubl
 // slices == 1).  TP > 0 fixes the rank count at compile time so that every
 // rank load of every trip is issued up front; TP == 0 reads it from the
 // arguments.
-template <int TRIPS, int TP, Source SRC>
-__global__ void __launch_bounds__(TRIPS == 1 && (SRC != Source::kFinalize || TP == 0)
+template <int TRIPS, int TP, Source SRC, int HC>
+__global__ void __launch_bounds__(TRIPS == 1 && (SRC != Source::kFinalize || TP == 0) && HC <= 4
                                       ? kTokenThreadsWide
                                       : kTokenThreads)
 boundary_kernel(const BoundaryArgs a) {
@@ -267,7 +271,7 @@ boundary_kernel(const BoundaryArgs a) {
 
   // Issue the streamed loads first: residual streams, gamma, and (fixed tp)
   // the partials, for every trip.
-  u32x4 res[TRIPS][kStreams], gam[TRIPS];
+  u32x4 res[TRIPS][HC], gam[TRIPS];
   constexpr int kHeld = TP > 0 ? TP : 1;
   u32x4 part[TRIPS][kHeld];
 #pragma unroll
@@ -284,8 +288,8 @@ boundary_kernel(const BoundaryArgs a) {
       for (int r = 0; r < TP; ++r) part[i][r] = load_stream(src + r * rs + col[i]);
     }
 #pragma unroll
-    for (int q = 0; q < kStreams; ++q)
-      res[i][q] = load_stream(a.residual + ((int64_t)t * kStreams + q) * H + col[i]);
+    for (int q = 0; q < HC; ++q)
+      res[i][q] = load_stream(a.residual + ((int64_t)t * HC + q) * H + col[i]);
     gam[i] = norm ? load_cached(a.gamma + col[i]) : u32x4{0, 0, 0, 0};
   }
   // Finalize: the routes are staged while those loads are in flight (the
@@ -294,8 +298,8 @@ boundary_kernel(const BoundaryArgs a) {
   // The token's mixes are scalar loads; keep them behind the vector loads so
   // that waiting for them does not delay the stream.
   __builtin_amdgcn_sched_barrier(0);
-  Mixes m;
-  load_mixes(a, t, m);
+  Mixes<HC> m;
+  load_mixes<HC>(a, t, m);
   // Split: the token slot's epoch word, read by wave 0 (its latency hides
   // behind the loads above).
   uint64_t callw = 0;
@@ -343,22 +347,22 @@ boundary_kernel(const BoundaryArgs a) {
     unpack8(pack8(sum), x);
 
     // a2: y_j = bf16(x * post_j (+) sum_s res_s * comb[s][j]), s ascending.
-    float r4[kStreams][8];
+    float r4[HC][8];
 #pragma unroll
-    for (int q = 0; q < kStreams; ++q) unpack8(res[i][q], r4[q]);
-    float y[kStreams][8];
+    for (int q = 0; q < HC; ++q) unpack8(res[i][q], r4[q]);
+    float y[HC][8];
 #pragma unroll
-    for (int j = 0; j < kStreams; ++j) {
+    for (int j = 0; j < HC; ++j) {
       float acc[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         float v = x[e] * m.post[j];
 #pragma unroll
-        for (int q = 0; q < kStreams; ++q) v = __builtin_fmaf(r4[q][e], m.comb[q * kStreams + j], v);
+        for (int q = 0; q < HC; ++q) v = __builtin_fmaf(r4[q][e], m.comb[q * HC + j], v);
         acc[e] = v;
       }
       const u32x4 packed = pack8(acc);
-      if (valid[i]) store_stream(a.residual_out + ((int64_t)t * kStreams + j) * H + col[i], packed);
+      if (valid[i]) store_stream(a.residual_out + ((int64_t)t * HC + j) * H + col[i], packed);
       unpack8(packed, y[j]);
     }
 
@@ -368,7 +372,7 @@ boundary_kernel(const BoundaryArgs a) {
     for (int e = 0; e < 8; ++e) {
       float v = 0.0f;
 #pragma unroll
-      for (int j = 0; j < kStreams; ++j) v = __builtin_fmaf(y[j][e], m.pre[j], v);
+      for (int j = 0; j < HC; ++j) v = __builtin_fmaf(y[j][e], m.pre[j], v);
       z[e] = v;
     }
     pfrag[i] = pack8(z);
@@ -448,42 +452,58 @@ boundary_kernel(const BoundaryArgs a) {
   }
 }
 
-template <int TRIPS, Source SRC>
+template <int TRIPS, Source SRC, int HC>
 hipError_t launch_tp(const BoundaryArgs &a, int threads, hipStream_t stream) {
   dim3 grid = a.slices > 1 ? dim3(a.slices, a.M) : dim3(a.M), block(threads);
-  if constexpr (SRC == Source::kFinalize) {
+  if constexpr (HC != kStreams) {
+    // Stream counts other than four take the runtime-rank kernel only.
+    hipLaunchKernelGGL((boundary_kernel<TRIPS, 0, SRC, HC>), grid, block, 0, stream, a);
+  } else if constexpr (SRC == Source::kFinalize) {
     // All 36 gathers in flight at once need one fragment per thread and at
     // most 512 threads (their registers).
     if (TRIPS == 1 && a.tp == 4 && a.fin.top_k <= 8 && threads <= kTokenThreads)
-      hipLaunchKernelGGL((boundary_kernel<1, 4, SRC>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((boundary_kernel<1, 4, SRC, HC>), grid, block, 0, stream, a);
     else
-      hipLaunchKernelGGL((boundary_kernel<TRIPS, 0, SRC>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((boundary_kernel<TRIPS, 0, SRC, HC>), grid, block, 0, stream, a);
   } else {
     switch (a.tp) {
-      case 1: hipLaunchKernelGGL((boundary_kernel<TRIPS, 1, SRC>), grid, block, 0, stream, a); break;
-      case 2: hipLaunchKernelGGL((boundary_kernel<TRIPS, 2, SRC>), grid, block, 0, stream, a); break;
-      case 4: hipLaunchKernelGGL((boundary_kernel<TRIPS, 4, SRC>), grid, block, 0, stream, a); break;
+      case 1: hipLaunchKernelGGL((boundary_kernel<TRIPS, 1, SRC, HC>), grid, block, 0, stream, a); break;
+      case 2: hipLaunchKernelGGL((boundary_kernel<TRIPS, 2, SRC, HC>), grid, block, 0, stream, a); break;
+      case 4: hipLaunchKernelGGL((boundary_kernel<TRIPS, 4, SRC, HC>), grid, block, 0, stream, a); break;
       case 8:
         // Four trips of eight held mailbox ranks would spill; that case takes
         // the runtime-tp kernel.
         if constexpr (TRIPS == 4 && SRC == Source::kMailbox)
-          hipLaunchKernelGGL((boundary_kernel<TRIPS, 0, SRC>), grid, block, 0, stream, a);
+          hipLaunchKernelGGL((boundary_kernel<TRIPS, 0, SRC, HC>), grid, block, 0, stream, a);
         else
-          hipLaunchKernelGGL((boundary_kernel<TRIPS, 8, SRC>), grid, block, 0, stream, a);
+          hipLaunchKernelGGL((boundary_kernel<TRIPS, 8, SRC, HC>), grid, block, 0, stream, a);
         break;
-      default: hipLaunchKernelGGL((boundary_kernel<TRIPS, 0, SRC>), grid, block, 0, stream, a); break;
+      default: hipLaunchKernelGGL((boundary_kernel<TRIPS, 0, SRC, HC>), grid, block, 0, stream, a); break;
     }
   }
   return hipGetLastError();
 }
 
+template <Source SRC, int HC>
+hipError_t launch_hc(const BoundaryArgs &a, hipStream_t stream) {
+  // Eight streams hold twice the registers: at most 512 threads (two or
+  // four fragments per thread past that).
+  const Geometry g = fragment_geometry(a.slices > 1 ? a.slice_frags : a.H / kFrag, HC <= 4);
+  switch (g.trips) {
+    case 1: return launch_tp<1, SRC, HC>(a, g.threads, stream);
+    case 2: return launch_tp<2, SRC, HC>(a, g.threads, stream);
+    default: return launch_tp<4, SRC, HC>(a, g.threads, stream);
+  }
+}
+
 template <Source SRC>
 hipError_t launch_src(const BoundaryArgs &a, hipStream_t stream) {
-  const Geometry g = fragment_geometry(a.slices > 1 ? a.slice_frags : a.H / kFrag, true);
-  switch (g.trips) {
-    case 1: return launch_tp<1, SRC>(a, g.threads, stream);
-    case 2: return launch_tp<2, SRC>(a, g.threads, stream);
-    default: return launch_tp<4, SRC>(a, g.threads, stream);
+  switch (a.hc) {
+    case 1: return launch_hc<SRC, 1>(a, stream);
+    case 2: return launch_hc<SRC, 2>(a, stream);
+    case 4: return launch_hc<SRC, 4>(a, stream);
+    case 8: return launch_hc<SRC, 8>(a, stream);
+    default: return hipErrorInvalidValue;
   }
 }
 

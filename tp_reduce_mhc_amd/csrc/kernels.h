@@ -76,10 +76,11 @@ struct BoundaryArgs {
   MailboxView mailbox;
   FinalizeView fin;
   int tp;
-  const uint16_t *residual;  // [M, 4, H]
-  const float *post;         // [M, 4]
-  const float *comb;         // [M, 4, 4] [source][target]
-  const float *pre;          // [M, 4] or null (residual only)
+  int hc;                    // residual streams: 1, 2, 4 or 8
+  const uint16_t *residual;  // [M, hc, H]
+  const float *post;         // [M, hc]
+  const float *comb;         // [M, hc, hc] [source][target]
+  const float *pre;          // [M, hc] or null (residual only)
   const uint16_t *gamma;     // [H] or null
   uint16_t *residual_out;    // [M, 4, H]
   uint16_t *layer_input;     // [M, H] or null

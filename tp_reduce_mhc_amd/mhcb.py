@@ -269,12 +269,14 @@ def boundary(partials: torch.Tensor, residual, post, comb, pre, norm_weight, nor
     split (default) the cached workspace lets small-M calls spread tokens
     over several workgroups.
 
-    Returns (residual_out [M,4,H], layer_input [M,H] or None,
+    residual [M, hc, H] with hc = 1, 2, 4 or 8.
+    Returns (residual_out [M,hc,H], layer_input [M,H] or None,
     (values [M,H] u8, scales u8) or None)."""
     tp, M, H = partials.shape
+    hc = residual.shape[1]
     dev = partials.device
     ws = workspace(dev) if split else None
-    residual_out = _bf16_empty((M, 4, H), dev)
+    residual_out = _bf16_empty((M, hc, H), dev)
     layer_input = None if pre is None else _bf16_empty((M, H), dev)
     values = scales = None
     if mxfp8:
@@ -282,7 +284,7 @@ def boundary(partials: torch.Tensor, residual, post, comb, pre, norm_weight, nor
         scales = torch.empty(mhcb_mxfp8_scale_bytes(M, H), dtype=torch.uint8, device=dev)
     mhcb_boundary(partials, M * H if tp > 1 else 0, None, residual, post, comb, pre, norm_weight,
                   residual_out, layer_input, values, scales, ws, ws.numel() if ws is not None else 0,
-                  M, H, 4, tp, norm_eps, stream)
+                  M, H, hc, tp, norm_eps, stream)
     return residual_out, layer_input, ((values, scales) if mxfp8 else None)
 
 
@@ -315,13 +317,15 @@ def finalize(gemm2, weights, idx, shared, residual, post, comb, pre, norm_weight
              two_shot: bool = False, mxfp8: bool = False, split: bool = True,
              routed_scaling_factor: float = 1.0, stream=None):
     """MoE finalize boundary.  gemm2 [tp, rows, H]; shared [tp, M, H];
-    weights (FP32 or BF16) / idx [M, top_k] (replicated) or [tp, M, top_k]."""
+    weights (FP32 or BF16) / idx [M, top_k] (replicated) or [tp, M, top_k];
+    residual [M, hc, H] (hc = 1, 2, 4 or 8)."""
     tp, rows, H = gemm2.shape
     M = shared.shape[1]
+    hc = residual.shape[1]
     top_k = weights.shape[-1]
     dev = gemm2.device
     per_rank = weights.dim() == 3
-    residual_out = _bf16_empty((M, 4, H), dev)
+    residual_out = _bf16_empty((M, hc, H), dev)
     layer_input = None if pre is None else _bf16_empty((M, H), dev)
     values = scales = None
     if mxfp8:
@@ -332,7 +336,7 @@ def finalize(gemm2, weights, idx, shared, residual, post, comb, pre, norm_weight
                      weights.dtype == torch.bfloat16, routed_scaling_factor, idx,
                      M * top_k if per_rank else 0, shared, M * H, residual, post, comb, pre,
                      norm_weight, residual_out, layer_input, values, scales, two_shot, ws,
-                     ws.numel() if ws is not None else 0, M, H, 4, tp, top_k, norm_eps, stream)
+                     ws.numel() if ws is not None else 0, M, H, hc, tp, top_k, norm_eps, stream)
     return residual_out, layer_input, ((values, scales) if mxfp8 else None)
 
 
@@ -366,10 +370,11 @@ class Mailbox:
 
     def boundary(self, M, residual, post, comb, pre, norm_weight, norm_eps, *, mxfp8=False,
                  stream=None):
-        """The consumer: the delayed-mHC boundary fed from this mailbox."""
-        H = self.hidden_size
+        """The consumer: the delayed-mHC boundary fed from this mailbox
+        (residual [M, hc, H], hc = 1, 2, 4 or 8)."""
+        H, hc = self.hidden_size, residual.shape[1]
         dev = residual.device
-        residual_out = _bf16_empty((M, 4, H), dev)
+        residual_out = _bf16_empty((M, hc, H), dev)
         layer_input = None if pre is None else _bf16_empty((M, H), dev)
         values = scales = None
         if mxfp8:
@@ -377,7 +382,7 @@ class Mailbox:
             scales = torch.empty(mhcb_mxfp8_scale_bytes(M, H), dtype=torch.uint8, device=dev)
         ws = workspace(dev)
         mhcb_boundary(None, 0, self, residual, post, comb, pre, norm_weight, residual_out,
-                      layer_input, values, scales, ws, ws.numel(), M, H, 4, self.tp, norm_eps,
+                      layer_input, values, scales, ws, ws.numel(), M, H, hc, self.tp, norm_eps,
                       stream)
         return residual_out, layer_input, ((values, scales) if mxfp8 else None)
 
