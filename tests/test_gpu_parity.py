@@ -636,6 +636,22 @@ def test_general_hc_delayed_finalize_and_mailbox(hc):
     assert_within_ulp(u16(li), li_ref, 1, "mailbox layer_input")
 
 
+@pytest.mark.parametrize("hc", [1, 2, 8])
+def test_general_hc_dsv41_shape(hc):
+    """hc_mult = 1, 2 and 8 at H=5120, tp=8 (ranks held in registers; eight
+    streams in two trips when unsplit): split and unsplit against the oracle."""
+    b = synth.dsv41_delayed(16, hc)
+    print(f"[gpu] {b.name}", flush=True)
+    ro_ref, li_ref, _ = oracle.boundary(b.partials, b.residual, b.post, b.comb, b.pre, b.gamma,
+                                        b.norm_eps, threads=8)
+    d = [dev(x) for x in (b.partials, b.residual, b.post, b.comb, b.pre, b.gamma)]
+    for split in (True, False):
+        ro, li, _ = mhc.boundary(*d, b.norm_eps, split=split)
+        torch.cuda.synchronize()
+        assert_bits_equal(u16(ro), ro_ref, f"residual_out split={split}")
+        assert_within_ulp(u16(li), li_ref, 1, f"layer_input split={split}")
+
+
 def test_mailbox_generations_cycle_and_match_direct():
     from oracle.mailbox_model import MailboxModel
     cap, H, tp = 64, 1024, 4

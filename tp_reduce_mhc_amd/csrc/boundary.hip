@@ -24,13 +24,13 @@
 namespace mhcb {
 
 // A workgroup covering `frags` fragments: 1, 2 or 4 fragments per thread,
-// at most kTokenThreads threads (frags <= 2048, i.e. hidden <= 16384); with
-// `wide`, one fragment per thread up to kTokenThreadsWide threads.  A token's
-// VALU work is then spread over more waves: at H=5120 ten one-fragment waves
-// put at most three fragments' work on a SIMD, five two-fragment waves four.
-Geometry fragment_geometry(int frags, bool wide) {
+// at most kTokenThreads threads (frags <= 2048, i.e. hidden <= 16384), or
+// one fragment per thread up to `wide_threads` threads.  A token's VALU work
+// is then spread over more waves: at H=5120 ten one-fragment waves put at
+// most three fragments' work on a SIMD, five two-fragment waves four.
+Geometry fragment_geometry(int frags, int wide_threads) {
   Geometry g;
-  if (wide && frags <= kTokenThreadsWide) {
+  if (frags <= wide_threads) {
     g.trips = 1;
     g.threads = (frags + kWave - 1) / kWave * kWave;
     return g;
@@ -226,10 +226,19 @@ __device__ float token_inv(const BoundaryArgs &a, int t, int s, double ss, doubl
 // slices == 1).  TP > 0 fixes the rank count at compile time so that every
 // rank load of every trip is issued up front; TP == 0 reads it from the
 // arguments.
+// Threads of a one-fragment-per-thread workgroup (0: none; at most
+// kTokenThreads then): eight streams hold twice the registers, and their
+// mailbox variant's poll path does not fit 768 threads' registers.
+template <Source SRC, int HC>
+constexpr int wide_threads() {
+  return HC <= kStreams ? kTokenThreadsWide : SRC == Source::kMailbox ? 0 : kTokenThreadsWide8;
+}
+
 template <int TRIPS, int TP, Source SRC, int HC>
-__global__ void __launch_bounds__(TRIPS == 1 && (SRC != Source::kFinalize || TP == 0) && HC <= 4
-                                      ? kTokenThreadsWide
-                                      : kTokenThreads)
+__global__ void __launch_bounds__((TRIPS > 1 || (SRC == Source::kFinalize && TP > 0) ||
+                                           wide_threads<SRC, HC>() == 0
+                                       ? kTokenThreads
+                                       : wide_threads<SRC, HC>()))
 boundary_kernel(const BoundaryArgs a) {
   __shared__ double red[kTokenThreadsWide / kWave + 1];
   __shared__ int32_t srow[SRC == Source::kFinalize ? kMaxRoutes : 1];
@@ -452,43 +461,48 @@ boundary_kernel(const BoundaryArgs a) {
   }
 }
 
+template <int TRIPS, int TP, Source SRC, int HC>
+void launch_one(const BoundaryArgs &a, dim3 grid, dim3 block, hipStream_t stream) {
+  hipLaunchKernelGGL((boundary_kernel<TRIPS, TP, SRC, HC>), grid, block, 0, stream, a);
+}
+
+template <int TRIPS, Source SRC, int HC>
+void launch_held(const BoundaryArgs &a, dim3 grid, dim3 block, hipStream_t stream) {
+  // Ranks held in registers (every load issued up front) for tp = 1, 2, 4
+  // and 8 with four streams; other stream counts for tp = 4 and 8 only, to
+  // bound the kernel count, and eight streams in one trip, or two from
+  // resident partials (more would spill).  Four trips of eight mailbox ranks
+  // would spill too.  Everything else takes the runtime-rank kernel.
+  constexpr bool kAll = HC == kStreams;
+  constexpr bool kHold4 = HC <= kStreams || TRIPS == 1 || (TRIPS == 2 && SRC == Source::kPartials);
+  constexpr bool kHold8 = kHold4 && !(TRIPS == 4 && SRC == Source::kMailbox);
+  if (kAll && a.tp == 1) launch_one<TRIPS, kAll ? 1 : 0, SRC, HC>(a, grid, block, stream);
+  else if (kAll && a.tp == 2) launch_one<TRIPS, kAll ? 2 : 0, SRC, HC>(a, grid, block, stream);
+  else if (kHold4 && a.tp == 4) launch_one<TRIPS, kHold4 ? 4 : 0, SRC, HC>(a, grid, block, stream);
+  else if (kHold8 && a.tp == 8) launch_one<TRIPS, kHold8 ? 8 : 0, SRC, HC>(a, grid, block, stream);
+  else launch_one<TRIPS, 0, SRC, HC>(a, grid, block, stream);
+}
+
 template <int TRIPS, Source SRC, int HC>
 hipError_t launch_tp(const BoundaryArgs &a, int threads, hipStream_t stream) {
-  dim3 grid = a.slices > 1 ? dim3(a.slices, a.M) : dim3(a.M), block(threads);
-  if constexpr (HC != kStreams) {
-    // Stream counts other than four take the runtime-rank kernel only.
-    hipLaunchKernelGGL((boundary_kernel<TRIPS, 0, SRC, HC>), grid, block, 0, stream, a);
-  } else if constexpr (SRC == Source::kFinalize) {
+  const dim3 grid = a.slices > 1 ? dim3(a.slices, a.M) : dim3(a.M), block(threads);
+  if constexpr (SRC == Source::kFinalize) {
     // All 36 gathers in flight at once need one fragment per thread and at
     // most 512 threads (their registers).
-    if (TRIPS == 1 && a.tp == 4 && a.fin.top_k <= 8 && threads <= kTokenThreads)
-      hipLaunchKernelGGL((boundary_kernel<1, 4, SRC, HC>), grid, block, 0, stream, a);
+    if (TRIPS == 1 && HC <= kStreams && a.tp == 4 && a.fin.top_k <= 8 && threads <= kTokenThreads)
+      launch_one<1, HC <= kStreams ? 4 : 0, SRC, HC>(a, grid, block, stream);
     else
-      hipLaunchKernelGGL((boundary_kernel<TRIPS, 0, SRC, HC>), grid, block, 0, stream, a);
+      launch_one<TRIPS, 0, SRC, HC>(a, grid, block, stream);
   } else {
-    switch (a.tp) {
-      case 1: hipLaunchKernelGGL((boundary_kernel<TRIPS, 1, SRC, HC>), grid, block, 0, stream, a); break;
-      case 2: hipLaunchKernelGGL((boundary_kernel<TRIPS, 2, SRC, HC>), grid, block, 0, stream, a); break;
-      case 4: hipLaunchKernelGGL((boundary_kernel<TRIPS, 4, SRC, HC>), grid, block, 0, stream, a); break;
-      case 8:
-        // Four trips of eight held mailbox ranks would spill; that case takes
-        // the runtime-tp kernel.
-        if constexpr (TRIPS == 4 && SRC == Source::kMailbox)
-          hipLaunchKernelGGL((boundary_kernel<TRIPS, 0, SRC, HC>), grid, block, 0, stream, a);
-        else
-          hipLaunchKernelGGL((boundary_kernel<TRIPS, 8, SRC, HC>), grid, block, 0, stream, a);
-        break;
-      default: hipLaunchKernelGGL((boundary_kernel<TRIPS, 0, SRC, HC>), grid, block, 0, stream, a); break;
-    }
+    launch_held<TRIPS, SRC, HC>(a, grid, block, stream);
   }
   return hipGetLastError();
 }
 
 template <Source SRC, int HC>
 hipError_t launch_hc(const BoundaryArgs &a, hipStream_t stream) {
-  // Eight streams hold twice the registers: at most 512 threads (two or
-  // four fragments per thread past that).
-  const Geometry g = fragment_geometry(a.slices > 1 ? a.slice_frags : a.H / kFrag, HC <= 4);
+  const Geometry g = fragment_geometry(a.slices > 1 ? a.slice_frags : a.H / kFrag,
+                                       wide_threads<SRC, HC>());
   switch (g.trips) {
     case 1: return launch_tp<1, SRC, HC>(a, g.threads, stream);
     case 2: return launch_tp<2, SRC, HC>(a, g.threads, stream);

@@ -18,6 +18,7 @@ constexpr int kWave = 64;
 constexpr int kMaxThreads = 1024;
 constexpr int kTokenThreads = 512;  // workgroup size bound of the per-token kernels
 constexpr int kTokenThreadsWide = 1024;  // the same with one fragment per thread
+constexpr int kTokenThreadsWide8 = 768;  // the same for eight residual streams
 constexpr uint16_t kSentinel = 0x8000;  // BF16 negative zero marks an empty slot
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

@@ -143,7 +143,7 @@ hipError_t launch_mixes(const float *mixes, const float *scale, const float *bas
 struct Geometry {
   int trips, threads;
 };
-Geometry fragment_geometry(int frags, bool wide = false);
+Geometry fragment_geometry(int frags, int wide_threads = 0);
 inline Geometry token_geometry(int H) { return fragment_geometry(H / 8); }
 
 hipError_t launch_zero(void *p, int64_t bytes, hipStream_t stream);
