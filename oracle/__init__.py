@@ -326,6 +326,21 @@ def boundary_glm(partials, residual, post, comb, fn, scale, base, gamma, rms_eps
     return res_out, mixes, layer, pre
 
 
+def boundary_glm_moe(gemm2, weights, idx, shared, residual, post, comb, fn, scale, base, gamma,
+                     rms_eps, hc_eps, norm_eps, *, replicated_routing=True,
+                     routed_scaling_factor=1.0, threads=1):
+    """GLM boundary of an MoE sublayer ([GLM] AllReduceMhcBoundary.__call__,
+    MoE branch): every rank publishes its contribution (a6, routing weights
+    FP32 or BF16 with the routed scaling factor), and the GLM boundary
+    (a1, a2, a3, a4) reads the published contributions as its rank partials.
+    Shapes as in finalize_contributions and boundary_glm."""
+    contrib = finalize_contributions(gemm2, weights, idx, shared,
+                                     replicated_routing=replicated_routing,
+                                     routed_scaling_factor=routed_scaling_factor, threads=threads)
+    return boundary_glm(contrib, residual, post, comb, fn, scale, base, gamma, rms_eps, hc_eps,
+                        norm_eps, threads=threads)
+
+
 def sinkhorn(logits, eps, repeat):
     """The page's Sinkhorn on one 4x4 logit matrix (row-major 16 floats)."""
     logits = _c(logits, np.float32).reshape(16)

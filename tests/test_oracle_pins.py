@@ -760,6 +760,49 @@ def test_finalize_equals_boundary_on_contributions():
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
+def _glm_moe_inputs(M, H, tp, top_k):
+    f = synth.moe_finalize(M, H=H, tp=tp, top_k=top_k, replicated_routing=False)
+    g = synth.glm(M, H=H, tp=tp)
+    return f, g
+
+
+def test_glm_moe_with_every_route_dropped_is_the_glm_boundary_on_shared():
+    """No rank holds any routed expert: each contribution is the rank's
+    shared-expert output with -0 made +0, so the MoE GLM boundary is the GLM
+    boundary on those shared outputs."""
+    f, g = _glm_moe_inputs(3, 256, 2, 2)
+    idx = np.full_like(f.idx, -1)
+    shared = f.shared.copy()
+    shared[0, 1, :5] = 0x8000
+    shared[1, 2, 7] = 0x8000
+    got = oracle.boundary_glm_moe(f.gemm2, f.weights, idx, shared, g.residual, g.post, g.comb,
+                                  g.fn, g.scale, g.base, g.gamma, 1e-6, 1e-6, 1e-6,
+                                  replicated_routing=False)
+    plain = np.where(shared == 0x8000, np.uint16(0), shared)
+    want = oracle.boundary_glm(plain, g.residual, g.post, g.comb, g.fn, g.scale, g.base, g.gamma,
+                               1e-6, 1e-6, 1e-6)
+    for a, b in zip(got, want):
+        assert np.array_equal(a, b)
+
+
+def test_glm_moe_single_unit_route_is_the_glm_boundary_on_the_rows():
+    """tp = 1, top_k = 1, weight 1, shared zero: the contribution is the
+    routed row itself, so the MoE GLM boundary is the GLM boundary on the
+    rows in route order."""
+    f, g = _glm_moe_inputs(4, 256, 1, 1)
+    weights = np.ones((4, 1), np.float32)
+    idx = np.array([[2], [0], [3], [1]], np.int32)
+    shared = np.zeros_like(f.shared)
+    got = oracle.boundary_glm_moe(f.gemm2, weights, idx, shared, g.residual, g.post, g.comb,
+                                  g.fn, g.scale, g.base, g.gamma, 1e-6, 1e-6, 1e-6)
+    rows = f.gemm2[:, idx[:, 0]]
+    rows = np.where(rows == 0x8000, np.uint16(0), rows)
+    want = oracle.boundary_glm(rows, g.residual, g.post, g.comb, g.fn, g.scale, g.base, g.gamma,
+                               1e-6, 1e-6, 1e-6)
+    for a, b in zip(got, want):
+        assert np.array_equal(a, b)
+
+
 # ---------------------------------------------------------------------------
 # a8 MXFP8
 # ---------------------------------------------------------------------------
