@@ -448,10 +448,11 @@ def main():
             extra[f"glm_M{M}"] = entry(ms, nbytes, M)
             log(f"glm M={M}: {extra[f'glm_M{M}']}")
             if M == 64:  # the tokens-per-workgroup choices at one size
-                for G in (1, 2, 4, 16):
+                for G in (1, 2, 4, 16, -16):
+                    name = f"glm_M64_tokens_per_wg{G}" if G > 0 else "glm_M64_two_pass_tiles"
                     ms, nbytes = bench_glm(torch, mhc, g, min(K, 100), min(W, 5), G)
-                    extra[f"glm_M64_tokens_per_wg{G}"] = entry(ms, nbytes, M)
-                    log(f"glm M=64 tokens_per_wg={G}: {extra[f'glm_M64_tokens_per_wg{G}']}")
+                    extra[name] = entry(ms, nbytes, M)
+                    log(f"glm M=64 tokens_per_wg={G}: {extra[name]}")
     if (want("mxfp8") or want("mailbox")) and not args.quick:
         b = synth.large_m_delayed(8192)
         if want("mxfp8"):

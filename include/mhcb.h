@@ -69,10 +69,12 @@ int64_t mhcb_mxfp8_scale_bytes(int64_t M, int64_t hidden_size);
  * state is ready for the next call, with any slice count, with no reset at
  * the end.  Calls that may run concurrently (on different streams) must not
  * share a workspace.
- * mhcb_workspace_bytes gives the size for a call: the sync state, plus for
- * the two-shot emulation (mhcb_finalize, two_shot = 1) the owner mailboxes
- * [tp][tp][ceil(M/tp)][hidden] and the reduced sums [M][hidden] (BF16).
- * Host-only; -1 on bad sizes. */
+ * mhcb_workspace_bytes gives the size for a call: the sync state, then a
+ * scratch area of at least 8 MiB that holds the per-slice partials of the
+ * two-pass GLM tiles (mhcb_boundary_glm, tokens_per_wg = -16) or, when
+ * larger, the two-shot emulation's (mhcb_finalize, two_shot = 1) owner
+ * mailboxes [tp][tp][ceil(M/tp)][hidden] and reduced sums [M][hidden]
+ * (BF16).  Host-only; -1 on bad sizes. */
 int64_t mhcb_workspace_bytes(int M, int hidden_size, int tp, int two_shot);
 
 /* Writes the workspace's sync state (a kernel on `stream`): status word and
@@ -86,7 +88,9 @@ int mhcb_workspace_init(void *workspace, int64_t workspace_bytes, hipStream_t st
 int mhcb_workspace_status(const void *workspace, hipStream_t stream);
 
 /* Tuning: workgroups per token (or per GLM tile) for calls with a
- * workspace (1..16; 0 = automatic, chosen by M from measurements).
+ * workspace (1..64, of which the exchanging splits use at most 16 and the
+ * two-pass GLM tiles at most 64; 0 = automatic, chosen by M from
+ * measurements).
  * Process-wide; returns the previous value.  The BF16 sums, streams and the
  * delayed / finalize layer inputs do not depend on it; the GLM GEMV is
  * summed over the slices in FP32, so its raw mixes may change in the last
@@ -154,8 +158,16 @@ int mhcb_boundary(const uint16_t *partials, int64_t rank_stride, const mhcb_mail
  * tokens_per_wg = 16: tiles of 16 tokens whose GEMV runs on the matrix
  * cores (needs a workspace); its FP32 sums are taken in another order, so
  * mixes_out may differ from the 1/2/4 results in the last bits (both agree
- * with the exact GEMV to about 1e-6 relative).  0 = chosen by M
- * (16 from M = 256 when a workspace is given).  hidden <= 8192.
+ * with the exact GEMV to about 1e-6 relative).  tokens_per_wg = -16: the
+ * same 16-token tiles in two passes, with no cross-workgroup exchange: a
+ * streaming pass writes residual_out and each column slice's partial GEMV
+ * rows and sum of squares to the workspace's scratch area, then a pass with
+ * one workgroup per token adds them in slice order and takes the collapse
+ * and RMSNorm from residual_out (needs a workspace of
+ * mhcb_workspace_bytes(...) bytes; results agree with the other forms to
+ * the same tolerance).  0 = automatic: -16 when the workspace has
+ * mhcb_workspace_bytes(...) bytes, else 16 from M = 256 when a smaller
+ * workspace is given, else 1 or 2.  hidden <= 8192.
  * workspace: optional for 1, 2, 4 (see mhcb_workspace_bytes); calls that
  * share one must be ordered on one stream. */
 int mhcb_boundary_glm(const uint16_t *partials, int64_t rank_stride, const uint16_t *residual,

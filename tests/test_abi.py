@@ -40,9 +40,13 @@ def test_host_only_helpers():
     assert mhc.mhcb_mxfp8_scale_bytes(8192, 5120) == 8192 * 160
     assert mhc.mhcb_mxfp8_scale_bytes(100, 5120) == 128 * 160
     assert mhc.mhcb_mxfp8_scale_bytes(1, 128) == 128 * 4
-    sync = mhc.mhcb_workspace_bytes(10, 512, 4, 0)
-    assert sync > 0 and sync % 256 == 0
-    assert mhc.mhcb_workspace_bytes(10, 512, 4, 1) == sync + (4 * 4 * 3 + 10) * 512 * 2
+    base = mhc.mhcb_workspace_bytes(10, 512, 4, 0)   # sync state + 8 MiB scratch
+    assert base > 8 << 20 and base % 256 == 0
+    sync = base - (8 << 20)
+    # The two-shot areas share the scratch: 8 MiB unless they need more.
+    assert mhc.mhcb_workspace_bytes(10, 512, 4, 1) == base
+    big = (8 * 8 * 512 + 4096) * 8192 * 2
+    assert mhc.mhcb_workspace_bytes(4096, 8192, 8, 1) == sync + big
     assert mhc.mhcb_workspace_bytes(10, 512, 0, 1) == -1
     prev = mhc.mhcb_set_token_slices(4)
     assert mhc.mhcb_set_token_slices(prev) == 4
@@ -117,6 +121,9 @@ def test_glm_mixes_finalize_quant_validation():
                tp=2, rms_eps=1e-6, hc_eps=1e-6, norm_eps=1e-6, stream=0)
     for kw, text in ((dict(tokens_per_wg=3), "tokens_per_wg"), (dict(hc_fn=None), "required"),
                      (dict(tokens_per_wg=16), "needs a workspace"),
+                     (dict(tokens_per_wg=-16), "needs a workspace"),
+                     (dict(tokens_per_wg=-16, workspace=FAKE, workspace_bytes=1 << 23),
+                      "needs a workspace"),
                      (dict(hidden_size=8200, rank_stride=4 * 8200), "exceeds"),
                      (dict(tokens_per_wg=4, hidden_size=8192, rank_stride=4 * 8192), "tokens_per_wg=4")):
         with pytest.raises(mhc.MhcbError, match=text):
@@ -135,7 +142,7 @@ def test_glm_mixes_finalize_quant_validation():
                hidden_size=512, hc_mult=4, tp=2, top_k=8, norm_eps=1e-6, stream=0)
     for kw, text in ((dict(top_k=0), "top_k"), (dict(tp=64, top_k=32), "exceeds"),
                      (dict(two_shot=1), "workspace"), (dict(rows=-1), "rows"),
-                     (dict(two_shot=1, workspace=FAKE + 8, workspace_bytes=1 << 23), "aligned"),
+                     (dict(two_shot=1, workspace=FAKE + 8, workspace_bytes=1 << 24), "aligned"),
                      (dict(two_shot=1, workspace=FAKE, workspace_bytes=1 << 10), "workspace_bytes")):
         with pytest.raises(mhc.MhcbError, match=text):
             mhc.mhcb_finalize(**{**fin, **kw})

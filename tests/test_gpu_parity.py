@@ -536,6 +536,52 @@ def test_glm_tiles_more_tokens_than_one_launch():
     check_glm_against_oracle(g, ro, mixes, li, "tiles M=1100")
 
 
+@pytest.mark.parametrize("M,H,tp,S", [(1, 6144, 8, 0), (17, 6144, 8, 0), (40, 2048, 3, 0),
+                                      (33, 512, 8, 0), (16, 8192, 8, 0), (5, 1024, 1, 0),
+                                      (3, 64, 2, 0), (20, 2048, 8, 4), (20, 2048, 4, 8),
+                                      (37, 6144, 8, 48), (19, 6144, 4, 16)])
+def test_glm_two_pass_tiles_match_oracle(M, H, tp, S):
+    """16-token tiles in two passes (tokens_per_wg=-16): a stream pass that
+    leaves per-slice partials in the workspace, then one workgroup per token.
+    Slices of 16 to 64 fragments, ragged last slices and tiles, fixed (4, 8)
+    and runtime rank counts."""
+    g = synth.glm(M, H=H, tp=tp)
+    prev = mhc.mhcb_set_token_slices(S)
+    try:
+        print(f"[gpu] {g.name} two-pass tiles, slices {S}", flush=True)
+        ro, mixes, li = run_glm(g, -16)
+    finally:
+        mhc.mhcb_set_token_slices(prev)
+    check_glm_against_oracle(g, ro, mixes, li, f"two-pass S={S}")
+
+
+def test_glm_two_pass_more_tokens_than_one_launch():
+    g = synth.glm(1100, H=256, tp=2)
+    print(f"[gpu] {g.name} two-pass tiles", flush=True)
+    ro, mixes, li = run_glm(g, -16)
+    check_glm_against_oracle(g, ro, mixes, li, "two-pass M=1100")
+
+
+def test_glm_two_pass_full_size_sampled():
+    """M = 512, H=6144, tp=8 in two passes, checked on sampled tokens, and
+    its streams equal to the exchanging tiles' bit for bit."""
+    g = synth.glm(512)
+    print(f"[gpu] {g.name} two-pass tiles", flush=True)
+    ro, mixes, li = run_glm(g, -16)
+    ro16, mixes16, _ = run_glm(g, 16)
+    assert_bits_equal(ro, ro16, "two-pass vs exchanging tiles residual_out")
+    assert (np.abs(mixes - mixes16) <= 2e-5 * (np.abs(mixes16) + 1)).all()
+    toks = np.array([0, 1, 15, 16, 255, 256, 300, 496, 510, 511])
+    ro_ref, mix_ref, li_ref, pre_ref = oracle.boundary_glm(
+        g.partials[:, toks], g.residual[toks], g.post[toks], g.comb[toks], g.fn, g.scale, g.base,
+        g.gamma, g.rms_eps, g.hc_eps, g.norm_eps, threads=8)
+    assert_bits_equal(ro[toks], ro_ref, "residual_out (sampled)")
+    err = np.abs(mixes[toks] - mix_ref)
+    assert (err <= 1e-5 * (np.abs(mix_ref) + 1)).all(), f"mixes: max err {err.max()}"
+    glm_layer_input_check(li[toks], li_ref, ro_ref, pre_ref.astype(np.float64),
+                          glm_pre(mixes[toks], g.scale, g.base, g.hc_eps), g.gamma, g.norm_eps)
+
+
 def test_glm_large_m_sampled():
     """M = 512 (H=6144, tp=8), the auto tokens-per-workgroup choice."""
     g = synth.glm(512)

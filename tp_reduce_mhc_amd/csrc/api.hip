@@ -42,6 +42,7 @@ constexpr int kMaxTp = 64;
 constexpr int kMaxRoutes = 1024;
 constexpr int64_t kDefaultSpin = 1 << 20;
 constexpr int kGlmTileMinM = 256;  // automatic matrix-core tiles from this M
+constexpr int kGlmTwoPassMinM = 1;  // automatic two-pass tiles from this M
 
 // Checks shared by the boundary variants ([DSV41] AllReduceMHC._check and
 // _consumer, _LamportMHCDeviceKernel.__init__).
@@ -173,9 +174,15 @@ int64_t mhcb_mxfp8_scale_bytes(int64_t M, int64_t hidden_size) {
 
 int64_t mhcb_workspace_bytes(int M, int hidden_size, int tp, int two_shot) {
   if (M < 0 || hidden_size < 0 || tp < 1) return -1;
-  if (!two_shot) return kSyncBytes;
-  const int64_t slots = ((int64_t)M + tp - 1) / tp;
-  return kSyncBytes + ((int64_t)tp * tp * slots + M) * hidden_size * 2;
+  // After the sync state: the two-shot owner areas, or the two-pass GLM
+  // partials (never used by the same call, so they share the space).
+  int64_t scratch = kGlmPartBytes;
+  if (two_shot) {
+    const int64_t slots = ((int64_t)M + tp - 1) / tp;
+    const int64_t own = ((int64_t)tp * tp * slots + M) * hidden_size * 2;
+    scratch = own > scratch ? own : scratch;
+  }
+  return kSyncBytes + scratch;
 }
 
 int mhcb_workspace_init(void *workspace, int64_t workspace_bytes, hipStream_t stream) {
@@ -199,7 +206,7 @@ int mhcb_workspace_status(const void *workspace, hipStream_t stream) {
 
 int mhcb_set_token_slices(int slices) {
   const int previous = g_slices_override;
-  g_slices_override = slices < 0 ? 0 : (slices > kMaxSlices ? kMaxSlices : slices);
+  g_slices_override = slices < 0 ? 0 : (slices > kGlmMaxParts ? kGlmMaxParts : slices);
   return previous;
 }
 
@@ -272,6 +279,46 @@ int mhcb_boundary_glm(const uint16_t *partials, int64_t rank_stride, const uint1
       !aligned(mixes_out, 4))
     return fail(MHCB_EALIGN, "%s: partials/hc_fn must be 16-byte aligned, rank_stride %% 8 == 0", fn);
   int G = tokens_per_wg;
+  // Automatic: two-pass tiles whenever the workspace holds their scratch
+  // (measured on MI355X, H=6144, tp=8, us per call, the previous automatic
+  // one-pass choice in brackets: M=1 9.4 (11.6), 16 11.7 (12.2), 64 12.6
+  // (15.0), 128 14.4 (19.3), 256 19.4-20.0 (23.5), 512 31.8-32.0 (34.0),
+  // 1024 56.7-58.0 (70.2)).
+  if (G == 0 && workspace && workspace_bytes >= kSyncBytes + kGlmPartBytes && M >= kGlmTwoPassMinM)
+    G = -kGlmTileTokens;
+  if (G == -kGlmTileTokens) {
+    // Two passes over 16-token tiles: slices of sf fragments (a multiple of
+    // 4, 16..64; 32 by default), partials in the workspace after the sync
+    // state, launches of at most kSyncTokens tokens.
+    const int64_t need = kSyncBytes + kGlmPartBytes;
+    if (!workspace || workspace_bytes < need)
+      return fail(MHCB_EINVAL, "%s: tokens_per_wg=-16 needs a workspace of %lld bytes", fn, (long long)need);
+    const int F = hidden_size / kFrag;
+    // Slices of 16 fragments up to M = 64, 32 beyond (M=64: 12.6 vs 13.2
+    // us; M=128: 14.4 vs 15.1; M=1024: 56.7 vs 60.8).
+    int sf = M <= 64 ? 16 : 32;
+    if (g_slices_override > 0) sf = (F + g_slices_override - 1) / g_slices_override;
+    sf = (sf + 3) / 4 * 4;
+    sf = sf < 16 ? 16 : sf > 64 ? 64 : sf;
+    GlmArgs a = {(F + sf - 1) / sf, sf, SyncView{}, partials, rank_stride, tp, residual, post, comb,
+                 hc_fn, scale, base, norm_weight, residual_out, mixes_out, layer_input, M,
+                 hidden_size, rms_eps, hc_eps, norm_eps, kGlmTileTokens,
+                 reinterpret_cast<float *>(static_cast<char *>(workspace) + kSyncBytes)};
+    const int64_t H = hidden_size;
+    for (int c = 0; c < M; c += kSyncTokens) {
+      GlmArgs b = a;
+      b.M = M - c < kSyncTokens ? M - c : kSyncTokens;
+      b.partials = partials + c * H;
+      b.residual = residual + c * kStreams * H;
+      b.post = post + (int64_t)c * kStreams;
+      b.comb = comb + (int64_t)c * kStreams * kStreams;
+      b.residual_out = residual_out + c * kStreams * H;
+      b.mixes_out = mixes_out + (int64_t)c * kMix;
+      b.layer_input = layer_input + c * H;
+      if ((rc = launched(launch_boundary_glm_two_pass(b, stream), fn))) return rc;
+    }
+    return ok();
+  }
   // Measured on MI355X (H=6144, tp=8): one token per workgroup below M=256
   // (M=128: 18.8 us; 16-token tiles: 22.3), 16-token tiles from M=256
   // (24.8 us; one token: 25.7, two: 28.7) and beyond (M=512: 33.2 us; one
@@ -279,7 +326,7 @@ int mhcb_boundary_glm(const uint16_t *partials, int64_t rank_stride, const uint1
   // beyond M=256.
   if (G == 0) G = workspace && M >= kGlmTileMinM ? kGlmTileTokens : (M <= 256 ? 1 : 2);
   if (G != 1 && G != 2 && G != 4 && G != kGlmTileTokens)
-    return fail(MHCB_EINVAL, "%s: tokens_per_wg=%d (0, 1, 2, 4 or 16)", fn, tokens_per_wg);
+    return fail(MHCB_EINVAL, "%s: tokens_per_wg=%d (0, 1, 2, 4, 16 or -16)", fn, tokens_per_wg);
   if (G == 4 && hidden_size > 6144)
     return fail(MHCB_EUNSUPPORTED, "%s: tokens_per_wg=4 needs hidden_size <= 6144", fn);
   if (G == kGlmTileTokens && !workspace)

@@ -739,6 +739,259 @@ glm_tile_kernel(const GlmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Two-pass tiles: the same 16-token matrix-core GEMV without any
+// cross-workgroup exchange.
+//
+// Pass 1, glm_stream_kernel: workgroup (s, grp) takes tokens grp*16 ..
+// grp*16+15 over the fragments [s * sf, (s + 1) * sf), one (token,
+// fragment) item per thread (16 * sf threads).  It streams the ranks and the
+// residual streams, writes residual_out, and leaves the slice's 24 partial
+// GEMV rows and its sum of squares of the token's streams in the scratch
+// area.  Small workgroups (sf = 16 or 32 fragments) keep several per compute
+// unit, so one workgroup's arithmetic runs while another's loads are in
+// flight.
+//
+// Pass 2, glm_finish_kernel: one workgroup per token, one fragment per
+// thread.  It adds the slices' partials in slice order, writes the raw
+// mixes, derives the pre-mix and takes the collapse and RMSNorm over the
+// residual_out rows the first pass just wrote.
+// ---------------------------------------------------------------------------
+
+constexpr int kStreamMaxThreads = 1024;
+
+struct StreamShared {
+  float post[kTile][kStreams];
+  float comb[kTile][kStreams * kStreams];
+};
+
+// Dynamic LDS of a stream workgroup: the tile's post-mixed streams (as in
+// the exchanging tiles), the per-item sums of squares, then the per-wave
+// GEMV partials [wave][token][row].
+__host__ __device__ inline size_t stream_dyn_bytes(int sf) {
+  return tile_dyn_bytes(sf) + (size_t)(sf / 4) * kTile * kMix * 4;
+}
+
+template <int TP>
+__global__ void __launch_bounds__(kStreamMaxThreads)
+glm_stream_kernel(const GlmArgs a) {
+  __shared__ StreamShared sh;
+  extern __shared__ __align__(16) char dyn[];
+  const int H = a.H, F = H / kFrag, tid = threadIdx.x, nt = blockDim.x;
+  const int lane = tid & (kWave - 1), wave = tid / kWave, waves = nt / kWave;
+  const int s = blockIdx.x, t0 = blockIdx.y * kTile, S = a.slices;
+  const int sf = a.slice_frags, first = s * sf, last = min(F, first + sf);
+  const int valid = min(kTile, a.M - t0);
+  const int tp = TP > 0 ? TP : a.tp;
+  const int rw = tile_row_words(sf);
+  u32x4 *ys = reinterpret_cast<u32x4 *>(dyn);
+  double *item = reinterpret_cast<double *>(dyn + tile_ys_bytes(sf));
+  float *wpart = reinterpret_cast<float *>(dyn + tile_dyn_bytes(sf));  // [wave][tok][row]
+  const int mi = lane & (kTile - 1), mq = lane >> 4;  // MFMA row, K chunk
+
+  // The tile's post and comb (20 floats a token; at least 256 threads).
+  constexpr int kMixVals = kTile * 20;
+  float mv[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int e = tid + u * nt, tok = e / 20, k = e % 20, tt = t0 + tok;
+    mv[u] = e < kMixVals && tok < valid
+                ? (k < kStreams ? a.post[(int64_t)tt * kStreams + k] : a.comb[(int64_t)tt * 16 + (k - kStreams)])
+                : 0.0f;
+  }
+  // This wave's hc_fn chunk (fragments first + 4*wave .. +3; sf / 4 waves,
+  // one chunk each), first in the queue: it is needed only after the
+  // streams.  (Loading it after the streams halves the registers, to 68,
+  // but measured no faster.)
+  FnChunk fc;
+  load_fn_chunk(a, mi, first + 4 * wave + mq, first + 4 * wave + mq < last, fc);
+
+  // The thread's item: token tid / sf, fragment first + tid % sf.
+  const int tok = tid / sf, fl = tid % sf, f = first + fl;
+  const bool live = tok < valid && f < last;
+  const int64_t col = live ? (int64_t)f * kFrag : 0;
+  const int64_t t = t0 + (live ? tok : 0);
+  u32x4 res[kStreams], part[TP > 0 ? TP : 1];
+#pragma unroll
+  for (int r = 0; r < kStreams; ++r)
+    res[r] = live ? load_stream(a.residual + (t * kStreams + r) * H + col) : u32x4{0, 0, 0, 0};
+  if constexpr (TP > 0) {
+#pragma unroll
+    for (int r = 0; r < TP; ++r)
+      part[r] = live ? load_stream(a.partials + r * a.rank_stride + t * H + col) : u32x4{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int e = tid + u * nt, tk = e / 20, k = e % 20;
+    if (e < kMixVals) {
+      if (k < kStreams) sh.post[tk][k] = mv[u];
+      else sh.comb[tk][k - kStreams] = mv[u];
+    }
+  }
+  __syncthreads();
+
+  // a1 + a2: rank sum, post-mix, residual_out; y to LDS.
+  float sum[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) sum[e] = 0.0f;
+  if constexpr (TP > 0) {
+#pragma unroll
+    for (int r = 0; r < TP; ++r) {
+      float v[8];
+      unpack8(part[r], v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sum[e] = sum[e] + v[e];
+    }
+  } else {
+    const uint16_t *src = a.partials + t * H + col;
+    for (int r0 = 0; r0 < tp; r0 += 8) {
+      u32x4 w[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        w[r] = live && r0 + r < tp ? load_stream(src + (r0 + r) * a.rank_stride) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        if (r0 + r >= tp) break;
+        float v[8];
+        unpack8(w[r], v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sum[e] = sum[e] + v[e];
+      }
+    }
+  }
+  float x[8];
+  unpack8(pack8(sum), x);
+  float r4[kStreams][8];
+#pragma unroll
+  for (int r = 0; r < kStreams; ++r) unpack8(res[r], r4[r]);
+  const int tk = live ? tok : 0;
+  double ysq = 0.0;
+#pragma unroll
+  for (int j = 0; j < kStreams; ++j) {
+    const float pj = sh.post[tk][j];
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float v = x[e] * pj;
+#pragma unroll
+      for (int r = 0; r < kStreams; ++r) v = __builtin_fmaf(r4[r][e], sh.comb[tk][r * kStreams + j], v);
+      acc[e] = v;
+    }
+    const u32x4 yj = live ? pack8(acc) : u32x4{0, 0, 0, 0};
+    if (live) {
+      // A plain store: the finish pass reads these rows back.
+      *reinterpret_cast<u32x4 *>(a.residual_out + (t * kStreams + j) * H + col) = yj;
+      ysq += (double)dot8(yj, yj, 0.0f);  // FP32 within the fragment
+    }
+    ys[tok * rw + j * sf + fl] = yj;
+  }
+  item[tid] = ysq;  // [tok][fl]
+  __syncthreads();
+
+  // a3 (partial): this wave's 4-fragment chunk of the 16 x 24 GEMV.
+  {
+    f32x4 c1 = {0.0f, 0.0f, 0.0f, 0.0f}, c2 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < kStreams; ++j) {
+      const u32x4 av = ys[mi * rw + j * sf + 4 * wave + mq];
+      c1 = mfma_bf16(av, fc.b1[j], c1);
+      c2 = mfma_bf16(av, fc.b2[j], c2);
+    }
+    // Lane l holds rows l % 16 and 16 + l % 16 of tokens 4*(l/16) .. +3.
+    float *wp = wpart + wave * kTile * kMix;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      wp[(4 * mq + e) * kMix + mi] = c1[e];
+      if (mi < kMix - kTile) wp[(4 * mq + e) * kMix + kTile + mi] = c2[e];
+    }
+  }
+  __syncthreads();
+  // The slice's partials: rows summed over the waves in order, the sum of
+  // squares over the fragments in order.
+  for (int e = tid; e < valid * kMix; e += nt) {
+    const int tkn = e / kMix, k = e % kMix;
+    float v = 0.0f;
+    for (int w = 0; w < waves; ++w) v += wpart[(w * kTile + tkn) * kMix + k];
+    a.parts[((int64_t)(t0 + tkn) * S + s) * kPartWords + k] = v;
+  }
+  if (tid < valid) {
+    double v = 0.0;
+    for (int q = 0; q < sf; ++q) v += item[tid * sf + q];
+    *reinterpret_cast<double *>(a.parts + ((int64_t)(t0 + tid) * S + s) * kPartWords + kPartSum) = v;
+  }
+}
+
+__global__ void __launch_bounds__(kMaxThreads)
+glm_finish_kernel(const GlmArgs a) {
+  __shared__ u32x4 staged[kGlmMaxParts * kPartWords / 4];  // the token's partials
+  __shared__ float mix[kMix];
+  __shared__ float pre[kStreams];
+  __shared__ double tot;
+  __shared__ double red[kMaxThreads / kWave];
+  const int H = a.H, F = H / kFrag, tid = threadIdx.x, S = a.slices;
+  const int64_t t = blockIdx.x;
+  const bool valid = tid < F;
+  const int64_t col = valid ? (int64_t)tid * kFrag : 0;
+  // The token's S x 128-byte partials, one 16-byte load per thread, issued
+  // with the residual_out rows.
+  const u32x4 *pt = reinterpret_cast<const u32x4 *>(a.parts + t * S * kPartWords);
+  for (int i = tid; i < S * (kPartWords / 4); i += blockDim.x) staged[i] = pt[i];
+  u32x4 y[kStreams];
+#pragma unroll
+  for (int j = 0; j < kStreams; ++j)
+    y[j] = valid ? load_cached(a.residual_out + (t * kStreams + j) * H + col) : u32x4{0, 0, 0, 0};
+  const u32x4 gam = valid ? load_cached(a.gamma + col) : u32x4{0, 0, 0, 0};
+  __syncthreads();
+  // Slice order: rows by threads 0..23, the binary64 sum by thread 24.
+  const float *sp = reinterpret_cast<const float *>(staged);
+  if (tid < kMix) {
+    float v = 0.0f;
+    for (int q = 0; q < S; ++q) v += sp[q * kPartWords + tid];
+    mix[tid] = v;
+  } else if (tid == kMix) {
+    double v = 0.0;
+    for (int q = 0; q < S; ++q) v += *reinterpret_cast<const double *>(sp + q * kPartWords + kPartSum);
+    tot = v;
+  }
+  __syncthreads();
+  // rstd over 4H; raw mixes out; pre_j = sigmoid(mix_j * scale0 + base_j) + hc_eps.
+  if (tid < kMix) {
+    const float rstd = (float)(1.0 / __builtin_sqrt((double)(float)tot / (4.0 * H) + (double)a.rms_eps));
+    const float m = mix[tid] * rstd;
+    a.mixes_out[t * kMix + tid] = m;
+    if (tid < kStreams) pre[tid] = sigmoid(__builtin_fmaf(m, a.scale[0], a.base[tid])) + a.hc_eps;
+  }
+  __syncthreads();
+  // a4: p = bf16((q0+q1)+(q2+q3)), q_j = y_j * pre_j; RMSNorm over H.
+  float qv[kStreams][8];
+#pragma unroll
+  for (int j = 0; j < kStreams; ++j) {
+    float yv[8];
+    unpack8(y[j], yv);
+    const float pj = pre[j];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qv[j][e] = yv[e] * pj;
+  }
+  float z[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) z[e] = (qv[0][e] + qv[1][e]) + (qv[2][e] + qv[3][e]);
+  const u32x4 p = pack8(z);
+  double pss[1] = {0.0};
+  float pv[8];
+  unpack8(p, pv);
+  if (valid) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pss[0] += (double)pv[e] * (double)pv[e];
+  }
+  block_sum<double, 1>(pss, red);
+  const float inv = (float)(1.0 / __builtin_sqrt((double)(float)pss[0] / (double)H + (double)a.norm_eps));
+  float g[8], o[8];
+  unpack8(gam, g);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = (pv[e] * inv) * g[e];
+  if (valid) store_stream(a.layer_input + t * H + col, pack8(o));
+}
+
+// ---------------------------------------------------------------------------
 // Side-stream mixes: one thread per token.
 // ---------------------------------------------------------------------------
 
@@ -850,6 +1103,38 @@ hipError_t launch_boundary_glm_tile(const GlmArgs &a, hipStream_t stream) {
   }
 #undef MHCB_TILE
 #undef MHCB_TILE_LAUNCH
+  return hipGetLastError();
+}
+
+// Two passes: 16 * sf threads per stream workgroup (sf a multiple of 4,
+// 16..64), then one workgroup per token.
+hipError_t launch_boundary_glm_two_pass(const GlmArgs &a, hipStream_t stream) {
+  const int sf = a.slice_frags, F = a.H / kFrag;
+  if (sf % 4 || sf < 16 || kTile * sf > kStreamMaxThreads || a.slices > kGlmMaxParts ||
+      (int64_t)a.slices * sf < F || a.H > kFrag * kMaxThreads)
+    return hipErrorInvalidValue;
+  const dim3 grid(a.slices, (a.M + kTile - 1) / kTile), block(kTile * sf);
+  const size_t lds = stream_dyn_bytes(sf);
+#define MHCB_STREAM_LAUNCH(TPP)                                                              \
+  if (lds > 65536) {                                                                         \
+    const hipError_t e = hipFuncSetAttribute((const void *)glm_stream_kernel<TPP>,            \
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,      \
+                                             (int)lds);                                      \
+    if (e != hipSuccess) return e;                                                           \
+  }                                                                                          \
+  hipLaunchKernelGGL((glm_stream_kernel<TPP>), grid, block, lds, stream, a);
+  if (a.tp == 8) {
+    MHCB_STREAM_LAUNCH(8)
+  } else if (a.tp == 4) {
+    MHCB_STREAM_LAUNCH(4)
+  } else {
+    MHCB_STREAM_LAUNCH(0)
+  }
+#undef MHCB_STREAM_LAUNCH
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int threads = (F + kWave - 1) / kWave * kWave;
+  hipLaunchKernelGGL(glm_finish_kernel, dim3(a.M), dim3(threads), 0, stream, a);
   return hipGetLastError();
 }
 

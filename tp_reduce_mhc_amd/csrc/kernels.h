@@ -60,6 +60,15 @@ static_assert(kCopySum2 == kCopySum1 + 8 * kMaxSlices && kCopyRows == kCopySum2 
 static_assert(kCopyBytes % 128 == 0 && kSlotCopy0 + 2 * kCopyBytes <= kSyncSlot, "slot layout");
 constexpr int64_t kSyncBytes = 256 + (int64_t)kSyncSlot * kSyncTokens;
 
+// Two-pass GLM tiles keep their per-(token, slice) partials after the sync
+// state (workspace + kSyncBytes): [tokens][slices][kPartWords] FP32 words,
+// the 24 GEMV rows, then the binary64 sum of squares at word 24.  The area
+// is plain scratch: the first pass writes every word the second pass reads.
+constexpr int kPartWords = 32;
+constexpr int kPartSum = 24;        // word offset of the binary64 sum
+constexpr int kGlmMaxParts = 64;    // slices of at least 16 fragments, H <= 8192
+constexpr int64_t kGlmPartBytes = (int64_t)kSyncTokens * kGlmMaxParts * kPartWords * 4;  // 8 MiB
+
 struct SyncView {
   uint32_t *status;   // cross-workgroup waits that gave up
   char *slots;        // [kSyncTokens][kSyncSlot]
@@ -125,6 +134,7 @@ struct GlmArgs {
   int M, H;
   float rms_eps, hc_eps, norm_eps;
   int tokens_per_wg;         // 1, 2 or 4
+  float *parts;              // two-pass tiles: [M][slices][kPartWords] partials
 };
 
 hipError_t launch_boundary_glm(const GlmArgs &a, hipStream_t stream);
@@ -132,6 +142,9 @@ hipError_t launch_boundary_glm(const GlmArgs &a, hipStream_t stream);
 // sync view), at most kSyncTokens tokens per launch.
 constexpr int kGlmTileTokens = 16;
 hipError_t launch_boundary_glm_tile(const GlmArgs &a, hipStream_t stream);
+// The same tiles in two passes (stream, then finish), exchanging nothing:
+// a.slices x a.slice_frags cover the hidden size, a.parts is the scratch.
+hipError_t launch_boundary_glm_two_pass(const GlmArgs &a, hipStream_t stream);
 
 hipError_t launch_mixes(const float *mixes, const float *scale, const float *base, float *post_out,
                         float *comb_out, int M, float hc_eps, float post_mult, int repeat,
