@@ -292,6 +292,65 @@ def bench_glm(torch, mhc, g, steps, warmup, tokens_per_wg=0):
     return ms, per_set
 
 
+def bytes_mixes(M):
+    """Side mixes: raw mixes in (96 B), post' and comb' out (16 + 64 B) per
+    token, scale and base once."""
+    return M * (96 + 16 + 64) + 27 * 4
+
+
+def bench_mixes(torch, mhc, M, steps, warmup):
+    import synth
+    raw, scale, base = synth.raw_mixes(M)
+    per_set = bytes_mixes(M)
+    sets = make_sets(torch, {"raw": dev(torch, raw)}, rotations(per_set, minimum=8))
+    scale, base = dev(torch, scale), dev(torch, base)
+    for s in sets:
+        s["post"] = torch.empty((M, 4, 1), dtype=torch.float32, device="cuda")
+        s["comb"] = torch.empty((M, 4, 4), dtype=torch.float32, device="cuda")
+
+    def call(i):
+        s = sets[i % len(sets)]
+        mhc.mhcb_mixes(s["raw"], scale, base, s["post"], s["comb"], M, 4, 1e-6, 2.0, 20)
+
+    return Timed(torch, call, steps, warmup).run(), per_set
+
+
+def bench_glm_with_side_mixes(torch, mhc, g, steps, warmup):
+    """The GLM boundary on the launching stream and the side mixes on a
+    second stream, each call joining the previous call's mixes first (the
+    GLM page's __call__ / join), all captured in one graph."""
+    per_set = bytes_glm(g.M, g.H, g.tp) + bytes_mixes(g.M) - g.M * 96 - 27 * 4
+    t = dict(partials=dev(torch, g.partials), residual=dev(torch, g.residual),
+             post=dev(torch, g.post), comb=dev(torch, g.comb))
+    sets = make_sets(torch, t, rotations(per_set))
+    fn, scale, base, gamma = (dev(torch, g.fn), dev(torch, g.scale), dev(torch, g.base),
+                              dev(torch, g.gamma))
+    for s in sets:
+        s["residual_out"] = torch.empty((g.M, 4, g.H), dtype=torch.bfloat16, device="cuda")
+        s["layer_input"] = torch.empty((g.M, g.H), dtype=torch.bfloat16, device="cuda")
+        s["mixes"] = torch.empty((g.M, 24), dtype=torch.float32, device="cuda")
+        s["post_next"] = torch.empty((g.M, 4, 1), dtype=torch.float32, device="cuda")
+        s["comb_next"] = torch.empty((g.M, 4, 4), dtype=torch.float32, device="cuda")
+    ws = mhc.workspace(torch.device("cuda", torch.cuda.current_device()))
+    side = torch.cuda.Stream()
+
+    def call(i):
+        s = sets[i % len(sets)]
+        cur = torch.cuda.current_stream()
+        cur.wait_stream(side)  # join the previous call's mixes
+        mhc.mhcb_boundary_glm(s["partials"], g.M * g.H, s["residual"], s["post"], s["comb"], fn,
+                              scale, base, gamma, s["residual_out"], s["mixes"], s["layer_input"],
+                              ws, ws.numel(), g.M, g.H, 4, g.tp, g.rms_eps, g.hc_eps, g.norm_eps, 0)
+        side.wait_stream(cur)
+        with torch.cuda.stream(side):
+            mhc.mhcb_mixes(s["mixes"], scale, base, s["post_next"], s["comb_next"], g.M, 4,
+                           g.hc_eps, g.post_mult, g.sinkhorn_repeat)
+        if i == steps - 1:
+            cur.wait_stream(side)  # the last call's mixes rejoin before the capture ends
+
+    return Timed(torch, call, steps, warmup).run(), per_set
+
+
 def copy_bandwidth(torch, nbytes=1 << 30, reps=20):
     """Achieved GB/s (read + write bytes) of a plain device-to-device copy
     of `nbytes`: the practical HBM ceiling next to the 8 TB/s peak."""
@@ -453,6 +512,15 @@ def main():
                     ms, nbytes = bench_glm(torch, mhc, g, min(K, 100), min(W, 5), G)
                     extra[name] = entry(ms, nbytes, M)
                     log(f"glm M=64 tokens_per_wg={G}: {extra[name]}")
+    if want("glm") and not args.quick:
+        for M in (64, 512):  # a5: the side-stream mixes, alone and beside the boundary
+            ms, nbytes = bench_mixes(torch, mhc, M, min(K, 100), min(W, 5))
+            extra[f"glm_side_mixes_M{M}"] = entry(ms, nbytes, M)
+            log(f"side mixes M={M}: {extra[f'glm_side_mixes_M{M}']}")
+            g = synth.glm(M)
+            ms, nbytes = bench_glm_with_side_mixes(torch, mhc, g, min(K, 100), min(W, 5))
+            extra[f"glm_M{M}_with_side_mixes"] = entry(ms, nbytes, M)
+            log(f"glm M={M} + side mixes on a second stream: {extra[f'glm_M{M}_with_side_mixes']}")
     if (want("mxfp8") or want("mailbox")) and not args.quick:
         b = synth.large_m_delayed(8192)
         if want("mxfp8"):

@@ -597,17 +597,21 @@ def test_glm_large_m_sampled():
                           glm_pre(mixes[toks], g.scale, g.base, g.hc_eps), g.gamma, g.norm_eps)
 
 
-@pytest.mark.parametrize("M", [1, 64, 513])
-def test_side_mixes_match_oracle(M):
+@pytest.mark.parametrize("M,spread", [(1, 1.0), (64, 1.0), (513, 1.0), (256, 4.0)])
+def test_side_mixes_match_oracle(M, spread):
+    """The side kernel uses FP32 hardware reciprocals and FP32 exp; spread
+    widens the raw mixes (and so the Sinkhorn logits) to stress them."""
     raw, scale, base = synth.raw_mixes(M)
+    raw = (raw * np.float32(spread)).astype(np.float32)
     post, comb = mhc.mixes(dev(raw), dev(scale), dev(base), 1e-6, 2.0, 20)
     torch.cuda.synchronize()
     p_ref, c_ref = oracle.side_mixes(raw, scale, base, 1e-6, 2.0, 20)
     post, comb = host(post).reshape(M, 4), host(comb)
     assert (np.abs(post - p_ref) <= 1e-5 * np.abs(p_ref) + 1e-7).all()
     assert (np.abs(comb - c_ref) <= 1e-5 * np.abs(c_ref) + 1e-7).all()
-    print(f"[gpu] side mixes M={M}: bit-exact post {np.array_equal(post, p_ref)}, "
-          f"comb {np.array_equal(comb, c_ref)}", flush=True)
+    rel = np.abs(comb - c_ref) / np.maximum(np.abs(c_ref), 1e-30)
+    print(f"[gpu] side mixes M={M} spread {spread}: bit-exact post {np.array_equal(post, p_ref)}, "
+          f"comb {np.array_equal(comb, c_ref)}, max comb rel err {rel.max():.2e}", flush=True)
 
 
 def test_glm_boundary_object_side_stream_and_join():

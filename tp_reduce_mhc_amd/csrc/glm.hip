@@ -992,57 +992,57 @@ glm_finish_kernel(const GlmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Side-stream mixes: one thread per token.
+// Side-stream mixes: sixteen lanes per token.
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ float rcp(float x) { return (float)(1.0 / (double)x); }
-__device__ __forceinline__ float expf_rounded(float x) { return (float)exp((double)x); }
+// The pages' side kernel is compiled with fast math; here the reciprocal is
+// the hardware's (v_rcp_f32, within 1 ulp) and exp the FP32 library one
+// (within 1 ulp).  Twenty Sinkhorn rounds of binary64 divisions in one
+// thread per token took about 7 us; errors of a few ulps stay far inside
+// the side kernel's 1e-5 relative tolerance.
+__device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float exp_fast(float x) { return expf(x); }
+__device__ __forceinline__ float sigmoid_fast(float x) { return 1.0f / (1.0f + expf(-x)); }
 
-__global__ void __launch_bounds__(64)
+// Sixteen lanes per token, lane e holding entry (e / 4, e % 4) of the 4x4
+// residual mix (source row, target column).  A row's sum is two xor
+// exchanges within its four lanes, a column's two exchanges at strides 4
+// and 8; every lane of a row (column) then holds ((a + b) + (c + d)) in the
+// page's pairing, the same bits on every lane because each addition is
+// commutative.
+constexpr int kMixLanes = 16;
+constexpr int kMixThreads = 256;
+
+__global__ void __launch_bounds__(kMixThreads)
 mixes_kernel(const float *mixes, const float *scale, const float *base, float *post_out,
              float *comb_out, int M, float eps, float post_mult, int repeat) {
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= M) return;
-  const float *row = mixes + (int64_t)t * kMix;
-  const float s1 = scale[1], s2 = scale[2];
-#pragma unroll
-  for (int j = 0; j < kStreams; ++j)
-    post_out[(int64_t)t * kStreams + j] =
-        sigmoid(__builtin_fmaf(row[kStreams + j], s1, base[kStreams + j])) * post_mult;
+  const int gid = blockIdx.x * blockDim.x + threadIdx.x;
+  const int t = gid / kMixLanes, e = gid % kMixLanes;
+  const bool live = t < M;                   // every lane takes part in the exchanges
+  const float *row = mixes + (int64_t)(live ? t : M - 1) * kMix;
+  if (live && e < kStreams)
+    post_out[(int64_t)t * kStreams + e] =
+        sigmoid_fast(__builtin_fmaf(row[kStreams + e], scale[1], base[kStreams + e])) * post_mult;
 
-  // Sinkhorn on the 4x4 residual mix, row-major (source rows).
-  float c[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) c[i] = __builtin_fmaf(row[8 + i], s2, base[8 + i]);
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    float *q = c + 4 * r;
-    const float peak = __builtin_fmaxf(__builtin_fmaxf(q[0], q[1]), __builtin_fmaxf(q[2], q[3]));
-#pragma unroll
-    for (int k = 0; k < 4; ++k) q[k] = expf_rounded(q[k] - peak);
-    const float inv = rcp((q[0] + q[1]) + (q[2] + q[3]));
-#pragma unroll
-    for (int k = 0; k < 4; ++k) q[k] = __builtin_fmaf(q[k], inv, eps);
-  }
+  // Sinkhorn on the 4x4 residual mix.
+  float c = __builtin_fmaf(row[8 + e], scale[2], base[8 + e]);
+  float peak = __builtin_fmaxf(c, __shfl_xor(c, 1, kWave));
+  peak = __builtin_fmaxf(peak, __shfl_xor(peak, 2, kWave));
+  c = exp_fast(c - peak);
+  float sum = c + __shfl_xor(c, 1, kWave);
+  sum = sum + __shfl_xor(sum, 2, kWave);
+  c = __builtin_fmaf(c, rcp(sum), eps);
   for (int it = 0; it < repeat; ++it) {
     if (it > 0) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float *q = c + 4 * r;
-        const float inv = rcp(((q[0] + q[1]) + (q[2] + q[3])) + eps);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) q[k] = q[k] * inv;
-      }
+      sum = c + __shfl_xor(c, 1, kWave);
+      sum = sum + __shfl_xor(sum, 2, kWave);
+      c = c * rcp(sum + eps);
     }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float inv = rcp(((c[k] + c[4 + k]) + (c[8 + k] + c[12 + k])) + eps);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) c[4 * r + k] = c[4 * r + k] * inv;
-    }
+    sum = c + __shfl_xor(c, 4, kWave);
+    sum = sum + __shfl_xor(sum, 8, kWave);
+    c = c * rcp(sum + eps);
   }
-#pragma unroll
-  for (int i = 0; i < 16; ++i) comb_out[(int64_t)t * 16 + i] = c[i];
+  if (live) comb_out[(int64_t)t * 16 + e] = c;
 }
 
 }  // namespace
@@ -1141,8 +1141,10 @@ hipError_t launch_boundary_glm_two_pass(const GlmArgs &a, hipStream_t stream) {
 hipError_t launch_mixes(const float *mixes, const float *scale, const float *base, float *post_out,
                         float *comb_out, int M, float hc_eps, float post_mult, int repeat,
                         hipStream_t stream) {
-  hipLaunchKernelGGL(mixes_kernel, dim3((M + 63) / 64), dim3(64), 0, stream, mixes, scale, base,
-                     post_out, comb_out, M, hc_eps, post_mult, repeat);
+  const int64_t threads = (int64_t)M * kMixLanes;
+  hipLaunchKernelGGL(mixes_kernel, dim3((unsigned)((threads + kMixThreads - 1) / kMixThreads)),
+                     dim3(kMixThreads), 0, stream, mixes, scale, base, post_out, comb_out, M,
+                     hc_eps, post_mult, repeat);
   return hipGetLastError();
 }
 
