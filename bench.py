@@ -267,6 +267,43 @@ def bench_finalize(torch, mhc, f, steps, warmup, two_shot=False, bf16_weights=Fa
     return ms, per_set + extra
 
 
+def bytes_glm_moe(M, H, tp, top_k):
+    """GLM boundary of an MoE sublayer: the ranks' expert rows and shared
+    rows, routes (FP32 weight + int32 index), residual, post/comb in, the
+    streams, raw mixes and layer input out, hc_fn and gamma once."""
+    return (M * (tp * (top_k + 1) * 2 * H + top_k * 8 + 9 * 2 * H + 80 + 96)
+            + 24 * 4 * H * 2 + 2 * H + 27 * 4)
+
+
+def bench_glm_moe(torch, mhc, M, H, tp, top_k, steps, warmup):
+    import synth
+    f = synth.moe_finalize(M, H=H, tp=tp, top_k=top_k)
+    g = synth.glm(M, H=H, tp=tp)
+    per_set = bytes_glm_moe(M, H, tp, top_k)
+    t = dict(gemm2=dev(torch, f.gemm2), weights=dev(torch, f.weights), idx=dev(torch, f.idx),
+             shared=dev(torch, f.shared), residual=dev(torch, g.residual), post=dev(torch, g.post),
+             comb=dev(torch, g.comb))
+    sets = make_sets(torch, t, rotations(per_set, minimum=2))
+    fn, scale, base, gamma = (dev(torch, g.fn), dev(torch, g.scale), dev(torch, g.base),
+                              dev(torch, g.gamma))
+    rows = f.gemm2.shape[1]
+    need = mhc.mhcb_finalize_glm_workspace_bytes(M, H, tp)
+    ws = mhc.new_workspace(need, "cuda")
+    for s in sets:
+        s["residual_out"] = torch.empty((M, 4, H), dtype=torch.bfloat16, device="cuda")
+        s["layer_input"] = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+        s["mixes"] = torch.empty((M, 24), dtype=torch.float32, device="cuda")
+
+    def call(i):
+        s = sets[i % len(sets)]
+        mhc.mhcb_finalize_glm(s["gemm2"], rows * H, rows, s["weights"], 0, 0, 1.0, s["idx"], 0,
+                              s["shared"], M * H, s["residual"], s["post"], s["comb"], fn, scale,
+                              base, gamma, s["residual_out"], s["mixes"], s["layer_input"], ws,
+                              need, M, H, 4, tp, top_k, g.rms_eps, g.hc_eps, g.norm_eps)
+
+    return Timed(torch, call, steps, warmup).run(), per_set
+
+
 def bench_glm(torch, mhc, g, steps, warmup, tokens_per_wg=0):
     per_set = bytes_glm(g.M, g.H, g.tp)
     t = dict(partials=dev(torch, g.partials), residual=dev(torch, g.residual),
@@ -521,6 +558,11 @@ def main():
             ms, nbytes = bench_glm_with_side_mixes(torch, mhc, g, min(K, 100), min(W, 5))
             extra[f"glm_M{M}_with_side_mixes"] = entry(ms, nbytes, M)
             log(f"glm M={M} + side mixes on a second stream: {extra[f'glm_M{M}_with_side_mixes']}")
+    if want("glm") and not args.quick:
+        for M in (64, 512):  # the GLM boundary of an MoE sublayer, H=6144 tp=4 top_k=8
+            ms, nbytes = bench_glm_moe(torch, mhc, M, 6144, 4, 8, min(K, 100), min(W, 5))
+            extra[f"glm_moe_tp4_k8_M{M}"] = entry(ms, nbytes, M)
+            log(f"glm moe M={M}: {extra[f'glm_moe_tp4_k8_M{M}']}")
     if (want("mxfp8") or want("mailbox")) and not args.quick:
         b = synth.large_m_delayed(8192)
         if want("mxfp8"):

@@ -235,6 +235,31 @@ int mhcb_finalize_ex(const uint16_t *gemm2_permuted, int64_t gemm2_rank_stride, 
                      int M, int hidden_size, int hc_mult, int tp, int top_k, float norm_eps,
                      hipStream_t stream);
 
+/* GLM boundary of an MoE sublayer ([GLM] AllReduceMhcBoundary.__call__ with
+ * an MoE output: the finalize publish of _QuadFinalizePublishDeviceKernel,
+ * then the GLM boundary on the published contributions).  Every rank's
+ * contribution
+ *   c_r[t] = sanitize(bf16(sum_{k asc, row valid} w[t][k] * gemm2_r[row] + shared_r[t]))
+ * (routing as in mhcb_finalize_ex: FP32 or BF16 weights times the routed
+ * scaling factor, rows outside [0, rows) skipped) is written rank-major into
+ * the workspace, and mhcb_boundary_glm's arithmetic then runs on them as
+ * its tp partials (two-pass tiles): residual_out, mixes_out [M, 24] and
+ * layer_input as there.  The workspace is required, of at least
+ * mhcb_finalize_glm_workspace_bytes(M, hidden_size, tp) bytes (the sync
+ * state, the two-pass scratch, then tp * M * hidden BF16 contributions).
+ * hc_mult = 4, hidden <= 8192. */
+int64_t mhcb_finalize_glm_workspace_bytes(int M, int hidden_size, int tp);
+int mhcb_finalize_glm(const uint16_t *gemm2_permuted, int64_t gemm2_rank_stride, int64_t rows,
+                      const void *expert_weights, int64_t weights_rank_stride, int weights_bf16,
+                      float routed_scaling_factor, const int32_t *permuted_idx,
+                      int64_t idx_rank_stride, const uint16_t *shared_output,
+                      int64_t shared_rank_stride, const uint16_t *residual, const float *post,
+                      const float *comb, const uint16_t *hc_fn, const float *scale,
+                      const float *base, const uint16_t *norm_weight, uint16_t *residual_out,
+                      float *mixes_out, uint16_t *layer_input, void *workspace,
+                      int64_t workspace_bytes, int M, int hidden_size, int hc_mult, int tp,
+                      int top_k, float rms_eps, float hc_eps, float norm_eps, hipStream_t stream);
+
 /* Standalone MXFP8 of a BF16 [M, hidden] array: the encoding of the
  * boundary's epilogue ([DSV41] _LamportMHCDeviceKernel, quantize): per 32
  * columns e = the smallest UE8M0 exponent with 2^(e-127) >= amax * fl(1/448),

@@ -146,6 +146,23 @@ def test_glm_mixes_finalize_quant_validation():
                      (dict(two_shot=1, workspace=FAKE, workspace_bytes=1 << 10), "workspace_bytes")):
         with pytest.raises(mhc.MhcbError, match=text):
             mhc.mhcb_finalize(**{**fin, **kw})
+    fglm = dict(gemm2_permuted=FAKE, gemm2_rank_stride=32 * 512, rows=32, expert_weights=FAKE,
+                weights_rank_stride=0, weights_bf16=0, routed_scaling_factor=1.0,
+                permuted_idx=FAKE, idx_rank_stride=0, shared_output=FAKE,
+                shared_rank_stride=4 * 512, residual=FAKE, post=FAKE, comb=FAKE, hc_fn=FAKE,
+                scale=FAKE, base=FAKE, norm_weight=FAKE, residual_out=FAKE, mixes_out=FAKE,
+                layer_input=FAKE, workspace=FAKE, workspace_bytes=1 << 30, M=4, hidden_size=512,
+                hc_mult=4, tp=2, top_k=8, rms_eps=1e-6, hc_eps=1e-6, norm_eps=1e-6, stream=0)
+    need = mhc.mhcb_finalize_glm_workspace_bytes(4, 512, 2)
+    assert need == mhc.mhcb_workspace_bytes(4, 512, 2, 0) + 2 * 4 * 512 * 2
+    for kw, text in ((dict(workspace=None), "workspace"), (dict(workspace_bytes=need - 1), "workspace_bytes"),
+                     (dict(workspace=FAKE + 64), "256-byte"), (dict(top_k=0), "top_k"),
+                     (dict(hc_mult=8), "only 4"), (dict(hc_fn=None), "required"),
+                     (dict(hidden_size=8200, shared_rank_stride=4 * 8200), "exceeds"),
+                     (dict(weights_bf16=2), "weights_bf16"),
+                     (dict(routed_scaling_factor=float("nan")), "finite")):
+        with pytest.raises(mhc.MhcbError, match=text):
+            mhc.mhcb_finalize_glm(**{**fglm, **kw})
     fin_ex = {**fin, "weights_bf16": 1, "routed_scaling_factor": 2.5}
     for kw, text in ((dict(weights_bf16=2), "weights_bf16"),
                      (dict(routed_scaling_factor=float("inf")), "finite"),

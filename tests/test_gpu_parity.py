@@ -887,3 +887,74 @@ def test_finalize_random_shapes(case):
         ro, li, _ = run_finalize(f, two_shot=two_shot, split=split)
         assert_bits_equal(ro, ro_ref, f"residual_out two_shot={two_shot} split={split}")
         assert_within_ulp(li, li_ref, 1, f"layer_input two_shot={two_shot} split={split}")
+
+
+# ---------------------------------------------------------------------------
+# GLM boundary of an MoE sublayer
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("case", [(16, 2048, 4, 8, True, 0.0, False, 1.0),
+                                  (37, 6144, 8, 8, False, 0.125, True, 2.5),
+                                  (3, 512, 2, 1, True, 0.0, False, 1.0),
+                                  (130, 1024, 4, 16, False, 0.3, False, 0.7),
+                                  (64, 6144, 4, 8, True, 0.0, True, 1.0)],
+                         ids=lambda c: f"M{c[0]}-H{c[1]}-tp{c[2]}-k{c[3]}-bf16w{int(c[6])}")
+def test_glm_moe_matches_oracle(case):
+    """mhcb_finalize_glm: the published contributions are bit-equal to the
+    oracle's, residual_out bit-exact, raw mixes within 1e-5 relative and the
+    layer input within the GLM band; replicated and per-rank routing with
+    dropped routes, FP32 and BF16 weights, routed scaling factors."""
+    M, H, tp, k, replicated, drop, bf16w, rsf = case
+    f = synth.moe_finalize(M, H=H, tp=tp, top_k=k, replicated_routing=replicated,
+                           drop_fraction=drop)
+    g = synth.glm(M, H=H, tp=tp)
+    w = synth.to_bf16_bits(f.weights) if bf16w else f.weights
+    print(f"[gpu] glm moe M={M} H={H} tp={tp} top_k={k} replicated={replicated} bf16w={bf16w}",
+          flush=True)
+    ro = torch.full((M, 4, H), float("nan"), dtype=torch.bfloat16, device="cuda")
+    mixes = torch.full((M, 24), float("nan"), dtype=torch.float32, device="cuda")
+    li = torch.full((M, H), float("nan"), dtype=torch.bfloat16, device="cuda")
+    need = mhc.mhcb_finalize_glm_workspace_bytes(M, H, tp)
+    ws = mhc.new_workspace(need, "cuda")
+    rows = f.gemm2.shape[1]
+    per_rank = 0 if replicated else M * k
+    mhc.mhcb_finalize_glm(dev(f.gemm2), rows * H, rows, dev(w), per_rank, bf16w, rsf, dev(f.idx),
+                          per_rank, dev(f.shared), M * H, dev(g.residual), dev(g.post),
+                          dev(g.comb), dev(g.fn), dev(g.scale), dev(g.base), dev(g.gamma), ro,
+                          mixes, li, ws, need, M, H, 4, tp, k, g.rms_eps, g.hc_eps, g.norm_eps)
+    torch.cuda.synchronize()
+    contrib_ref = oracle.finalize_contributions(f.gemm2, w, f.idx, f.shared,
+                                                replicated_routing=replicated,
+                                                routed_scaling_factor=rsf, threads=8)
+    off = need - tp * M * H * 2
+    contrib = ws[off:need].view(torch.int16).cpu().numpy().view(np.uint16).reshape(tp, M, H)
+    assert_bits_equal(contrib, contrib_ref, "published contributions")
+    ro_ref, mix_ref, li_ref, pre_ref = oracle.boundary_glm_moe(
+        f.gemm2, w, f.idx, f.shared, g.residual, g.post, g.comb, g.fn, g.scale, g.base, g.gamma,
+        g.rms_eps, g.hc_eps, g.norm_eps, replicated_routing=replicated,
+        routed_scaling_factor=rsf, threads=8)
+    assert_bits_equal(u16(ro), ro_ref, "residual_out")
+    mixes = host(mixes)
+    err = np.abs(mixes - mix_ref)
+    assert (err <= 1e-5 * (np.abs(mix_ref) + 1)).all(), f"mixes: max err {err.max()}"
+    one, two = glm_layer_input_check(u16(li), li_ref, ro_ref, pre_ref.astype(np.float64),
+                                     glm_pre(mixes, g.scale, g.base, g.hc_eps), g.gamma,
+                                     g.norm_eps)
+    print(f"[gpu]   layer_input 1-ulp {one}, 2+ ulp {two}", flush=True)
+
+
+def test_glm_moe_python_helper_matches_entry_point():
+    """finalize_glm (outputs and workspace allocated by the binding) gives
+    the same bits as the C entry point on a fresh workspace."""
+    f = synth.moe_finalize(20, H=1024, tp=4, top_k=8)
+    g = synth.glm(20, H=1024, tp=4)
+    ro, mixes, li = mhc.finalize_glm(dev(f.gemm2), dev(f.weights), dev(f.idx), dev(f.shared),
+                                     dev(g.residual), dev(g.post), dev(g.comb), dev(g.fn),
+                                     dev(g.scale), dev(g.base), dev(g.gamma), g.rms_eps, g.hc_eps,
+                                     g.norm_eps)
+    torch.cuda.synchronize()
+    ro_ref, mix_ref, li_ref, _ = oracle.boundary_glm_moe(
+        f.gemm2, f.weights, f.idx, f.shared, g.residual, g.post, g.comb, g.fn, g.scale, g.base,
+        g.gamma, g.rms_eps, g.hc_eps, g.norm_eps, threads=8)
+    assert_bits_equal(u16(ro), ro_ref, "residual_out")
+    assert (np.abs(host(mixes) - mix_ref) <= 1e-5 * (np.abs(mix_ref) + 1)).all()

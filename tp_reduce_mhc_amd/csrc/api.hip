@@ -149,6 +149,73 @@ void choose_slices(BoundaryArgs &a, void *ws, int target, int max_slices) {
   if (a.slices > 1) a.sync = sync_view(ws);
 }
 
+// The two-pass GLM tiles on validated arguments: slices of sf fragments (a
+// multiple of 4, 16..64), partials in the workspace after the sync state,
+// launches of at most kSyncTokens tokens.
+int glm_two_pass(const char *fn, const uint16_t *partials, int64_t rank_stride,
+                 const uint16_t *residual, const float *post, const float *comb,
+                 const uint16_t *hc_fn, const float *scale, const float *base,
+                 const uint16_t *norm_weight, uint16_t *residual_out, float *mixes_out,
+                 uint16_t *layer_input, void *workspace, int M, int hidden_size, int tp,
+                 float rms_eps, float hc_eps, float norm_eps, hipStream_t stream) {
+  const int F = hidden_size / kFrag;
+  // Slices of 16 fragments up to M = 64, 32 beyond (M=64: 12.6 vs 13.2
+  // us; M=128: 14.4 vs 15.1; M=1024: 56.7 vs 60.8).
+  int sf = M <= 64 ? 16 : 32;
+  if (g_slices_override > 0) sf = (F + g_slices_override - 1) / g_slices_override;
+  sf = (sf + 3) / 4 * 4;
+  sf = sf < 16 ? 16 : sf > 64 ? 64 : sf;
+  GlmArgs a = {(F + sf - 1) / sf, sf, SyncView{}, partials, rank_stride, tp, residual, post, comb,
+               hc_fn, scale, base, norm_weight, residual_out, mixes_out, layer_input, M,
+               hidden_size, rms_eps, hc_eps, norm_eps, kGlmTileTokens,
+               reinterpret_cast<float *>(static_cast<char *>(workspace) + kSyncBytes)};
+  const int64_t H = hidden_size;
+  for (int c = 0; c < M; c += kSyncTokens) {
+    GlmArgs b = a;
+    b.M = M - c < kSyncTokens ? M - c : kSyncTokens;
+    b.partials = partials + c * H;
+    b.residual = residual + c * kStreams * H;
+    b.post = post + (int64_t)c * kStreams;
+    b.comb = comb + (int64_t)c * kStreams * kStreams;
+    b.residual_out = residual_out + c * kStreams * H;
+    b.mixes_out = mixes_out + (int64_t)c * kMix;
+    b.layer_input = layer_input + c * H;
+    const int rc = launched(launch_boundary_glm_two_pass(b, stream), fn);
+    if (rc) return rc;
+  }
+  return ok();
+}
+
+// Checks the MoE routing arguments shared by the finalize entry points
+// ([DSV41] AllReduceMHC.finalize) and fills the view.
+int check_routes(const char *fn, const uint16_t *gemm2_permuted, int64_t gemm2_rank_stride,
+                 int64_t rows, const void *expert_weights, int64_t weights_rank_stride,
+                 int weights_bf16, float routed_scaling_factor, const int32_t *permuted_idx,
+                 int64_t idx_rank_stride, const uint16_t *shared_output,
+                 int64_t shared_rank_stride, int tp, int top_k, FinalizeView *f) {
+  if (top_k < 1) return fail(MHCB_EINVAL, "%s: top_k=%d < 1", fn, top_k);
+  if (weights_bf16 != 0 && weights_bf16 != 1)
+    return fail(MHCB_EINVAL, "%s: weights_bf16=%d (0 = FP32, 1 = BF16)", fn, weights_bf16);
+  if (!std::isfinite(routed_scaling_factor))
+    return fail(MHCB_EINVAL, "%s: routed_scaling_factor must be finite", fn);
+  if ((int64_t)tp * top_k > kMaxRoutes)
+    return fail(MHCB_EINVAL, "%s: tp * top_k = %d exceeds %d", fn, tp * top_k, kMaxRoutes);
+  if (rows < 0) return fail(MHCB_EINVAL, "%s: rows=%lld < 0", fn, (long long)rows);
+  if (!gemm2_permuted || !expert_weights || !permuted_idx || !shared_output)
+    return fail(MHCB_EINVAL, "%s: gemm2_permuted, expert_weights, permuted_idx and shared_output are required", fn);
+  if (gemm2_rank_stride < 0 || weights_rank_stride < 0 || idx_rank_stride < 0 || shared_rank_stride < 0)
+    return fail(MHCB_EINVAL, "%s: negative rank stride", fn);
+  if (!aligned(gemm2_permuted, 16) || !aligned(shared_output, 16) || gemm2_rank_stride % kFrag ||
+      shared_rank_stride % kFrag)
+    return fail(MHCB_EALIGN, "%s: BF16 inputs must be 16-byte aligned with rank strides %% 8 == 0", fn);
+  if (!aligned(expert_weights, weights_bf16 ? 2 : 4) || !aligned(permuted_idx, 4))
+    return fail(MHCB_EALIGN, "%s: expert_weights must be aligned to its element (4 bytes FP32, 2 BF16), permuted_idx to 4", fn);
+  *f = FinalizeView{gemm2_permuted, gemm2_rank_stride, rows, expert_weights, weights_rank_stride,
+                    weights_bf16, routed_scaling_factor, permuted_idx, idx_rank_stride,
+                    shared_output, shared_rank_stride, top_k};
+  return MHCB_OK;
+}
+
 MailboxView view_of(const mhcb_mailbox *mb) {
   MailboxView v;
   v.slots = mb->slots;
@@ -287,37 +354,12 @@ int mhcb_boundary_glm(const uint16_t *partials, int64_t rank_stride, const uint1
   if (G == 0 && workspace && workspace_bytes >= kSyncBytes + kGlmPartBytes && M >= kGlmTwoPassMinM)
     G = -kGlmTileTokens;
   if (G == -kGlmTileTokens) {
-    // Two passes over 16-token tiles: slices of sf fragments (a multiple of
-    // 4, 16..64; 32 by default), partials in the workspace after the sync
-    // state, launches of at most kSyncTokens tokens.
     const int64_t need = kSyncBytes + kGlmPartBytes;
     if (!workspace || workspace_bytes < need)
       return fail(MHCB_EINVAL, "%s: tokens_per_wg=-16 needs a workspace of %lld bytes", fn, (long long)need);
-    const int F = hidden_size / kFrag;
-    // Slices of 16 fragments up to M = 64, 32 beyond (M=64: 12.6 vs 13.2
-    // us; M=128: 14.4 vs 15.1; M=1024: 56.7 vs 60.8).
-    int sf = M <= 64 ? 16 : 32;
-    if (g_slices_override > 0) sf = (F + g_slices_override - 1) / g_slices_override;
-    sf = (sf + 3) / 4 * 4;
-    sf = sf < 16 ? 16 : sf > 64 ? 64 : sf;
-    GlmArgs a = {(F + sf - 1) / sf, sf, SyncView{}, partials, rank_stride, tp, residual, post, comb,
-                 hc_fn, scale, base, norm_weight, residual_out, mixes_out, layer_input, M,
-                 hidden_size, rms_eps, hc_eps, norm_eps, kGlmTileTokens,
-                 reinterpret_cast<float *>(static_cast<char *>(workspace) + kSyncBytes)};
-    const int64_t H = hidden_size;
-    for (int c = 0; c < M; c += kSyncTokens) {
-      GlmArgs b = a;
-      b.M = M - c < kSyncTokens ? M - c : kSyncTokens;
-      b.partials = partials + c * H;
-      b.residual = residual + c * kStreams * H;
-      b.post = post + (int64_t)c * kStreams;
-      b.comb = comb + (int64_t)c * kStreams * kStreams;
-      b.residual_out = residual_out + c * kStreams * H;
-      b.mixes_out = mixes_out + (int64_t)c * kMix;
-      b.layer_input = layer_input + c * H;
-      if ((rc = launched(launch_boundary_glm_two_pass(b, stream), fn))) return rc;
-    }
-    return ok();
+    return glm_two_pass(fn, partials, rank_stride, residual, post, comb, hc_fn, scale, base,
+                        norm_weight, residual_out, mixes_out, layer_input, workspace, M,
+                        hidden_size, tp, rms_eps, hc_eps, norm_eps, stream);
   }
   // Measured on MI355X (H=6144, tp=8): one token per workgroup below M=256
   // (M=128: 18.8 us; 16-token tiles: 22.3), 16-token tiles from M=256
@@ -392,6 +434,51 @@ int mhcb_boundary_glm(const uint16_t *partials, int64_t rank_stride, const uint1
   return launched(launch_boundary_glm(a, stream), fn);
 }
 
+int64_t mhcb_finalize_glm_workspace_bytes(int M, int hidden_size, int tp) {
+  if (M < 0 || hidden_size < 0 || tp < 1) return -1;
+  return kSyncBytes + kGlmPartBytes + (int64_t)tp * M * hidden_size * 2;
+}
+
+int mhcb_finalize_glm(const uint16_t *gemm2_permuted, int64_t gemm2_rank_stride, int64_t rows,
+                      const void *expert_weights, int64_t weights_rank_stride, int weights_bf16,
+                      float routed_scaling_factor, const int32_t *permuted_idx,
+                      int64_t idx_rank_stride, const uint16_t *shared_output,
+                      int64_t shared_rank_stride, const uint16_t *residual, const float *post,
+                      const float *comb, const uint16_t *hc_fn, const float *scale,
+                      const float *base, const uint16_t *norm_weight, uint16_t *residual_out,
+                      float *mixes_out, uint16_t *layer_input, void *workspace,
+                      int64_t workspace_bytes, int M, int hidden_size, int hc_mult, int tp,
+                      int top_k, float rms_eps, float hc_eps, float norm_eps, hipStream_t stream) {
+  const char *fn = "mhcb_finalize_glm";
+  if (!hc_fn || !scale || !base || !norm_weight || !mixes_out || !layer_input)
+    return fail(MHCB_EINVAL, "%s: hc_fn, scale, base, norm_weight, mixes_out and layer_input are required", fn);
+  int rc = check_common(fn, residual, post, comb, scale, norm_weight, residual_out, layer_input,
+                        nullptr, nullptr, M, hidden_size, hc_mult, tp, false);
+  if (rc) return rc;
+  if (hidden_size > kMaxHiddenGlm)
+    return fail(MHCB_EUNSUPPORTED, "%s: hidden_size=%d exceeds %d", fn, hidden_size, kMaxHiddenGlm);
+  if (!aligned(hc_fn, 16) || !aligned(base, 4) || !aligned(mixes_out, 4))
+    return fail(MHCB_EALIGN, "%s: hc_fn must be 16-byte aligned, base and mixes_out 4-byte", fn);
+  FinalizeView f;
+  if ((rc = check_routes(fn, gemm2_permuted, gemm2_rank_stride, rows, expert_weights,
+                         weights_rank_stride, weights_bf16, routed_scaling_factor, permuted_idx,
+                         idx_rank_stride, shared_output, shared_rank_stride, tp, top_k, &f)))
+    return rc;
+  const int64_t need = mhcb_finalize_glm_workspace_bytes(M, hidden_size, tp);
+  if (!workspace)
+    return fail(MHCB_EINVAL, "%s: a workspace of %lld bytes is required", fn, (long long)need);
+  if ((rc = check_workspace(fn, workspace, workspace_bytes, need))) return rc;
+  // Publish: every rank's contribution, rank-major after the two-pass
+  // partials; then the GLM boundary reads them as its rank partials.
+  uint16_t *contrib = reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) + kSyncBytes +
+                                                   kGlmPartBytes);
+  if ((rc = launched(launch_finalize_to_owners(f, tp, 1, M, hidden_size, contrib, stream), fn)))
+    return rc;
+  return glm_two_pass(fn, contrib, (int64_t)M * hidden_size, residual, post, comb, hc_fn, scale,
+                      base, norm_weight, residual_out, mixes_out, layer_input, workspace, M,
+                      hidden_size, tp, rms_eps, hc_eps, norm_eps, stream);
+}
+
 int mhcb_mixes(const float *mixes, const float *scale, const float *base, float *post_out,
                float *comb_out, int M, int hc_mult, float hc_eps, float post_mult,
                int sinkhorn_repeat, hipStream_t stream) {
@@ -422,26 +509,11 @@ static int finalize_impl(const char *fn, const uint16_t *gemm2_permuted, int64_t
   int rc = check_common(fn, residual, post, comb, pre, norm_weight, residual_out, layer_input,
                         mxfp8_values, mxfp8_scales, M, hidden_size, hc_mult, tp, true);
   if (rc) return rc;
-  if (top_k < 1) return fail(MHCB_EINVAL, "%s: top_k=%d < 1", fn, top_k);
-  if (weights_bf16 != 0 && weights_bf16 != 1)
-    return fail(MHCB_EINVAL, "%s: weights_bf16=%d (0 = FP32, 1 = BF16)", fn, weights_bf16);
-  if (!std::isfinite(routed_scaling_factor))
-    return fail(MHCB_EINVAL, "%s: routed_scaling_factor must be finite", fn);
-  if ((int64_t)tp * top_k > kMaxRoutes)
-    return fail(MHCB_EINVAL, "%s: tp * top_k = %d exceeds %d", fn, tp * top_k, kMaxRoutes);
-  if (rows < 0) return fail(MHCB_EINVAL, "%s: rows=%lld < 0", fn, (long long)rows);
-  if (!gemm2_permuted || !expert_weights || !permuted_idx || !shared_output)
-    return fail(MHCB_EINVAL, "%s: gemm2_permuted, expert_weights, permuted_idx and shared_output are required", fn);
-  if (gemm2_rank_stride < 0 || weights_rank_stride < 0 || idx_rank_stride < 0 || shared_rank_stride < 0)
-    return fail(MHCB_EINVAL, "%s: negative rank stride", fn);
-  if (!aligned(gemm2_permuted, 16) || !aligned(shared_output, 16) || gemm2_rank_stride % kFrag ||
-      shared_rank_stride % kFrag)
-    return fail(MHCB_EALIGN, "%s: BF16 inputs must be 16-byte aligned with rank strides %% 8 == 0", fn);
-  if (!aligned(expert_weights, weights_bf16 ? 2 : 4) || !aligned(permuted_idx, 4))
-    return fail(MHCB_EALIGN, "%s: expert_weights must be aligned to its element (4 bytes FP32, 2 BF16), permuted_idx to 4", fn);
-  FinalizeView f = {gemm2_permuted, gemm2_rank_stride, rows, expert_weights, weights_rank_stride,
-                    weights_bf16, routed_scaling_factor, permuted_idx, idx_rank_stride,
-                    shared_output, shared_rank_stride, top_k};
+  FinalizeView f;
+  if ((rc = check_routes(fn, gemm2_permuted, gemm2_rank_stride, rows, expert_weights,
+                         weights_rank_stride, weights_bf16, routed_scaling_factor, permuted_idx,
+                         idx_rank_stride, shared_output, shared_rank_stride, tp, top_k, &f)))
+    return rc;
   BoundaryArgs a = {};
   a.tp = tp;
   a.hc = hc_mult;
@@ -473,7 +545,7 @@ static int finalize_impl(const char *fn, const uint16_t *gemm2_permuted, int64_t
   uint16_t *own = reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) + kSyncBytes);
   const int64_t slots = ((int64_t)M + tp - 1) / tp;
   uint16_t *reduced = own + (int64_t)tp * tp * slots * hidden_size;
-  hipError_t e = launch_finalize_to_owners(f, tp, M, hidden_size, own, stream);
+  hipError_t e = launch_finalize_to_owners(f, tp, tp, M, hidden_size, own, stream);
   if (e == hipSuccess) e = launch_owner_reduce(own, tp, M, hidden_size, reduced, stream);
   if (e != hipSuccess) return launched(e, fn);
   a.source = Source::kPartials;

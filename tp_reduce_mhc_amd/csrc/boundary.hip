@@ -525,18 +525,20 @@ hipError_t launch_src(const BoundaryArgs &a, hipStream_t stream) {
 // Two-shot emulation
 // ---------------------------------------------------------------------------
 
-// Every rank's contribution of token t (blockIdx.x) into owner t % tp,
-// slot t / tp: own[owner][rank][slot][H]
-// (_QuadFinalizePublishDeviceKernel.kernel, two-shot branch).
+// Every rank's contribution of token t (blockIdx.x) into owner t % owners,
+// slot t / owners: own[owner][rank][slot][H]
+// (_QuadFinalizePublishDeviceKernel.kernel: the two-shot branch with
+// owners = tp; with owners = 1 the one-shot publish, own[rank][t][H], the
+// contributions the GLM boundary of an MoE sublayer reads as its partials).
 __global__ void __launch_bounds__(kTokenThreads)
-finalize_to_owners_kernel(const FinalizeView f, int tp, int M, int H, uint16_t *own) {
+finalize_to_owners_kernel(const FinalizeView f, int tp, int owners, int M, int H, uint16_t *own) {
   __shared__ int32_t srow[kMaxRoutes];
   __shared__ float sw[kMaxRoutes];
   const int t = blockIdx.x, F = H / kFrag;
   stage_routes(f, tp, t, srow, sw);
-  const int64_t slots = (M + tp - 1) / tp;
-  const int owner = t % tp;
-  const int64_t slot = t / tp;
+  const int64_t slots = (M + owners - 1) / owners;
+  const int owner = t % owners;
+  const int64_t slot = t / owners;
   for (int fr = threadIdx.x; fr < F; fr += blockDim.x) {
     const int64_t col = (int64_t)fr * kFrag;
     for (int r = 0; r < tp; ++r) {
@@ -703,11 +705,11 @@ hipError_t launch_zero(void *p, int64_t bytes, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_finalize_to_owners(const FinalizeView &fin, int tp, int M, int H, uint16_t *own,
-                                     hipStream_t stream) {
+hipError_t launch_finalize_to_owners(const FinalizeView &fin, int tp, int owners, int M, int H,
+                                     uint16_t *own, hipStream_t stream) {
   const Geometry g = token_geometry(H);
-  hipLaunchKernelGGL(finalize_to_owners_kernel, dim3(M), dim3(g.threads), 0, stream, fin, tp, M, H,
-                     own);
+  hipLaunchKernelGGL(finalize_to_owners_kernel, dim3(M), dim3(g.threads), 0, stream, fin, tp,
+                     owners, M, H, own);
   return hipGetLastError();
 }
 

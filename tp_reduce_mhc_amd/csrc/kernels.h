@@ -101,9 +101,10 @@ struct BoundaryArgs {
 
 hipError_t launch_boundary(const BoundaryArgs &a, hipStream_t stream);
 
-// Two-shot emulation: every rank's finalize contribution into the owner
-// mailboxes own[t % tp][rank][t / tp][H], then the owners' reduced sums.
-hipError_t launch_finalize_to_owners(const FinalizeView &fin, int tp, int M, int H,
+// Every rank's finalize contribution into own[t % owners][rank][t / owners][H]:
+// the two-shot owner mailboxes (owners = tp) or the rank-major published
+// contributions (owners = 1).  Then, two-shot, the owners' reduced sums.
+hipError_t launch_finalize_to_owners(const FinalizeView &fin, int tp, int owners, int M, int H,
                                      uint16_t *own, hipStream_t stream);
 hipError_t launch_owner_reduce(const uint16_t *own, int tp, int M, int H, uint16_t *reduced,
                                hipStream_t stream);

@@ -73,6 +73,10 @@ _SIGNATURES = {
                            _P, _P, _P, _I, _P, _I64, _I, _I, _I, _I, _I, _F, _P]),
     "mhcb_finalize_ex": (_I, [_P, _I64, _I64, _P, _I64, _I, _F, _P, _I64, _P, _I64, _P, _P, _P, _P,
                               _P, _P, _P, _P, _P, _I, _P, _I64, _I, _I, _I, _I, _I, _F, _P]),
+    "mhcb_finalize_glm_workspace_bytes": (_I64, [_I, _I, _I]),
+    "mhcb_finalize_glm": (_I, [_P, _I64, _I64, _P, _I64, _I, _F, _P, _I64, _P, _I64, _P, _P, _P,
+                               _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I, _I, _I, _I, _I, _F, _F,
+                               _F, _P]),
     "mhcb_quant_mxfp8": (_I, [_P, _P, _P, _I, _I, _P]),
     "mhcb_mailbox_init": (_I, [_MB, _P]),
     "mhcb_publish": (_I, [_MB, _P, _I64, _I, _I, _I, _P]),
@@ -238,7 +242,7 @@ _WORKSPACES = {}
 
 
 def workspace(device=None, *, M: int = 0, hidden_size: int = 0, tp: int = 1,
-              two_shot: bool = False) -> torch.Tensor:
+              two_shot: bool = False, nbytes: int = 0) -> torch.Tensor:
     """An initialized workspace on `device`, cached per (device, size):
     the sync state of the token-split calls, plus the two-shot scratch when
     asked.  Calls on different streams need their own (fresh=True is not
@@ -246,7 +250,7 @@ def workspace(device=None, *, M: int = 0, hidden_size: int = 0, tp: int = 1,
     device = torch.device(device if device is not None else "cuda")
     if device.index is None:
         device = torch.device("cuda", torch.cuda.current_device())
-    need = mhcb_workspace_bytes(M, hidden_size, tp, int(two_shot))
+    need = max(mhcb_workspace_bytes(M, hidden_size, tp, int(two_shot)), nbytes)
     key = (device.index, need)
     ws = _WORKSPACES.get(key)
     if ws is None:
@@ -301,6 +305,51 @@ def boundary_glm(partials, residual, post, comb, hc_fn, scale, base, norm_weight
                       norm_weight, residual_out, mixes, layer_input, ws, ws.numel(), M, H, 4, tp,
                       rms_eps, hc_eps, norm_eps, tokens_per_wg, stream)
     return residual_out, mixes, layer_input
+
+
+def mhcb_finalize_glm_workspace_bytes(M: int, hidden_size: int, tp: int) -> int:
+    return _lib.mhcb_finalize_glm_workspace_bytes(M, hidden_size, tp)
+
+
+def mhcb_finalize_glm(gemm2_permuted, gemm2_rank_stride, rows, expert_weights, weights_rank_stride,
+                      weights_bf16, routed_scaling_factor, permuted_idx, idx_rank_stride,
+                      shared_output, shared_rank_stride, residual, post, comb, hc_fn, scale, base,
+                      norm_weight, residual_out, mixes_out, layer_input, workspace,
+                      workspace_bytes, M, hidden_size, hc_mult, tp, top_k, rms_eps, hc_eps,
+                      norm_eps, stream=None) -> None:
+    _check(_lib.mhcb_finalize_glm(_ptr(gemm2_permuted), gemm2_rank_stride, rows,
+                                  _ptr(expert_weights), weights_rank_stride, int(weights_bf16),
+                                  routed_scaling_factor, _ptr(permuted_idx), idx_rank_stride,
+                                  _ptr(shared_output), shared_rank_stride, _ptr(residual),
+                                  _ptr(post), _ptr(comb), _ptr(hc_fn), _ptr(scale), _ptr(base),
+                                  _ptr(norm_weight), _ptr(residual_out), _ptr(mixes_out),
+                                  _ptr(layer_input), _ptr(workspace), workspace_bytes, M,
+                                  hidden_size, hc_mult, tp, top_k, rms_eps, hc_eps, norm_eps,
+                                  _stream(stream)))
+
+
+def finalize_glm(gemm2, weights, idx, shared, residual, post, comb, hc_fn, scale, base,
+                 norm_weight, rms_eps, hc_eps, norm_eps, *, routed_scaling_factor: float = 1.0,
+                 stream=None):
+    """GLM boundary of an MoE sublayer.  gemm2 [tp, rows, H]; shared
+    [tp, M, H]; weights (FP32 or BF16) / idx [M, top_k] (replicated) or
+    [tp, M, top_k]; the rest as boundary_glm.  Returns (residual_out
+    [M,4,H], raw mixes [M,24], layer_input [M,H])."""
+    tp, rows, H = gemm2.shape
+    M = shared.shape[1]
+    top_k = weights.shape[-1]
+    dev = gemm2.device
+    per_rank = weights.dim() == 3
+    residual_out = _bf16_empty((M, 4, H), dev)
+    mixes_out = torch.empty((M, 24), dtype=torch.float32, device=dev)
+    layer_input = _bf16_empty((M, H), dev)
+    ws = workspace(dev, nbytes=mhcb_finalize_glm_workspace_bytes(M, H, tp))
+    mhcb_finalize_glm(gemm2, rows * H, rows, weights, M * top_k if per_rank else 0,
+                      weights.dtype == torch.bfloat16, routed_scaling_factor, idx,
+                      M * top_k if per_rank else 0, shared, M * H, residual, post, comb, hc_fn,
+                      scale, base, norm_weight, residual_out, mixes_out, layer_input, ws,
+                      ws.numel(), M, H, 4, tp, top_k, rms_eps, hc_eps, norm_eps, stream)
+    return residual_out, mixes_out, layer_input
 
 
 def mixes(raw_mixes, scale, base, hc_eps, post_mult, sinkhorn_repeat, *, stream=None):
