@@ -539,7 +539,9 @@ finalize_to_owners_kernel(const FinalizeView f, int tp, int owners, int M, int H
   const int64_t slots = (M + owners - 1) / owners;
   const int owner = t % owners;
   const int64_t slot = t / owners;
-  for (int fr = threadIdx.x; fr < F; fr += blockDim.x) {
+  // Column chunk blockIdx.y of gridDim.y (small M spreads a token's
+  // fragments over several workgroups).
+  for (int fr = blockIdx.y * blockDim.x + threadIdx.x; fr < F; fr += gridDim.y * blockDim.x) {
     const int64_t col = (int64_t)fr * kFrag;
     for (int r = 0; r < tp; ++r) {
       const u32x4 c = finalize_fragment(f, srow + r * f.top_k, sw + r * f.top_k, r, t, H, col);
@@ -707,8 +709,22 @@ hipError_t launch_zero(void *p, int64_t bytes, hipStream_t stream) {
 
 hipError_t launch_finalize_to_owners(const FinalizeView &fin, int tp, int owners, int M, int H,
                                      uint16_t *own, hipStream_t stream) {
-  const Geometry g = token_geometry(H);
-  hipLaunchKernelGGL(finalize_to_owners_kernel, dim3(M), dim3(g.threads), 0, stream, fin, tp,
+  // One workgroup per token, or below 256 tokens the token's fragments in
+  // chunks of at least one wave, about 512 workgroups in all: every rank's
+  // gathers of a fragment are one dependent round trip each, so the round
+  // trips of many workgroups must overlap.
+  const int F = H / kFrag;
+  int chunks = M < 256 ? (512 + M - 1) / M : 1;
+  const int max_chunks = (F + kWave - 1) / kWave;
+  chunks = chunks > max_chunks ? max_chunks : chunks;
+  const int wide = token_geometry(H).threads;  // at most kTokenThreads
+  int threads = wide;
+  if (chunks > 1) {
+    threads = ((F + chunks - 1) / chunks + kWave - 1) / kWave * kWave;
+    threads = threads > wide ? wide : threads;
+    chunks = (F + threads - 1) / threads;  // the kernel's loop strides over any remainder
+  }
+  hipLaunchKernelGGL(finalize_to_owners_kernel, dim3(M, chunks), dim3(threads), 0, stream, fin, tp,
                      owners, M, H, own);
   return hipGetLastError();
 }
