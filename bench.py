@@ -66,7 +66,7 @@ def bytes_glm(M, H, tp):
 
 # The files the headline kernel (boundary_kernel) is compiled from: a change
 # to any of them invalidates the committed counter summary.
-HEADLINE_SOURCES = ("boundary.hip", "device.h", "kernels.h", "sync.h")
+HEADLINE_SOURCES = ("boundary.hip", "device.h", "kernels.h", "sync.h", "finalize.h")
 
 
 def source_hash():

@@ -157,7 +157,8 @@ int glm_two_pass(const char *fn, const uint16_t *partials, int64_t rank_stride,
                  const uint16_t *hc_fn, const float *scale, const float *base,
                  const uint16_t *norm_weight, uint16_t *residual_out, float *mixes_out,
                  uint16_t *layer_input, void *workspace, int M, int hidden_size, int tp,
-                 float rms_eps, float hc_eps, float norm_eps, hipStream_t stream) {
+                 float rms_eps, float hc_eps, float norm_eps, const FinalizeView *fin,
+                 hipStream_t stream) {
   const int F = hidden_size / kFrag;
   // Slices of 16 fragments up to M = 64, 32 beyond (M=64: 12.6 vs 13.2
   // us; M=128: 14.4 vs 15.1; M=1024: 56.7 vs 60.8).
@@ -169,6 +170,7 @@ int glm_two_pass(const char *fn, const uint16_t *partials, int64_t rank_stride,
                hc_fn, scale, base, norm_weight, residual_out, mixes_out, layer_input, M,
                hidden_size, rms_eps, hc_eps, norm_eps, kGlmTileTokens,
                reinterpret_cast<float *>(static_cast<char *>(workspace) + kSyncBytes)};
+  if (fin) a.fin = *fin;  // the ranks' contributions from MoE routes (partials unused)
   const int64_t H = hidden_size;
   for (int c = 0; c < M; c += kSyncTokens) {
     GlmArgs b = a;
@@ -180,6 +182,13 @@ int glm_two_pass(const char *fn, const uint16_t *partials, int64_t rank_stride,
     b.residual_out = residual_out + c * kStreams * H;
     b.mixes_out = mixes_out + (int64_t)c * kMix;
     b.layer_input = layer_input + c * H;
+    if (fin) {  // this launch's tokens of the routes and shared rows
+      const int64_t k = fin->top_k;
+      b.partials = nullptr;
+      b.fin.weights = static_cast<const char *>(fin->weights) + c * k * (fin->w_bf16 ? 2 : 4);
+      b.fin.idx = fin->idx + c * k;
+      b.fin.shared = fin->shared + c * H;
+    }
     const int rc = launched(launch_boundary_glm_two_pass(b, stream), fn);
     if (rc) return rc;
   }
@@ -359,7 +368,7 @@ int mhcb_boundary_glm(const uint16_t *partials, int64_t rank_stride, const uint1
       return fail(MHCB_EINVAL, "%s: tokens_per_wg=-16 needs a workspace of %lld bytes", fn, (long long)need);
     return glm_two_pass(fn, partials, rank_stride, residual, post, comb, hc_fn, scale, base,
                         norm_weight, residual_out, mixes_out, layer_input, workspace, M,
-                        hidden_size, tp, rms_eps, hc_eps, norm_eps, stream);
+                        hidden_size, tp, rms_eps, hc_eps, norm_eps, nullptr, stream);
   }
   // Measured on MI355X (H=6144, tp=8): one token per workgroup below M=256
   // (M=128: 18.8 us; 16-token tiles: 22.3), 16-token tiles from M=256
@@ -468,15 +477,21 @@ int mhcb_finalize_glm(const uint16_t *gemm2_permuted, int64_t gemm2_rank_stride,
   if (!workspace)
     return fail(MHCB_EINVAL, "%s: a workspace of %lld bytes is required", fn, (long long)need);
   if ((rc = check_workspace(fn, workspace, workspace_bytes, need))) return rc;
-  // Publish: every rank's contribution, rank-major after the two-pass
-  // partials; then the GLM boundary reads them as its rank partials.
+  // Up to kGlmTileRoutes routes a token: the stream pass computes the
+  // ranks' contributions itself.  Beyond: publish every rank's
+  // contribution, rank-major after the two-pass partials, and run the GLM
+  // boundary on them as its rank partials.
+  if ((int64_t)tp * top_k <= kGlmTileRoutes)
+    return glm_two_pass(fn, nullptr, 0, residual, post, comb, hc_fn, scale, base, norm_weight,
+                        residual_out, mixes_out, layer_input, workspace, M, hidden_size, tp,
+                        rms_eps, hc_eps, norm_eps, &f, stream);
   uint16_t *contrib = reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) + kSyncBytes +
                                                    kGlmPartBytes);
   if ((rc = launched(launch_finalize_to_owners(f, tp, 1, M, hidden_size, contrib, stream), fn)))
     return rc;
   return glm_two_pass(fn, contrib, (int64_t)M * hidden_size, residual, post, comb, hc_fn, scale,
                       base, norm_weight, residual_out, mixes_out, layer_input, workspace, M,
-                      hidden_size, tp, rms_eps, hc_eps, norm_eps, stream);
+                      hidden_size, tp, rms_eps, hc_eps, norm_eps, nullptr, stream);
 }
 
 int mhcb_mixes(const float *mixes, const float *scale, const float *base, float *post_out,

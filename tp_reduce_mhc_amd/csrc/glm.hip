@@ -19,6 +19,9 @@
 #include "device.h"
 #include "kernels.h"
 #include "sync.h"
+#include "finalize.h"
+
+#include <type_traits>
 
 namespace mhcb {
 namespace {
@@ -771,10 +774,39 @@ __host__ __device__ inline size_t stream_dyn_bytes(int sf) {
   return tile_dyn_bytes(sf) + (size_t)(sf / 4) * kTile * kMix * 4;
 }
 
-template <int TP>
+// The tile's MoE routes (FIN): [token][rank][k] rows and weights, as the
+// per-token kernels stage them (stage_routes): weights widened from BF16
+// when so given, times the routed scaling factor when not 1, and 0 for a
+// route whose row is -1.
+struct TileRoutes {
+  int32_t row[kTile * kGlmTileRoutes];
+  float w[kTile * kGlmTileRoutes];
+};
+struct NoRoutes {};
+
+__device__ __forceinline__ void stage_tile_routes(const FinalizeView &f, int tp, int t0, int valid,
+                                                  TileRoutes &rt) {
+  const int per = tp * f.top_k;
+  for (int i = threadIdx.x; i < valid * per; i += blockDim.x) {
+    const int tok = i / per, rem = i % per, r = rem / f.top_k, k = rem % f.top_k;
+    const int64_t t = t0 + tok;
+    const int64_t e = r * f.w_stride + t * f.top_k + k;
+    const int32_t row = f.idx[r * f.i_stride + t * f.top_k + k];
+    float w = f.w_bf16 ? __uint_as_float((uint32_t)static_cast<const uint16_t *>(f.weights)[e] << 16)
+                       : static_cast<const float *>(f.weights)[e];
+    if (f.w_scale != 1.0f) w = w * f.w_scale;
+    rt.row[i] = row;
+    rt.w[i] = row == -1 ? 0.0f : w;
+  }
+}
+
+// TP = fixed rank count of the partials (0: runtime); FIN = the ranks'
+// contributions are MoE finalize outputs computed from a.fin (TP = 0).
+template <int TP, bool FIN>
 __global__ void __launch_bounds__(kStreamMaxThreads)
 glm_stream_kernel(const GlmArgs a) {
   __shared__ StreamShared sh;
+  __shared__ std::conditional_t<FIN, TileRoutes, NoRoutes> routes;
   extern __shared__ __align__(16) char dyn[];
   const int H = a.H, F = H / kFrag, tid = threadIdx.x, nt = blockDim.x;
   const int lane = tid & (kWave - 1), wave = tid / kWave, waves = nt / kWave;
@@ -827,13 +859,26 @@ glm_stream_kernel(const GlmArgs a) {
       else sh.comb[tk][k - kStreams] = mv[u];
     }
   }
+  if constexpr (FIN) stage_tile_routes(a.fin, tp, t0, valid, routes);
   __syncthreads();
 
   // a1 + a2: rank sum, post-mix, residual_out; y to LDS.
   float sum[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) sum[e] = 0.0f;
-  if constexpr (TP > 0) {
+  if constexpr (FIN) {
+    // a6 then a1: each rank's contribution (BF16, sanitized), added in rank
+    // order.
+    const int per = tp * a.fin.top_k;
+    for (int r = 0; r < tp; ++r) {
+      if (!live) break;
+      const int o = tok * per + r * a.fin.top_k;
+      float v[8];
+      unpack8(finalize_fragment(a.fin, routes.row + o, routes.w + o, r, (int)t, H, col), v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sum[e] = sum[e] + v[e];
+    }
+  } else if constexpr (TP > 0) {
 #pragma unroll
     for (int r = 0; r < TP; ++r) {
       float v[8];
@@ -1115,20 +1160,23 @@ hipError_t launch_boundary_glm_two_pass(const GlmArgs &a, hipStream_t stream) {
     return hipErrorInvalidValue;
   const dim3 grid(a.slices, (a.M + kTile - 1) / kTile), block(kTile * sf);
   const size_t lds = stream_dyn_bytes(sf);
-#define MHCB_STREAM_LAUNCH(TPP)                                                              \
+#define MHCB_STREAM_LAUNCH(TPP, FINN)                                                        \
   if (lds > 65536) {                                                                         \
-    const hipError_t e = hipFuncSetAttribute((const void *)glm_stream_kernel<TPP>,            \
+    const hipError_t e = hipFuncSetAttribute((const void *)glm_stream_kernel<TPP, FINN>,      \
                                              hipFuncAttributeMaxDynamicSharedMemorySize,      \
                                              (int)lds);                                      \
     if (e != hipSuccess) return e;                                                           \
   }                                                                                          \
-  hipLaunchKernelGGL((glm_stream_kernel<TPP>), grid, block, lds, stream, a);
-  if (a.tp == 8) {
-    MHCB_STREAM_LAUNCH(8)
+  hipLaunchKernelGGL((glm_stream_kernel<TPP, FINN>), grid, block, lds, stream, a);
+  if (a.fin.gemm2) {
+    if (a.tp * a.fin.top_k > kGlmTileRoutes) return hipErrorInvalidValue;
+    MHCB_STREAM_LAUNCH(0, true)
+  } else if (a.tp == 8) {
+    MHCB_STREAM_LAUNCH(8, false)
   } else if (a.tp == 4) {
-    MHCB_STREAM_LAUNCH(4)
+    MHCB_STREAM_LAUNCH(4, false)
   } else {
-    MHCB_STREAM_LAUNCH(0)
+    MHCB_STREAM_LAUNCH(0, false)
   }
 #undef MHCB_STREAM_LAUNCH
   hipError_t e = hipGetLastError();

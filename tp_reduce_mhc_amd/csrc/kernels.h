@@ -67,6 +67,7 @@ constexpr int64_t kSyncBytes = 256 + (int64_t)kSyncSlot * kSyncTokens;
 constexpr int kPartWords = 32;
 constexpr int kPartSum = 24;        // word offset of the binary64 sum
 constexpr int kGlmMaxParts = 64;    // slices of at least 16 fragments, H <= 8192
+constexpr int kGlmTileRoutes = 128; // tp * top_k a two-pass MoE tile stages in LDS
 constexpr int64_t kGlmPartBytes = (int64_t)kSyncTokens * kGlmMaxParts * kPartWords * 4;  // 8 MiB
 
 struct SyncView {
@@ -136,6 +137,7 @@ struct GlmArgs {
   float rms_eps, hc_eps, norm_eps;
   int tokens_per_wg;         // 1, 2 or 4
   float *parts;              // two-pass tiles: [M][slices][kPartWords] partials
+  FinalizeView fin;          // two-pass tiles of an MoE sublayer (gemm2 NULL: partials)
 };
 
 hipError_t launch_boundary_glm(const GlmArgs &a, hipStream_t stream);
