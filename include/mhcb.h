@@ -241,13 +241,15 @@ int mhcb_finalize_ex(const uint16_t *gemm2_permuted, int64_t gemm2_rank_stride, 
  * contribution
  *   c_r[t] = sanitize(bf16(sum_{k asc, row valid} w[t][k] * gemm2_r[row] + shared_r[t]))
  * (routing as in mhcb_finalize_ex: FP32 or BF16 weights times the routed
- * scaling factor, rows outside [0, rows) skipped) is written rank-major into
- * the workspace, and mhcb_boundary_glm's arithmetic then runs on them as
- * its tp partials (two-pass tiles): residual_out, mixes_out [M, 24] and
- * layer_input as there.  The workspace is required, of at least
+ * scaling factor, rows outside [0, rows) skipped) takes the place of rank
+ * r's partial in mhcb_boundary_glm's arithmetic (two-pass tiles):
+ * residual_out, mixes_out [M, 24] and layer_input as there.  Up to 128
+ * routes a token (tp * top_k) the stream pass computes the contributions
+ * itself; beyond, they are first written rank-major into the workspace.
+ * The workspace is required, of at least
  * mhcb_finalize_glm_workspace_bytes(M, hidden_size, tp) bytes (the sync
- * state, the two-pass scratch, then tp * M * hidden BF16 contributions).
- * hc_mult = 4, hidden <= 8192. */
+ * state, the two-pass scratch, then room for tp * M * hidden BF16
+ * contributions).  hc_mult = 4, hidden <= 8192. */
 int64_t mhcb_finalize_glm_workspace_bytes(int M, int hidden_size, int tp);
 int mhcb_finalize_glm(const uint16_t *gemm2_permuted, int64_t gemm2_rank_stride, int64_t rows,
                       const void *expert_weights, int64_t weights_rank_stride, int weights_bf16,
