@@ -189,3 +189,19 @@ def test_product_path_does_not_touch_the_oracle():
             text = open(path).read()
             assert "import oracle" not in text and "from oracle" not in text, path
             assert "liboracle" not in text and "oracle_" not in text, path
+
+
+def test_binding_fails_loudly_without_the_library(tmp_path):
+    """The Python binding has no fallback: without libmhcb.so it refuses to
+    import."""
+    import shutil
+    import subprocess
+    import sys
+    src = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "tp_reduce_mhc_amd")
+    pkg = tmp_path / "tp_reduce_mhc_amd"
+    pkg.mkdir()
+    for name in ("__init__.py", "mhcb.py"):
+        shutil.copy(os.path.join(src, name), pkg / name)
+    r = subprocess.run([sys.executable, "-c", "import tp_reduce_mhc_amd"], cwd=tmp_path,
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0 and "libmhcb.so is missing" in r.stderr
