@@ -747,12 +747,12 @@ glm_tile_kernel(const GlmArgs a) {
 //
 // Pass 1, glm_stream_kernel: workgroup (s, grp) takes tokens grp*16 ..
 // grp*16+15 over the fragments [s * sf, (s + 1) * sf), one (token,
-// fragment) item per thread (16 * sf threads).  It streams the ranks and the
-// residual streams, writes residual_out, and leaves the slice's 24 partial
-// GEMV rows and its sum of squares of the token's streams in the scratch
-// area.  Small workgroups (sf = 16 or 32 fragments) keep several per compute
-// unit, so one workgroup's arithmetic runs while another's loads are in
-// flight.
+// fragment) item per thread (16 * sf threads).  It streams the ranks (for
+// an MoE sublayer: computes each rank's contribution from the tile's routes)
+// and the residual streams, writes residual_out, and leaves the slice's 24
+// partial GEMV rows and its sum of squares of the token's streams in the
+// scratch area.  Workgroups are small (sf = 16 or 32 fragments), several to
+// a compute unit.
 //
 // Pass 2, glm_finish_kernel: one workgroup per token, one fragment per
 // thread.  It adds the slices' partials in slice order, writes the raw
