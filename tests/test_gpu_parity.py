@@ -989,3 +989,32 @@ def test_glm_moe_python_helper_matches_entry_point():
         g.gamma, g.rms_eps, g.hc_eps, g.norm_eps, threads=8)
     assert_bits_equal(u16(ro), ro_ref, "residual_out")
     assert (np.abs(host(mixes) - mix_ref) <= 1e-5 * (np.abs(mix_ref) + 1)).all()
+
+
+@pytest.mark.parametrize("M", [16, 300])
+def test_glm_auto_with_sync_only_workspace(M):
+    """A workspace that holds only the sync state (no two-pass scratch): the
+    automatic choice falls back to the exchanging forms (one token per
+    workgroup below M = 256, 16-token tiles from there) and still matches
+    the oracle."""
+    g = synth.glm(M)
+    sync_only = mhc.mhcb_workspace_bytes(0, 0, 1, 0) - (8 << 20)  # less the 8 MiB scratch
+    ws = mhc.new_workspace(sync_only, "cuda")
+    ro = torch.full((M, 4, g.H), float("nan"), dtype=torch.bfloat16, device="cuda")
+    mixes = torch.full((M, 24), float("nan"), dtype=torch.float32, device="cuda")
+    li = torch.full((M, g.H), float("nan"), dtype=torch.bfloat16, device="cuda")
+    print(f"[gpu] {g.name} automatic, sync-only workspace of {sync_only} bytes", flush=True)
+    mhc.mhcb_boundary_glm(dev(g.partials), M * g.H, dev(g.residual), dev(g.post), dev(g.comb),
+                          dev(g.fn), dev(g.scale), dev(g.base), dev(g.gamma), ro, mixes, li, ws,
+                          sync_only, M, g.H, 4, g.tp, g.rms_eps, g.hc_eps, g.norm_eps, 0)
+    torch.cuda.synchronize()
+    assert mhc.mhcb_workspace_status(ws) == mhc.MHCB_OK
+    toks = np.arange(M) if M <= 16 else np.array([0, 1, 15, 16, 150, 255, 256, 299])
+    ro_ref, mix_ref, li_ref, pre_ref = oracle.boundary_glm(
+        g.partials[:, toks], g.residual[toks], g.post[toks], g.comb[toks], g.fn, g.scale, g.base,
+        g.gamma, g.rms_eps, g.hc_eps, g.norm_eps, threads=8)
+    assert_bits_equal(u16(ro)[toks], ro_ref, "residual_out")
+    mixes = host(mixes)[toks]
+    assert (np.abs(mixes - mix_ref) <= 1e-5 * (np.abs(mix_ref) + 1)).all()
+    glm_layer_input_check(u16(li)[toks], li_ref, ro_ref, pre_ref.astype(np.float64),
+                          glm_pre(mixes, g.scale, g.base, g.hc_eps), g.gamma, g.norm_eps)
