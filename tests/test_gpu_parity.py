@@ -924,7 +924,8 @@ def test_finalize_random_shapes(case):
                                   (130, 1024, 4, 16, False, 0.3, False, 0.7),
                                   (64, 6144, 4, 8, True, 0.0, True, 1.0),
                                   (1100, 256, 2, 4, False, 0.2, True, 1.5),
-                                  (24, 1024, 8, 32, False, 0.1, False, 1.0)],
+                                  (24, 1024, 8, 32, False, 0.1, False, 1.0),
+                                  (10, 1024, 3, 6, False, 0.2, True, 1.0)],
                          ids=lambda c: f"M{c[0]}-H{c[1]}-tp{c[2]}-k{c[3]}-bf16w{int(c[6])}")
 def test_glm_moe_matches_oracle(case):
     """mhcb_finalize_glm: residual_out bit-exact, raw mixes within 1e-5

@@ -801,9 +801,13 @@ __device__ __forceinline__ void stage_tile_routes(const FinalizeView &f, int tp,
 }
 
 // TP = fixed rank count of the partials (0: runtime); FIN = the ranks'
-// contributions are MoE finalize outputs computed from a.fin (TP = 0).
+// contributions are MoE finalize outputs computed from a.fin (TP = 0: one
+// rank's gathers at a time; TP = 2: two ranks' at a time, top_k <= 8, in
+// workgroups of at most kStreamPairThreads).
+constexpr int kStreamPairThreads = 256;
+
 template <int TP, bool FIN>
-__global__ void __launch_bounds__(kStreamMaxThreads)
+__global__ void __launch_bounds__(FIN && TP == 2 ? kStreamPairThreads : kStreamMaxThreads)
 glm_stream_kernel(const GlmArgs a) {
   __shared__ StreamShared sh;
   __shared__ std::conditional_t<FIN, TileRoutes, NoRoutes> routes;
@@ -813,7 +817,8 @@ glm_stream_kernel(const GlmArgs a) {
   const int s = blockIdx.x, t0 = blockIdx.y * kTile, S = a.slices;
   const int sf = a.slice_frags, first = s * sf, last = min(F, first + sf);
   const int valid = min(kTile, a.M - t0);
-  const int tp = TP > 0 ? TP : a.tp;
+  constexpr int kHeld = FIN ? 0 : TP;  // partials held in registers (FIN: TP picks the gather form)
+  const int tp = kHeld > 0 ? kHeld : a.tp;
   const int rw = tile_row_words(sf);
   u32x4 *ys = reinterpret_cast<u32x4 *>(dyn);
   double *item = reinterpret_cast<double *>(dyn + tile_ys_bytes(sf));
@@ -842,13 +847,13 @@ glm_stream_kernel(const GlmArgs a) {
   const bool live = tok < valid && f < last;
   const int64_t col = live ? (int64_t)f * kFrag : 0;
   const int64_t t = t0 + (live ? tok : 0);
-  u32x4 res[kStreams], part[TP > 0 ? TP : 1];
+  u32x4 res[kStreams], part[kHeld > 0 ? kHeld : 1];
 #pragma unroll
   for (int r = 0; r < kStreams; ++r)
     res[r] = live ? load_stream(a.residual + (t * kStreams + r) * H + col) : u32x4{0, 0, 0, 0};
-  if constexpr (TP > 0) {
+  if constexpr (kHeld > 0) {
 #pragma unroll
-    for (int r = 0; r < TP; ++r)
+    for (int r = 0; r < kHeld; ++r)
       part[r] = live ? load_stream(a.partials + r * a.rank_stride + t * H + col) : u32x4{0, 0, 0, 0};
   }
 #pragma unroll
@@ -866,7 +871,54 @@ glm_stream_kernel(const GlmArgs a) {
   float sum[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) sum[e] = 0.0f;
-  if constexpr (FIN) {
+  if constexpr (FIN && TP == 2) {
+    // a6 then a1, two ranks' gathers in flight at a time (top_k <= 8): the
+    // same contributions as finalize_fragment, added in rank order.
+    const int per = tp * a.fin.top_k, K = a.fin.top_k;
+    for (int r0 = 0; r0 < tp; r0 += 2) {
+      if (!live) break;
+      u32x4 rows[2][8], shv[2];
+      bool ok[2][8];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int r = r0 + q, o = tok * per + r * K;
+        const bool have = r < tp;
+        const uint16_t *g = a.fin.gemm2 + r * a.fin.g_stride + col;
+        shv[q] = have ? load_stream(a.fin.shared + r * a.fin.s_stride + t * H + col) : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int32_t row = have && k < K ? routes.row[o + k] : -1;
+          ok[q][k] = row >= 0 && row < a.fin.rows;
+          rows[q][k] = ok[q][k] ? load_stream(g + (int64_t)row * H) : u32x4{0, 0, 0, 0};
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        if (r0 + q >= tp) break;
+        const int o = tok * per + (r0 + q) * K;
+        float acc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          if (!ok[q][k]) continue;
+          const float w = routes.w[o + k];
+          float v[8];
+          unpack8(rows[q][k], v);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(v[e], w, acc[e]);
+        }
+        float sv[8];
+        unpack8(shv[q], sv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = acc[e] + sv[e];
+        float v[8];
+        unpack8(sanitize4(pack8(acc)), v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sum[e] = sum[e] + v[e];
+      }
+    }
+  } else if constexpr (FIN) {
     // a6 then a1: each rank's contribution (BF16, sanitized), added in rank
     // order.
     const int per = tp * a.fin.top_k;
@@ -878,9 +930,9 @@ glm_stream_kernel(const GlmArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) sum[e] = sum[e] + v[e];
     }
-  } else if constexpr (TP > 0) {
+  } else if constexpr (kHeld > 0) {
 #pragma unroll
-    for (int r = 0; r < TP; ++r) {
+    for (int r = 0; r < kHeld; ++r) {
       float v[8];
       unpack8(part[r], v);
 #pragma unroll
@@ -1170,7 +1222,11 @@ hipError_t launch_boundary_glm_two_pass(const GlmArgs &a, hipStream_t stream) {
   hipLaunchKernelGGL((glm_stream_kernel<TPP, FINN>), grid, block, lds, stream, a);
   if (a.fin.gemm2) {
     if (a.tp * a.fin.top_k > kGlmTileRoutes) return hipErrorInvalidValue;
-    MHCB_STREAM_LAUNCH(0, true)
+    if (a.tp > 1 && a.fin.top_k <= 8 && kTile * sf <= kStreamPairThreads) {
+      MHCB_STREAM_LAUNCH(2, true)
+    } else {
+      MHCB_STREAM_LAUNCH(0, true)
+    }
   } else if (a.tp == 8) {
     MHCB_STREAM_LAUNCH(8, false)
   } else if (a.tp == 4) {
