@@ -452,7 +452,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="",
                     help="comma-separated workloads to run alone for profiling (headline, sweep, "
-                         "finalize, glm, mxfp8, mailbox, copy); prints no JSON")
+                         "finalize, glm, mixes, glm_moe, mxfp8, mailbox, copy); prints no JSON")
     ap.add_argument("--slices", type=int, default=0,
                     help="workgroups per token for small-M calls (0 = the library's choice)")
     ap.add_argument("--eager", action="store_true",
@@ -549,7 +549,7 @@ def main():
                     ms, nbytes = bench_glm(torch, mhc, g, min(K, 100), min(W, 5), G)
                     extra[name] = entry(ms, nbytes, M)
                     log(f"glm M=64 tokens_per_wg={G}: {extra[name]}")
-    if want("glm") and not args.quick:
+    if want("mixes") and not args.quick:
         for M in (64, 512):  # a5: the side-stream mixes, alone and beside the boundary
             ms, nbytes = bench_mixes(torch, mhc, M, min(K, 100), min(W, 5))
             extra[f"glm_side_mixes_M{M}"] = entry(ms, nbytes, M)
@@ -558,7 +558,7 @@ def main():
             ms, nbytes = bench_glm_with_side_mixes(torch, mhc, g, min(K, 100), min(W, 5))
             extra[f"glm_M{M}_with_side_mixes"] = entry(ms, nbytes, M)
             log(f"glm M={M} + side mixes on a second stream: {extra[f'glm_M{M}_with_side_mixes']}")
-    if want("glm") and not args.quick:
+    if want("glm_moe") and not args.quick:
         for M in (64, 512):  # the GLM boundary of an MoE sublayer, H=6144 tp=4 top_k=8
             ms, nbytes = bench_glm_moe(torch, mhc, M, 6144, 4, 8, min(K, 100), min(W, 5))
             extra[f"glm_moe_tp4_k8_M{M}"] = entry(ms, nbytes, M)
