@@ -858,10 +858,13 @@ def test_delayed_random_shapes(case):
 
 
 @pytest.mark.parametrize("case", [(0, 5, 1024, 3, 1), (1, 33, 3072, 8, 2), (2, 2, 8192, 2, 4),
-                                  (3, 70, 512, 8, 16), (4, 300, 2048, 5, 0), (5, 17, 6144, 12, 16)],
+                                  (3, 70, 512, 8, 16), (4, 300, 2048, 5, 0), (5, 17, 6144, 12, 16),
+                                  (6, 45, 1536, 6, -16), (7, 129, 4096, 16, -16), (8, 7, 256, 7, -16)],
                          ids=lambda c: f"M{c[1]}-H{c[2]}-tp{c[3]}-G{c[4]}")
 def test_glm_random_shapes(case):
-    """GLM on mixed shapes, tokens per workgroup and tiles, against the oracle."""
+    """GLM on mixed shapes, tokens per workgroup, exchanging tiles and two
+    passes (-16; tp = 16 takes the runtime rank loop in two rounds of eight),
+    against the oracle."""
     i, M, H, tp, G = case
     g = synth.glm(M, H=H, tp=tp, name=f"glm-random-{i}")
     if G == 4 and H > 6144:
