@@ -52,6 +52,8 @@ _SIGNATURES = {
         _I, [_P, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _I, _I,
              _P, _P, _P, _P, _P, _F, _I, _I, _I, _I, _P, _P, _P, _P, _I]),
     "oracle_glm_mixes_token": (None, [_P, _P, _P, _P, _I, _F, _F, _P, _P]),
+    "oracle_glm_pre": (None, [_P, _P, _P, _F, _P]),
+    "oracle_glm_collapse_rmsnorm": (_I, [_P, _P, _P, _I, _F, _P]),
     "oracle_boundary_glm": (
         _I, [_P, _I64, _I, _P, _P, _P, _P, _P, _P, _P, _F, _F, _F, _I, _I, _P, _P, _P, _P, _I]),
     "oracle_sinkhorn": (None, [_P, _F, _I, _P]),
@@ -297,6 +299,35 @@ def glm_mixes_token(y, fn, scale, base, rms_eps, hc_eps):
     lib().oracle_glm_mixes_token(_ptr(y), _ptr(fn), _ptr(scale), _ptr(base), H, rms_eps, hc_eps,
                                  _ptr(mixes), _ptr(pre))
     return mixes, pre
+
+
+def glm_pre(mixes, scale, base, hc_eps):
+    """[GLM] _BoundaryDeviceKernel.kernel: pre [M, 4] from raw mixes [M, 24]
+    (only columns 0..3 are read): sigmoid(mixes_j * scale[0] + base[j]) + hc_eps."""
+    mixes = _c(mixes, np.float32).reshape(-1, 24)
+    scale = _c(scale, np.float32).reshape(3)
+    base = _c(base, np.float32).reshape(24)
+    pre = np.empty((mixes.shape[0], 4), np.float32)
+    f = lib().oracle_glm_pre
+    for t in range(mixes.shape[0]):
+        f(_ptr(mixes[t]), _ptr(scale), _ptr(base), hc_eps, _ptr(pre[t]))
+    return pre
+
+
+def glm_collapse_rmsnorm(y, pre, gamma, norm_eps):
+    """[GLM] _BoundaryDeviceKernel.kernel, the last steps: y [M, 4, H] u16
+    (the new streams), pre [M, 4] f32 -> layer input [M, H] u16, with the
+    pairwise collapse (q0+q1)+(q2+q3) and RMSNorm over H."""
+    y = _c(y, np.uint16)
+    M, _, H = y.shape
+    pre = _c(pre, np.float32).reshape(M, 4)
+    gamma = _c(gamma, np.uint16).reshape(H)
+    out = np.empty((M, H), np.uint16)
+    f = lib().oracle_glm_collapse_rmsnorm
+    for t in range(M):
+        _check(f(_ptr(y[t]), _ptr(pre[t]), _ptr(gamma), H, norm_eps, _ptr(out[t])),
+               "glm_collapse_rmsnorm")
+    return out
 
 
 def boundary_glm(partials, residual, post, comb, fn, scale, base, gamma, rms_eps, hc_eps,

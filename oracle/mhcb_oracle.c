@@ -493,12 +493,21 @@ typedef struct {
   uint16_t *layer_input;
 } glm_ctx;
 
+/* [GLM] _BoundaryDeviceKernel.kernel: the pre-mix of one token from its
+ * raw mixes, pre_j = sigmoid(mixes_j * scale[0] + base[j]) + hc_eps for the
+ * four streams (the product-sum is one FMA, reading R3). */
+void oracle_glm_pre(const float mixes[NMIX], const float *scale, const float *base,
+                    float hc_eps, float pre[NSTREAM]) {
+  for (int j = 0; j < NSTREAM; ++j)
+    pre[j] = oracle_sigmoid(fmaf(mixes[j], scale[0], base[j])) + hc_eps;
+}
+
 /* [GLM] _BoundaryDeviceKernel.kernel, after the post-mix of token t (y holds
  * its 4 x H new streams):
  *   g_k  = sum over j, c of fn[k][j*H + c] * y_j[c]      (k < 24)
  *   g_24 = sum over j, c of y_j[c]^2
  *   rstd = 1 / sqrt(g_24 / (4H) + rms_eps);  mixes_k = g_k * rstd
- *   pre_j = sigmoid(mixes_j * scale[0] + base[j]) + hc_eps   (FMA reading)
+ *   pre  = oracle_glm_pre(mixes)
  * The products of BF16 values are exact in binary64; the sums are binary64,
  * rounded to binary32 once. */
 void oracle_glm_mixes_token(const uint16_t *y, const uint16_t *fn, const float *scale,
@@ -515,16 +524,31 @@ void oracle_glm_mixes_token(const uint16_t *y, const uint16_t *fn, const float *
     }
   float rstd = inv_rms((float)g[NMIX], 4.0 * H, rms_eps);
   for (int k = 0; k < NMIX; ++k) mixes[k] = (float)g[k] * rstd;
-  for (int j = 0; j < NSTREAM; ++j)
-    pre[j] = oracle_sigmoid(fmaf(mixes[j], scale[0], base[j])) + hc_eps;
+  oracle_glm_pre(mixes, scale, base, hc_eps, pre);
+}
+
+/* [GLM] _BoundaryDeviceKernel.kernel, last steps of a token: its four new
+ * streams y [4][H] collapse with the pre-mix, p = bf16((q0+q1)+(q2+q3)),
+ * q_j = y_j * pre_j (collapse_glm), then RMSNorm over H with norm_weight
+ * (rmsnorm_token): out [H].  0 on success, 2 when out of memory. */
+int oracle_glm_collapse_rmsnorm(const uint16_t *y, const float pre[NSTREAM],
+                                const uint16_t *gamma, int H, float norm_eps, uint16_t *out) {
+  uint16_t *p = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)H);
+  if (!p) return 2;
+  for (int c = 0; c < H; ++c) {
+    uint16_t yc[NSTREAM];
+    for (int j = 0; j < NSTREAM; ++j) yc[j] = y[(int64_t)j * H + c];
+    p[c] = collapse_glm(yc, pre);
+  }
+  rmsnorm_token(p, gamma, H, norm_eps, out);
+  free(p);
+  return 0;
 }
 
 static void glm_tokens(void *arg, int t0, int t1) {
   glm_ctx *a = (glm_ctx *)arg;
   int H = a->H;
   uint16_t *y = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)NSTREAM * (size_t)H);
-  uint16_t *p = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)H);
-  uint16_t *out = (uint16_t *)malloc(sizeof(uint16_t) * (size_t)H);
   for (int t = t0; t < t1; ++t) {
     const float *post = a->post + (int64_t)t * NSTREAM;
     const float *comb = a->comb + (int64_t)t * NSTREAM * NSTREAM;
@@ -539,17 +563,9 @@ static void glm_tokens(void *arg, int t0, int t1) {
     oracle_glm_mixes_token(y, a->fn, a->scale, a->base, H, a->rms_eps, a->hc_eps, mixes, pre);
     memcpy(a->mixes_out + (int64_t)t * NMIX, mixes, sizeof mixes);
     if (a->pre_out) memcpy(a->pre_out + (int64_t)t * NSTREAM, pre, sizeof pre);
-    for (int c = 0; c < H; ++c) {
-      uint16_t yc[NSTREAM];
-      for (int j = 0; j < NSTREAM; ++j) yc[j] = y[(int64_t)j * H + c];
-      p[c] = collapse_glm(yc, pre);
-    }
-    rmsnorm_token(p, a->gamma, H, a->norm_eps, out);
-    memcpy(a->layer_input + (int64_t)t * H, out, sizeof(uint16_t) * (size_t)H);
+    oracle_glm_collapse_rmsnorm(y, pre, a->gamma, H, a->norm_eps, a->layer_input + (int64_t)t * H);
   }
   free(y);
-  free(p);
-  free(out);
 }
 
 /* [GLM] AllReduceMhcBoundary.__call__ with _BoundaryDeviceKernel: as
@@ -573,32 +589,44 @@ int oracle_boundary_glm(const uint16_t *partials, int64_t rank_stride, int tp,
 /* a5  side-stream mixes: post-mix and Sinkhorn residual mix                 */
 /* ------------------------------------------------------------------------ */
 
-/* [GLM] _MixesDeviceKernel._sinkhorn, on a 4x4 row-major matrix of logits:
- * each row is exponentiated after subtracting its max, scaled by the
- * reciprocal of its sum (q0+q1)+(q2+q3) and offset by eps (FMA reading);
- * then `repeat` rounds, each of which (except the first) divides every row
- * by its sum plus eps and then divides every column by its sum plus eps. */
+/* Sinkhorn-Knopp on a 4x4 matrix with an eps floor ([GLM]
+ * _MixesDeviceKernel._sinkhorn).  Mathematically: make every row a softmax
+ * of its logits (offset by eps), then alternately scale the columns and the
+ * rows so that each sums to one.  What the bits depend on, and is kept from
+ * the page: four entries are always added as (a + b) + (c + d); the softmax
+ * takes exp(x - rowmax), multiplies by the reciprocal of the row sum and
+ * adds eps in one fused step; every later normalization multiplies by the
+ * reciprocal of (sum + eps); the first round scales only the columns, each
+ * later round the rows and then the columns.  `repeat` counts the column
+ * steps (0: the softmax alone). */
+
+/* (a + b) + (c + d) over entries first, first + stride, ... of c. */
+static float pair_sum4(const float *c, int first, int stride) {
+  return (c[first] + c[first + stride]) + (c[first + 2 * stride] + c[first + 3 * stride]);
+}
+
+/* Scales the four entries first, first + stride, ... by 1/(their sum + eps). */
+static void normalize4(float *c, int first, int stride, float eps) {
+  float inv = oracle_rcp(pair_sum4(c, first, stride) + eps);
+  for (int i = 0; i < 4; ++i) c[first + i * stride] = c[first + i * stride] * inv;
+}
+
+/* Row r of the logits becomes fma(exp(x - max), 1/sum, eps). */
+static void softmax_row_eps(float *c, int r, float eps) {
+  float *row = c + 4 * r;
+  float peak = fmaxf(fmaxf(row[0], row[1]), fmaxf(row[2], row[3]));
+  for (int k = 0; k < 4; ++k) row[k] = oracle_exp(row[k] - peak);
+  float inv = oracle_rcp(pair_sum4(row, 0, 1));
+  for (int k = 0; k < 4; ++k) row[k] = fmaf(row[k], inv, eps);
+}
+
 void oracle_sinkhorn(const float logits[16], float eps, int repeat, float c[16]) {
   for (int i = 0; i < 16; ++i) c[i] = logits[i];
-  for (int r = 0; r < 4; ++r) {
-    float *row = c + 4 * r;
-    float peak = fmaxf(fmaxf(row[0], row[1]), fmaxf(row[2], row[3]));
-    for (int k = 0; k < 4; ++k) row[k] = oracle_exp(row[k] - peak);
-    float inv = oracle_rcp((row[0] + row[1]) + (row[2] + row[3]));
-    for (int k = 0; k < 4; ++k) row[k] = fmaf(row[k], inv, eps);
-  }
-  for (int it = 0; it < repeat; ++it) {
-    if (it > 0) {
-      for (int r = 0; r < 4; ++r) {
-        float *row = c + 4 * r;
-        float inv = oracle_rcp(((row[0] + row[1]) + (row[2] + row[3])) + eps);
-        for (int k = 0; k < 4; ++k) row[k] = row[k] * inv;
-      }
-    }
-    for (int k = 0; k < 4; ++k) {
-      float inv = oracle_rcp(((c[k] + c[4 + k]) + (c[8 + k] + c[12 + k])) + eps);
-      for (int r = 0; r < 4; ++r) c[4 * r + k] = c[4 * r + k] * inv;
-    }
+  for (int r = 0; r < 4; ++r) softmax_row_eps(c, r, eps);
+  for (int round = 0; round < repeat; ++round) {
+    if (round > 0)
+      for (int r = 0; r < 4; ++r) normalize4(c, 4 * r, 1, eps);  /* rows    */
+    for (int k = 0; k < 4; ++k) normalize4(c, k, 4, eps);        /* columns */
   }
 }
 

@@ -518,6 +518,97 @@ def test_glm_boundary_uses_its_own_pre_mix():
     assert np.array_equal(m2, mixes[1]) and np.array_equal(p2, pre[1])
 
 
+def test_glm_pre_from_mixes_closed_forms_and_slices():
+    """pre_j = sigmoid(mixes_j * scale[0] + base[j]) + hc_eps.  Arguments that
+    are exactly 0 give 1/2 + eps; sigma(x) + sigma(-x) = 1; only mixes[0:4],
+    scale[0] and base[0:4] are read; against float64 with the argument formed
+    from exact rationals and rounded once (the fused product-sum)."""
+    eps = 2.0 ** -10
+    mixes = np.zeros((1, 24), np.float32)
+    mixes[0, :4] = [2.0, -4.0, 0.5, 8.0]
+    scale = np.array([0.25, 9.0, 9.0], np.float32)
+    base = np.full(24, 7.0, np.float32)
+    base[:4] = [-0.5, 1.0, -0.125, -2.0]
+    assert (oracle.glm_pre(mixes, scale, base, eps) == np.float32(0.5 + eps)).all()
+
+    rng = np.random.default_rng(21)
+    mixes = (rng.standard_normal((40, 24)) * 3).astype(np.float32)
+    scale = rng.uniform(0.1, 0.4, 3).astype(np.float32)
+    base = rng.standard_normal(24).astype(np.float32)
+    pre = oracle.glm_pre(mixes, scale, base, 0.0)
+    neg = oracle.glm_pre(-mixes, scale, -base, 0.0)
+    assert np.abs(pre.astype(np.float64) + neg - 1.0).max() <= 2.0 ** -23
+    m2, s2, b2 = mixes.copy(), scale.copy(), base.copy()
+    m2[:, 4:] += 1.0
+    s2[1:] += 1.0
+    b2[4:] += 1.0
+    assert np.array_equal(oracle.glm_pre(m2, s2, b2, 0.0), pre)
+    for t in range(mixes.shape[0]):
+        for j in range(4):
+            x = f32(exact(mixes[t, j]) * exact(scale[0]) + exact(base[j]))
+            want = np.float32(1.0 / (1.0 + np.exp(-x)))
+            assert f32_ulp_distance(pre[t, j], want) <= 1
+
+
+def test_glm_collapse_rmsnorm_one_hot_pre_is_textbook_rmsnorm():
+    """pre = e_j: the pairwise collapse is y_j exactly (the other products
+    are zeros), and the layer input is the float64 textbook RMSNorm of y_j
+    times gamma within 1 BF16 ulp."""
+    rng = np.random.default_rng(22)
+    M, H = 3, 384
+    y = rand_bf16((M, 4, H), 1.0, rng)
+    gamma = rand_bf16(H, 1.0, rng)
+    for j in range(4):
+        pre = np.zeros((M, 4), np.float32)
+        pre[:, j] = 1.0
+        out = oracle.glm_collapse_rmsnorm(y, pre, gamma, 1e-6)
+        v = bf16_value(y[:, j]).astype(np.float64)
+        ref = v / np.sqrt((v ** 2).mean(axis=1, keepdims=True) + 1e-6) * bf16_value(gamma)
+        assert bf16_ulp_distance(out, torch_bf16(ref)).max() <= 1
+
+
+def test_glm_collapse_pairwise_designed_case():
+    """Streams (2, 2^-23, 2^-23, -2), pre 1/2: (q0+q1)+(q2+q3) = 2^-24, so
+    with eps = 0 and gamma = 1 every output is exactly 1.0; a sequential sum
+    (or FMA chain) would give 0 and a NaN output."""
+    H = 16
+    col = np.array([0x4000, 0x3400, 0x3400, 0xC000], np.uint16)
+    y = np.broadcast_to(col[None, :, None], (2, 4, H)).copy()
+    out = oracle.glm_collapse_rmsnorm(y, np.full((2, 4), 0.5, np.float32),
+                                      np.full(H, 0x3F80, np.uint16), 0.0)
+    assert (out == 0x3F80).all()
+
+
+def test_glm_collapse_exact_rational_and_textbook_rmsnorm():
+    """Random streams and pre-mixes: the collapse p = bf16((q0+q1)+(q2+q3)),
+    q_j = fl(y_j * pre_j), evaluated with exact rationals rounded at each
+    step, then the float64 textbook RMSNorm of p: within 1 BF16 ulp."""
+    rng = np.random.default_rng(23)
+    M, H = 2, 96
+    y = rand_bf16((M, 4, H), 1.0, rng)
+    pre = rng.uniform(0.0, 1.0, (M, 4)).astype(np.float32)
+    gamma = rand_bf16(H, 1.0, rng)
+    out = oracle.glm_collapse_rmsnorm(y, pre, gamma, 1e-6)
+    p = np.empty((M, H), np.float64)
+    for t in range(M):
+        for c in range(H):
+            q = [f32(exact(bf16_value(y[t, j, c])) * exact(pre[t, j])) for j in range(4)]
+            z = f32(exact(f32(exact(q[0]) + exact(q[1]))) + exact(f32(exact(q[2]) + exact(q[3]))))
+            p[t, c] = bf16_value(bf16_bits_of(exact(z)))
+    ref = p / np.sqrt((p ** 2).mean(axis=1, keepdims=True) + 1e-6) * bf16_value(gamma)
+    assert bf16_ulp_distance(out, torch_bf16(ref)).max() <= 1
+
+
+def test_glm_collapse_rmsnorm_is_the_last_step_of_boundary_glm():
+    """Fed the oracle's own streams and raw mixes, glm_pre and
+    glm_collapse_rmsnorm give the GLM boundary's pre-mix and layer input."""
+    g = synth.glm(3, H=256, tp=3)
+    ro, mixes, li, pre = oracle.boundary_glm(g.partials, g.residual, g.post, g.comb, g.fn, g.scale,
+                                             g.base, g.gamma, g.rms_eps, g.hc_eps, g.norm_eps)
+    assert np.array_equal(oracle.glm_pre(mixes, g.scale, g.base, g.hc_eps), pre)
+    assert np.array_equal(oracle.glm_collapse_rmsnorm(ro, pre, g.gamma, g.norm_eps), li)
+
+
 # ---------------------------------------------------------------------------
 # a5 sigmoid, post', Sinkhorn
 # ---------------------------------------------------------------------------
