@@ -32,6 +32,7 @@ METRIC = "fused reduce+mHC+RMSNorm: achieved HBM GB/s, tokens/s; µs/call at M=1
 HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 << 20
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "boundary_dsv41_M128_traffic.txt")
+TRACE_FILE = os.path.join(ROOT, "profiles", "boundary_dsv41_M128_trace.txt")
 
 
 def log(msg):
@@ -76,20 +77,35 @@ def source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic():
-    """HBM bytes per launch of the headline kernel from the committed
-    rocprofv3 counter summary, if it was taken on the current kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
+def profile_fields(path):
+    """The `key: value` lines of a committed rocprofv3 summary, if it was
+    taken on the current kernel sources (its source_hash matches)."""
+    if not os.path.exists(path):
         return None
     fields = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    if fields.get("source_hash") != source_hash():
-        return None
+    return fields if fields.get("source_hash") == source_hash() else None
+
+
+def measured_traffic():
+    """HBM bytes per launch of the headline kernel from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source."""
+    fields = profile_fields(TRAFFIC_FILE)
     try:
-        return float(fields["hbm_bytes_per_launch"])
+        return float(fields["hbm_bytes_per_launch"]) if fields else None
+    except (KeyError, ValueError):
+        return None
+
+
+def traced_kernel_us():
+    """(mean, median) duration in us of the headline kernel from the
+    committed rocprofv3 kernel trace, if it was taken on the current source."""
+    fields = profile_fields(TRACE_FILE)
+    try:
+        return (float(fields["kernel_mean_us"]), float(fields["kernel_median_us"])) if fields else None
     except (KeyError, ValueError):
         return None
 
@@ -198,7 +214,7 @@ def bench_delayed(torch, mhc, b, steps, warmup, mxfp8=False, check=False):
                           b.norm_eps)
 
     ms = Timed(torch, call, steps, warmup).run()
-    mhc.mhcb_workspace_status(ws)
+    mhc.workspace_status(ws)
     if check:
         # Every rotation set's output of the graph replay equals an eager call.
         for s in sets[:3]:
@@ -374,7 +390,8 @@ def bench_glm_with_side_mixes(torch, mhc, g, steps, warmup):
     def call(i):
         s = sets[i % len(sets)]
         cur = torch.cuda.current_stream()
-        cur.wait_stream(side)  # join the previous call's mixes
+        if i > 0:
+            cur.wait_stream(side)  # join the previous call's mixes (none before the first)
         mhc.mhcb_boundary_glm(s["partials"], g.M * g.H, s["residual"], s["post"], s["comb"], fn,
                               scale, base, gamma, s["residual_out"], s["mixes"], s["layer_input"],
                               ws, ws.numel(), g.M, g.H, 4, g.tp, g.rms_eps, g.hc_eps, g.norm_eps, 0)
@@ -436,9 +453,22 @@ def cpu_baseline(b, cpu_seconds=12.0, wall_cap_s=20.0):
     nbytes = bytes_delayed(b.M, b.H, b.tp)
     return {"value": round(nbytes / sec / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "tokens_per_s": round(b.M / sec, 1),
-            "us_per_call": round(sec * 1e6, 1),
+            "us_per_call": round(sec * 1e6, 1), "cpu_model": cpu_model(),
+            "host_cpus": os.cpu_count(),
             "sample": f"{reps} calls of the same workload ({b.name}), median wall time, "
                       f"{threads} threads, about {sum(times) * threads:.0f} s of CPU work"}
+
+
+def cpu_model():
+    """The host CPU's model name (/proc/cpuinfo), as lscpu reports it."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 # ---------------------------------------------------------------------------
@@ -484,6 +514,7 @@ def main():
         ms, nbytes, nsets = bench_delayed(torch, mhc, b, K, W, check=True)
         gbps = nbytes / (ms * 1e-3) / 1e9
         traffic = measured_traffic()
+        traced = traced_kernel_us()
         result.update({
             "metric": METRIC, "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": K,
             "warmup": W, "ms_per_step": round(ms, 6), "higher_is_better": True, "scaling": "weak",
@@ -494,7 +525,14 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBS, 4),
                          "traffic": traffic, "kernel": "boundary_kernel (delayed mHC, tp 8)",
-                         "algorithmic_bytes_per_launch": int(nbytes)},
+                         "algorithmic_bytes_per_launch": int(nbytes),
+                         # The same fraction from the committed kernel trace
+                         # (profiles/, mean launch duration under rocprofv3),
+                         # while it matches the current sources; else null.
+                         "frac_from_trace": (round(nbytes / (traced[0] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+                                             if traced else None),
+                         "trace_mean_us": traced[0] if traced else None,
+                         "trace_median_us": traced[1] if traced else None},
         })
         if not only:
             result["roofline"]["measured_copy_GBps"] = copy_bandwidth(torch)
@@ -507,9 +545,9 @@ def main():
 
     if want("sweep") and not args.quick:
         sweep = {}
-        for M in (1, 8, 32, 64, 128):
+        for M in (1, 8, 32, 64, 128, 256, 512, 1024, 2048, 4096):
             b = synth.dsv41_delayed(M)
-            ms, nbytes, _ = bench_delayed(torch, mhc, b, min(K, 200), W)
+            ms, nbytes, _ = bench_delayed(torch, mhc, b, min(K, 200 if M <= 512 else 50), W)
             sweep[f"M{M}"] = entry(ms, nbytes, M)
             log(f"sweep M={M}: {sweep[f'M{M}']}")
         result["sweep_dsv41_delayed"] = sweep

@@ -45,7 +45,9 @@ enum mhcb_status {
   MHCB_EALIGN = 2,       /* pointer or stride breaks the alignment rules     */
   MHCB_EUNSUPPORTED = 3, /* valid per the pages but not handled by libmhcb   */
   MHCB_ELAUNCH = 4,      /* the HIP runtime rejected a launch                */
-  MHCB_ETIMEOUT = 5      /* a mailbox poll gave up (see mhcb_mailbox_status) */
+  MHCB_ETIMEOUT = 5      /* a bounded wait gave up: the value a caller reports */
+                         /* once a status word (mhcb_workspace_status,       */
+                         /* mhcb_mailbox_status) reads non-zero              */
 };
 
 /* Message of the calling thread's last failed call ("" if none). */
@@ -69,43 +71,65 @@ int64_t mhcb_mxfp8_scale_bytes(int64_t M, int64_t hidden_size);
  * state is ready for the next call, with any slice count, with no reset at
  * the end.  Calls that may run concurrently (on different streams) must not
  * share a workspace.
+ * Co-residency: the workgroups of one token wait for one another (bounded
+ * by the workspace's spin limit).  They are dispatched consecutively, so on
+ * an otherwise idle device the wait ends as soon as the slowest one stores
+ * its value.  A kernel running concurrently that leaves fewer free
+ * workgroup slots than a token's slice count (at most 16) can keep a slice
+ * from starting until the others give up: those slices' results are then
+ * NaN and the time-out is counted (mhcb_workspace_status).
  * mhcb_workspace_bytes gives the size for a call: the sync state, then a
  * scratch area of at least 8 MiB that holds the per-slice partials of the
  * two-pass GLM tiles (mhcb_boundary_glm, tokens_per_wg = -16) or, when
  * larger, the two-shot emulation's (mhcb_finalize, two_shot = 1) owner
  * mailboxes [tp][tp][ceil(M/tp)][hidden] and reduced sums [M][hidden]
- * (BF16).  Host-only; -1 on bad sizes. */
+ * (BF16).  mhcb_finalize_workspace_bytes is the same function under the
+ * name the finalize call's documentation uses.  Host-only; -1 on bad
+ * sizes. */
 int64_t mhcb_workspace_bytes(int M, int hidden_size, int tp, int two_shot);
+int64_t mhcb_finalize_workspace_bytes(int M, int hidden_size, int tp, int two_shot);
 
 /* Writes the workspace's sync state (a kernel on `stream`): status word and
- * epochs zero, every exchange word the empty marker.  After a timed-out call
- * (see mhcb_workspace_status) the status stays set until the workspace is
- * initialized again. */
+ * epochs zero, the spin limit back to its default, every exchange word the
+ * empty marker.  After a timed-out call the status stays set until the
+ * workspace is initialized again. */
 int mhcb_workspace_init(void *workspace, int64_t workspace_bytes, hipStream_t stream);
 
-/* Synchronizes `stream`; MHCB_ETIMEOUT if a cross-workgroup wait of a call
- * that used this workspace gave up (bounded spin), else MHCB_OK. */
-int mhcb_workspace_status(const void *workspace, hipStream_t stream);
+/* Sets the number of re-reads after which a cross-workgroup wait of a call
+ * on this workspace gives up (a kernel on `stream`, ordered before later
+ * calls on it).  <= 0 restores the default, about a second of polling. */
+int mhcb_workspace_set_spin_limit(void *workspace, int64_t spin_limit, hipStream_t stream);
+
+/* Enqueues on `stream` a copy of the workspace's time-out count (cross-
+ * workgroup waits of calls on this workspace that gave up since
+ * mhcb_workspace_init) into *status_out: device memory, or pinned host
+ * memory the device can write.  Never synchronizes; read *status_out after
+ * the stream has reached that point. */
+int mhcb_workspace_status(const void *workspace, uint32_t *status_out, hipStream_t stream);
 
 /* Tuning: workgroups per token (or per GLM tile) for calls with a
  * workspace (1..64, of which the exchanging splits use at most 16 and the
  * two-pass GLM tiles at most 64; 0 = automatic, chosen by M from
- * measurements).
- * Process-wide; returns the previous value.  The BF16 sums, streams and the
- * delayed / finalize layer inputs do not depend on it; the GLM GEMV is
- * summed over the slices in FP32, so its raw mixes may change in the last
- * bits. */
+ * measurements).  Applies to the later calls of the calling thread only
+ * (thread-local; other threads keep their own setting); returns the
+ * calling thread's previous value.  The BF16 sums, streams and the delayed
+ * / finalize layer inputs do not depend on it; the GLM GEMV is summed over
+ * the slices in FP32, so its raw mixes may change in the last bits. */
 int mhcb_set_token_slices(int slices);
 
 /* Three-generation Lamport mailbox ([GLM] AllReduceMhcBoundary.__init__,
  * [DSV41] module text): slots[generation][rank][token][hidden] BF16, every
  * empty slot holding the sentinel 0x8000 (BF16 -0); stage_state = {ACTIVE,
- * NEXT}; status counts consumer polls that gave up.  All three pointers are
- * caller-owned device memory; the struct itself is read on the host only. */
+ * NEXT} of the rank that owns this view (on the pages every rank keeps its
+ * own; two descriptors may share `slots` with separate stage_state, as a
+ * peer publishing into this mailbox does); status[0] counts consumer polls
+ * that gave up, status[1] the fragments the consumer found still empty
+ * and re-read until they landed.  All three pointers are caller-owned
+ * device memory; the struct itself is read on the host only. */
 typedef struct mhcb_mailbox {
   uint16_t *slots;       /* [generations][tp][capacity][hidden_size]       */
   int32_t *stage_state;  /* [2]: ACTIVE, NEXT                              */
-  int32_t *status;       /* [1]: poll time-outs since mhcb_mailbox_init    */
+  int32_t *status;       /* [2]: poll time-outs, late fragments            */
   int generations;       /* must be 3                                      */
   int tp;                /* ranks                                          */
   int capacity;          /* max tokens per call                            */
@@ -123,7 +147,10 @@ typedef struct mhcb_mailbox {
  *             inv = 1/sqrt(sum_c p^2 / hidden + norm_eps)
  * Inputs: partials = tp BF16 [M, hidden] arrays rank_stride elements apart
  * (NULL iff mailbox is given: then the ACTIVE generation is polled until no
- * element is the sentinel, NEXT is advanced and the slots are reset);
+ * element is the sentinel, NEXT is advanced and the slots are reset; a
+ * fragment still empty after spin_limit re-reads is read as NaN, so that
+ * token's layer input and those columns of its residual_out come out NaN,
+ * and the time-out is counted in status[0]);
  * residual [M, hc, hidden] BF16; post, pre [M, hc] FP32; comb [M, hc, hc]
  * FP32 indexed [source][target]; norm_weight [hidden] BF16 (hc = hc_mult).
  * Outputs: residual_out [M, hc, hidden] = y; layer_input [M, hidden] = out;
@@ -281,9 +308,11 @@ int mhcb_mailbox_init(const mhcb_mailbox *mailbox, hipStream_t stream);
 int mhcb_publish(const mhcb_mailbox *mailbox, const uint16_t *partials, int64_t rank_stride,
                  int rank_begin, int rank_count, int M, hipStream_t stream);
 
-/* Synchronizes `stream`, then returns MHCB_ETIMEOUT if any consumer poll of
- * this mailbox gave up since mhcb_mailbox_init, else MHCB_OK. */
-int mhcb_mailbox_status(const mhcb_mailbox *mailbox, hipStream_t stream);
+/* Enqueues on `stream` a copy of the mailbox's two status words (poll
+ * time-outs and late fragments since mhcb_mailbox_init) into status_out[2]:
+ * device memory, or pinned host memory the device can write.  Never
+ * synchronizes. */
+int mhcb_mailbox_status(const mhcb_mailbox *mailbox, int32_t *status_out, hipStream_t stream);
 
 #ifdef __cplusplus
 }

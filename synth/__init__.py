@@ -6,8 +6,14 @@ tests take their inputs from here, and neither is imported by it.
 
 Draws use numpy's PCG64 generator (``numpy.random.default_rng``).  FP32 draws
 are stored as BF16 by round-to-nearest-even through torch's CPU conversion.
-Every workload is a pure function of (workload, M): the same call gives the
-same bits on any machine with this numpy.
+The delayed-boundary and GLM workloads draw each token's rows (partials,
+residual streams, mixes) from a generator seeded by (workload, shape, token)
+and the weights (norm weight, hc_fn, scale, base) from one seeded by
+(workload, shape): a workload at M tokens is the first M tokens of the same
+workload at any larger M, so an M sweep takes prefixes.  The MoE workload
+keeps one generator per (workload, M), because its row indices are a
+permutation of all M * top_k rows.  The same call gives the same bits on any
+machine with this numpy.
 
 The residual mix ``comb`` is a doubly stochastic 4x4 matrix per token:
 exp of N(0,1) logits followed by 20 rounds of textbook Sinkhorn-Knopp (row,
@@ -40,13 +46,44 @@ def _normal_bf16(rng, shape, std):
     return to_bf16_bits(rng.standard_normal(shape, dtype=np.float32) * np.float32(std))
 
 
-def doubly_stochastic(rng, m: int, rounds: int = 20, hc: int = HC) -> np.ndarray:
-    """[m, hc, hc] float32: Sinkhorn-Knopp (textbook, float64) of exp(N(0,1))."""
-    a = np.exp(rng.standard_normal((m, hc, hc)))
+def _token_rng(workload: int, shape: tuple, t: int) -> np.random.Generator:
+    return np.random.default_rng([workload, *shape, t])
+
+
+def _token_rows(workload, shape, M, tp, H, hc, partial_std, post_pre=True):
+    """Per-token draws: partials [tp, M, H] and residual [M, hc, H] as BF16
+    bits, post / pre [M, hc] U(0,1) (pre only with post_pre) and the
+    Sinkhorn logits of comb [M, hc, hc] N(0,1), token t from its own
+    generator."""
+    partials = np.empty((tp, M, H), np.float32)
+    residual = np.empty((M, hc, H), np.float32)
+    post = np.empty((M, hc), np.float32)
+    pre = np.empty((M, hc), np.float32)
+    logits = np.empty((M, hc, hc))
+    for t in range(M):
+        rng = _token_rng(workload, shape, t)
+        partials[:, t] = rng.standard_normal((tp, H), dtype=np.float32) * np.float32(partial_std)
+        residual[t] = rng.standard_normal((hc, H), dtype=np.float32)
+        post[t] = rng.uniform(0.0, 1.0, hc)
+        if post_pre:
+            pre[t] = rng.uniform(0.0, 1.0, hc)
+        logits[t] = rng.standard_normal((hc, hc))
+    return (to_bf16_bits(partials), to_bf16_bits(residual), post, pre,
+            sinkhorn_knopp(np.exp(logits)))
+
+
+def sinkhorn_knopp(a: np.ndarray, rounds: int = 20) -> np.ndarray:
+    """[m, hc, hc] positive float64 -> float32, textbook Sinkhorn-Knopp
+    (row, then column normalization, `rounds` times): an input recipe."""
     for _ in range(rounds):
         a = a / a.sum(axis=2, keepdims=True)
         a = a / a.sum(axis=1, keepdims=True)
     return a.astype(np.float32)
+
+
+def doubly_stochastic(rng, m: int, rounds: int = 20, hc: int = HC) -> np.ndarray:
+    """[m, hc, hc] float32: Sinkhorn-Knopp (textbook, float64) of exp(N(0,1))."""
+    return sinkhorn_knopp(np.exp(rng.standard_normal((m, hc, hc))), rounds)
 
 
 @dataclass
@@ -121,12 +158,11 @@ def _gamma(rng, h):
 
 def boundary(workload: int, M: int, H: int, tp: int, partial_std: float,
              name: str = "", hc: int = HC) -> Boundary:
-    """hc residual streams (4 unless given)."""
-    rng = _rng(workload, M)
-    partials = _normal_bf16(rng, (tp, M, H), partial_std)
-    residual = _normal_bf16(rng, (M, hc, H), 1.0)
-    post, comb, pre = _mixes(rng, M, hc)
-    gamma = _gamma(rng, H)
+    """hc residual streams (4 unless given); token t's rows depend only on
+    (workload, H, tp, hc, t), so smaller M are prefixes of larger ones."""
+    shape = (H, tp, hc)
+    partials, residual, post, pre, comb = _token_rows(workload, shape, M, tp, H, hc, partial_std)
+    gamma = _gamma(np.random.default_rng([workload, *shape]), H)
     return Boundary(name or f"boundary-H{H}-tp{tp}-M{M}", M, H, tp, partials, residual,
                     post, comb, pre, gamma)
 
@@ -150,12 +186,10 @@ def large_m_delayed(M: int = 8192) -> Boundary:
 
 
 def glm(M: int, H: int = 6144, tp: int = 8, name: str = "") -> Glm:
-    """GLM-style boundary: hc_fn N(0,0.02), scale U(0.1,0.4), base N(0,1)."""
-    rng = _rng(3, M * 100000 + H)
-    partials = _normal_bf16(rng, (tp, M, H), 0.5)
-    residual = _normal_bf16(rng, (M, HC, H), 1.0)
-    post = rng.uniform(0.0, 1.0, (M, HC)).astype(np.float32)
-    comb = doubly_stochastic(rng, M)
+    """GLM-style boundary: hc_fn N(0,0.02), scale U(0.1,0.4), base N(0,1);
+    token t's rows depend only on (H, tp, t), the weights on H."""
+    partials, residual, post, _, comb = _token_rows(3, (H, tp), M, tp, H, HC, 0.5, post_pre=False)
+    rng = np.random.default_rng([3, H])
     fn = _normal_bf16(rng, (MIX, HC * H), 0.02)
     scale = rng.uniform(0.1, 0.4, 3).astype(np.float32)
     base = rng.standard_normal(MIX).astype(np.float32)

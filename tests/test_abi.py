@@ -51,6 +51,44 @@ def test_host_only_helpers():
     prev = mhc.mhcb_set_token_slices(4)
     assert mhc.mhcb_set_token_slices(prev) == 4
     assert mhc.mhcb_version().count(".") == 2
+    for args in ((10, 512, 4, 0), (10, 512, 4, 1), (4096, 8192, 8, 1), (10, 512, 0, 1)):
+        assert mhc.mhcb_finalize_workspace_bytes(*args) == mhc.mhcb_workspace_bytes(*args)
+
+
+def test_token_slices_setting_is_per_thread():
+    """mhcb_set_token_slices changes the calling thread's setting only."""
+    import threading
+    import tp_reduce_mhc_amd as mhc
+    prev = mhc.mhcb_set_token_slices(7)
+    seen = {}
+
+    def other():
+        seen["initial"] = mhc.mhcb_set_token_slices(3)
+        seen["own"] = mhc.mhcb_set_token_slices(0)
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen == {"initial": 0, "own": 3}
+    assert mhc.mhcb_set_token_slices(prev) == 7
+
+
+def test_status_and_spin_limit_validation():
+    """The status reads and the spin-limit setter validate before launching."""
+    import tp_reduce_mhc_amd as mhc
+    with pytest.raises(mhc.MhcbError, match="required"):
+        mhc.mhcb_workspace_status(FAKE, None, 0)
+    with pytest.raises(mhc.MhcbError, match="required"):
+        mhc.mhcb_workspace_status(None, FAKE, 0)
+    with pytest.raises(mhc.MhcbError, match="256-byte"):
+        mhc.mhcb_workspace_status(FAKE + 16, FAKE, 0)
+    with pytest.raises(mhc.MhcbError, match="required"):
+        mhc.mhcb_workspace_set_spin_limit(None, 5, 0)
+    mb = mhc.mhcb_mailbox(FAKE, FAKE, FAKE, 3, 2, 8, 512, 0)
+    with pytest.raises(mhc.MhcbError, match="required"):
+        mhc.mhcb_mailbox_status(mb, None, 0)
+    with pytest.raises(mhc.MhcbError, match="aligned"):
+        mhc.mhcb_mailbox_status(mb, FAKE + 2, 0)
 
 
 FAKE = 0x10000  # an aligned non-null address; validation fails before any use of it

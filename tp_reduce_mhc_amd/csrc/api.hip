@@ -40,7 +40,6 @@ constexpr int kMaxHidden = 16384;
 constexpr int kMaxHiddenGlm = 8192;
 constexpr int kMaxTp = 64;
 constexpr int kMaxRoutes = 1024;
-constexpr int64_t kDefaultSpin = 1 << 20;
 constexpr int kGlmTileMinM = 256;  // automatic matrix-core tiles from this M
 constexpr int kGlmTwoPassMinM = 1;  // automatic two-pass tiles from this M
 
@@ -88,7 +87,7 @@ int check_mailbox(const char *fn, const mhcb_mailbox *mb, int H, int tp, int M) 
   return MHCB_OK;
 }
 
-int g_slices_override = 0;  // mhcb_set_token_slices (0 = automatic)
+thread_local int g_slices_override = 0;  // mhcb_set_token_slices (0 = automatic), per calling thread
 
 // Compute units of the current device (cached per device).
 int device_cus() {
@@ -118,9 +117,9 @@ int check_workspace(const char *fn, const void *ws, int64_t bytes, int64_t need)
 SyncView sync_view(void *ws) {
   char *b = static_cast<char *>(ws);
   SyncView v;
-  v.status = reinterpret_cast<uint32_t *>(b);
+  v.status = reinterpret_cast<uint32_t *>(b + kHeaderStatus);
+  v.limit = reinterpret_cast<const int64_t *>(b + kHeaderSpinLimit);
   v.slots = b + 256;
-  v.spin_limit = 1 << 20;
   return v;
 }
 
@@ -269,15 +268,28 @@ int mhcb_workspace_init(void *workspace, int64_t workspace_bytes, hipStream_t st
   return launched(launch_sync_init(workspace, stream), fn);
 }
 
-int mhcb_workspace_status(const void *workspace, hipStream_t stream) {
-  const char *fn = "mhcb_workspace_status";
+int64_t mhcb_finalize_workspace_bytes(int M, int hidden_size, int tp, int two_shot) {
+  return mhcb_workspace_bytes(M, hidden_size, tp, two_shot);
+}
+
+int mhcb_workspace_set_spin_limit(void *workspace, int64_t spin_limit, hipStream_t stream) {
+  const char *fn = "mhcb_workspace_set_spin_limit";
   if (!workspace) return fail(MHCB_EINVAL, "%s: workspace is required", fn);
-  hipError_t e = hipStreamSynchronize(stream);
-  uint32_t status = 0;
-  if (e == hipSuccess) e = hipMemcpy(&status, workspace, sizeof status, hipMemcpyDeviceToHost);
-  if (e != hipSuccess) return fail(MHCB_ELAUNCH, "%s: %s", fn, hipGetErrorString(e));
-  if (status) return fail(MHCB_ETIMEOUT, "%s: %u cross-workgroup wait(s) gave up", fn, status);
-  return ok();
+  if (!aligned(workspace, 256)) return fail(MHCB_EALIGN, "%s: workspace must be 256-byte aligned", fn);
+  return launched(launch_store_word64(reinterpret_cast<int64_t *>(static_cast<char *>(workspace) +
+                                                                  kHeaderSpinLimit),
+                                      spin_limit, stream),
+                  fn);
+}
+
+int mhcb_workspace_status(const void *workspace, uint32_t *status_out, hipStream_t stream) {
+  const char *fn = "mhcb_workspace_status";
+  if (!workspace || !status_out) return fail(MHCB_EINVAL, "%s: workspace and status_out are required", fn);
+  if (!aligned(workspace, 256) || !aligned(status_out, 4))
+    return fail(MHCB_EALIGN, "%s: workspace must be 256-byte aligned, status_out 4-byte", fn);
+  return launched(launch_copy_words(static_cast<const uint32_t *>(workspace) + kHeaderStatus / 4,
+                                    status_out, 1, stream),
+                  fn);
 }
 
 int mhcb_set_token_slices(int slices) {
@@ -647,15 +659,15 @@ int mhcb_publish(const mhcb_mailbox *mailbox, const uint16_t *partials, int64_t 
                                  rank_count, M, stream), fn);
 }
 
-int mhcb_mailbox_status(const mhcb_mailbox *mailbox, hipStream_t stream) {
+int mhcb_mailbox_status(const mhcb_mailbox *mailbox, int32_t *status_out, hipStream_t stream) {
   const char *fn = "mhcb_mailbox_status";
-  if (!mailbox || !mailbox->status) return fail(MHCB_EINVAL, "%s: mailbox status word is required", fn);
-  hipError_t e = hipStreamSynchronize(stream);
-  int32_t status = 0;
-  if (e == hipSuccess) e = hipMemcpy(&status, mailbox->status, sizeof status, hipMemcpyDeviceToHost);
-  if (e != hipSuccess) return fail(MHCB_ELAUNCH, "%s: %s", fn, hipGetErrorString(e));
-  if (status != 0) return fail(MHCB_ETIMEOUT, "%s: %d mailbox poll(s) gave up", fn, status);
-  return ok();
+  if (!mailbox || !mailbox->status || !status_out)
+    return fail(MHCB_EINVAL, "%s: the mailbox status words and status_out are required", fn);
+  if (!aligned(mailbox->status, 4) || !aligned(status_out, 4))
+    return fail(MHCB_EALIGN, "%s: status words must be 4-byte aligned", fn);
+  return launched(launch_copy_words(reinterpret_cast<const uint32_t *>(mailbox->status),
+                                    reinterpret_cast<uint32_t *>(status_out), 2, stream),
+                  fn);
 }
 
 }  // extern "C"

@@ -71,19 +71,28 @@ __device__ __forceinline__ void accumulate(float (&s)[8], u32x4 w) {
   for (int e = 0; e < 8; ++e) s[e] = s[e] + v[e];
 }
 
-// Waits until no element of a mailbox fragment is the sentinel, with a
-// bounded number of re-reads; a time-out is counted in `status` and the
-// fragment is used as read.
-__device__ __forceinline__ u32x4 poll(const uint16_t *p, u32x4 w, const MailboxView &mb) {
+__device__ __forceinline__ bool fragment_has_sentinel(u32x4 w) {
+  return has_sentinel(w[0]) || has_sentinel(w[1]) || has_sentinel(w[2]) || has_sentinel(w[3]);
+}
+
+// Waits until no element of a mailbox fragment is the sentinel, re-reading
+// it at device scope at most spin_limit times.  A fragment still not all
+// there then reads as BF16 NaN, so the token's results come out NaN rather
+// than wrong, and the time-out is counted in status[0].  With `count`, a
+// fragment that had to be re-read is counted in status[1].
+__device__ __forceinline__ u32x4 poll(const uint16_t *p, u32x4 w, const MailboxView &mb,
+                                      bool count) {
+  if (!fragment_has_sentinel(w)) return w;
+  if (count) atomicAdd(mb.status + 1, 1);
   int64_t spins = 0;
-  while ((has_sentinel(w[0]) || has_sentinel(w[1]) || has_sentinel(w[2]) || has_sentinel(w[3]))) {
+  do {
     if (++spins > mb.spin_limit) {
       atomicAdd(mb.status, 1);
-      break;
+      return u32x4{kPoisonBf16x2, kPoisonBf16x2, kPoisonBf16x2, kPoisonBf16x2};
     }
     __builtin_amdgcn_s_sleep(1);
     w = load_agent(p);
-  }
+  } while (fragment_has_sentinel(w));
   return w;
 }
 
@@ -169,9 +178,8 @@ __device__ float token_inv(const BoundaryArgs &a, int t, int s, double ss, doubl
     if (a.slices > 1) {
       char *slot = token_slot(a.sync, t);
       const SlotCall c = unpack_call(callw);
-      char *area = slot + copy_offset(c.epoch);
-      if (lane == 0) slot_store64(area, kCopySum1 + 8 * s, total);
-      total = wave_gather_sum64(a.sync, area, kCopySum1, a.slices);
+      if (lane == 0 && !c.broken) slot_store64(slot + copy_offset(c.epoch), kCopySum1 + 8 * s, total);
+      total = wave_gather_sum64(a.sync, slot, c, kCopySum1, a.slices);  // NaN if broken
       if (lane == 0) advance_epoch(slot, c, a.slices);  // after this slice's last read
     }
     if (lane == 0)
@@ -292,14 +300,22 @@ boundary_kernel(const BoundaryArgs a) {
                                             t, H, col[i]));
       } else if constexpr (TP > 0) {
         if constexpr (SRC == Source::kMailbox) {
-          // Slow path only for fragments that are not all there yet.
+          // Slow path only for fragments that are not all there yet; a wave
+          // counts its late fragments with one atomic.
           bool dirty = false;
+          int late = 0;  // the wave's late fragments (ballots: uniform over the active lanes)
 #pragma unroll
-          for (int r = 0; r < TP; ++r)
-#pragma unroll
-            for (int k = 0; k < 4; ++k) dirty |= has_sentinel(part[i][r][k]);
-          if (dirty) {
-            for (int r = 0; r < TP; ++r) part[i][r] = poll(src + r * rs + col[i], part[i][r], a.mailbox);
+          for (int r = 0; r < TP; ++r) {
+            const bool d = fragment_has_sentinel(part[i][r]);
+            dirty |= d;
+            late += __popcll(__ballot(d));
+          }
+          if (late) {
+            const uint64_t act = __ballot(true);
+            if ((tid & (kWave - 1)) == __builtin_ctzll(act)) atomicAdd(a.mailbox.status + 1, late);
+            if (dirty)
+              for (int r = 0; r < TP; ++r)
+                part[i][r] = poll(src + r * rs + col[i], part[i][r], a.mailbox, false);
           }
         }
 #pragma unroll
@@ -308,7 +324,7 @@ boundary_kernel(const BoundaryArgs a) {
         for (int r = 0; r < tp; ++r) {
           const uint16_t *p = src + r * rs + col[i];
           u32x4 w = load_stream(p);
-          if constexpr (SRC == Source::kMailbox) w = poll(p, w, a.mailbox);
+          if constexpr (SRC == Source::kMailbox) w = poll(p, w, a.mailbox, true);
           accumulate(sum, w);
         }
       }
@@ -548,7 +564,8 @@ mailbox_init_kernel(MailboxView mb, int64_t frags) {
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     mb.stage_state[0] = 0;
     mb.stage_state[1] = 0;
-    *mb.status = 0;
+    mb.status[0] = 0;
+    mb.status[1] = 0;
   }
 }
 
@@ -621,6 +638,15 @@ quant_kernel(const uint16_t *x, uint8_t *values, uint8_t *scales, int M, int H) 
   }
 }
 
+__global__ void __launch_bounds__(64) copy_words_kernel(const uint32_t *src, uint32_t *dst, int count) {
+  if ((int)threadIdx.x < count)
+    dst[threadIdx.x] = __hip_atomic_load(src + threadIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ void __launch_bounds__(64) store_word64_kernel(int64_t *dst, int64_t value) {
+  if (threadIdx.x == 0) __hip_atomic_store(dst, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __global__ void __launch_bounds__(256) zero_kernel(uint32_t *p, int64_t words) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words;
        i += (int64_t)gridDim.x * blockDim.x)
@@ -658,6 +684,17 @@ hipError_t launch_sync_init(void *workspace, hipStream_t stream) {
   const int64_t words = kSyncBytes / 4;
   hipLaunchKernelGGL(sync_init_kernel, dim3(grid_for(words, 256)), dim3(256), 0, stream,
                      static_cast<uint32_t *>(workspace), words);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_words(const uint32_t *src, uint32_t *dst, int count, hipStream_t stream) {
+  if (count < 1 || count > 64) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(copy_words_kernel, dim3(1), dim3(64), 0, stream, src, dst, count);
+  return hipGetLastError();
+}
+
+hipError_t launch_store_word64(int64_t *dst, int64_t value, hipStream_t stream) {
+  hipLaunchKernelGGL(store_word64_kernel, dim3(1), dim3(64), 0, stream, dst, value);
   return hipGetLastError();
 }
 

@@ -20,6 +20,7 @@ constexpr int kTokenThreads = 512;  // workgroup size bound of the per-token ker
 constexpr int kTokenThreadsWide = 1024;  // the same with one fragment per thread
 constexpr int kTokenThreadsWide8 = 768;  // the same for eight residual streams
 constexpr uint16_t kSentinel = 0x8000;  // BF16 negative zero marks an empty slot
+constexpr uint32_t kPoisonBf16x2 = 0x7FC07FC0u;  // two BF16 quiet NaNs
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));

@@ -117,9 +117,12 @@ __device__ __forceinline__ int needed_pair(const RowList &l, int S, int j) {
   return S == 1 || j < 2 ? j : needed_row(l, S, j + 2) >> 1;
 }
 
-// A token's exchange area for this call, from its slot's epoch word.
-__device__ __forceinline__ char *call_area(const GlmArgs &a, int t, uint64_t callw) {
-  return token_slot(a.sync, t) + copy_offset(unpack_call(callw).epoch);
+// Stores one 8-byte value into token t's exchange area of this call (from
+// its slot's epoch word), unless the slot is broken.
+__device__ __forceinline__ void call_store(const GlmArgs &a, int t, uint64_t callw, int offset,
+                                           uint64_t v) {
+  const SlotCall c = unpack_call(callw);
+  if (!c.broken) slot_store_u64(token_slot(a.sync, t) + copy_offset(c.epoch), offset, v);
 }
 
 template <int G>
@@ -148,7 +151,7 @@ __device__ void exchange(const GlmArgs &a, GlmShared<G> &sh, int t0, int s, doub
       if (t0 + g < a.M) {
         const uint64_t w = (uint64_t)__builtin_bit_cast(uint32_t, sh.mix[g][2 * p]) |
                            ((uint64_t)__builtin_bit_cast(uint32_t, sh.mix[g][2 * p + 1]) << 32);
-        slot_store_u64(call_area(a, t0 + g, sh.callw[g]), kCopyRows + kRowsEntry * s + 8 * p, w);
+        call_store(a, t0 + g, sh.callw[g], kCopyRows + kRowsEntry * s + 8 * p, w);
       }
     }
   }
@@ -156,7 +159,7 @@ __device__ void exchange(const GlmArgs &a, GlmShared<G> &sh, int t0, int s, doub
     double v = 0.0;  // sums[tid], without indexing a register array at run time
 #pragma unroll
     for (int g = 0; g < G; ++g) v = g == tid ? sums[g] : v;
-    slot_store64(call_area(a, t0 + tid, sh.callw[tid]), sum + 8 * s, v);
+    call_store(a, t0 + tid, sh.callw[tid], sum + 8 * s, __builtin_bit_cast(uint64_t, v));
   }
   if (rows) {
     const RowList l = row_list(S, s);
@@ -165,7 +168,8 @@ __device__ void exchange(const GlmArgs &a, GlmShared<G> &sh, int t0, int s, doub
       if (j >= pair_count(l, S) || t0 + g >= a.M) continue;
       const int p = needed_pair(l, S, j);
       uint64_t w[kMaxSlices];
-      gather64(a.sync, call_area(a, t0 + g, sh.callw[g]), kCopyRows + 8 * p, kRowsEntry, S, w);
+      gather64(a.sync, token_slot(a.sync, t0 + g), unpack_call(sh.callw[g]), kCopyRows + 8 * p,
+               kRowsEntry, S, w);
       float lo = 0.0f, hi = 0.0f;
 #pragma unroll
       for (int q = 0; q < kMaxSlices; ++q) {
@@ -178,7 +182,8 @@ __device__ void exchange(const GlmArgs &a, GlmShared<G> &sh, int t0, int s, doub
     }
   }
   if (tid < G)
-    sh.tot[tid] = t0 + tid < a.M ? gather_sum64(a.sync, call_area(a, t0 + tid, sh.callw[tid]), sum, S)
+    sh.tot[tid] = t0 + tid < a.M ? gather_sum64(a.sync, token_slot(a.sync, t0 + tid),
+                                                unpack_call(sh.callw[tid]), sum, S)
                                  : 0.0;
   __syncthreads();
 #pragma unroll
@@ -461,10 +466,11 @@ __device__ void tile_exchange(const GlmArgs &a, TileShared &sh, int t0, int s, i
       const int tok = e / kPairs, p = e % kPairs;
       const uint64_t w = (uint64_t)__builtin_bit_cast(uint32_t, sh.mix[tok][2 * p]) |
                          ((uint64_t)__builtin_bit_cast(uint32_t, sh.mix[tok][2 * p + 1]) << 32);
-      slot_store_u64(call_area(a, t0 + tok, sh.callw[tok]), kCopyRows + kRowsEntry * s + 8 * p, w);
+      call_store(a, t0 + tok, sh.callw[tok], kCopyRows + kRowsEntry * s + 8 * p, w);
     }
   }
-  if (tid < valid) slot_store64(call_area(a, t0 + tid, sh.callw[tid]), sum + 8 * s, sh.tot[tid]);
+  if (tid < valid)
+    call_store(a, t0 + tid, sh.callw[tid], sum + 8 * s, __builtin_bit_cast(uint64_t, sh.tot[tid]));
   __syncthreads();  // every thread has read its own sh values before they are replaced
   // Work items: the row pairs this slice needs of each token (with rows; a
   // stride of 12 per token keeps them within one pass), then the sums.
@@ -476,7 +482,8 @@ __device__ void tile_exchange(const GlmArgs &a, TileShared &sh, int t0, int s, i
       if (j >= np) continue;
       const int p = needed_pair(l, S, j);
       uint64_t w[kMaxSlices];
-      gather64(a.sync, call_area(a, t0 + tok, sh.callw[tok]), kCopyRows + 8 * p, kRowsEntry, S, w);
+      gather64(a.sync, token_slot(a.sync, t0 + tok), unpack_call(sh.callw[tok]), kCopyRows + 8 * p,
+               kRowsEntry, S, w);
       float lo = 0.0f, hi = 0.0f;
 #pragma unroll
       for (int q = 0; q < kMaxSlices; ++q) {
@@ -488,7 +495,8 @@ __device__ void tile_exchange(const GlmArgs &a, TileShared &sh, int t0, int s, i
       sh.mix[tok][2 * p + 1] = hi;
     } else {
       const int tok = e - row_items;
-      sh.tot[tok] = gather_sum64(a.sync, call_area(a, t0 + tok, sh.callw[tok]), sum, S);
+      sh.tot[tok] = gather_sum64(a.sync, token_slot(a.sync, t0 + tok), unpack_call(sh.callw[tok]),
+                                 sum, S);
     }
   }
   __syncthreads();

@@ -17,7 +17,7 @@ enum class Source : int {
 struct MailboxView {
   uint16_t *slots;       // [3][tp][capacity][H]
   int32_t *stage_state;  // [ACTIVE, NEXT]
-  int32_t *status;       // poll time-outs
+  int32_t *status;       // [2]: polls that gave up, fragments that were re-read
   int capacity;
   int64_t spin_limit;
 };
@@ -70,10 +70,16 @@ constexpr int kGlmMaxParts = 64;    // slices of at least 16 fragments, H <= 819
 constexpr int kGlmTileRoutes = 128; // tp * top_k a two-pass MoE tile stages in LDS
 constexpr int64_t kGlmPartBytes = (int64_t)kSyncTokens * kGlmMaxParts * kPartWords * 4;  // 8 MiB
 
+// The workspace header (its first 256 bytes): the time-out count, then the
+// spin limit of the cross-workgroup waits (re-reads before a wait gives up;
+// 0 or less: kDefaultSpin), which mhcb_workspace_set_spin_limit writes.
+constexpr int kHeaderStatus = 0, kHeaderSpinLimit = 8;
+constexpr int64_t kDefaultSpin = 1 << 20;  // about a second of polling
+
 struct SyncView {
-  uint32_t *status;   // cross-workgroup waits that gave up
-  char *slots;        // [kSyncTokens][kSyncSlot]
-  int64_t spin_limit;
+  uint32_t *status;       // header: cross-workgroup waits that gave up
+  const int64_t *limit;   // header: spin limit
+  char *slots;            // [kSyncTokens][kSyncSlot]
 };
 
 struct BoundaryArgs {
@@ -164,5 +170,9 @@ inline Geometry token_geometry(int H) { return fragment_geometry(H / 8); }
 
 hipError_t launch_zero(void *p, int64_t bytes, hipStream_t stream);
 hipError_t launch_sync_init(void *workspace, hipStream_t stream);
+// Stream-ordered copy of `count` 32-bit words (status reads that never
+// synchronize), and a store of one 64-bit word.
+hipError_t launch_copy_words(const uint32_t *src, uint32_t *dst, int count, hipStream_t stream);
+hipError_t launch_store_word64(int64_t *dst, int64_t value, hipStream_t stream);
 
 }  // namespace mhcb

@@ -61,8 +61,10 @@ _SIGNATURES = {
     "mhcb_version": (ctypes.c_char_p, []),
     "mhcb_mxfp8_scale_bytes": (_I64, [_I64, _I64]),
     "mhcb_workspace_bytes": (_I64, [_I, _I, _I, _I]),
+    "mhcb_finalize_workspace_bytes": (_I64, [_I, _I, _I, _I]),
     "mhcb_workspace_init": (_I, [_P, _I64, _P]),
-    "mhcb_workspace_status": (_I, [_P, _P]),
+    "mhcb_workspace_set_spin_limit": (_I, [_P, _I64, _P]),
+    "mhcb_workspace_status": (_I, [_P, _P, _P]),
     "mhcb_set_token_slices": (_I, [_I]),
     "mhcb_boundary": (_I, [_P, _I64, _MB, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64,
                            _I, _I, _I, _I, _F, _P]),
@@ -80,7 +82,7 @@ _SIGNATURES = {
     "mhcb_quant_mxfp8": (_I, [_P, _P, _P, _I, _I, _P]),
     "mhcb_mailbox_init": (_I, [_MB, _P]),
     "mhcb_publish": (_I, [_MB, _P, _I64, _I, _I, _I, _P]),
-    "mhcb_mailbox_status": (_I, [_MB, _P]),
+    "mhcb_mailbox_status": (_I, [_MB, _P, _P]),
 }
 
 for _name, (_res, _args) in _SIGNATURES.items():
@@ -138,17 +140,38 @@ def mhcb_workspace_bytes(M: int, hidden_size: int, tp: int, two_shot: int) -> in
     return _lib.mhcb_workspace_bytes(M, hidden_size, tp, int(two_shot))
 
 
+def mhcb_finalize_workspace_bytes(M: int, hidden_size: int, tp: int, two_shot: int) -> int:
+    return _lib.mhcb_finalize_workspace_bytes(M, hidden_size, tp, int(two_shot))
+
+
 def mhcb_workspace_init(workspace, workspace_bytes, stream=None) -> None:
     _check(_lib.mhcb_workspace_init(_ptr(workspace), workspace_bytes, _stream(stream)))
 
 
-def mhcb_workspace_status(workspace, stream=None) -> int:
-    rc = _lib.mhcb_workspace_status(_ptr(workspace), _stream(stream))
-    _check(rc)
-    return rc
+def mhcb_workspace_set_spin_limit(workspace, spin_limit, stream=None) -> None:
+    _check(_lib.mhcb_workspace_set_spin_limit(_ptr(workspace), spin_limit, _stream(stream)))
+
+
+def mhcb_workspace_status(workspace, status_out, stream=None) -> None:
+    """Enqueues a copy of the workspace's time-out count into status_out
+    (a one-element int32/uint32 device tensor); never synchronizes."""
+    _check(_lib.mhcb_workspace_status(_ptr(workspace), _ptr(status_out), _stream(stream)))
+
+
+def workspace_status(workspace, stream=None) -> int:
+    """MHCB_OK, or raises MhcbError(ETIMEOUT) when a cross-workgroup wait of
+    a call on `workspace` gave up.  Waits for `stream` (the helper reads the
+    copied word on the host)."""
+    out = torch.zeros(1, dtype=torch.int32, device=workspace.device)
+    mhcb_workspace_status(workspace, out, stream)
+    n = int(out.item())
+    if n:
+        raise MhcbError(MHCB_ETIMEOUT, f"{n} cross-workgroup wait(s) gave up")
+    return MHCB_OK
 
 
 def mhcb_set_token_slices(slices: int) -> int:
+    """Per calling thread (the library keeps the setting thread-local)."""
     return _lib.mhcb_set_token_slices(slices)
 
 
@@ -223,11 +246,21 @@ def mhcb_publish(mailbox, partials, rank_stride, rank_begin, rank_count, M, stre
                              _stream(stream)))
 
 
-def mhcb_mailbox_status(mailbox, stream=None) -> int:
-    """Synchronizes the stream; returns MHCB_OK or raises MhcbError(ETIMEOUT)."""
-    rc = _lib.mhcb_mailbox_status(_mb(mailbox), _stream(stream))
-    _check(rc)
-    return rc
+def mhcb_mailbox_status(mailbox, status_out, stream=None) -> None:
+    """Enqueues a copy of the mailbox's two status words (poll time-outs,
+    late fragments) into status_out (two int32 on the device)."""
+    _check(_lib.mhcb_mailbox_status(_mb(mailbox), _ptr(status_out), _stream(stream)))
+
+
+def mailbox_status(mailbox, stream=None):
+    """(poll time-outs, late fragments) since mhcb_mailbox_init; waits for
+    `stream`."""
+    m = mailbox.struct if isinstance(mailbox, Mailbox) else mailbox
+    device = mailbox.status.device if isinstance(mailbox, Mailbox) else "cuda"
+    out = torch.zeros(2, dtype=torch.int32, device=device)
+    _check(_lib.mhcb_mailbox_status(ctypes.byref(m), _ptr(out), _stream(stream)))
+    timeouts, late = (int(v) for v in out.tolist())
+    return timeouts, late
 
 
 # ---------------------------------------------------------------------------
@@ -242,27 +275,35 @@ _WORKSPACES = {}
 
 
 def workspace(device=None, *, M: int = 0, hidden_size: int = 0, tp: int = 1,
-              two_shot: bool = False, nbytes: int = 0) -> torch.Tensor:
-    """An initialized workspace on `device`, cached per (device, size):
-    the sync state of the token-split calls, plus the two-shot scratch when
-    asked.  Calls on different streams need their own (fresh=True is not
-    offered: allocate with new_workspace)."""
+              two_shot: bool = False, nbytes: int = 0, stream=None) -> torch.Tensor:
+    """An initialized workspace of at least the size the arguments ask for
+    (mhcb_workspace_bytes, or nbytes if larger), one per (device, stream):
+    calls on one stream are ordered, so they may share it, and calls on
+    different streams get different ones.  The cached workspace only grows:
+    a larger request replaces it (allocated and initialized on `stream`),
+    so memory stays bounded by the largest call."""
     device = torch.device(device if device is not None else "cuda")
     if device.index is None:
         device = torch.device("cuda", torch.cuda.current_device())
     need = max(mhcb_workspace_bytes(M, hidden_size, tp, int(two_shot)), nbytes)
-    key = (device.index, need)
+    handle = _stream(stream) or 0
+    key = (device.index, handle)
     ws = _WORKSPACES.get(key)
-    if ws is None:
-        ws = new_workspace(need, device)
+    if ws is None or ws.numel() < need:
+        ws = new_workspace(need, device, stream)
         _WORKSPACES[key] = ws
     return ws
 
 
 def new_workspace(nbytes: int, device, stream=None) -> torch.Tensor:
-    """A fresh workspace of `nbytes` (256-byte aligned by torch), initialized
-    by mhcb_workspace_init on `stream` (the current stream by default)."""
-    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    """A fresh workspace of `nbytes` (256-byte aligned by torch), allocated
+    for and initialized by mhcb_workspace_init on `stream` (the current
+    stream by default)."""
+    if stream is not None and not isinstance(stream, int):
+        with torch.cuda.stream(stream):
+            ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    else:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
     mhcb_workspace_init(ws, nbytes, stream)
     return ws
 
@@ -279,7 +320,7 @@ def boundary(partials: torch.Tensor, residual, post, comb, pre, norm_weight, nor
     tp, M, H = partials.shape
     hc = residual.shape[1]
     dev = partials.device
-    ws = workspace(dev) if split else None
+    ws = workspace(dev, stream=stream) if split else None
     residual_out = _bf16_empty((M, hc, H), dev)
     layer_input = None if pre is None else _bf16_empty((M, H), dev)
     values = scales = None
@@ -300,7 +341,7 @@ def boundary_glm(partials, residual, post, comb, hc_fn, scale, base, norm_weight
     residual_out = _bf16_empty((M, 4, H), dev)
     mixes = torch.empty((M, 24), dtype=torch.float32, device=dev)
     layer_input = _bf16_empty((M, H), dev)
-    ws = workspace(dev)
+    ws = workspace(dev, stream=stream)
     mhcb_boundary_glm(partials, M * H if tp > 1 else 0, residual, post, comb, hc_fn, scale, base,
                       norm_weight, residual_out, mixes, layer_input, ws, ws.numel(), M, H, 4, tp,
                       rms_eps, hc_eps, norm_eps, tokens_per_wg, stream)
@@ -343,7 +384,7 @@ def finalize_glm(gemm2, weights, idx, shared, residual, post, comb, hc_fn, scale
     residual_out = _bf16_empty((M, 4, H), dev)
     mixes_out = torch.empty((M, 24), dtype=torch.float32, device=dev)
     layer_input = _bf16_empty((M, H), dev)
-    ws = workspace(dev, nbytes=mhcb_finalize_glm_workspace_bytes(M, H, tp))
+    ws = workspace(dev, nbytes=mhcb_finalize_glm_workspace_bytes(M, H, tp), stream=stream)
     mhcb_finalize_glm(gemm2, rows * H, rows, weights, M * top_k if per_rank else 0,
                       weights.dtype == torch.bfloat16, routed_scaling_factor, idx,
                       M * top_k if per_rank else 0, shared, M * H, residual, post, comb, hc_fn,
@@ -380,7 +421,8 @@ def finalize(gemm2, weights, idx, shared, residual, post, comb, pre, norm_weight
     if mxfp8:
         values = torch.empty((M, H), dtype=torch.uint8, device=dev)
         scales = torch.empty(mhcb_mxfp8_scale_bytes(M, H), dtype=torch.uint8, device=dev)
-    ws = workspace(dev, M=M, hidden_size=H, tp=tp, two_shot=True) if (two_shot or split) else None
+    ws = (workspace(dev, M=M, hidden_size=H, tp=tp, two_shot=two_shot, stream=stream)
+          if (two_shot or split) else None)
     mhcb_finalize_ex(gemm2, rows * H, rows, weights, M * top_k if per_rank else 0,
                      weights.dtype == torch.bfloat16, routed_scaling_factor, idx,
                      M * top_k if per_rank else 0, shared, M * H, residual, post, comb, pre,
@@ -404,7 +446,7 @@ class Mailbox:
     def __init__(self, tp: int, capacity: int, hidden_size: int, device, spin_limit: int = 0):
         self.slots = torch.empty((3, tp, capacity, hidden_size), dtype=torch.bfloat16, device=device)
         self.stage_state = torch.zeros(2, dtype=torch.int32, device=device)
-        self.status = torch.zeros(1, dtype=torch.int32, device=device)
+        self.status = torch.zeros(2, dtype=torch.int32, device=device)
         self.struct = mhcb_mailbox(self.slots.data_ptr(), self.stage_state.data_ptr(),
                                    self.status.data_ptr(), 3, tp, capacity, hidden_size, spin_limit)
         self.tp, self.capacity, self.hidden_size = tp, capacity, hidden_size
@@ -429,14 +471,29 @@ class Mailbox:
         if mxfp8:
             values = torch.empty((M, H), dtype=torch.uint8, device=dev)
             scales = torch.empty(mhcb_mxfp8_scale_bytes(M, H), dtype=torch.uint8, device=dev)
-        ws = workspace(dev)
+        ws = workspace(dev, stream=stream)
         mhcb_boundary(None, 0, self, residual, post, comb, pre, norm_weight, residual_out,
                       layer_input, values, scales, ws, ws.numel(), M, H, hc, self.tp, norm_eps,
                       stream)
         return residual_out, layer_input, ((values, scales) if mxfp8 else None)
 
+    def peer_view(self) -> "Mailbox":
+        """A second descriptor of the same slots with its own stage state and
+        status words: the view a peer rank publishes through (on the pages
+        each rank advances its own stage state)."""
+        peer = Mailbox.__new__(Mailbox)
+        peer.slots = self.slots
+        peer.stage_state = torch.zeros_like(self.stage_state)
+        peer.status = torch.zeros_like(self.status)
+        peer.struct = mhcb_mailbox(self.slots.data_ptr(), peer.stage_state.data_ptr(),
+                                   peer.status.data_ptr(), 3, self.tp, self.capacity,
+                                   self.hidden_size, self.struct.spin_limit)
+        peer.tp, peer.capacity, peer.hidden_size = self.tp, self.capacity, self.hidden_size
+        return peer
+
     def status_ok(self, stream=None) -> bool:
-        return mhcb_mailbox_status(self, stream) == MHCB_OK
+        """True when no consumer poll of this mailbox gave up; waits for `stream`."""
+        return mailbox_status(self, stream)[0] == 0
 
 
 class GlmBoundary:
