@@ -205,6 +205,28 @@ int mhcb_boundary_glm(const uint16_t *partials, int64_t rank_stride, const uint1
                       int hc_mult, int tp, float rms_eps, float hc_eps, float norm_eps,
                       int tokens_per_wg, hipStream_t stream);
 
+/* mhcb_boundary_glm for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * arguments without a workspace, always the two-pass 16-token tiles
+ * (tokens_per_wg = -16; the same kernels, so the results are bit-identical
+ * to mhcb_boundary_glm with a workspace of mhcb_workspace_bytes bytes).
+ * Their per-slice partials go to a static device array of 8 MiB that the
+ * library holds on each GPU it runs on until the process ends; the call
+ * itself allocates and frees nothing.  Every call on a GPU shares that
+ * GPU's array: calls that may overlap on one GPU (concurrent streams, or
+ * with this library's other users of the array) race and must be ordered
+ * by the caller.  A launch takes at most 1024 tokens (larger M is issued as
+ * several launches on `stream`) and hidden <= 8192 (EUNSUPPORTED beyond), so
+ * its partials (at most 1024 x 64 x 128 bytes) always fit the array.  The
+ * first call on a device looks up the array's address there. */
+int mhcb_boundary_glm_noalloc(const uint16_t *partials, int64_t rank_stride,
+                              const uint16_t *residual, const float *post, const float *comb,
+                              const uint16_t *hc_fn, const float *scale, const float *base,
+                              const uint16_t *norm_weight, uint16_t *residual_out,
+                              float *mixes_out, uint16_t *layer_input, int M, int hidden_size,
+                              int hc_mult, int tp, float rms_eps, float hc_eps, float norm_eps,
+                              hipStream_t stream);
+
 /* Side-stream mixes for the next boundary ([GLM] _MixesDeviceKernel):
  *   post_out[t][j] = sigmoid(mixes[t][4+j] * scale[1] + base[4+j]) * post_mult
  *   comb_out[t]    = Sinkhorn(mixes[t][8+i] * scale[2] + base[8+i]), 4x4

@@ -5,12 +5,21 @@
 #include <stdio.h>
 
 #include <cmath>
+#include <mutex>
 
 #include "../../include/mhcb.h"
 #include "device.h"
 #include "kernels.h"
 
 using namespace mhcb;
+
+// Scratch of mhcb_boundary_glm_noalloc, for callers that cannot allocate:
+// a file-scope device array, one copy per GPU the library runs on, held
+// until the process ends.  Host code never passes `scratch` itself to a
+// kernel (on the host the name is only a stand-in): static_scratch() looks
+// up each device's address once with hipGetSymbolAddress and keeps it.
+constexpr int64_t kScratchBytes = mhcb::kGlmPartBytes;  // 8 MiB
+static __device__ __align__(256) char scratch[kScratchBytes];
 
 namespace {
 
@@ -148,14 +157,20 @@ void choose_slices(BoundaryArgs &a, void *ws, int target, int max_slices) {
   if (a.slices > 1) a.sync = sync_view(ws);
 }
 
+// The per-slice partials of the two-pass GLM tiles in a workspace: after
+// its sync state.
+float *workspace_parts(void *workspace) {
+  return reinterpret_cast<float *>(static_cast<char *>(workspace) + kSyncBytes);
+}
+
 // The two-pass GLM tiles on validated arguments: slices of sf fragments (a
-// multiple of 4, 16..64), partials in the workspace after the sync state,
-// launches of at most kSyncTokens tokens.
+// multiple of 4, 16..64), partials in `parts` (kGlmPartBytes, reused by
+// every launch), launches of at most kSyncTokens tokens.
 int glm_two_pass(const char *fn, const uint16_t *partials, int64_t rank_stride,
                  const uint16_t *residual, const float *post, const float *comb,
                  const uint16_t *hc_fn, const float *scale, const float *base,
                  const uint16_t *norm_weight, uint16_t *residual_out, float *mixes_out,
-                 uint16_t *layer_input, void *workspace, int M, int hidden_size, int tp,
+                 uint16_t *layer_input, float *parts, int M, int hidden_size, int tp,
                  float rms_eps, float hc_eps, float norm_eps, const FinalizeView *fin,
                  hipStream_t stream) {
   const int F = hidden_size / kFrag;
@@ -167,8 +182,7 @@ int glm_two_pass(const char *fn, const uint16_t *partials, int64_t rank_stride,
   sf = sf < 16 ? 16 : sf > 64 ? 64 : sf;
   GlmArgs a = {(F + sf - 1) / sf, sf, SyncView{}, partials, rank_stride, tp, residual, post, comb,
                hc_fn, scale, base, norm_weight, residual_out, mixes_out, layer_input, M,
-               hidden_size, rms_eps, hc_eps, norm_eps, kGlmTileTokens,
-               reinterpret_cast<float *>(static_cast<char *>(workspace) + kSyncBytes)};
+               hidden_size, rms_eps, hc_eps, norm_eps, kGlmTileTokens, parts};
   if (fin) a.fin = *fin;  // the ranks' contributions from MoE routes (partials unused)
   const int64_t H = hidden_size;
   for (int c = 0; c < M; c += kSyncTokens) {
@@ -224,6 +238,29 @@ int check_routes(const char *fn, const uint16_t *gemm2_permuted, int64_t gemm2_r
   return MHCB_OK;
 }
 
+// Checks of the GLM boundary's arguments ([GLM] AllReduceMhcBoundary.__call__),
+// shared by its entry points.
+int check_glm(const char *fn, const uint16_t *partials, int64_t rank_stride,
+              const uint16_t *residual, const float *post, const float *comb,
+              const uint16_t *hc_fn, const float *scale, const float *base,
+              const uint16_t *norm_weight, const uint16_t *residual_out, const float *mixes_out,
+              const uint16_t *layer_input, int M, int hidden_size, int hc_mult, int tp) {
+  if (!partials || !hc_fn || !scale || !base || !norm_weight || !mixes_out || !layer_input)
+    return fail(MHCB_EINVAL, "%s: partials, hc_fn, scale, base, norm_weight, mixes_out and layer_input are required", fn);
+  // The GLM pre-mix is derived in-kernel from scale/base: check the normalized path.
+  int rc = check_common(fn, residual, post, comb, scale, norm_weight, residual_out, layer_input,
+                        nullptr, nullptr, M, hidden_size, hc_mult, tp, false);
+  if (rc) return rc;
+  if (hidden_size > kMaxHiddenGlm)
+    return fail(MHCB_EUNSUPPORTED, "%s: hidden_size=%d exceeds %d", fn, hidden_size, kMaxHiddenGlm);
+  if (tp > 1 && rank_stride < (int64_t)M * hidden_size && rank_stride != 0)
+    return fail(MHCB_EINVAL, "%s: rank_stride=%lld overlaps a rank's [M, hidden] block", fn, (long long)rank_stride);
+  if (!aligned(partials, 16) || rank_stride % kFrag || !aligned(hc_fn, 16) || !aligned(base, 4) ||
+      !aligned(mixes_out, 4))
+    return fail(MHCB_EALIGN, "%s: partials/hc_fn must be 16-byte aligned, rank_stride %% 8 == 0", fn);
+  return MHCB_OK;
+}
+
 MailboxView view_of(const mhcb_mailbox *mb) {
   MailboxView v;
   v.slots = mb->slots;
@@ -232,6 +269,29 @@ MailboxView view_of(const mhcb_mailbox *mb) {
   v.capacity = mb->capacity;
   v.spin_limit = mb->spin_limit > 0 ? mb->spin_limit : kDefaultSpin;
   return v;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch` (looked up on its first use).
+int static_scratch(const char *fn, float **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MHCB_ELAUNCH, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MHCB_EUNSUPPORTED, "%s: device %d beyond the %d the library tracks", fn, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(MHCB_ELAUNCH, "%s: hipGetSymbolAddress(scratch): %s", fn, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = static_cast<float *>(g_scratch_ptr[dev]);
+  return MHCB_OK;
 }
 
 }  // namespace
@@ -352,20 +412,10 @@ int mhcb_boundary_glm(const uint16_t *partials, int64_t rank_stride, const uint1
                       float rms_eps, float hc_eps, float norm_eps, int tokens_per_wg,
                       hipStream_t stream) {
   const char *fn = "mhcb_boundary_glm";
-  if (!partials || !hc_fn || !scale || !base || !norm_weight || !mixes_out || !layer_input)
-    return fail(MHCB_EINVAL, "%s: partials, hc_fn, scale, base, norm_weight, mixes_out and layer_input are required", fn);
-  // The GLM pre-mix is derived in-kernel from scale/base: check the normalized path.
-  int rc = check_common(fn, residual, post, comb, scale, norm_weight, residual_out, layer_input,
-                        nullptr, nullptr, M, hidden_size, hc_mult, tp, false);
+  int rc = check_glm(fn, partials, rank_stride, residual, post, comb, hc_fn, scale, base,
+                     norm_weight, residual_out, mixes_out, layer_input, M, hidden_size, hc_mult, tp);
   if (rc) return rc;
   if ((rc = check_workspace(fn, workspace, workspace_bytes, kSyncBytes))) return rc;
-  if (hidden_size > kMaxHiddenGlm)
-    return fail(MHCB_EUNSUPPORTED, "%s: hidden_size=%d exceeds %d", fn, hidden_size, kMaxHiddenGlm);
-  if (tp > 1 && rank_stride < (int64_t)M * hidden_size && rank_stride != 0)
-    return fail(MHCB_EINVAL, "%s: rank_stride=%lld overlaps a rank's [M, hidden] block", fn, (long long)rank_stride);
-  if (!aligned(partials, 16) || rank_stride % kFrag || !aligned(hc_fn, 16) || !aligned(base, 4) ||
-      !aligned(mixes_out, 4))
-    return fail(MHCB_EALIGN, "%s: partials/hc_fn must be 16-byte aligned, rank_stride %% 8 == 0", fn);
   int G = tokens_per_wg;
   // Automatic: two-pass tiles whenever the workspace holds their scratch
   // (measured on MI355X, H=6144, tp=8, us per call, the previous automatic
@@ -379,8 +429,9 @@ int mhcb_boundary_glm(const uint16_t *partials, int64_t rank_stride, const uint1
     if (!workspace || workspace_bytes < need)
       return fail(MHCB_EINVAL, "%s: tokens_per_wg=-16 needs a workspace of %lld bytes", fn, (long long)need);
     return glm_two_pass(fn, partials, rank_stride, residual, post, comb, hc_fn, scale, base,
-                        norm_weight, residual_out, mixes_out, layer_input, workspace, M,
-                        hidden_size, tp, rms_eps, hc_eps, norm_eps, nullptr, stream);
+                        norm_weight, residual_out, mixes_out, layer_input,
+                        workspace_parts(workspace), M, hidden_size, tp, rms_eps, hc_eps, norm_eps,
+                        nullptr, stream);
   }
   // Measured on MI355X (H=6144, tp=8): one token per workgroup below M=256
   // (M=128: 18.8 us; 16-token tiles: 22.3), 16-token tiles from M=256
@@ -455,6 +506,31 @@ int mhcb_boundary_glm(const uint16_t *partials, int64_t rank_stride, const uint1
   return launched(launch_boundary_glm(a, stream), fn);
 }
 
+int mhcb_boundary_glm_noalloc(const uint16_t *partials, int64_t rank_stride,
+                              const uint16_t *residual, const float *post, const float *comb,
+                              const uint16_t *hc_fn, const float *scale, const float *base,
+                              const uint16_t *norm_weight, uint16_t *residual_out,
+                              float *mixes_out, uint16_t *layer_input, int M, int hidden_size,
+                              int hc_mult, int tp, float rms_eps, float hc_eps, float norm_eps,
+                              hipStream_t stream) {
+  const char *fn = "mhcb_boundary_glm_noalloc";
+  int rc = check_glm(fn, partials, rank_stride, residual, post, comb, hc_fn, scale, base,
+                     norm_weight, residual_out, mixes_out, layer_input, M, hidden_size, hc_mult, tp);
+  if (rc) return rc;
+  // The two-pass tiles' partials of one launch: at most kSyncTokens tokens
+  // x kGlmMaxParts slices of kPartWords words; hidden_size <= 8192 keeps
+  // the slices within kGlmMaxParts.
+  const int64_t need = (int64_t)kSyncTokens * kGlmMaxParts * kPartWords * 4;
+  if (need > kScratchBytes)
+    return fail(MHCB_EINVAL, "%s: needs %lld bytes of scratch, the static array holds %lld", fn,
+                (long long)need, (long long)kScratchBytes);
+  float *parts = nullptr;
+  if ((rc = static_scratch(fn, &parts))) return rc;
+  return glm_two_pass(fn, partials, rank_stride, residual, post, comb, hc_fn, scale, base,
+                      norm_weight, residual_out, mixes_out, layer_input, parts, M, hidden_size, tp,
+                      rms_eps, hc_eps, norm_eps, nullptr, stream);
+}
+
 int64_t mhcb_finalize_glm_workspace_bytes(int M, int hidden_size, int tp) {
   if (M < 0 || hidden_size < 0 || tp < 1) return -1;
   return kSyncBytes + kGlmPartBytes + (int64_t)tp * M * hidden_size * 2;
@@ -495,15 +571,16 @@ int mhcb_finalize_glm(const uint16_t *gemm2_permuted, int64_t gemm2_rank_stride,
   // boundary on them as its rank partials.
   if ((int64_t)tp * top_k <= kGlmTileRoutes)
     return glm_two_pass(fn, nullptr, 0, residual, post, comb, hc_fn, scale, base, norm_weight,
-                        residual_out, mixes_out, layer_input, workspace, M, hidden_size, tp,
-                        rms_eps, hc_eps, norm_eps, &f, stream);
+                        residual_out, mixes_out, layer_input, workspace_parts(workspace), M,
+                        hidden_size, tp, rms_eps, hc_eps, norm_eps, &f, stream);
   uint16_t *contrib = reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) + kSyncBytes +
                                                    kGlmPartBytes);
   if ((rc = launched(launch_finalize_to_owners(f, tp, 1, M, hidden_size, contrib, stream), fn)))
     return rc;
   return glm_two_pass(fn, contrib, (int64_t)M * hidden_size, residual, post, comb, hc_fn, scale,
-                      base, norm_weight, residual_out, mixes_out, layer_input, workspace, M,
-                      hidden_size, tp, rms_eps, hc_eps, norm_eps, nullptr, stream);
+                      base, norm_weight, residual_out, mixes_out, layer_input,
+                      workspace_parts(workspace), M, hidden_size, tp, rms_eps, hc_eps, norm_eps,
+                      nullptr, stream);
 }
 
 int mhcb_mixes(const float *mixes, const float *scale, const float *base, float *post_out,

@@ -70,6 +70,8 @@ _SIGNATURES = {
                            _I, _I, _I, _I, _F, _P]),
     "mhcb_boundary_glm": (_I, [_P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I64,
                                _I, _I, _I, _I, _F, _F, _F, _I, _P]),
+    "mhcb_boundary_glm_noalloc": (_I, [_P, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I,
+                                       _I, _I, _F, _F, _F, _P]),
     "mhcb_mixes": (_I, [_P, _P, _P, _P, _P, _I, _I, _F, _F, _I, _P]),
     "mhcb_finalize": (_I, [_P, _I64, _I64, _P, _I64, _P, _I64, _P, _I64, _P, _P, _P, _P, _P, _P,
                            _P, _P, _P, _I, _P, _I64, _I, _I, _I, _I, _I, _F, _P]),
@@ -194,6 +196,16 @@ def mhcb_boundary_glm(partials, rank_stride, residual, post, comb, hc_fn, scale,
                                   _ptr(residual_out), _ptr(mixes_out), _ptr(layer_input),
                                   _ptr(workspace), workspace_bytes, M, hidden_size, hc_mult, tp,
                                   rms_eps, hc_eps, norm_eps, tokens_per_wg, _stream(stream)))
+
+
+def mhcb_boundary_glm_noalloc(partials, rank_stride, residual, post, comb, hc_fn, scale, base,
+                              norm_weight, residual_out, mixes_out, layer_input, M, hidden_size,
+                              hc_mult, tp, rms_eps, hc_eps, norm_eps, stream=None) -> None:
+    _check(_lib.mhcb_boundary_glm_noalloc(_ptr(partials), rank_stride, _ptr(residual), _ptr(post),
+                                          _ptr(comb), _ptr(hc_fn), _ptr(scale), _ptr(base),
+                                          _ptr(norm_weight), _ptr(residual_out), _ptr(mixes_out),
+                                          _ptr(layer_input), M, hidden_size, hc_mult, tp, rms_eps,
+                                          hc_eps, norm_eps, _stream(stream)))
 
 
 def mhcb_mixes(mixes, scale, base, post_out, comb_out, M, hc_mult, hc_eps, post_mult,
