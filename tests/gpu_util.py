@@ -115,8 +115,10 @@ def glm_layer_input_check(got_li, ref_li, y, pre_ref, pre_got, gamma, norm_eps):
 
 # Secondary GLM layer-input check against the oracle's own pre-mix: at most
 # this fraction of the elements may be 2 or more BF16 ulps away (inside the
-# tie-aware band); the strict check is on the kernel's own pre-mix.
-GLM_TWO_ULP_CAP = 2e-4
+# tie-aware band); the strict check is on the kernel's own pre-mix.  The
+# largest fraction measured over the GPU suite is 1.2e-5 (6 of 491,520 at
+# M=300 in the exchanging tiles).
+GLM_TWO_ULP_CAP = 5e-5
 
 
 def mixes_error_stats(mixes, mix_ref):
@@ -142,6 +144,10 @@ def check_glm_outputs(what, ro, mixes, li, ro_ref, mix_ref, li_ref, pre_ref, sca
     assert_bits_equal(ro, ro_ref, f"residual_out {what}")
     err = np.abs(mixes.astype(np.float64) - mix_ref)
     assert (err <= 1e-5 * (np.abs(mix_ref) + 1)).all(), f"mixes {what}: max err {err.max()}"
+    # Relative error of each token's mix vector (norm-wise), the bar that
+    # does not depend on how close a single entry is to a cancelling zero.
+    norm_rel = np.linalg.norm(err, axis=1) / np.maximum(np.linalg.norm(mix_ref, axis=1), 1e-30)
+    assert norm_rel.max() <= 1e-5, f"mixes {what}: norm-wise relative error {norm_rel.max():.2e}"
     pre_k = oracle.glm_pre(mixes, scale, base, hc_eps)
     want = oracle.glm_collapse_rmsnorm(ro, pre_k, gamma, norm_eps)
     off = assert_within_ulp(li, want, 1, f"GLM layer_input {what} (oracle on the kernel's pre-mix)")
@@ -151,8 +157,8 @@ def check_glm_outputs(what, ro, mixes, li, ro_ref, mix_ref, li_ref, pre_ref, sca
     assert two <= cap, f"GLM layer_input {what}: {two} elements 2+ ulps from the oracle (cap {cap})"
     abs_err, rel_err = mixes_error_stats(mixes, mix_ref)
     stats = dict(strict_off=off, vs_oracle_1ulp=one, vs_oracle_2ulp=two, elements=int(li.size),
-                 mix_abs=abs_err, mix_rel=rel_err)
+                 mix_abs=abs_err, mix_rel=rel_err, mix_norm_rel=float(norm_rel.max()))
     print(f"[gpu]   {what}: layer_input vs oracle-on-kernel-pre: {off} off by 1 ulp; vs oracle: "
           f"{one} at 1 ulp, {two} at 2+ of {li.size}; mixes max abs {abs_err:.2e}, "
-          f"max rel (|ref|>=0.01) {rel_err:.2e}", flush=True)
+          f"max rel (|ref|>=0.01) {rel_err:.2e}, norm-wise {norm_rel.max():.2e}", flush=True)
     return stats
