@@ -563,12 +563,15 @@ def test_glm_tiles_more_tokens_than_one_launch():
 @pytest.mark.parametrize("M,H,tp,S", [(1, 6144, 8, 0), (17, 6144, 8, 0), (40, 2048, 3, 0),
                                       (33, 512, 8, 0), (16, 8192, 8, 0), (5, 1024, 1, 0),
                                       (3, 64, 2, 0), (20, 2048, 8, 4), (20, 2048, 4, 8),
-                                      (37, 6144, 8, 48), (19, 6144, 4, 16)])
+                                      (37, 6144, 8, 48), (19, 6144, 4, 16),
+                                      (600, 2048, 8, 0), (333, 6144, 8, 0), (200, 8192, 4, 0),
+                                      (400, 6144, 8, 48), (1100, 6144, 4, 0), (250, 1000, 8, 0)])
 def test_glm_two_pass_tiles_match_oracle(M, H, tp, S):
     """16-token tiles in two passes (tokens_per_wg=-16): a stream pass that
     leaves per-slice partials in the workspace, then one workgroup per token.
     Slices of 16 to 64 fragments, ragged last slices and tiles, fixed (4, 8)
-    and runtime rank counts."""
+    and runtime rank counts, tile counts that are not multiples of eight and
+    more tokens than one launch takes."""
     g = synth.glm(M, H=H, tp=tp)
     prev = mhc.mhcb_set_token_slices(S)
     try:
