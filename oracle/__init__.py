@@ -11,6 +11,7 @@ arrays.  BF16 arrays are ``numpy.uint16`` bit patterns.
 Sources (web pages, cited by title and section in ``mhcb_oracle.c``):
   vllm.models.glm5next.nvidia.specialized_decode.all_reduce_mhc        (GLM)
   vllm.models.deepseek_v41.nvidia.ops.cute_dsl.all_reduce_mhc          (DSV4.1)
+  vllm.models.glm5next.nvidia.specialized_decode.indexer               (indexer)
 
 Every function here is pinned by ``tests/test_oracle_pins.py``.
 """
@@ -59,6 +60,7 @@ _SIGNATURES = {
     "oracle_sinkhorn": (None, [_P, _F, _I, _P]),
     "oracle_side_mixes": (_I, [_P, _P, _P, _I, _F, _F, _I, _P, _P]),
     "oracle_quant_mxfp8": (_I, [_P, _I, _I, _P, _P]),
+    "oracle_indexer_projection": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P]),
 }
 
 
@@ -403,3 +405,21 @@ def quant_mxfp8(x):
     rc = lib().oracle_quant_mxfp8(_ptr(x), M, H, _ptr(values), _ptr(scales))
     _check(rc, "quant_mxfp8")
     return values, scales
+
+
+def indexer_projection(x, w, key, heads, gate):
+    """[indexer] IndexerProjection.__call__: x [M, K] u16 (BF16), w [key +
+    heads + gate, K] u16 -> (key [M, key] u16, head weights [M, heads] f32,
+    gate [M, gate] u16); each output the binary64 dot product rounded to
+    binary32, then to BF16 for the key and gate parts."""
+    x = _c(x, np.uint16)
+    w = _c(w, np.uint16)
+    M, K = x.shape
+    assert w.shape == (key + heads + gate, K)
+    key_out = np.empty((M, key), np.uint16)
+    heads_out = np.empty((M, heads), np.float32)
+    gate_out = np.empty((M, gate), np.uint16)
+    _check(lib().oracle_indexer_projection(_ptr(x), _ptr(w), M, K, key, heads, gate,
+                                           _ptr(key_out), _ptr(heads_out), _ptr(gate_out)),
+           "indexer_projection")
+    return key_out, heads_out, gate_out

@@ -12,6 +12,8 @@
  *           (GLM-5.3-Flash boundary with the in-kernel prenorm GEMV)
  *   [DSV41] vllm.models.deepseek_v41.nvidia.ops.cute_dsl.all_reduce_mhc
  *           (DSV4.1 delayed-mHC boundary, MoE finalize, two-shot, MXFP8)
+ *   [IDX]   vllm.models.glm5next.nvidia.specialized_decode.indexer
+ *           (the DSA indexer's fused input projection)
  *
  * Precision.  The pages store BF16 and compute in FP32 in a stated order.
  * This file follows that order with IEEE binary32 operations; it is built
@@ -646,6 +648,36 @@ int oracle_side_mixes(const float *mixes, const float *scale, const float *base,
     for (int i = 0; i < 16; ++i) logits[i] = fmaf(row[8 + i], scale[2], base[8 + i]);
     oracle_sinkhorn(logits, hc_eps, repeat, comb_out + (int64_t)t * 16);
   }
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* DSA indexer projection                                                    */
+/* ------------------------------------------------------------------------ */
+
+/* [IDX] vllm.models.glm5next.nvidia.specialized_decode.indexer,
+ * IndexerProjection.__call__: one product of the layer input x [M, K] with
+ * the concatenated weight rows w [key + heads + gate, K] (the indexer key
+ * rows, the head-weight rows, the kpool gate rows, in that order), each
+ * part written in its own type: key [M, key] BF16, head weights [M, heads]
+ * FP32, gate [M, gate] BF16.  The products of BF16 values are exact and the
+ * page leaves the order of the sum open: the sum is taken in binary64 and
+ * rounded to binary32 once, then to BF16 for the key and gate parts. */
+int oracle_indexer_projection(const uint16_t *x, const uint16_t *w, int M, int K, int key,
+                              int heads, int gate, uint16_t *key_out, float *heads_out,
+                              uint16_t *gate_out) {
+  if (M < 0 || K <= 0 || key < 0 || heads < 0 || gate < 0) return 1;
+  const int rows = key + heads + gate;
+  for (int t = 0; t < M; ++t)
+    for (int r = 0; r < rows; ++r) {
+      double s = 0.0;
+      for (int k = 0; k < K; ++k)
+        s += (double)bf(x[(int64_t)t * K + k]) * (double)bf(w[(int64_t)r * K + k]);
+      const float f = (float)s;
+      if (r < key) key_out[(int64_t)t * key + r] = tobf(f);
+      else if (r < key + heads) heads_out[(int64_t)t * heads + (r - key)] = f;
+      else gate_out[(int64_t)t * gate + (r - key - heads)] = tobf(f);
+    }
   return 0;
 }
 

@@ -1055,3 +1055,49 @@ def test_mailbox_model_cycles_and_resets():
         assert got[0, 0, 0] == 0 and np.array_equal(got[1], x[1])
         assert mb.stage[1] == (g + 1) % 3
         assert (mb.slots == 0x8000).all()
+
+
+# ---------------------------------------------------------------------------
+# DSA indexer projection
+# ---------------------------------------------------------------------------
+
+def test_indexer_one_hot_rows_pick_input_columns():
+    """Weight row r = 1.0 at one column c_r: every output is x[t, c_r], exact
+    in each part's type, so the part boundaries and the row order (key rows,
+    then head rows, then gate rows) are pinned."""
+    rng = np.random.default_rng(31)
+    M, K, key, heads, gate = 5, 256, 16, 8, 24
+    x = rand_bf16((M, K), 1.0, rng)
+    cols = rng.permutation(K)[:key + heads + gate]
+    w = np.zeros((key + heads + gate, K), np.uint16)
+    w[np.arange(len(cols)), cols] = 0x3F80
+    k_out, h_out, g_out = oracle.indexer_projection(x, w, key, heads, gate)
+    assert np.array_equal(k_out, x[:, cols[:key]])
+    assert np.array_equal(h_out, bf16_value(x[:, cols[key:key + heads]]))
+    assert np.array_equal(g_out, x[:, cols[key + heads:]])
+
+
+def test_indexer_matches_float64_matmul():
+    """Against numpy's float64 product (a library routine): the head weights
+    within one binary32 ulp, the BF16 parts within one BF16 ulp."""
+    rng = np.random.default_rng(32)
+    M, K, key, heads, gate = 3, 1024, 16, 8, 16
+    x = rand_bf16((M, K), 1.0, rng)
+    w = rand_bf16((key + heads + gate, K), 0.02, rng)
+    k_out, h_out, g_out = oracle.indexer_projection(x, w, key, heads, gate)
+    ref = bf16_value(x).astype(np.float64) @ bf16_value(w).astype(np.float64).T
+    assert f32_ulp_distance(h_out, ref[:, key:key + heads].astype(np.float32)).max() <= 1
+    assert bf16_ulp_distance(k_out, torch_bf16(ref[:, :key].astype(np.float32))).max() <= 1
+    assert bf16_ulp_distance(g_out, torch_bf16(ref[:, key + heads:].astype(np.float32))).max() <= 1
+
+
+def test_indexer_sum_is_rounded_once():
+    """A row whose products cancel except for a tiny term: 1 + 2^-30 - 1
+    summed exactly gives 2^-30 (a rounding per addition would lose it)."""
+    K = 8
+    x = np.zeros((1, K), np.uint16)
+    x[0, :3] = [0x3F80, 0x3080, 0xBF80]          # 1, 2^-30, -1
+    w = np.zeros((1, K), np.uint16)
+    w[0, :3] = 0x3F80
+    _, h_out, _ = oracle.indexer_projection(x, w, 0, 1, 0)
+    assert h_out[0, 0] == np.float32(2.0 ** -30)
