@@ -405,6 +405,30 @@ def bench_glm_with_side_mixes(torch, mhc, g, steps, warmup):
     return Timed(torch, call, steps, warmup).run(), per_set
 
 
+def bytes_indexer(M, K, key, heads, gate):
+    """The weight rows once, the tokens' inputs, the three outputs."""
+    return (key + heads + gate) * K * 2 + M * (K * 2 + key * 2 + heads * 4 + gate * 2)
+
+
+def bench_indexer(torch, mhc, ix, steps, warmup):
+    per_set = bytes_indexer(ix.M, ix.K, ix.key, ix.heads, ix.gate)
+    sets = make_sets(torch, {"x": dev(torch, ix.x), "w": dev(torch, ix.w)},
+                     rotations(per_set, minimum=4))
+    for s in sets:
+        s["key"] = torch.empty((ix.M, ix.key), dtype=torch.bfloat16, device="cuda")
+        s["heads"] = torch.empty((ix.M, ix.heads), dtype=torch.float32, device="cuda")
+        s["gate"] = torch.empty((ix.M, ix.gate), dtype=torch.bfloat16, device="cuda")
+    nbytes = mhc.mhcb_indexer_workspace_bytes(ix.M, ix.K, ix.key, ix.heads, ix.gate)
+    ws = mhc.indexer_workspace(nbytes) if nbytes else None
+
+    def call(i):
+        s = sets[i % len(sets)]
+        mhc.mhcb_indexer_projection(s["x"], s["w"], s["key"], s["heads"], s["gate"], ws, nbytes,
+                                    ix.M, ix.K, ix.key, ix.heads, ix.gate)
+
+    return Timed(torch, call, steps, warmup).run(), per_set
+
+
 def copy_bandwidth(torch, nbytes=1 << 30, reps=20):
     """Achieved GB/s (read + write bytes) of a plain device-to-device copy
     of `nbytes`: the practical HBM ceiling next to the 8 TB/s peak."""
@@ -482,7 +506,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", default="",
                     help="comma-separated workloads to run alone for profiling (headline, sweep, "
-                         "finalize, glm, mixes, glm_moe, mxfp8, mailbox, copy); prints no JSON")
+                         "finalize, glm, mixes, glm_moe, indexer, mxfp8, mailbox, copy); prints no "
+                         "JSON")
     ap.add_argument("--slices", type=int, default=0,
                     help="workgroups per token for small-M calls (0 = the library's choice)")
     ap.add_argument("--eager", action="store_true",
@@ -601,6 +626,12 @@ def main():
             ms, nbytes = bench_glm_moe(torch, mhc, M, 6144, 4, 8, min(K, 100), min(W, 5))
             extra[f"glm_moe_tp4_k8_M{M}"] = entry(ms, nbytes, M)
             log(f"glm moe M={M}: {extra[f'glm_moe_tp4_k8_M{M}']}")
+    if want("indexer") and not args.quick:
+        for M in (1, 4, 8, 16, 64, 256):  # the DSA indexer projection, K=6144, 128 + 32 + 128 rows
+            ix = synth.indexer(M)
+            ms, nbytes = bench_indexer(torch, mhc, ix, min(K, 100), min(W, 5))
+            extra[f"indexer_projection_M{M}"] = entry(ms, nbytes, M)
+            log(f"indexer M={M}: {extra[f'indexer_projection_M{M}']}")
     if (want("mxfp8") or want("mailbox")) and not args.quick:
         b = synth.large_m_delayed(8192)
         if want("mxfp8"):

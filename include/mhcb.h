@@ -10,6 +10,8 @@
  *   [GLM]   vllm.models.glm5next.nvidia.specialized_decode.all_reduce_mhc
  *           (AllReduceMhcBoundary.__call__ / .join, _BoundaryDeviceKernel,
  *            _GroupBoundaryDeviceKernel, _MixesDeviceKernel, _PublishDeviceKernel)
+ *   [IDX]   vllm.models.glm5next.nvidia.specialized_decode.indexer
+ *           (IndexerProjection, _ProjectionKernel)
  *
  * Conventions for every entry point
  *  - Pointers are DEVICE pointers owned by the caller unless stated; the
@@ -310,6 +312,35 @@ int mhcb_finalize_glm(const uint16_t *gemm2_permuted, int64_t gemm2_rank_stride,
                       float *mixes_out, uint16_t *layer_input, void *workspace,
                       int64_t workspace_bytes, int M, int hidden_size, int hc_mult, int tp,
                       int top_k, float rms_eps, float hc_eps, float norm_eps, hipStream_t stream);
+
+/* DSA indexer input projection ([IDX] vllm.models.glm5next.nvidia
+ * .specialized_decode.indexer, IndexerProjection.__call__ /
+ * _ProjectionKernel): the layer input x [M, K] BF16 times the concatenated
+ * weight rows weight [key_rows + heads + gate_rows, K] BF16 (the indexer
+ * key rows, the head-weight rows, the kpool gate rows, in that order),
+ *   out[t][r] = sum_k x[t][k] * weight[r][k]   (FP32; products exact)
+ * each part written in its own type: key_out [M, key_rows] BF16 (nearest
+ * even), heads_out [M, heads] FP32, gate_out [M, gate_rows] BF16.
+ *
+ * workspace: NULL, or at least mhcb_indexer_workspace_bytes(...) bytes,
+ * 256-byte aligned, set to zero by mhcb_indexer_workspace_init (or any
+ * zero fill) before its first use.  With a workspace and few tokens, K is
+ * cut into ranges summed by different workgroups (partials and per-block
+ * counters in the workspace; every call leaves the counters at zero again),
+ * which spreads the weight read over the whole device; without one each
+ * output is summed by a single workgroup.  Calls that share a workspace
+ * must not overlap (same stream, or ordered).  Each output is summed in a
+ * fixed order for a given M, device and workspace choice, so results repeat
+ * bit for bit.  The workspace size depends on the current device's compute
+ * unit count (0 when K is not split).  K a multiple of 128 up to 65536 and
+ * at most 4096 rows (EUNSUPPORTED beyond); M >= 1; a part with no rows may
+ * pass NULL for its output. */
+int64_t mhcb_indexer_workspace_bytes(int M, int K, int key_rows, int heads, int gate_rows);
+int mhcb_indexer_workspace_init(void *workspace, int64_t workspace_bytes, hipStream_t stream);
+int mhcb_indexer_projection(const uint16_t *x, const uint16_t *weight, uint16_t *key_out,
+                            float *heads_out, uint16_t *gate_out, void *workspace,
+                            int64_t workspace_bytes, int M, int K, int key_rows, int heads,
+                            int gate_rows, hipStream_t stream);
 
 /* Standalone MXFP8 of a BF16 [M, hidden] array: the encoding of the
  * boundary's epilogue ([DSV41] _LamportMHCDeviceKernel, quantize): per 32

@@ -240,3 +240,30 @@ def raw_mixes(M: int, seed: int = 5):
 def bf16_matrix(M: int, H: int, std: float = 1.0, seed: int = 6) -> np.ndarray:
     """[M, H] BF16 bits ~ N(0, std): input of the standalone MXFP8 quantizer."""
     return _normal_bf16(_rng(seed, M * 100000 + H), (M, H), std)
+
+
+@dataclass
+class Indexer:
+    """Inputs of the DSA indexer projection: x [M, K] (the layer input) and
+    the concatenated weight rows [key + heads + gate, K]."""
+    name: str
+    M: int
+    K: int
+    key: int
+    heads: int
+    gate: int
+    x: np.ndarray               # [M, K] u16
+    w: np.ndarray               # [key + heads + gate, K] u16
+
+
+def indexer(M: int, K: int = 6144, key: int = 128, heads: int = 32, gate: int = 128,
+            name: str = "") -> Indexer:
+    """Indexer projection: x ~ N(0,1) per token (token t's row from its own
+    generator, so smaller M are prefixes), weight rows ~ N(0, 0.02)."""
+    x = np.empty((M, K), np.float32)
+    for t in range(M):
+        x[t] = _token_rng(7, (K,), t).standard_normal(K, dtype=np.float32)
+    rows = key + heads + gate
+    w = _normal_bf16(np.random.default_rng([7, K, key, heads, gate]), (rows, K), 0.02)
+    return Indexer(name or f"indexer-K{K}-k{key}-h{heads}-g{gate}-M{M}", M, K, key, heads, gate,
+                   to_bf16_bits(x), w)

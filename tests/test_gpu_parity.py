@@ -17,7 +17,7 @@ import oracle
 import synth
 from tests.gpu_util import (assert_bits_equal, assert_within_ulp, check_glm_outputs, dev, host,
                             u16)
-from tests.numerics import bf16_value
+from tests.numerics import bf16_ulp_distance, bf16_value
 
 pytestmark = pytest.mark.gpu
 
@@ -1121,3 +1121,110 @@ def test_glm_auto_with_sync_only_workspace(M):
     check_glm_outputs(f"sync-only workspace M={M}", u16(ro)[toks], host(mixes)[toks],
                       u16(li)[toks], ro_ref, mix_ref, li_ref, pre_ref, g.scale, g.base, g.gamma,
                       g.hc_eps, g.norm_eps)
+
+
+# ---------------------------------------------------------------------------
+# DSA indexer projection
+# ---------------------------------------------------------------------------
+
+def run_indexer(ix, workspace=None):
+    """One projection; `workspace` None runs without one, "cached" with the
+    binding's zeroed per-stream workspace, else the given tensor."""
+    M, K = ix.M, ix.K
+    key = torch.full((M, ix.key), float("nan"), dtype=torch.bfloat16, device="cuda")
+    heads = torch.full((M, ix.heads), float("nan"), dtype=torch.float32, device="cuda")
+    gate = torch.full((M, ix.gate), float("nan"), dtype=torch.bfloat16, device="cuda")
+    nbytes = 0
+    if workspace is not None:
+        nbytes = mhc.mhcb_indexer_workspace_bytes(M, K, ix.key, ix.heads, ix.gate)
+        if isinstance(workspace, str):
+            workspace = mhc.indexer_workspace(nbytes) if nbytes else None
+        else:
+            nbytes = workspace.numel()
+    mhc.mhcb_indexer_projection(dev(ix.x), dev(ix.w), key, heads, gate, workspace, nbytes, M, K,
+                                ix.key, ix.heads, ix.gate)
+    torch.cuda.synchronize()
+    return u16(key), host(heads), u16(gate)
+
+
+def check_indexer(ix, got):
+    """The projection's outputs against the oracle's exact dot products s
+    (binary64, rounded once): the FP32 head weights within 1e-5 (|s| + 1)
+    and 1e-5 norm-wise per token; each BF16 key and gate output a correct
+    rounding of a value within that same FP32 tolerance of s (so within 1
+    BF16 ulp of the oracle's BF16 value unless the sum cancels to near
+    zero)."""
+    key, heads, gate = ix.key, ix.heads, ix.gate
+    k_got, h_got, g_got = got
+    k_ref, h_ref, g_ref = oracle.indexer_projection(ix.x, ix.w, key, heads, gate)
+    rows = key + heads + gate
+    _, s_all, _ = oracle.indexer_projection(ix.x, ix.w, 0, rows, 0)   # every row in FP32
+    s_all = s_all.astype(np.float64)
+    tol = 1e-5 * (np.abs(s_all) + 1)
+    for name, g, ref, cols in (("key", k_got, k_ref, slice(0, key)),
+                               ("gate", g_got, g_ref, slice(key + heads, rows))):
+        if g.size == 0:
+            continue
+        s = s_all[:, cols]
+        # half a BF16 ulp of the value: a binary32 ulp is 2^-16 of a BF16 one
+        half_ulp = np.spacing((np.abs(s) + tol[:, cols]).astype(np.float32)).astype(np.float64) * 2.0 ** 15
+        d = np.abs(bf16_value(g).astype(np.float64) - s)
+        assert (d <= tol[:, cols] + half_ulp).all(), f"indexer {name}: max excess {(d - tol[:, cols] - half_ulp).max():.3g}"
+        diff = bf16_ulp_distance(g, ref)
+        print(f"[gpu]   {name}: {int((diff > 0).sum())} of {g.size} differ from the oracle's BF16 "
+              f"(max {int(diff.max())} ulps, at |s| = {np.abs(s.reshape(-1)[np.argmax(diff)]):.2e})",
+              flush=True)
+    if heads:
+        err = np.abs(h_got.astype(np.float64) - h_ref)
+        assert (err <= 1e-5 * (np.abs(h_ref) + 1)).all(), f"head weights: max err {err.max()}"
+        rel = np.linalg.norm(err, axis=1) / np.maximum(np.linalg.norm(h_ref, axis=1), 1e-30)
+        assert rel.max() <= 1e-5, f"head weights: norm-wise {rel.max():.2e}"
+        print(f"[gpu]   head weights max abs {err.max():.2e}, norm-wise {rel.max():.2e}", flush=True)
+
+
+@pytest.mark.parametrize("M,K,key,heads,gate,workspace",
+                         [(1, 6144, 128, 32, 128, True), (16, 6144, 128, 32, 128, True),
+                          (64, 6144, 128, 32, 128, True), (256, 6144, 128, 32, 128, True),
+                          (300, 6144, 128, 32, 128, True), (5, 6144, 128, 32, 128, True),
+                          (1, 6144, 128, 32, 128, False), (256, 6144, 128, 32, 128, False),
+                          (33, 1024, 16, 8, 24, True), (1100, 2048, 128, 32, 128, True),
+                          (7, 128, 8, 0, 8, True), (3, 65536, 8, 4, 4, True),
+                          (4, 2048, 128, 32, 128, True), (9, 6144, 128, 32, 128, True),
+                          (2500, 1024, 128, 32, 128, True)],
+                         ids=lambda v: str(v))
+def test_indexer_projection_matches_oracle(M, K, key, heads, gate, workspace):
+    """mhcb_indexer_projection against the oracle (bars in check_indexer).
+    The one-workgroup-per-row form (M <= 4) and the matrix-core form
+    (M >= 5) with K split over workgroups
+    (workspace) or summed by one workgroup (none, or K too short to split),
+    every output block shape (M=64, 256, 300), ragged token and row tiles,
+    the largest K, an empty part; results repeat bit for bit."""
+    ix = synth.indexer(M, K, key, heads, gate)
+    print(f"[gpu] {ix.name} workspace={workspace}", flush=True)
+    got = run_indexer(ix, "cached" if workspace else None)
+    check_indexer(ix, got)
+    again = run_indexer(ix, "cached" if workspace else None)
+    assert all(np.array_equal(p, q) for p, q in zip(again, got)), "not repeatable"
+
+
+def test_indexer_workspace_reused_across_sizes():
+    """One workspace, zeroed once, serves calls of different M in a row (the
+    kernels leave its counters at zero, and no call's partials overlap the
+    counters of another launch shape: M=300 writes partials where M=1100
+    would keep counters 64..161 if the counter area followed the call's
+    block count): each call matches a call on a fresh workspace bit for bit,
+    and the oracle."""
+    sizes = [1, 256, 16, 300, 1100, 1, 64]
+    need = max(mhc.mhcb_indexer_workspace_bytes(M, 6144, 128, 32, 128) for M in sizes)
+    shared = torch.empty(need, dtype=torch.uint8, device="cuda")
+    mhc.mhcb_indexer_workspace_init(shared, need)
+    for M in sizes:
+        ix = synth.indexer(M)
+        print(f"[gpu] {ix.name} on the shared workspace", flush=True)
+        got = run_indexer(ix, shared)
+        nbytes = max(mhc.mhcb_indexer_workspace_bytes(M, 6144, 128, 32, 128), 256)
+        fresh = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        mhc.mhcb_indexer_workspace_init(fresh, nbytes)
+        ref = run_indexer(ix, fresh)
+        assert all(np.array_equal(p, q) for p, q in zip(got, ref)), f"M={M}: shared differs from fresh"
+        check_indexer(ix, got)

@@ -11,6 +11,8 @@ from .mhcb import (  # noqa: F401
     mhcb_finalize_glm, mhcb_finalize_glm_workspace_bytes, finalize_glm, mhcb_workspace_bytes,
     mhcb_workspace_init, mhcb_workspace_status, mhcb_set_token_slices, new_workspace, workspace,
     mhcb_finalize_workspace_bytes, mhcb_workspace_set_spin_limit, workspace_status, mailbox_status,
+    mhcb_indexer_workspace_bytes, mhcb_indexer_workspace_init, mhcb_indexer_projection,
+    indexer_projection, indexer_workspace,
     mhcb_last_error, mhcb_mailbox, mhcb_mailbox_init, mhcb_mailbox_status, mhcb_mixes,
     mhcb_mxfp8_scale_bytes, mhcb_publish, mhcb_quant_mxfp8, mhcb_version, mixes, quant_mxfp8)
 

@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIBRARY = os.path.join(HERE, "libmhcb.so")
 BUILD_DIR = os.path.join(os.path.dirname(HERE), "_build")
-SOURCES = ["api.hip", "boundary.hip", "glm.hip"]
+SOURCES = ["api.hip", "boundary.hip", "glm.hip", "indexer.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -51,6 +51,8 @@ constexpr int kMaxTp = 64;
 constexpr int kMaxRoutes = 1024;
 constexpr int kGlmTileMinM = 256;  // automatic matrix-core tiles from this M
 constexpr int kGlmTwoPassMinM = 1;  // automatic two-pass tiles from this M
+constexpr int kIndexerMaxRows = 4096;
+constexpr int kIndexerMaxK = 65536;
 
 // Checks shared by the boundary variants ([DSV41] AllReduceMHC._check and
 // _consumer, _LamportMHCDeviceKernel.__init__).
@@ -692,6 +694,60 @@ int mhcb_finalize_ex(const uint16_t *gemm2_permuted, int64_t gemm2_rank_stride, 
                        post, comb, pre, norm_weight, residual_out, layer_input, mxfp8_values,
                        mxfp8_scales, two_shot, workspace, workspace_bytes, M, hidden_size,
                        hc_mult, tp, top_k, norm_eps, stream);
+}
+
+// Validates the indexer's sizes; fills `rows`.
+int check_indexer(const char *fn, int M, int K, int key_rows, int heads, int gate_rows, int &rows) {
+  if (M < 1) return fail(MHCB_EINVAL, "%s: M=%d < 1", fn, M);
+  if (key_rows < 0 || heads < 0 || gate_rows < 0 || key_rows + heads + gate_rows < 1)
+    return fail(MHCB_EINVAL, "%s: rows (%d, %d, %d) must be >= 0 with at least one", fn, key_rows,
+                heads, gate_rows);
+  rows = key_rows + heads + gate_rows;
+  if (rows > kIndexerMaxRows) return fail(MHCB_EUNSUPPORTED, "%s: %d rows exceed %d", fn, rows, kIndexerMaxRows);
+  if (K <= 0 || K % 128 || K > kIndexerMaxK)
+    return fail(MHCB_EUNSUPPORTED, "%s: K=%d must be a positive multiple of 128 up to %d", fn, K, kIndexerMaxK);
+  return MHCB_OK;
+}
+
+int64_t mhcb_indexer_workspace_bytes(int M, int K, int key_rows, int heads, int gate_rows) {
+  int rows = 0;
+  if (check_indexer("mhcb_indexer_workspace_bytes", M, K, key_rows, heads, gate_rows, rows))
+    return -1;
+  return plan_indexer(M, K, rows, device_cus(), true).workspace_bytes;
+}
+
+int mhcb_indexer_workspace_init(void *workspace, int64_t workspace_bytes, hipStream_t stream) {
+  const char *fn = "mhcb_indexer_workspace_init";
+  if (!workspace || workspace_bytes < 0) return fail(MHCB_EINVAL, "%s: a workspace is required", fn);
+  if (!aligned(workspace, 256)) return fail(MHCB_EALIGN, "%s: workspace must be 256-byte aligned", fn);
+  return launched(launch_zero(workspace, workspace_bytes, stream), fn);
+}
+
+int mhcb_indexer_projection(const uint16_t *x, const uint16_t *weight, uint16_t *key_out,
+                            float *heads_out, uint16_t *gate_out, void *workspace,
+                            int64_t workspace_bytes, int M, int K, int key_rows, int heads,
+                            int gate_rows, hipStream_t stream) {
+  const char *fn = "mhcb_indexer_projection";
+  int rows = 0;
+  if (const int rc = check_indexer(fn, M, K, key_rows, heads, gate_rows, rows)) return rc;
+  if (!x || !weight || (key_rows && !key_out) || (heads && !heads_out) || (gate_rows && !gate_out))
+    return fail(MHCB_EINVAL, "%s: x, weight and every non-empty part's output are required", fn);
+  if (!aligned(x, 16) || !aligned(weight, 16) || (key_out && !aligned(key_out, 2)) ||
+      (heads_out && !aligned(heads_out, 4)) || (gate_out && !aligned(gate_out, 2)))
+    return fail(MHCB_EALIGN, "%s: x and weight must be 16-byte aligned", fn);
+  const IndexerPlan p = plan_indexer(M, K, rows, device_cus(), workspace != nullptr);
+  if (workspace) {
+    if (workspace_bytes < p.workspace_bytes)
+      return fail(MHCB_EINVAL, "%s: workspace_bytes=%lld < %lld (mhcb_indexer_workspace_bytes)", fn,
+                  (long long)workspace_bytes, (long long)p.workspace_bytes);
+    if (!aligned(workspace, 256)) return fail(MHCB_EALIGN, "%s: workspace must be 256-byte aligned", fn);
+  }
+  char *ws = static_cast<char *>(workspace);
+  IndexerArgs a = {x, weight, key_out, heads_out, gate_out,
+                   p.splits > 1 ? reinterpret_cast<float *>(ws + p.counter_bytes) : nullptr,
+                   p.splits > 1 ? reinterpret_cast<uint32_t *>(ws) : nullptr,
+                   M, K, key_rows, heads, gate_rows, rows};
+  return launched(launch_indexer(a, p, stream), fn);
 }
 
 int mhcb_quant_mxfp8(const uint16_t *x, uint8_t *values, uint8_t *scales, int M, int hidden_size,

@@ -26,21 +26,7 @@
 namespace mhcb {
 namespace {
 
-typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-
 constexpr int kGlmWideThreads = 768;  // G = 4 workgroups: hidden <= 6144
-
-// Each word is copied to a scalar before the bit cast: a bit cast applied
-// directly to an ext_vector element (a[i]) was compiled to read element 0
-// for every i by this toolchain.
-__device__ __forceinline__ float dot8(u32x4 a, u32x4 b, float acc) {
-  const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, aw[i]),
-                                          __builtin_bit_cast(bf16x2v, bw[i]), acc, false);
-  return acc;
-}
 
 // Wave64 reduce-scatter of N (32 or 64) values per lane: returns on every
 // lane the wave total of value index (N == 64 ? lane : lane / 2).  Each

@@ -82,6 +82,9 @@ _SIGNATURES = {
                                _P, _P, _P, _P, _P, _P, _P, _P, _I64, _I, _I, _I, _I, _I, _F, _F,
                                _F, _P]),
     "mhcb_quant_mxfp8": (_I, [_P, _P, _P, _I, _I, _P]),
+    "mhcb_indexer_workspace_bytes": (_I64, [_I, _I, _I, _I, _I]),
+    "mhcb_indexer_workspace_init": (_I, [_P, _I64, _P]),
+    "mhcb_indexer_projection": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I, _I, _I, _I, _I, _P]),
     "mhcb_mailbox_init": (_I, [_MB, _P]),
     "mhcb_publish": (_I, [_MB, _P, _I64, _I, _I, _I, _P]),
     "mhcb_mailbox_status": (_I, [_MB, _P, _P]),
@@ -247,6 +250,59 @@ def mhcb_finalize_ex(gemm2_permuted, gemm2_rank_stride, rows, expert_weights, we
 def mhcb_quant_mxfp8(x, values, scales, M, hidden_size, stream=None) -> None:
     _check(_lib.mhcb_quant_mxfp8(_ptr(x), _ptr(values), _ptr(scales), M, hidden_size,
                                  _stream(stream)))
+
+
+def mhcb_indexer_workspace_bytes(M: int, K: int, key_rows: int, heads: int, gate_rows: int) -> int:
+    n = _lib.mhcb_indexer_workspace_bytes(M, K, key_rows, heads, gate_rows)
+    if n < 0:
+        raise MhcbError(MHCB_EINVAL, mhcb_last_error())
+    return n
+
+
+def mhcb_indexer_workspace_init(workspace, nbytes: int, stream=None) -> None:
+    _check(_lib.mhcb_indexer_workspace_init(_ptr(workspace), nbytes, _stream(stream)))
+
+
+def mhcb_indexer_projection(x, weight, key_out, heads_out, gate_out, workspace, workspace_bytes,
+                            M, K, key_rows, heads, gate_rows, stream=None) -> None:
+    _check(_lib.mhcb_indexer_projection(_ptr(x), _ptr(weight), _ptr(key_out), _ptr(heads_out),
+                                        _ptr(gate_out), _ptr(workspace), workspace_bytes, M, K,
+                                        key_rows, heads, gate_rows, _stream(stream)))
+
+
+_indexer_workspaces: dict = {}
+
+
+def indexer_workspace(nbytes: int, device=None, stream=None):
+    """The zeroed indexer workspace of (device, stream), grown to the
+    largest size asked for so far (a new one is zeroed; the kernels leave
+    the counters at zero)."""
+    dev = torch.device(device if device is not None else "cuda")
+    if dev.index is None:
+        dev = torch.device("cuda", torch.cuda.current_device())
+    key = (dev, _stream(stream) or 0)
+    ws = _indexer_workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        mhcb_indexer_workspace_init(ws, ws.numel(), stream)
+        _indexer_workspaces[key] = ws
+    return ws
+
+
+def indexer_projection(x, weight, key_rows: int, heads: int, gate_rows: int, *, stream=None):
+    """DSA indexer projection of x [M, K] (BF16) with weight [key_rows + heads
+    + gate_rows, K] (BF16); returns (key [M, key_rows] BF16, head weights
+    [M, heads] FP32, gate [M, gate_rows] BF16)."""
+    M, K = x.shape
+    dev = x.device
+    key = _bf16_empty((M, key_rows), dev)
+    w = torch.empty((M, heads), dtype=torch.float32, device=dev)
+    gate = _bf16_empty((M, gate_rows), dev)
+    nbytes = mhcb_indexer_workspace_bytes(M, K, key_rows, heads, gate_rows)
+    ws = indexer_workspace(nbytes, dev, stream) if nbytes > 0 else None
+    mhcb_indexer_projection(x, weight, key, w, gate, ws, nbytes, M, K, key_rows, heads, gate_rows,
+                            stream)
+    return key, w, gate
 
 
 def mhcb_mailbox_init(mailbox, stream=None) -> None:
