@@ -23,7 +23,9 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# MHCB_ORACLE_LIB points the checker at another build of mhcb_oracle.c (the
+# mutation test loads deliberately broken copies this way, on the CPU).
+_LIB_PATH = os.environ.get("MHCB_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 _P = ctypes.c_void_p

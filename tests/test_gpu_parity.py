@@ -1171,9 +1171,11 @@ def check_indexer(ix, got):
         d = np.abs(bf16_value(g).astype(np.float64) - s)
         assert (d <= tol[:, cols] + half_ulp).all(), f"indexer {name}: max excess {(d - tol[:, cols] - half_ulp).max():.3g}"
         diff = bf16_ulp_distance(g, ref)
+        far = diff > 2
         print(f"[gpu]   {name}: {int((diff > 0).sum())} of {g.size} differ from the oracle's BF16 "
-              f"(max {int(diff.max())} ulps, at |s| = {np.abs(s.reshape(-1)[np.argmax(diff)]):.2e})",
-              flush=True)
+              f"(max {int(diff.max())} ulps, at |s| = {np.abs(s.reshape(-1)[np.argmax(diff)]):.2e}); "
+              f"{int(far.sum())} more than 2 ulps away, largest |s| among them "
+              f"{(np.abs(s)[far].max() if far.any() else 0.0):.2e}", flush=True)
     if heads:
         err = np.abs(h_got.astype(np.float64) - h_ref)
         assert (err <= 1e-5 * (np.abs(h_ref) + 1)).all(), f"head weights: max err {err.max()}"

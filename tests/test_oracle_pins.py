@@ -358,6 +358,59 @@ def test_rmsnorm_multiplies_left_to_right_designed_case():
     assert li[0, 0] == 0x3D31
 
 
+def test_rmsnorm_gamma_after_the_normalizer_designed_case():
+    """out = bf16((p * inv) * gamma), with gamma applied last: on the row
+    p = (0xBD70, 0xBEC5), gamma_0 = 0x3F76 that order gives 0xBE51, while
+    (p * gamma) * inv and p * (inv * gamma) give 0xBE52 (all three checked
+    here with exact rationals; inv = fl(1/sqrt(fl(ss)/H + eps)) with the
+    exact sum of squares of two BF16 values)."""
+    import math
+    H = 2
+    p = np.array([0xBD70, 0xBEC5], np.uint16)
+    gamma = np.array([0x3F76, 0x3F86], np.uint16)
+    residual = np.zeros((1, 4, H), np.uint16)
+    residual[0, 0] = p
+    pre = np.array([[1.0, 0.0, 0.0, 0.0]], np.float32)
+    _, li, _ = oracle.boundary(np.zeros((1, 1, H), np.uint16), residual,
+                               np.zeros((1, 4), np.float32), np.eye(4, dtype=np.float32)[None],
+                               pre, gamma, 1e-6)
+    ss = sum(exact(bf16_value(v)) ** 2 for v in p)
+    inv = exact(np.float32(1.0 / math.sqrt(f32(ss) / H + float(np.float32(1e-6)))))
+    p0, g0 = exact(bf16_value(p[0])), exact(bf16_value(gamma[0]))
+    left = bf16_bits_of(exact(f32(exact(f32(p0 * inv)) * g0)))
+    gamma_first = bf16_bits_of(exact(f32(exact(f32(p0 * g0)) * inv)))
+    inv_gamma = bf16_bits_of(exact(f32(p0 * exact(f32(inv * g0)))))
+    assert (left, gamma_first, inv_gamma) == (0xBE51, 0xBE52, 0xBE52)
+    assert li[0, 0] == left
+
+
+def test_sinkhorn_first_round_brute_force():
+    """repeat = 1: the first step (rows of fma(exp(c - rowmax), 1/sum, eps))
+    followed by one column step only, c <- fl(c * fl(1/fl(s + eps))) with s
+    the column's (c0 + c1) + (c2 + c3); no row step in the first round.
+    With eps = 1e-3 a row step there would scale every entry by about
+    1/(1 + 5 eps), far above the rounding checked here exactly."""
+    import math
+    eps = np.float32(1e-3)
+    for _ in range(30):
+        logits = RNG.standard_normal(16).astype(np.float32)
+        got = oracle.sinkhorn(logits, float(eps), 1).reshape(16)
+        c = [0.0] * 16
+        for r in range(4):
+            row = logits[4 * r:4 * r + 4]
+            peak = max(row)
+            e = [np.float32(math.exp(float(np.float32(v - peak)))) for v in row]
+            s = np.float32(np.float32(e[0] + e[1]) + np.float32(e[2] + e[3]))
+            inv = np.float32(1.0 / float(s))
+            for k in range(4):
+                c[4 * r + k] = f32(exact(e[k]) * exact(inv) + exact(eps))
+        for k in range(4):
+            s = f32(exact(f32(exact(c[k]) + exact(c[4 + k]))) + exact(f32(exact(c[8 + k]) + exact(c[12 + k]))))
+            inv = f32(1 / exact(f32(exact(s) + exact(eps))))
+            for r in range(4):
+                assert got[4 * r + k] == np.float32(f32(exact(c[4 * r + k]) * exact(inv)))
+
+
 def test_sinkhorn_first_step_brute_force():
     """repeat = 0 leaves the first step alone: rows of exp(c - rowmax), each
     scaled by the rounded reciprocal of (q0+q1)+(q2+q3) and offset by eps in
@@ -716,6 +769,21 @@ def test_finalize_single_route_unit_weight_is_the_row():
     c = oracle.finalize_contributions(gemm2, w, idx, shared)
     want = np.where(gemm2[:, idx[:, 0]] == 0x8000, 0, gemm2[:, idx[:, 0]])
     assert np.array_equal(c, want)
+
+
+def test_finalize_never_publishes_negative_zero():
+    """A contribution that rounds to BF16 negative zero is published as +0
+    (negative zero is the mailbox's empty marker): the route row -2^-126
+    (0x8080) times the weight 2^-20 is the binary32 subnormal -2^-146, which
+    rounds to BF16 -0; the oracle returns 0x0000."""
+    H = 8
+    gemm2 = np.full((1, 1, H), 0x8080, np.uint16)
+    w = np.array([[2.0 ** -20]], np.float32)
+    idx = np.zeros((1, 1), np.int32)
+    c = oracle.finalize_contributions(gemm2, w, idx, np.zeros((1, 1, H), np.uint16))
+    # the exact product -2^-146 rounds to a BF16 zero
+    assert bf16_bits_of(exact(bf16_value(np.uint16(0x8080))) * exact(w[0, 0])) == 0x0000
+    assert (c == 0x0000).all()
 
 
 def test_finalize_dropped_routes_leave_the_shared_expert():

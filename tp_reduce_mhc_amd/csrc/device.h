@@ -40,9 +40,6 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// A fragment as 8 floats (exact widening) and back.
-typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-
 // Dot product of 8 BF16 pairs (v_dot2c_f32_bf16: exact products, FP32
 // sums) added to acc.  Each word is copied to a scalar before the bit cast:
 // a bit cast applied directly to an ext_vector element (a[i]) was compiled
@@ -51,11 +48,12 @@ __device__ __forceinline__ float dot8(u32x4 a, u32x4 b, float acc) {
   const uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, aw[i]),
-                                          __builtin_bit_cast(bf16x2v, bw[i]), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, aw[i]),
+                                          __builtin_bit_cast(bf16x2, bw[i]), acc, false);
   return acc;
 }
 
+// A fragment as 8 floats (exact widening) and back.
 __device__ __forceinline__ void unpack8(u32x4 w, float (&f)[8]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
