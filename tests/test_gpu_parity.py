@@ -306,7 +306,8 @@ def test_graph_replays_match_eager_calls():
     own) and
     replayed three times, with eager calls on the same workspace in between,
     give the eager results every time (the tags the exchanges wait for are
-    read from the workspace at each replay, not frozen into the graph)."""
+    read from the workspace at each replay, not frozen into the graph), and
+    those results match the oracle to each call's parity bar."""
     b = synth.boundary(17, 8, 1024, 8, 0.5, "graph-delayed")
     f = synth.moe_finalize(8, H=1024)
     g = synth.glm(40, H=2048)
@@ -386,6 +387,34 @@ def test_graph_replays_match_eager_calls():
     epochs, _, copies, status = sync_state(ws)
     assert status == 0 and epochs.max() > 0
     assert (copies[np.arange(1024), epochs % 2] == EMPTY).all(), "the next call's copy is empty"
+
+    # The replayed results (bit-equal to the eager ones) against the oracle.
+    ro_ref, li_ref, _ = oracle.boundary(b.partials, b.residual, b.post, b.comb, b.pre, b.gamma,
+                                        b.norm_eps, threads=8)
+    assert_bits_equal(u16(outs["b_ro"]), ro_ref, "graph delayed residual_out")
+    assert_within_ulp(u16(outs["b_li"]), li_ref, 1, "graph delayed layer_input")
+    v_q, s_q = oracle.quant_mxfp8(u16(outs["b_li"]))
+    assert_bits_equal(outs["b_v"].cpu().numpy(), v_q, "graph mxfp8 values")
+    assert_bits_equal(outs["b_s"].cpu().numpy(), s_q, "graph mxfp8 scales")
+    ro_ref, li_ref, _ = oracle.finalize(f.gemm2, f.weights, f.idx, f.shared, f.residual, f.post,
+                                        f.comb, f.pre, f.gamma, f.norm_eps, threads=8)
+    assert_bits_equal(u16(outs["f_ro"]), ro_ref, "graph finalize residual_out")
+    assert_within_ulp(u16(outs["f_li"]), li_ref, 1, "graph finalize layer_input")
+    check_glm_against_oracle(g, u16(outs["g_ro"]), host(outs["g_mx"]), u16(outs["g_li"]),
+                             "graph glm tiles")
+    check_glm_against_oracle(g, u16(outs["g2_ro"]), host(outs["g2_mx"]), u16(outs["g2_li"]),
+                             "graph glm two passes")
+    p_ref, c_ref = oracle.side_mixes(host(outs["g2_mx"]), g.scale, g.base, g.hc_eps, g.post_mult,
+                                     g.sinkhorn_repeat)
+    post_n, comb_n = host(outs["x_post"]).reshape(-1, 4), host(outs["x_comb"])
+    assert (np.abs(post_n - p_ref) <= 1e-5 * np.abs(p_ref) + 1e-7).all(), "graph side post"
+    assert (np.abs(comb_n - c_ref) <= 1e-5 * np.abs(c_ref) + 1e-7).all(), "graph side comb"
+    ro_ref, mix_ref, li_ref, pre_ref = oracle.boundary_glm_moe(
+        f.gemm2, f.weights, f.idx, f.shared, f.residual, f.post, f.comb, gm.fn, gm.scale, gm.base,
+        gm.gamma, gm.rms_eps, gm.hc_eps, gm.norm_eps, threads=8)
+    check_glm_outputs("graph glm moe", u16(outs["m_ro"]), host(outs["m_mx"]), u16(outs["m_li"]),
+                      ro_ref, mix_ref, li_ref, pre_ref, gm.scale, gm.base, gm.gamma, gm.hc_eps,
+                      gm.norm_eps)
 
 
 def test_cross_token_independence_and_determinism():

@@ -64,33 +64,37 @@ __device__ __forceinline__ void store_output(const IndexerArgs &a, int64_t t, in
   }
 }
 
-// A workgroup's E = TT * RT outputs per thread are contiguous in the
-// block (one token, E consecutive rows), so its partials move as E / 2
-// 8-byte device-scope words (one 4-byte word when E = 1).
+// A thread's E = TT * RT partial sums move as E / 2 8-byte device-scope
+// words (one 4-byte word when E = 1).  Word j of thread tid sits at word
+// j * 256 + tid of the block's area, so each store or load instruction of a
+// wave covers one contiguous stretch of memory: device-scope stores are
+// written through, and scattered 8-byte stores would each cost a partial
+// sector write.
 template <int E>
 struct PartialWords {
   static constexpr int kWords = E > 1 ? E / 2 : 1;
-  __device__ static void store(float *p, const float (&v)[E]) {
+  __device__ static void store(float *area, int tid, const float (&v)[E]) {
     if constexpr (E == 1) {
-      __hip_atomic_store(reinterpret_cast<uint32_t *>(p), __builtin_bit_cast(uint32_t, v[0]),
-                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(reinterpret_cast<uint32_t *>(area) + tid,
+                         __builtin_bit_cast(uint32_t, v[0]), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
     } else {
 #pragma unroll
       for (int j = 0; j < kWords; ++j) {
         const uint64_t w = (uint64_t)__builtin_bit_cast(uint32_t, v[2 * j]) |
                            (uint64_t)__builtin_bit_cast(uint32_t, v[2 * j + 1]) << 32;
-        __hip_atomic_store(reinterpret_cast<uint64_t *>(p) + j, w, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(reinterpret_cast<uint64_t *>(area) + j * 256 + tid, w,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
   }
-  __device__ static uint64_t load(const float *p, int j) {
+  __device__ static uint64_t load(const float *area, int tid, int j) {
     if constexpr (E == 1)
-      return __hip_atomic_load(reinterpret_cast<const uint32_t *>(p), __ATOMIC_RELAXED,
+      return __hip_atomic_load(reinterpret_cast<const uint32_t *>(area) + tid, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
     else
-      return __hip_atomic_load(reinterpret_cast<const uint64_t *>(p) + j, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+      return __hip_atomic_load(reinterpret_cast<const uint64_t *>(area) + j * 256 + tid,
+                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __device__ static float value(uint64_t w, int e) {
     return __builtin_bit_cast(float, (uint32_t)(E == 1 ? w : (e & 1) ? w >> 32 : w));
@@ -187,7 +191,7 @@ indexer_kernel(const IndexerArgs a, const int groups, const int blocks, const in
   constexpr int kTile = kIdxTile * kIdxTile;
   constexpr int E = TT * RT;               // outputs per thread
   constexpr int kThreads = W * kWave;
-  static_assert(W % kIdxFold == 0 && kThreads >= E * kTile / E, "block shape");
+  static_assert(W % kIdxFold == 0 && kThreads >= kTile, "block shape");
   using Words = PartialWords<E>;
   __shared__ float red[kIdxFold][E * kTile];
   __shared__ int last;
@@ -310,11 +314,11 @@ indexer_kernel(const IndexerArgs a, const int groups, const int blocks, const in
     return;
   }
 
-  // Partials: [split][block][element], read back by the block's last
-  // workgroup in range order.
+  // Partials: [split][block][E * 256 values, word-major], read back by the
+  // block's last workgroup in range order.
   const int64_t plane = (int64_t)blocks * E * kTile;
-  float *mine = a.parts + (int64_t)block * E * kTile + i0;
-  if (active) Words::store(mine + split * plane, v);
+  float *area = a.parts + (int64_t)block * E * kTile;
+  if (active) Words::store(area + split * plane, tid, v);
   __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are complete
   __syncthreads();
   uint32_t *counter = a.counters + block;
@@ -335,7 +339,7 @@ indexer_kernel(const IndexerArgs a, const int groups, const int blocks, const in
     for (int q = 0; q < 8; ++q)
 #pragma unroll
       for (int j = 0; j < Words::kWords; ++j)
-        w[q][j] = s0 + q < S ? Words::load(mine + (s0 + q) * plane, j) : 0;
+        w[q][j] = s0 + q < S ? Words::load(area + (s0 + q) * plane, tid, j) : 0;
 #pragma unroll
     for (int q = 0; q < 8; ++q)
       if (s0 + q < S)
@@ -366,10 +370,21 @@ IndexerPlan plan_indexer(int M, int K, int rows, int cus, bool workspace) {
     p.row_groups = (row_tiles + rt - 1) / rt;
     return (int64_t)p.groups * p.row_groups;
   };
+  // Launch shapes measured on MI355X (K=6144, 288 rows, M = 8 .. 4096, HIP
+  // graphs over cold inputs), best of blocks {1x1, 2x2, 4x2} x {1, 2, 4, 8}
+  // K ranges x {4, 8, 16} waves: 1x1 blocks up to four token tiles, 2x2 up
+  // to sixteen, 4x2 beyond; eight K ranges (one per XCD) while there are
+  // at most 96 blocks, four up to the counter area's 1024; 8 waves at
+  // M <= 16, for 2x2 blocks past eight token tiles and for 4x2 blocks with
+  // eight ranges, else 4.  (M=256: 15.0 us against 21.7 with the rule this
+  // replaced; M=4096: 87 against 110.)  A single range (no workspace, or
+  // more blocks than counters) takes 16 waves once a wave would have more
+  // than eight chunks, so that more of its loads are in flight.
   int64_t blocks;
+  int64_t splits = 1;
   if (workspace) {
-    // Larger blocks re-read fewer operands; K ranges make up the count.
-    blocks = tiles <= 2 ? shape(1, 1) : tiles <= 8 ? shape(2, 2) : shape(4, 2);
+    blocks = tiles <= 4 ? shape(1, 1) : tiles <= 16 ? shape(2, 2) : shape(4, 2);
+    splits = blocks <= 96 ? 8 : blocks <= kIndexerCounters ? 4 : 1;
   } else {
     // Without K ranges, the largest block that still gives a workgroup per
     // compute unit.
@@ -377,22 +392,15 @@ IndexerPlan plan_indexer(int M, int K, int rows, int cus, bool workspace) {
     if (blocks < cus) blocks = shape(2, 2);
     if (blocks < cus) blocks = shape(1, 1);
   }
-  // K ranges: about one workgroup per compute unit, a multiple of 8 from 5
-  // on (one range per XCD, so a range's operands stay in one L2), at least
-  // one 32-column chunk per wave, at most kIndexerMaxSplits.
-  int64_t splits = workspace && blocks <= kIndexerCounters ? (cus + blocks - 1) / blocks : 1;
-  if (splits > 4) splits = (splits + 7) / 8 * 8;
-  const int by_k = K / 32 / 4;
+  const int by_k = K / 32 / 4;  // at least one 32-column chunk per wave of 4
   if (splits > by_k) splits = by_k;
-  if (splits > kIndexerMaxSplits) splits = kIndexerMaxSplits;
   p.splits = splits < 1 ? 1 : (int)splits;
   p.blocks = (int)blocks;
-  // Waves: enough that a range's chunks are all loaded in one round of two
-  // per wave (4, 8 or 16 waves; 16 for longer ranges).
-  const int range = (K / 32 + p.splits - 1) / p.splits;
-  p.waves = range <= 8 ? 4 : range <= 16 ? 8 : 16;
-  // The counters sit in a fixed area at the start of the workspace, so
-  // calls with other launch shapes never write partials over them.
+  if (tiles <= 1) p.waves = 8;
+  else if (p.tt == 2) p.waves = tiles > 8 ? 8 : 4;
+  else if (p.tt == 4) p.waves = p.splits == 8 ? 8 : 4;
+  else p.waves = 4;
+  if (p.splits == 1 && (int64_t)K / 32 > 8 * p.waves) p.waves = 16;
   p.counter_bytes = kIndexerCounters * 4;
   p.workspace_bytes =
       p.splits > 1 ? p.counter_bytes + (int64_t)p.splits * blocks * p.tt * p.rt * kIdxTile * kIdxTile * 4 : 0;
