@@ -218,6 +218,54 @@ def test_glm_mixes_finalize_quant_validation():
         mhc.mhcb_workspace_init(FAKE + 64, 1 << 23, 0)
 
 
+def _indexer(**kw):
+    import tp_reduce_mhc_amd as mhc
+    args = dict(x=FAKE, weight=FAKE, key_out=FAKE, heads_out=FAKE, gate_out=FAKE, workspace=None,
+                workspace_bytes=0, M=16, K=6144, key_rows=128, heads=32, gate_rows=128, stream=0)
+    args.update(kw)
+    return mhc.mhcb_indexer_projection(**args)
+
+
+@pytest.mark.parametrize("kw,code,text", [
+    (dict(M=0), "EINVAL", "M=0"),
+    (dict(K=100), "EUNSUPPORTED", "multiple of 128"),
+    (dict(K=65536 + 128), "EUNSUPPORTED", "multiple of 128"),
+    (dict(key_rows=4096, heads=1, gate_rows=0), "EUNSUPPORTED", "rows exceed"),
+    (dict(key_rows=0, heads=0, gate_rows=0), "EINVAL", "at least one"),
+    (dict(key_rows=-1), "EINVAL", "at least one"),
+    (dict(x=None), "EINVAL", "required"),
+    (dict(heads_out=None), "EINVAL", "required"),
+    (dict(x=FAKE + 8), "EALIGN", "16-byte"),
+    (dict(heads_out=FAKE + 2), "EALIGN", "element-aligned"),
+    (dict(workspace=FAKE, workspace_bytes=16), "EINVAL", "mhcb_indexer_workspace_bytes"),
+    (dict(workspace=FAKE + 64, workspace_bytes=1 << 30), "EALIGN", "256-byte"),
+])
+def test_indexer_validation(kw, code, text):
+    """The indexer projection validates its sizes, pointers, alignment and
+    workspace before anything is launched."""
+    import tp_reduce_mhc_amd as mhc
+    with pytest.raises(mhc.MhcbError, match=text) as e:
+        _indexer(**kw)
+    assert e.value.code == getattr(mhc, "MHCB_" + code)
+
+
+def test_indexer_workspace_bytes():
+    """No workspace where K is not split: the one-workgroup-per-row form
+    (M <= 4) and more output blocks than the counter area holds; a fixed
+    counter area plus the partials otherwise, growing with M; -1 for sizes
+    the call rejects."""
+    import tp_reduce_mhc_amd as mhc
+    assert mhc.mhcb_indexer_workspace_bytes(4, 6144, 128, 32, 128) == 0
+    assert mhc.mhcb_indexer_workspace_bytes(8192, 6144, 128, 32, 128) == 0
+    small = mhc.mhcb_indexer_workspace_bytes(16, 6144, 128, 32, 128)
+    large = mhc.mhcb_indexer_workspace_bytes(256, 6144, 128, 32, 128)
+    assert 4096 < small < large and small % 4 == 0
+    with pytest.raises(mhc.MhcbError):
+        mhc.mhcb_indexer_workspace_bytes(16, 100, 128, 32, 128)
+    with pytest.raises(mhc.MhcbError, match="required"):
+        mhc.mhcb_indexer_workspace_init(None, 256, 0)
+
+
 def test_product_path_does_not_touch_the_oracle():
     """The binding and the HIP sources never import, load or name the
     oracle's library or module."""

@@ -734,7 +734,7 @@ int mhcb_indexer_projection(const uint16_t *x, const uint16_t *weight, uint16_t 
     return fail(MHCB_EINVAL, "%s: x, weight and every non-empty part's output are required", fn);
   if (!aligned(x, 16) || !aligned(weight, 16) || (key_out && !aligned(key_out, 2)) ||
       (heads_out && !aligned(heads_out, 4)) || (gate_out && !aligned(gate_out, 2)))
-    return fail(MHCB_EALIGN, "%s: x and weight must be 16-byte aligned", fn);
+    return fail(MHCB_EALIGN, "%s: x and weight must be 16-byte aligned, the outputs element-aligned", fn);
   const IndexerPlan p = plan_indexer(M, K, rows, device_cus(), workspace != nullptr);
   if (workspace) {
     if (workspace_bytes < p.workspace_bytes)
