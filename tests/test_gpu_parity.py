@@ -1221,6 +1221,7 @@ def check_indexer(ix, got):
                           (33, 1024, 16, 8, 24, True), (1100, 2048, 128, 32, 128, True),
                           (7, 128, 8, 0, 8, True), (3, 65536, 8, 4, 4, True),
                           (4, 2048, 128, 32, 128, True), (9, 6144, 128, 32, 128, True),
+                          (4, 6144, 128, 32, 128, True), (8, 6144, 128, 32, 128, True),
                           (2500, 1024, 128, 32, 128, True)],
                          ids=lambda v: str(v))
 def test_indexer_projection_matches_oracle(M, K, key, heads, gate, workspace):

@@ -10,6 +10,7 @@
 #include "../../include/mhcb.h"
 #include "device.h"
 #include "kernels.h"
+#include "indexer.h"
 
 using namespace mhcb;
 

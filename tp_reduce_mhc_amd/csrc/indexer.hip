@@ -7,19 +7,22 @@
 // [M, heads] FP32, gate [M, gate] BF16.  The products of BF16 values are
 // exact in FP32; only the order of the sum is the kernel's.
 //
-// gfx950 design: v_mfma_f32_16x16x32_bf16 with tokens as the M dimension
-// (16-token tiles, a tile's missing tokens padded with the last one) and
-// weight rows as the N dimension.  A workgroup owns an output block of TT
-// token tiles x RT row tiles and one of S contiguous ranges of the 32-column
-// chunks of K; its W waves (4, 8 or 16, so that the range is loaded in one
-// or a few rounds) take every W-th chunk of the range, loading each chunk's
-// TT + RT operands once (16 bytes a lane, straight from global memory in the
-// MFMA operand layout) for TT * RT products.  The waves' tiles are added in
-// a fixed order through LDS.
+// gfx950 design, two forms:
+// - Up to kIndexerGemvMaxM tokens, indexer_gemv_kernel: one workgroup per
+//   weight row, v_dot2c_f32_bf16 over coalesced 16-byte chunks.
+// - Otherwise indexer_kernel: v_mfma_f32_16x16x32_bf16 with tokens as the M
+//   dimension (16-token tiles, a tile's missing tokens padded with the last
+//   one) and weight rows as the N dimension.  A workgroup owns an output
+//   block of TT token tiles x RT row tiles and one of S contiguous ranges of
+//   the 32-column chunks of K; its W waves take every W-th chunk of the
+//   range, loading each chunk's TT + RT operands once (16 bytes a lane,
+//   straight from global memory in the MFMA operand layout) for TT * RT
+//   products.  The waves' tiles are added in a fixed order through LDS.
+//   (TT, RT, S, W) come from plan_indexer, a rule fitted to measurements.
 //
-// With S = 1 that sum is the output.  With S > 1 (few tokens: the weight is
-// spread over about one workgroup per compute unit) each workgroup stores
-// its block's partial sums in the workspace, and the last of the block's S
+// With S = 1 that sum is the output.  With S > 1 (a workspace, and few
+// enough blocks; S = 8 puts one range on each XCD) each workgroup stores its
+// block's partial sums in the workspace, and the last of the block's S
 // workgroups to finish, found with a device-scope counter, adds the S
 // partials in range order and writes the output; it also sets the counter
 // back to zero for the next call.  Nobody waits, and each output is a sum in
@@ -36,7 +39,7 @@
 // used: it would write back and invalidate the XCD's whole L2, which holds
 // the operands other workgroups re-read.
 #include "device.h"
-#include "kernels.h"
+#include "indexer.h"
 
 namespace mhcb {
 namespace {
@@ -101,10 +104,11 @@ struct PartialWords {
   }
 };
 
-// Few tokens (M <= 4 * NG; used up to kIndexerGemvMaxM, where it is
-// measured faster than the matrix-core form): one workgroup per weight row, the
-// whole row read in one coalesced pass (thread i takes the 16-byte chunks
-// i, i + 256, ...), each token's dot product accumulated with
+// Few tokens (M <= kIndexerGemvMaxM = 4, where it measured faster than the
+// matrix-core form; four token groups at M = 16 took 16.9 us against 8.3):
+// one workgroup per weight row, the whole row read in one coalesced pass
+// (thread i takes the 16-byte chunks i, i + 256, ...), each token's dot
+// product accumulated with
 // v_dot2c_f32_bf16 (exact BF16 products, FP32 sums), then added over the
 // workgroup in a fixed order: a butterfly within each wave, then the waves
 // in order.  The weight read is spread over one workgroup per row (288 for
@@ -114,9 +118,8 @@ constexpr int kGemvWaves = 4;
 constexpr int kGemvThreads = kGemvWaves * kWave;
 constexpr int kGemvPiece = 4;  // 16-byte chunks per thread per round
 
-template <int NG>
 __global__ void __launch_bounds__(kGemvThreads) indexer_gemv_kernel(const IndexerArgs a) {
-  constexpr int kTok = 4 * NG;
+  constexpr int kTok = kIndexerGemvMaxM;
   __shared__ float red[kGemvWaves][kTok];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int row = blockIdx.x, K = a.K, M = a.M, chunks = K / 8;
@@ -126,34 +129,25 @@ __global__ void __launch_bounds__(kGemvThreads) indexer_gemv_kernel(const Indexe
   for (int t = 0; t < kTok; ++t) acc[t] = 0.0f;
 
   for (int j0 = tid; j0 < chunks; j0 += kGemvPiece * kGemvThreads) {
-    u32x4 w[kGemvPiece];
+    u32x4 w[kGemvPiece], xv[kTok][kGemvPiece];
 #pragma unroll
     for (int p = 0; p < kGemvPiece; ++p) {
       const int c = j0 + p * kGemvThreads;
       w[p] = c < chunks ? load_cached(wr + (int64_t)c * 8) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int t = 0; t < kTok; ++t)
+        xv[t][p] = t < M && c < chunks ? load_cached(a.x + (int64_t)t * K + (int64_t)c * 8)
+                                       : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      if (4 * g >= M) break;  // uniform
-      u32x4 xv[4][kGemvPiece];
+    for (int t = 0; t < kTok; ++t)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int p = 0; p < kGemvPiece; ++p) {
-          const int t = 4 * g + q, c = j0 + p * kGemvThreads;
-          xv[q][p] = t < M && c < chunks ? load_cached(a.x + (int64_t)t * K + (int64_t)c * 8)
-                                         : u32x4{0, 0, 0, 0};
-        }
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int p = 0; p < kGemvPiece; ++p) acc[4 * g + q] = dot8(xv[q][p], w[p], acc[4 * g + q]);
-    }
+      for (int p = 0; p < kGemvPiece; ++p) acc[t] = dot8(xv[t][p], w[p], acc[t]);
   }
 
 #pragma unroll
   for (int t = 0; t < kTok; ++t) {
-    if (4 * (t / 4) >= M) break;  // uniform
+    if (t >= M) break;  // uniform
     float v = acc[t];
 #pragma unroll
     for (int o = kWave / 2; o >= 1; o /= 2) v += __shfl_xor(v, o, kWave);
@@ -354,14 +348,14 @@ indexer_kernel(const IndexerArgs a, const int groups, const int blocks, const in
 IndexerPlan plan_indexer(int M, int K, int rows, int cus, bool workspace) {
   IndexerPlan p;
   if (M <= kIndexerGemvMaxM) {
-    p.gemv_groups = (M + 3) / 4;
+    p.gemv = true;
     p.tt = p.rt = p.groups = p.row_groups = p.splits = 1;
     p.blocks = rows;
     p.waves = kGemvWaves;
     p.counter_bytes = p.workspace_bytes = 0;
     return p;
   }
-  p.gemv_groups = 0;
+  p.gemv = false;
   const int tiles = (M + kIdxTile - 1) / kIdxTile, row_tiles = (rows + kIdxTile - 1) / kIdxTile;
   auto shape = [&](int tt, int rt) {
     p.tt = tt;
@@ -424,9 +418,9 @@ void launch_shape(const IndexerArgs &a, const IndexerPlan &p, hipStream_t stream
 }  // namespace
 
 hipError_t launch_indexer(const IndexerArgs &a, const IndexerPlan &p, hipStream_t stream) {
-  if (p.gemv_groups) {
-    if (a.K % 8 || p.gemv_groups != 1 || a.M > 4) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(indexer_gemv_kernel<1>, dim3(a.rows), dim3(kGemvThreads), 0, stream, a);
+  if (p.gemv) {
+    if (a.K % 8 || a.M > kIndexerGemvMaxM) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(indexer_gemv_kernel, dim3(a.rows), dim3(kGemvThreads), 0, stream, a);
     return hipGetLastError();
   }
   if (a.K % 32 || p.splits < 1 || (p.splits > 1 && (!a.parts || !a.counters)) ||
