@@ -1222,12 +1222,13 @@ def check_indexer(ix, got):
                           (7, 128, 8, 0, 8, True), (3, 65536, 8, 4, 4, True),
                           (4, 2048, 128, 32, 128, True), (9, 6144, 128, 32, 128, True),
                           (4, 6144, 128, 32, 128, True), (8, 6144, 128, 32, 128, True),
+                          (6, 6144, 128, 32, 128, True),
                           (2500, 1024, 128, 32, 128, True)],
                          ids=lambda v: str(v))
 def test_indexer_projection_matches_oracle(M, K, key, heads, gate, workspace):
     """mhcb_indexer_projection against the oracle (bars in check_indexer).
-    The one-workgroup-per-row form (M <= 4) and the matrix-core form
-    (M >= 5) with K split over workgroups
+    The one-workgroup-per-row form (M <= 4 and 5 .. 6) and the matrix-core
+    form (M >= 7) with K split over workgroups
     (workspace) or summed by one workgroup (none, or K too short to split),
     every output block shape (M=64, 256, 300), ragged token and row tiles,
     the largest K, an empty part; results repeat bit for bit."""

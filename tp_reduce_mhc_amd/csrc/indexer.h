@@ -19,12 +19,12 @@ struct IndexerArgs {
   uint32_t *counters;    // one per output block, zero between calls (splits > 1)
   int M, K, key, heads, gate, rows;
 };
-constexpr int kIndexerGemvMaxM = 4;  // tokens of the one-workgroup-per-row form, at most
+constexpr int kIndexerGemvMaxM = 6;  // tokens of the one-workgroup-per-row form, at most
 constexpr int kIndexerCounters = 1024;  // output blocks of a call with K ranges, at most
 // The launch shape of one projection: output blocks of tt token tiles x rt
 // row tiles, K cut into `splits` ranges, and the workspace that needs.
 struct IndexerPlan {
-  bool gemv;             // one workgroup per weight row (M <= kIndexerGemvMaxM)
+  int gemv;              // 4 or 8: one workgroup per weight row, that many tokens at most; 0: MFMA blocks
   int tt, rt, groups, row_groups, blocks, splits, waves;
   int64_t counter_bytes, workspace_bytes;
 };

@@ -8,8 +8,8 @@
 // exact in FP32; only the order of the sum is the kernel's.
 //
 // gfx950 design, two forms:
-// - Up to kIndexerGemvMaxM tokens, indexer_gemv_kernel: one workgroup per
-//   weight row, v_dot2c_f32_bf16 over coalesced 16-byte chunks.
+// - Up to kIndexerGemvMaxM (6) tokens, indexer_gemv_kernel: one workgroup
+//   per weight row, v_dot2c_f32_bf16 over coalesced 16-byte chunks.
 // - Otherwise indexer_kernel: v_mfma_f32_16x16x32_bf16 with tokens as the M
 //   dimension (16-token tiles, a tile's missing tokens padded with the last
 //   one) and weight rows as the N dimension.  A workgroup owns an output
@@ -104,9 +104,12 @@ struct PartialWords {
   }
 };
 
-// Few tokens (M <= kIndexerGemvMaxM = 4, where it measured faster than the
-// matrix-core form; four token groups at M = 16 took 16.9 us against 8.3):
-// one workgroup per weight row, the whole row read in one coalesced pass
+// Few tokens (M <= kIndexerGemvMaxM = 6, where it measured faster than the
+// matrix-core form: M = 5 / 6 took 5.0 / 5.4 us against 6.2 / 6.2; at M = 8
+// the two were within 3% and over cold inputs the matrix cores won, 6.8
+// against 7.0 us; sixteen tokens in four groups took 16.9 us against 8.3),
+// TOK = 4 or 8 tokens a launch (TOK = 8 at M <= 4 cost 4.7 us against 4.3:
+// its registers halve the waves a SIMD holds): one workgroup per weight row, the whole row read in one coalesced pass
 // (thread i takes the 16-byte chunks i, i + 256, ...), each token's dot
 // product accumulated with
 // v_dot2c_f32_bf16 (exact BF16 products, FP32 sums), then added over the
@@ -118,8 +121,9 @@ constexpr int kGemvWaves = 4;
 constexpr int kGemvThreads = kGemvWaves * kWave;
 constexpr int kGemvPiece = 4;  // 16-byte chunks per thread per round
 
+template <int TOK>
 __global__ void __launch_bounds__(kGemvThreads) indexer_gemv_kernel(const IndexerArgs a) {
-  constexpr int kTok = kIndexerGemvMaxM;
+  constexpr int kTok = TOK;
   __shared__ float red[kGemvWaves][kTok];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int row = blockIdx.x, K = a.K, M = a.M, chunks = K / 8;
@@ -348,14 +352,14 @@ indexer_kernel(const IndexerArgs a, const int groups, const int blocks, const in
 IndexerPlan plan_indexer(int M, int K, int rows, int cus, bool workspace) {
   IndexerPlan p;
   if (M <= kIndexerGemvMaxM) {
-    p.gemv = true;
+    p.gemv = M <= 4 ? 4 : 8;
     p.tt = p.rt = p.groups = p.row_groups = p.splits = 1;
     p.blocks = rows;
     p.waves = kGemvWaves;
     p.counter_bytes = p.workspace_bytes = 0;
     return p;
   }
-  p.gemv = false;
+  p.gemv = 0;
   const int tiles = (M + kIdxTile - 1) / kIdxTile, row_tiles = (rows + kIdxTile - 1) / kIdxTile;
   auto shape = [&](int tt, int rt) {
     p.tt = tt;
@@ -419,8 +423,11 @@ void launch_shape(const IndexerArgs &a, const IndexerPlan &p, hipStream_t stream
 
 hipError_t launch_indexer(const IndexerArgs &a, const IndexerPlan &p, hipStream_t stream) {
   if (p.gemv) {
-    if (a.K % 8 || a.M > kIndexerGemvMaxM) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(indexer_gemv_kernel, dim3(a.rows), dim3(kGemvThreads), 0, stream, a);
+    if (a.K % 8 || a.M > p.gemv || (p.gemv != 4 && p.gemv != 8)) return hipErrorInvalidValue;
+    if (p.gemv == 4)
+      hipLaunchKernelGGL(indexer_gemv_kernel<4>, dim3(a.rows), dim3(kGemvThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL(indexer_gemv_kernel<8>, dim3(a.rows), dim3(kGemvThreads), 0, stream, a);
     return hipGetLastError();
   }
   if (a.K % 32 || p.splits < 1 || (p.splits > 1 && (!a.parts || !a.counters)) ||
