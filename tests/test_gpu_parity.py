@@ -307,7 +307,9 @@ def test_graph_replays_match_eager_calls():
     replayed three times, with eager calls on the same workspace in between,
     give the eager results every time (the tags the exchanges wait for are
     read from the workspace at each replay, not frozen into the graph), and
-    those results match the oracle to each call's parity bar."""
+    those results match the oracle to each call's parity bar.  The DSA
+    indexer projection with K ranges is in the graph too; its counters are
+    zero again after the last replay."""
     b = synth.boundary(17, 8, 1024, 8, 0.5, "graph-delayed")
     f = synth.moe_finalize(8, H=1024)
     g = synth.glm(40, H=2048)
@@ -341,6 +343,18 @@ def test_graph_replays_match_eager_calls():
     gm = synth.glm(f.M, H=f.H, tp=f.tp)
     dgm = {k: dev(getattr(gm, k)) for k in ("fn", "scale", "base", "gamma")}
     ws_moe = mhc.new_workspace(mhc.mhcb_finalize_glm_workspace_bytes(f.M, f.H, f.tp), "cuda")
+    # The DSA indexer projection with K ranges (its counters must be back
+    # at zero after every call and replay).
+    ix = synth.indexer(16, K=2048)
+    dix = {"x": dev(ix.x), "w": dev(ix.w)}
+    ix_bytes = mhc.mhcb_indexer_workspace_bytes(ix.M, ix.K, ix.key, ix.heads, ix.gate)
+    assert ix_bytes > 0
+    ws_ix = torch.empty(ix_bytes, dtype=torch.uint8, device="cuda")
+    mhc.mhcb_indexer_workspace_init(ws_ix, ix_bytes)
+    outs["i_key"] = torch.empty((ix.M, ix.key), dtype=torch.bfloat16, device="cuda")
+    outs["i_heads"] = torch.empty((ix.M, ix.heads), dtype=torch.float32, device="cuda")
+    outs["i_gate"] = torch.empty((ix.M, ix.gate), dtype=torch.bfloat16, device="cuda")
+    eager_ix = [torch.empty_like(outs[k]) for k in ("i_key", "i_heads", "i_gate")]
 
     def calls():
         mhc.mhcb_boundary(db["partials"], b.M * b.H, None, db["residual"], db["post"], db["comb"],
@@ -365,6 +379,9 @@ def test_graph_replays_match_eager_calls():
                               dgm["fn"], dgm["scale"], dgm["base"], dgm["gamma"], outs["m_ro"],
                               outs["m_mx"], outs["m_li"], ws_moe, ws_moe.numel(), f.M, f.H, 4,
                               f.tp, f.top_k, gm.rms_eps, gm.hc_eps, gm.norm_eps)
+        mhc.mhcb_indexer_projection(dix["x"], dix["w"], outs["i_key"], outs["i_heads"],
+                                    outs["i_gate"], ws_ix, ix_bytes, ix.M, ix.K, ix.key, ix.heads,
+                                    ix.gate)
 
     calls()
     torch.cuda.synchronize()
@@ -379,6 +396,8 @@ def test_graph_replays_match_eager_calls():
         for v in outs.values():
             v.fill_(0x5A if v.dtype == torch.uint8 else float("nan"))
         run_boundary_split(b, ws)                       # eager work on the same workspace
+        mhc.mhcb_indexer_projection(dix["x"], dix["w"], *eager_ix, ws_ix, ix_bytes, ix.M, ix.K,
+                                    ix.key, ix.heads, ix.gate)  # and on the indexer's
         graph.replay()
         torch.cuda.synchronize()
         for k, v in outs.items():
@@ -415,6 +434,8 @@ def test_graph_replays_match_eager_calls():
     check_glm_outputs("graph glm moe", u16(outs["m_ro"]), host(outs["m_mx"]), u16(outs["m_li"]),
                       ro_ref, mix_ref, li_ref, pre_ref, gm.scale, gm.base, gm.gamma, gm.hc_eps,
                       gm.norm_eps)
+    check_indexer(ix, (u16(outs["i_key"]), host(outs["i_heads"]), u16(outs["i_gate"])))
+    assert not ws_ix[:4096].any(), "indexer counters back at zero"
 
 
 def test_cross_token_independence_and_determinism():
