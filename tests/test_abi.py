@@ -266,6 +266,22 @@ def test_indexer_workspace_bytes():
         mhc.mhcb_indexer_workspace_init(None, 256, 0)
 
 
+def test_indexer_projection_object_validates_shapes():
+    """IndexerProjection rejects weights that are not 2-D BF16 with one K,
+    before any device work."""
+    import torch
+    import tp_reduce_mhc_amd as mhc
+    k, h, g = (torch.zeros((r, 256), dtype=torch.bfloat16) for r in (16, 8, 8))
+    with pytest.raises(ValueError, match="share K"):
+        mhc.IndexerProjection(k, h, torch.zeros((8, 128), dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="BF16"):
+        mhc.IndexerProjection(k, h.float(), g)
+    proj = mhc.IndexerProjection(k, h, g)
+    assert (proj.key, proj.heads, proj.gate) == (16, 8, 8) and proj.weight.shape == (32, 256)
+    with pytest.raises(ValueError, match="K"):
+        proj(torch.zeros((2, 128), dtype=torch.bfloat16))
+
+
 def test_product_path_does_not_touch_the_oracle():
     """The binding and the HIP sources never import, load or name the
     oracle's library or module."""

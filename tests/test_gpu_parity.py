@@ -1261,6 +1261,22 @@ def test_indexer_projection_matches_oracle(M, K, key, heads, gate, workspace):
     assert all(np.array_equal(p, q) for p, q in zip(again, got)), "not repeatable"
 
 
+def test_indexer_projection_object_matches_the_entry_point():
+    """mhc.IndexerProjection (the page's class: the three weight parts held
+    concatenated, called on x) gives the bits of mhcb_indexer_projection on
+    the concatenated weight, in both forms (M = 3 and 40)."""
+    for M in (3, 40):
+        ix = synth.indexer(M, K=2048)
+        w = dev(ix.w)
+        proj = mhc.IndexerProjection(w[:ix.key], w[ix.key:ix.key + ix.heads], w[ix.key + ix.heads:])
+        print(f"[gpu] {ix.name} through IndexerProjection", flush=True)
+        got = proj(dev(ix.x))
+        torch.cuda.synchronize()
+        want = run_indexer(ix, "cached")
+        assert np.array_equal(u16(got[0]), want[0]) and np.array_equal(host(got[1]), want[1])
+        assert np.array_equal(u16(got[2]), want[2])
+
+
 def test_indexer_workspace_reused_across_sizes():
     """One workspace, zeroed once, serves calls of different M in a row (the
     kernels leave its counters at zero, and no call's partials overlap the

@@ -6,7 +6,7 @@ package is its thin Python binding.  See ``tp_reduce_mhc_amd.mhcb``.
 """
 from .mhcb import (  # noqa: F401
     EXPORTED, LIBRARY_PATH, MHCB_EALIGN, MHCB_EINVAL, MHCB_ELAUNCH, MHCB_ETIMEOUT,
-    MHCB_EUNSUPPORTED, MHCB_OK, GlmBoundary, Mailbox, MhcbError, boundary, boundary_glm, finalize,
+    MHCB_EUNSUPPORTED, MHCB_OK, GlmBoundary, IndexerProjection, Mailbox, MhcbError, boundary, boundary_glm, finalize,
     mhcb_boundary, mhcb_boundary_glm, mhcb_boundary_glm_noalloc, mhcb_finalize, mhcb_finalize_ex,
     mhcb_finalize_glm, mhcb_finalize_glm_workspace_bytes, finalize_glm, mhcb_workspace_bytes,
     mhcb_workspace_init, mhcb_workspace_status, mhcb_set_token_slices, new_workspace, workspace,

@@ -564,6 +564,31 @@ class Mailbox:
         return mailbox_status(self, stream)[0] == 0
 
 
+class IndexerProjection:
+    """The DSA indexer projection over fixed weights (the indexer page's
+    IndexerProjection): the key rows [key_rows, K], the head-weight rows
+    [heads, K] and the kpool gate rows [gate_rows, K] (BF16) held as one
+    concatenated [key_rows + heads + gate_rows, K] matrix; calling it on the
+    layer input x [M, K] returns (key [M, key_rows] BF16, head weights
+    [M, heads] FP32, gate [M, gate_rows] BF16)."""
+
+    def __init__(self, key_weight, head_weight, gate_weight):
+        parts = (key_weight, head_weight, gate_weight)
+        if any(w.dtype != torch.bfloat16 or w.dim() != 2 for w in parts):
+            raise ValueError("indexer weights must be 2-D BF16 tensors")
+        K = key_weight.shape[1]
+        if any(w.shape[1] != K for w in parts):
+            raise ValueError("indexer weights must share K")
+        self.key, self.heads, self.gate = (w.shape[0] for w in parts)
+        self.weight = torch.cat(parts).contiguous()
+
+    def __call__(self, x, *, stream=None):
+        if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[1] != self.weight.shape[1]:
+            raise ValueError("x must be a BF16 [M, K] tensor with the weights' K")
+        return indexer_projection(x.contiguous(), self.weight, self.key, self.heads, self.gate,
+                                  stream=stream)
+
+
 class GlmBoundary:
     """The GLM boundary with its side stream: each call runs the boundary on
     the current stream and the post/Sinkhorn mixes on a side stream; `join`
