@@ -1243,7 +1243,7 @@ def check_indexer(ix, got):
                           (7, 128, 8, 0, 8, True), (3, 65536, 8, 4, 4, True),
                           (4, 2048, 128, 32, 128, True), (9, 6144, 128, 32, 128, True),
                           (4, 6144, 128, 32, 128, True), (8, 6144, 128, 32, 128, True),
-                          (6, 6144, 128, 32, 128, True),
+                          (6, 6144, 128, 32, 128, True), (17, 128, 4000, 64, 32, True),
                           (2500, 1024, 128, 32, 128, True)],
                          ids=lambda v: str(v))
 def test_indexer_projection_matches_oracle(M, K, key, heads, gate, workspace):
@@ -1252,7 +1252,8 @@ def test_indexer_projection_matches_oracle(M, K, key, heads, gate, workspace):
     form (M >= 7) with K split over workgroups
     (workspace) or summed by one workgroup (none, or K too short to split),
     every output block shape (M=64, 256, 300), ragged token and row tiles,
-    the largest K, an empty part; results repeat bit for bit."""
+    the largest K and the most rows (4096), an empty part; results repeat
+    bit for bit."""
     ix = synth.indexer(M, K, key, heads, gate)
     print(f"[gpu] {ix.name} workspace={workspace}", flush=True)
     got = run_indexer(ix, "cached" if workspace else None)
