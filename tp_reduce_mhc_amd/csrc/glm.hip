@@ -1021,16 +1021,20 @@ glm_finish_kernel(const GlmArgs a) {
   const int H = a.H, F = H / kFrag, tid = threadIdx.x, S = a.slices;
   const int64_t t = blockIdx.x;
   const bool valid = tid < F;
-  const int64_t col = valid ? (int64_t)tid * kFrag : 0;
-  // The token's S x 128-byte partials, one 16-byte load per thread, issued
-  // with the residual_out rows.
-  const u32x4 *pt = reinterpret_cast<const u32x4 *>(a.parts + t * S * kPartWords);
-  for (int i = tid; i < S * (kPartWords / 4); i += blockDim.x) staged[i] = pt[i];
+  const int64_t col = valid ? (int64_t)tid * kFrag : 0;  // in bounds for every thread
+  // Every load is issued before the first wait: the token's residual_out
+  // rows, gamma and the pre-mix's scale and bias (a thread past the last
+  // fragment reads column 0 and leaves it unused), then its S x 128-byte
+  // partials, staged through LDS.
+  // (With the partials first, their LDS store waited for them before the
+  // rows were even requested: two round trips in a row.)
   u32x4 y[kStreams];
 #pragma unroll
-  for (int j = 0; j < kStreams; ++j)
-    y[j] = valid ? load_cached(a.residual_out + (t * kStreams + j) * H + col) : u32x4{0, 0, 0, 0};
-  const u32x4 gam = valid ? load_cached(a.gamma + col) : u32x4{0, 0, 0, 0};
+  for (int j = 0; j < kStreams; ++j) y[j] = load_cached(a.residual_out + (t * kStreams + j) * H + col);
+  const u32x4 gam = load_cached(a.gamma + col);
+  const float scale0 = a.scale[0], base_j = a.base[tid < kStreams ? tid : 0];
+  const u32x4 *pt = reinterpret_cast<const u32x4 *>(a.parts + t * S * kPartWords);
+  for (int i = tid; i < S * (kPartWords / 4); i += blockDim.x) staged[i] = pt[i];
   __syncthreads();
   // Slice order: rows by threads 0..23, the binary64 sum by thread 24.
   const float *sp = reinterpret_cast<const float *>(staged);
@@ -1049,7 +1053,7 @@ glm_finish_kernel(const GlmArgs a) {
     const float rstd = (float)(1.0 / __builtin_sqrt((double)(float)tot / (4.0 * H) + (double)a.rms_eps));
     const float m = mix[tid] * rstd;
     a.mixes_out[t * kMix + tid] = m;
-    if (tid < kStreams) pre[tid] = sigmoid(__builtin_fmaf(m, a.scale[0], a.base[tid])) + a.hc_eps;
+    if (tid < kStreams) pre[tid] = sigmoid(__builtin_fmaf(m, scale0, base_j)) + a.hc_eps;
   }
   __syncthreads();
   // a4: p = bf16((q0+q1)+(q2+q3)), q_j = y_j * pre_j; RMSNorm over H.
