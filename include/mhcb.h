@@ -322,19 +322,22 @@ int mhcb_finalize_glm(const uint16_t *gemm2_permuted, int64_t gemm2_rank_stride,
  * each part written in its own type: key_out [M, key_rows] BF16 (nearest
  * even), heads_out [M, heads] FP32, gate_out [M, gate_rows] BF16.
  *
- * workspace: NULL, or at least mhcb_indexer_workspace_bytes(...) bytes,
- * 256-byte aligned, set to zero by mhcb_indexer_workspace_init (or any
- * zero fill) before its first use.  With a workspace and few tokens, K is
- * cut into ranges summed by different workgroups (partials and per-block
- * counters in the workspace; every call leaves the counters at zero again),
- * which spreads the weight read over the whole device; without one each
- * output is summed by a single workgroup.  Calls that share a workspace
- * must not overlap (same stream, or ordered).  Each output is summed in a
- * fixed order for a given M, device and workspace choice, so results repeat
- * bit for bit.  The workspace size depends on the current device's compute
- * unit count (0 when K is not split).  K a multiple of 128 up to 65536 and
- * at most 4096 rows (EUNSUPPORTED beyond); M >= 1; a part with no rows may
- * pass NULL for its output. */
+ * Up to six tokens, each weight row is summed by one workgroup and no
+ * workspace is used.  From seven tokens on, a workspace lets K be cut into
+ * ranges summed by different workgroups, which spreads the weight read over
+ * the device: partial sums and per-block counters (a fixed 4 KiB area at its
+ * start) live in the workspace, and every call leaves the counters at zero
+ * again.  Without a workspace, each output is summed by a single workgroup.
+ *
+ * workspace: NULL, or at least mhcb_indexer_workspace_bytes(...) bytes
+ * (which depends on M, K and the row counts; 0 where K is not cut),
+ * 256-byte aligned, set to zero by mhcb_indexer_workspace_init (or any zero
+ * fill) before its first use; EINVAL if smaller.  Calls that share a
+ * workspace must not overlap (same stream, or ordered).  Each output is
+ * summed in a fixed order for a given M and workspace choice, so results
+ * repeat bit for bit.  K a multiple of 128 up to 65536 and at most 4096 rows
+ * (EUNSUPPORTED beyond); M >= 1; a part with no rows may pass NULL for its
+ * output. */
 int64_t mhcb_indexer_workspace_bytes(int M, int K, int key_rows, int heads, int gate_rows);
 int mhcb_indexer_workspace_init(void *workspace, int64_t workspace_bytes, hipStream_t stream);
 int mhcb_indexer_projection(const uint16_t *x, const uint16_t *weight, uint16_t *key_out,
