@@ -104,19 +104,19 @@ struct PartialWords {
   }
 };
 
-// Few tokens (M <= kIndexerGemvMaxM = 6, where it measured faster than the
-// matrix-core form: M = 5 / 6 took 5.0 / 5.4 us against 6.2 / 6.2; at M = 8
-// the two were within 3% and over cold inputs the matrix cores won, 6.8
-// against 7.0 us; sixteen tokens in four groups took 16.9 us against 8.3),
-// TOK = 4 or 8 tokens a launch (TOK = 8 at M <= 4 cost 4.7 us against 4.3:
-// its registers halve the waves a SIMD holds): one workgroup per weight row, the whole row read in one coalesced pass
-// (thread i takes the 16-byte chunks i, i + 256, ...), each token's dot
-// product accumulated with
-// v_dot2c_f32_bf16 (exact BF16 products, FP32 sums), then added over the
-// workgroup in a fixed order: a butterfly within each wave, then the waves
-// in order.  The weight read is spread over one workgroup per row (288 for
-// the 288-row projection), with no partials and no second pass; the tokens'
+// Few tokens (M <= kIndexerGemvMaxM = 6), indexer_gemv_kernel<TOK>, TOK = 4
+// or 8 tokens a launch: one workgroup per weight row (288 for the 288-row
+// projection), the whole row read in one coalesced pass (thread i takes the
+// 16-byte chunks i, i + 256, ...).  Each token's dot product accumulates
+// with v_dot2c_f32_bf16 (exact BF16 products, FP32 sums) and is added over
+// the workgroup in a fixed order: a butterfly within each wave, then the
+// waves in order.  There are no partials and no second pass; the tokens'
 // rows are re-read from L2 by every workgroup.
+// Measured on MI355X: M = 5 / 6 took 5.0 / 5.4 us against 6.2 / 6.2 with
+// the matrix-core form; at M = 8 the two were within 3% and over cold
+// inputs the matrix cores won (6.8 against 7.0 us); sixteen tokens in four
+// groups took 16.9 us against 8.3.  TOK = 8 at M <= 4 cost 4.7 us against
+// 4.3 for TOK = 4: its registers halve the waves a SIMD holds.
 constexpr int kGemvWaves = 4;
 constexpr int kGemvThreads = kGemvWaves * kWave;
 constexpr int kGemvPiece = 4;  // 16-byte chunks per thread per round
