@@ -282,6 +282,40 @@ def test_indexer_projection_object_validates_shapes():
         proj(torch.zeros((2, 128), dtype=torch.bfloat16))
 
 
+def test_workspace_cache_grows_by_doubling_and_keeps_replaced_buffers():
+    """The binding's per-(device, stream) workspace caches: a request no
+    larger than the cached buffer reuses it; a larger one replaces it with a
+    buffer at least twice its size and keeps the old one alive (a captured
+    graph or queued call may still use it), so the retired buffers never add
+    up to more than the live one."""
+    from tp_reduce_mhc_amd import mhcb
+
+    class Buf:
+        def __init__(self, n):
+            self.n = n
+
+        def numel(self):
+            return self.n
+
+    made, cache, retired_before = [], {}, len(mhcb._RETIRED)
+
+    def make(n):
+        made.append(n)
+        return Buf(n)
+
+    try:
+        for need in (100, 150, 90, 400, 1000, 1001):
+            live = mhcb._cached(cache, ("dev", 0), need, make)
+            assert live.numel() >= need
+        assert made == [100, 200, 400, 1000, 2000]
+        retired = mhcb._RETIRED[retired_before:]
+        assert [b.numel() for b in retired] == [100, 200, 400, 1000]
+        assert sum(b.numel() for b in retired) <= live.numel()
+        assert mhcb._cached(cache, ("dev", 1), 10, make).numel() == 10  # another stream
+    finally:
+        del mhcb._RETIRED[retired_before:]
+
+
 def test_product_path_does_not_touch_the_oracle():
     """The binding and the HIP sources never import, load or name the
     oracle's library or module."""

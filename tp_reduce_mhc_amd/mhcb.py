@@ -275,18 +275,19 @@ _indexer_workspaces: dict = {}
 
 def indexer_workspace(nbytes: int, device=None, stream=None):
     """The zeroed indexer workspace of (device, stream), grown to the
-    largest size asked for so far (a new one is zeroed; the kernels leave
-    the counters at zero)."""
+    largest size asked for so far (a new one is zeroed on `stream`; the
+    kernels leave the counters at zero).  Growth keeps the replaced buffer
+    alive, as ``workspace`` does."""
     dev = torch.device(device if device is not None else "cuda")
     if dev.index is None:
         dev = torch.device("cuda", torch.cuda.current_device())
-    key = (dev, _stream(stream) or 0)
-    ws = _indexer_workspaces.get(key)
-    if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+
+    def make(size):
+        ws = _alloc_on(size, dev, stream)
         mhcb_indexer_workspace_init(ws, ws.numel(), stream)
-        _indexer_workspaces[key] = ws
-    return ws
+        return ws
+
+    return _cached(_indexer_workspaces, (dev.index, _stream(stream) or 0), max(nbytes, 256), make)
 
 
 def indexer_projection(x, weight, key_rows: int, heads: int, gate_rows: int, *, stream=None):
@@ -340,6 +341,31 @@ def _bf16_empty(shape, device):
 
 
 _WORKSPACES = {}
+# Buffers a cache has replaced: a graph captured with one, or a call still
+# queued on another stream, keeps using it, so it is never handed back to
+# torch's allocator.  Growth at least doubles, so together they are never
+# larger than the buffer that replaced them.
+_RETIRED: list = []
+
+
+def _alloc_on(nbytes: int, device, stream) -> torch.Tensor:
+    """nbytes of device memory allocated for `stream` (torch's allocator
+    then orders its reuse after the work queued there)."""
+    if stream is not None and not isinstance(stream, int):
+        with torch.cuda.stream(stream):
+            return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _cached(cache: dict, key, need: int, make) -> torch.Tensor:
+    ws = cache.get(key)
+    if ws is None or ws.numel() < need:
+        if ws is not None:
+            need = max(need, 2 * ws.numel())
+            _RETIRED.append(ws)
+        ws = make(need)
+        cache[key] = ws
+    return ws
 
 
 def workspace(device=None, *, M: int = 0, hidden_size: int = 0, tp: int = 1,
@@ -348,30 +374,22 @@ def workspace(device=None, *, M: int = 0, hidden_size: int = 0, tp: int = 1,
     (mhcb_workspace_bytes, or nbytes if larger), one per (device, stream):
     calls on one stream are ordered, so they may share it, and calls on
     different streams get different ones.  The cached workspace only grows:
-    a larger request replaces it (allocated and initialized on `stream`),
-    so memory stays bounded by the largest call."""
+    a larger request replaces it with one at least twice its size
+    (allocated and initialized on `stream`); the replaced one stays
+    allocated, so memory stays within twice the largest call's."""
     device = torch.device(device if device is not None else "cuda")
     if device.index is None:
         device = torch.device("cuda", torch.cuda.current_device())
     need = max(mhcb_workspace_bytes(M, hidden_size, tp, int(two_shot)), nbytes)
-    handle = _stream(stream) or 0
-    key = (device.index, handle)
-    ws = _WORKSPACES.get(key)
-    if ws is None or ws.numel() < need:
-        ws = new_workspace(need, device, stream)
-        _WORKSPACES[key] = ws
-    return ws
+    return _cached(_WORKSPACES, (device.index, _stream(stream) or 0), need,
+                   lambda size: new_workspace(size, device, stream))
 
 
 def new_workspace(nbytes: int, device, stream=None) -> torch.Tensor:
     """A fresh workspace of `nbytes` (256-byte aligned by torch), allocated
     for and initialized by mhcb_workspace_init on `stream` (the current
     stream by default)."""
-    if stream is not None and not isinstance(stream, int):
-        with torch.cuda.stream(stream):
-            ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
-    else:
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    ws = _alloc_on(nbytes, device, stream)
     mhcb_workspace_init(ws, nbytes, stream)
     return ws
 
