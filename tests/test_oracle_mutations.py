@@ -86,6 +86,10 @@ MUTANTS = [
     ("indexer: FP32 sum",
      "      double s = 0.0;\n      for (int k = 0; k < K; ++k)\n        s += (double)bf(x[(int64_t)t * K + k]) * (double)bf(w[(int64_t)r * K + k]);",
      "      float s = 0.0f;\n      for (int k = 0; k < K; ++k)\n        s += bf(x[(int64_t)t * K + k]) * bf(w[(int64_t)r * K + k]);"),
+    ("indexer: weight indexed column-major",
+     "(double)bf(w[(int64_t)r * K + k]);", "(double)bf(w[(int64_t)k * rows + r]);"),
+    ("indexer: last K column dropped", "      for (int k = 0; k < K; ++k)\n        s += (double)",
+     "      for (int k = 0; k < K - 1; ++k)\n        s += (double)"),
 ]
 
 
