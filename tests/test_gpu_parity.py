@@ -813,6 +813,72 @@ def test_mailbox_large_m_with_mxfp8():
     assert (u16(mb.slots) == 0x8000).all()
 
 
+def test_graph_replays_mailbox_publish_and_consume():
+    """The mailbox chain captured in one HIP graph: the producer's publish of
+    all tp ranks, then the mailbox-fed boundary split over slices of a
+    workspace.  Four replays, with an eager publish + consume pair on other
+    inputs after the first and third (so replays start from different
+    generations): the kernels read the generation from stage_state at run
+    time, so after every replay stage_state and every slot equal the host
+    model's, and the outputs equal the oracle's to the parity bar."""
+    from oracle.mailbox_model import MailboxModel
+    cap, H, tp, M = 32, 1024, 4, 9
+    b = synth.boundary(41, M, H, tp, 0.5, "graph-mailbox")
+    e = synth.boundary(42, M, H, tp, 0.5, "graph-mailbox-eager")
+    mb = mhc.Mailbox(tp, cap, H, "cuda")
+    mb.init()
+    model = MailboxModel(tp, cap, H)
+    ws = mhc.new_workspace(mhc.mhcb_workspace_bytes(0, 0, 1, 0), "cuda")
+    names = ("partials", "residual", "post", "comb", "pre", "gamma")
+    db, de = ({k: dev(getattr(x, k)) for k in names} for x in (b, e))
+    ro = torch.empty((M, 4, H), dtype=torch.bfloat16, device="cuda")
+    li = torch.empty((M, H), dtype=torch.bfloat16, device="cuda")
+    ro_e, li_e = torch.empty_like(ro), torch.empty_like(li)
+
+    def chain(d, ro_out, li_out):
+        mhc.mhcb_publish(mb, d["partials"], M * H, 0, tp, M)
+        mhc.mhcb_boundary(None, 0, mb, d["residual"], d["post"], d["comb"], d["pre"], d["gamma"],
+                          ro_out, li_out, None, None, ws, ws.numel(), M, H, 4, tp, b.norm_eps)
+
+    def check(label, x, ro_got, li_got):
+        assert mb.status_ok(), label
+        assert np.array_equal(host(mb.stage_state), model.stage), f"{label}: stage_state"
+        assert_bits_equal(u16(mb.slots), model.slots, f"{label}: slots")
+        ro_ref, li_ref, _ = oracle.boundary(x.partials, x.residual, x.post, x.comb, x.pre,
+                                            x.gamma, x.norm_eps)
+        assert_bits_equal(u16(ro_got), ro_ref, f"{label}: residual_out")
+        assert_within_ulp(u16(li_got), li_ref, 1, f"{label}: layer_input")
+
+    chain(db, ro, li)  # eager first call (and warm-up)
+    torch.cuda.synchronize()
+    model.publish(b.partials)
+    model.consume(M)
+    check("eager", b, ro, li)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        chain(db, ro, li)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(mb.stage_state), model.stage), "capture ran nothing"
+    for rep in range(4):
+        print(f"[gpu] mailbox graph replay {rep}", flush=True)
+        ro.fill_(float("nan"))
+        li.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        model.publish(b.partials)
+        model.consume(M)
+        check(f"replay {rep}", b, ro, li)
+        if rep % 2 == 0:
+            chain(de, ro_e, li_e)
+            torch.cuda.synchronize()
+            model.publish(e.partials)
+            model.consume(M)
+            check(f"eager after replay {rep}", e, ro_e, li_e)
+    assert mhc.workspace_status(ws) == mhc.MHCB_OK
+
+
 def test_mailbox_poll_gives_up_with_a_bounded_spin():
     """A consumer whose producer never publishes: a tiny spin limit makes
     every poll give up (all kernels exit normally), the status words count
