@@ -229,15 +229,17 @@ def bench_delayed(torch, mhc, b, steps, warmup, mxfp8=False, check=False):
     return ms, per_set, len(sets)
 
 
-def bench_mailbox(torch, mhc, b, steps, warmup):
-    """Producer (publish of all tp partials) + mailbox-fed consumer with the
-    MXFP8 epilogue, per step."""
+def bench_mailbox(torch, mhc, b, steps, warmup, mxfp8=True):
+    """Producer (publish of all tp partials) + mailbox-fed consumer (with the
+    MXFP8 epilogue when `mxfp8`), per step, over rotating input sets."""
     mb = mhc.Mailbox(b.tp, b.M, b.H, "cuda")
     mb.init()
-    sets = delayed_sets(torch, b, 2)
+    nbytes = bytes_delayed(b.M, b.H, b.tp, mxfp8) + bytes_mailbox_extra(b.M, b.H, b.tp)
+    sets = delayed_sets(torch, b, rotations(nbytes, minimum=2))
     for s in sets:
-        s["values"] = torch.empty((b.M, b.H), dtype=torch.uint8, device="cuda")
-        s["scales"] = torch.empty(mhc.mhcb_mxfp8_scale_bytes(b.M, b.H), dtype=torch.uint8, device="cuda")
+        s["values"] = torch.empty((b.M, b.H), dtype=torch.uint8, device="cuda") if mxfp8 else None
+        s["scales"] = (torch.empty(mhc.mhcb_mxfp8_scale_bytes(b.M, b.H), dtype=torch.uint8,
+                                   device="cuda") if mxfp8 else None)
 
     ws = mhc.workspace(torch.device("cuda", torch.cuda.current_device()))
 
@@ -250,7 +252,7 @@ def bench_mailbox(torch, mhc, b, steps, warmup):
 
     ms = Timed(torch, call, steps, warmup).run()
     assert mb.status_ok()
-    return ms, bytes_delayed(b.M, b.H, b.tp, True) + bytes_mailbox_extra(b.M, b.H, b.tp)
+    return ms, nbytes
 
 
 def bench_finalize(torch, mhc, f, steps, warmup, two_shot=False, bf16_weights=False, scale=1.0):
@@ -642,6 +644,11 @@ def main():
             ms, nbytes = bench_mailbox(torch, mhc, b, 10, 2)
             extra["mailbox_mxfp8_M8192"] = entry(ms, nbytes, 8192)
             log(f"mailbox M=8192: {extra['mailbox_mxfp8_M8192']}")
+            for M in (1, 64):  # publish + consume at decode sizes (H=5120, tp=8)
+                bm = synth.dsv41_delayed(M)
+                ms, nbytes = bench_mailbox(torch, mhc, bm, min(K, 200), W, mxfp8=False)
+                extra[f"mailbox_publish_consume_M{M}"] = entry(ms, nbytes, M)
+                log(f"mailbox publish + consume M={M}: {extra[f'mailbox_publish_consume_M{M}']}")
     if "copy" in only:
         # Calibration for the HBM byte counters: a plain device copy of a
         # known size (read n bytes, write n bytes), launched `steps` times.
