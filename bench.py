@@ -412,7 +412,10 @@ def bytes_indexer(M, K, key, heads, gate):
     return (key + heads + gate) * K * 2 + M * (K * 2 + key * 2 + heads * 4 + gate * 2)
 
 
-def bench_indexer(torch, mhc, ix, steps, warmup):
+def bench_indexer(torch, mhc, ix, steps, warmup, torch_matmul=False):
+    """The DSA indexer projection over rotating input sets; with
+    `torch_matmul`, torch's x @ w.T (hipBLASLt) on the same sets, timed the
+    same way, as the library GEMM to compare with."""
     per_set = bytes_indexer(ix.M, ix.K, ix.key, ix.heads, ix.gate)
     sets = make_sets(torch, {"x": dev(torch, ix.x), "w": dev(torch, ix.w)},
                      rotations(per_set, minimum=4))
@@ -425,8 +428,11 @@ def bench_indexer(torch, mhc, ix, steps, warmup):
 
     def call(i):
         s = sets[i % len(sets)]
-        mhc.mhcb_indexer_projection(s["x"], s["w"], s["key"], s["heads"], s["gate"], ws, nbytes,
-                                    ix.M, ix.K, ix.key, ix.heads, ix.gate)
+        if torch_matmul:
+            torch.matmul(s["x"], s["w"].t())
+        else:
+            mhc.mhcb_indexer_projection(s["x"], s["w"], s["key"], s["heads"], s["gate"], ws,
+                                        nbytes, ix.M, ix.K, ix.key, ix.heads, ix.gate)
 
     return Timed(torch, call, steps, warmup).run(), per_set
 
@@ -629,11 +635,15 @@ def main():
             extra[f"glm_moe_tp4_k8_M{M}"] = entry(ms, nbytes, M)
             log(f"glm moe M={M}: {extra[f'glm_moe_tp4_k8_M{M}']}")
     if want("indexer") and not args.quick:
-        for M in (1, 4, 6, 8, 16, 64, 256):  # the DSA indexer projection, K=6144, 128 + 32 + 128 rows
+        for M in (1, 4, 6, 8, 16, 64, 256, 1024, 4096):  # K=6144, 128 + 32 + 128 rows
             ix = synth.indexer(M)
             ms, nbytes = bench_indexer(torch, mhc, ix, min(K, 100), min(W, 5))
             extra[f"indexer_projection_M{M}"] = entry(ms, nbytes, M)
             log(f"indexer M={M}: {extra[f'indexer_projection_M{M}']}")
+            ms, nbytes = bench_indexer(torch, mhc, ix, min(K, 100), min(W, 5), torch_matmul=True)
+            extra[f"indexer_projection_M{M}_torch_matmul"] = entry(ms, nbytes, M)
+            log(f"indexer M={M}, torch x @ w.T: {extra[f'indexer_projection_M{M}_torch_matmul']}")
+            del ix
     if (want("mxfp8") or want("mailbox")) and not args.quick:
         b = synth.large_m_delayed(8192)
         if want("mxfp8"):
