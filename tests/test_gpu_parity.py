@@ -813,6 +813,53 @@ def test_mailbox_large_m_with_mxfp8():
     assert (u16(mb.slots) == 0x8000).all()
 
 
+def test_workspace_cache_growth_keeps_a_captured_graph_valid():
+    """A graph captured with the binding's cached workspace of a stream keeps
+    working after a larger request on that stream replaces the workspace:
+    the replaced buffer stays allocated (new allocations on the stream,
+    filled with garbage, do not land on it), and replays give the eager
+    results bit for bit."""
+    b = synth.boundary(51, 9, 1024, 8, 0.5, "cache-growth")
+    st = torch.cuda.Stream()
+    ws = mhc.workspace("cuda", stream=st)
+    d = {k: dev(getattr(b, k)) for k in ("partials", "residual", "post", "comb", "pre", "gamma")}
+    ro = torch.empty((b.M, 4, b.H), dtype=torch.bfloat16, device="cuda")
+    li = torch.empty((b.M, b.H), dtype=torch.bfloat16, device="cuda")
+
+    def call():
+        mhc.mhcb_boundary(d["partials"], b.M * b.H, None, d["residual"], d["post"], d["comb"],
+                          d["pre"], d["gamma"], ro, li, None, None, ws, ws.numel(), b.M, b.H, 4,
+                          b.tp, b.norm_eps, st)
+
+    st.wait_stream(torch.cuda.current_stream())
+    call()
+    torch.cuda.synchronize()
+    want_ro, want_li = ro.clone(), li.clone()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=st):
+        call()
+    torch.cuda.synchronize()
+    old_ptr, n = ws.data_ptr(), ws.numel()
+    bigger = mhc.workspace("cuda", stream=st, nbytes=n + 1)
+    assert bigger.data_ptr() != old_ptr and bigger.numel() >= 2 * n
+    del ws  # only the cache's record of the replaced buffer is left
+    with torch.cuda.stream(st):
+        junk = [torch.full((n,), 0x5A, dtype=torch.uint8, device="cuda") for _ in range(4)]
+    torch.cuda.synchronize()
+    assert all(j.data_ptr() != old_ptr for j in junk), "the replaced workspace was handed out again"
+    for rep in range(2):
+        ro.fill_(float("nan"))
+        li.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ro.view(torch.int16), want_ro.view(torch.int16)), f"replay {rep}"
+        assert torch.equal(li.view(torch.int16), want_li.view(torch.int16)), f"replay {rep}"
+    ro_ref, li_ref, _ = oracle.boundary(b.partials, b.residual, b.post, b.comb, b.pre, b.gamma,
+                                        b.norm_eps)
+    assert_bits_equal(u16(ro), ro_ref, "residual_out")
+    assert_within_ulp(u16(li), li_ref, 1, "layer_input")
+
+
 def test_graph_replays_mailbox_publish_and_consume():
     """The mailbox chain captured in one HIP graph: the producer's publish of
     all tp ranks, then the mailbox-fed boundary split over slices of a
