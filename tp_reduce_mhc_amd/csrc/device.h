@@ -135,10 +135,44 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // deterministic run to run.
 // ---------------------------------------------------------------------------
 
+// Lane exchanges within rows of sixteen lanes as DPP moves (a VALU operand
+// modifier, no LDS crossbar): lane i reads lane i ^ X.  xor 1 and 2 are
+// quad permutations, xor 8 a rotation of the row by eight, xor 4 the quad
+// reversal (xor 3) followed by the half-row mirror (xor 7).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int X>
+__device__ __forceinline__ uint32_t row_xor_u32(uint32_t v) {
+  static_assert(X == 1 || X == 2 || X == 4 || X == 8, "within a 16-lane row");
+  if constexpr (X == 1) return dpp_u32<0xB1>(v);         // quad_perm 1,0,3,2
+  else if constexpr (X == 2) return dpp_u32<0x4E>(v);    // quad_perm 2,3,0,1
+  else if constexpr (X == 4) return dpp_u32<0x141>(dpp_u32<0x1B>(v));
+  else return dpp_u32<0x128>(v);                         // row_ror 8
+}
+template <int X>
+__device__ __forceinline__ float row_xor(float v) {
+  return __uint_as_float(row_xor_u32<X>(__float_as_uint(v)));
+}
+template <int X>
+__device__ __forceinline__ double row_xor(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint64_t lo = row_xor_u32<X>((uint32_t)u), hi = row_xor_u32<X>((uint32_t)(u >> 32));
+  return __builtin_bit_cast(double, lo | (hi << 32));
+}
+
+// The butterfly v + (lane ^ 32), + (lane ^ 16), ..., + (lane ^ 1): every
+// lane ends with the same bits.  The two cross-row steps are shuffles, the
+// four within a row DPP moves.
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
-#pragma unroll
-  for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  v += __shfl_xor(v, 32, kWave);
+  v += __shfl_xor(v, 16, kWave);
+  v += row_xor<8>(v);
+  v += row_xor<4>(v);
+  v += row_xor<2>(v);
+  v += row_xor<1>(v);
   return v;
 }
 

@@ -1099,20 +1099,6 @@ __device__ __forceinline__ float rcp(float x) { return __builtin_amdgcn_rcpf(x);
 __device__ __forceinline__ float exp_fast(float x) { return expf(x); }
 __device__ __forceinline__ float sigmoid_fast(float x) { return 1.0f / (1.0f + expf(-x)); }
 
-// Lane exchanges within rows of sixteen lanes as DPP moves (a VALU
-// operand modifier, no LDS crossbar): lane i reads lane i ^ m.  xor 1 and 2
-// are quad permutations, xor 8 a rotation of the row by eight, xor 4 the
-// quad reversal (xor 3) followed by the half-row mirror (xor 7).
-template <int CTRL>
-__device__ __forceinline__ float dpp_move(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
-                                                               0xF, 0xF, false));
-}
-__device__ __forceinline__ float lane_xor1(float v) { return dpp_move<0xB1>(v); }   // quad_perm 1,0,3,2
-__device__ __forceinline__ float lane_xor2(float v) { return dpp_move<0x4E>(v); }   // quad_perm 2,3,0,1
-__device__ __forceinline__ float lane_xor4(float v) { return dpp_move<0x141>(dpp_move<0x1B>(v)); }
-__device__ __forceinline__ float lane_xor8(float v) { return dpp_move<0x128>(v); }  // row_ror 8
-
 // Sixteen lanes per token, lane e holding entry (e / 4, e % 4) of the 4x4
 // residual mix (source row, target column).  A row's sum is two xor
 // exchanges within its four lanes, a column's two exchanges at strides 4
@@ -1135,20 +1121,20 @@ mixes_kernel(const float *mixes, const float *scale, const float *base, float *p
 
   // Sinkhorn on the 4x4 residual mix.
   float c = __builtin_fmaf(row[8 + e], scale[2], base[8 + e]);
-  float peak = __builtin_fmaxf(c, lane_xor1(c));
-  peak = __builtin_fmaxf(peak, lane_xor2(peak));
+  float peak = __builtin_fmaxf(c, row_xor<1>(c));
+  peak = __builtin_fmaxf(peak, row_xor<2>(peak));
   c = exp_fast(c - peak);
-  float sum = c + lane_xor1(c);
-  sum = sum + lane_xor2(sum);
+  float sum = c + row_xor<1>(c);
+  sum = sum + row_xor<2>(sum);
   c = __builtin_fmaf(c, rcp(sum), eps);
   for (int it = 0; it < repeat; ++it) {
     if (it > 0) {
-      sum = c + lane_xor1(c);
-      sum = sum + lane_xor2(sum);
+      sum = c + row_xor<1>(c);
+      sum = sum + row_xor<2>(sum);
       c = c * rcp(sum + eps);
     }
-    sum = c + lane_xor4(c);
-    sum = sum + lane_xor8(sum);
+    sum = c + row_xor<4>(c);
+    sum = sum + row_xor<8>(sum);
     c = c * rcp(sum + eps);
   }
   if (live) comb_out[(int64_t)t * 16 + e] = c;

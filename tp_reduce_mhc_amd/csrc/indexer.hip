@@ -152,9 +152,7 @@ __global__ void __launch_bounds__(kGemvThreads) indexer_gemv_kernel(const Indexe
 #pragma unroll
   for (int t = 0; t < kTok; ++t) {
     if (t >= M) break;  // uniform
-    float v = acc[t];
-#pragma unroll
-    for (int o = kWave / 2; o >= 1; o /= 2) v += __shfl_xor(v, o, kWave);
+    const float v = wave_sum(acc[t]);
     if (lane == 0) red[wave][t] = v;
   }
   __syncthreads();
