@@ -162,13 +162,39 @@ __device__ __forceinline__ double row_xor(double v) {
   return __builtin_bit_cast(double, lo | (hi << 32));
 }
 
+// Lane i ^ 16 and i ^ 32 through gfx950's row swaps: permlane16_swap(v, v)
+// gives rows (0, 0, 2, 2) and (1, 1, 3, 3) of v, permlane32_swap(v, v) its
+// lower and its upper half twice; each lane takes the one that is not its
+// own.
+__device__ __forceinline__ uint32_t lane_id() {
+  return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+template <int X>
+__device__ __forceinline__ uint32_t cross_xor_u32(uint32_t v) {
+  static_assert(X == 16 || X == 32, "across rows");
+  const u32x2 s = X == 16 ? __builtin_amdgcn_permlane16_swap(v, v, false, false)
+                          : __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return (lane_id() & X) ? s.x : s.y;
+}
+template <int X>
+__device__ __forceinline__ float cross_xor(float v) {
+  return __uint_as_float(cross_xor_u32<X>(__float_as_uint(v)));
+}
+template <int X>
+__device__ __forceinline__ double cross_xor(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint64_t lo = cross_xor_u32<X>((uint32_t)u), hi = cross_xor_u32<X>((uint32_t)(u >> 32));
+  return __builtin_bit_cast(double, lo | (hi << 32));
+}
+
 // The butterfly v + (lane ^ 32), + (lane ^ 16), ..., + (lane ^ 1): every
-// lane ends with the same bits.  The two cross-row steps are shuffles, the
-// four within a row DPP moves.
+// lane ends with the same bits.  The two cross-row steps are row swaps, the
+// four within a row DPP moves; no step goes through the LDS crossbar.
+// Every lane of the wave must call it.
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
-  v += __shfl_xor(v, 32, kWave);
-  v += __shfl_xor(v, 16, kWave);
+  v += cross_xor<32>(v);
+  v += cross_xor<16>(v);
   v += row_xor<8>(v);
   v += row_xor<4>(v);
   v += row_xor<2>(v);
