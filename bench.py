@@ -654,7 +654,7 @@ def main():
             ms, nbytes = bench_mailbox(torch, mhc, b, 10, 2)
             extra["mailbox_mxfp8_M8192"] = entry(ms, nbytes, 8192)
             log(f"mailbox M=8192: {extra['mailbox_mxfp8_M8192']}")
-            for M in (1, 64):  # publish + consume at decode sizes (H=5120, tp=8)
+            for M in (1, 8, 32, 64):  # publish + consume at decode sizes (H=5120, tp=8)
                 bm = synth.dsv41_delayed(M)
                 ms, nbytes = bench_mailbox(torch, mhc, bm, min(K, 200), W, mxfp8=False)
                 extra[f"mailbox_publish_consume_M{M}"] = entry(ms, nbytes, M)
