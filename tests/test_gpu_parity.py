@@ -62,6 +62,14 @@ def test_dsv41_delayed_boundary_sweep(M):
     check_boundary(synth.dsv41_delayed(M))
 
 
+@pytest.mark.parametrize("M,H", [(130, 1024), (129, 3072), (200, 5120), (256, 5120), (131, 7168)])
+def test_balanced_four_wave_form(M, H):
+    """The four-wave form (more than 128 unsplit tokens of 256 FF + 128
+    fragments, eight ranks): FF = 0, 1, 2 and 3, every element against the
+    oracle (streams bit-exact, layer input within 1 ulp)."""
+    check_boundary(synth.boundary(80 + H // 1024, M, H, 8, 0.5, f"balanced-H{H}-tp8-M{M}"))
+
+
 def test_bf16_sum_is_bit_exact_through_the_probe():
     """post = 1, comb = 0 expose the BF16 rank sum in every output stream."""
     b = synth.dsv41_delayed(32)

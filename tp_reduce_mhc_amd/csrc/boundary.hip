@@ -17,6 +17,8 @@
 // 16-byte coalesced loads of consecutive fragments per lane, wave64
 // butterflies plus an LDS step for the sum of squares (no clusters), every
 // load of a token issued before its first use.
+#include <type_traits>
+
 #include "device.h"
 #include "kernels.h"
 #include "sync.h"
@@ -438,6 +440,158 @@ boundary_kernel(const BoundaryArgs a) {
   }
 }
 
+// A chunk of a token row: a 16-byte fragment (E = 8 BF16 values) or half
+// of one (E = 4).
+template <int E>
+struct Chunk {
+  using W = std::conditional_t<E == 8, u32x4, u32x2>;
+  static __device__ __forceinline__ W load(const uint16_t *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const W *>(p));
+  }
+  static __device__ __forceinline__ W load_cached(const uint16_t *p) {
+    return *reinterpret_cast<const W *>(p);
+  }
+  static __device__ __forceinline__ void store(uint16_t *p, W w) {
+    __builtin_nontemporal_store(w, reinterpret_cast<W *>(p));
+  }
+  static __device__ __forceinline__ void unpack(W w, float (&f)[E]) {
+#pragma unroll
+    for (int i = 0; i < E / 2; ++i) {
+      f[2 * i] = lo_bf16(w[i]);
+      f[2 * i + 1] = hi_bf16(w[i]);
+    }
+  }
+  static __device__ __forceinline__ W pack(const float (&f)[E]) {
+    W w;
+#pragma unroll
+    for (int i = 0; i < E / 2; ++i) w[i] = pack_bf16(f[2 * i], f[2 * i + 1]);
+    return w;
+  }
+};
+
+// One chunk of the balanced kernel below, the same steps as
+// boundary_kernel: a1 rank sum from 0 in rank order, a2 post-mix (stores
+// residual_out), a4 collapse; returns the BF16 collapse and adds its
+// squares to ss.
+template <int E, int TP>
+__device__ __forceinline__ typename Chunk<E>::W
+balanced_chunk(const typename Chunk<E>::W (&part)[TP], const typename Chunk<E>::W (&res)[kStreams],
+               const Mixes<kStreams> &m, uint16_t *out, int64_t H, double &ss) {
+  using C = Chunk<E>;
+  float sum[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) sum[e] = 0.0f;
+#pragma unroll
+  for (int r = 0; r < TP; ++r) {
+    float v[E];
+    C::unpack(part[r], v);
+#pragma unroll
+    for (int e = 0; e < E; ++e) sum[e] = sum[e] + v[e];
+  }
+  float x[E];
+  C::unpack(C::pack(sum), x);
+  float r4[kStreams][E], y[kStreams][E];
+#pragma unroll
+  for (int q = 0; q < kStreams; ++q) C::unpack(res[q], r4[q]);
+#pragma unroll
+  for (int j = 0; j < kStreams; ++j) {
+    float acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      float v = x[e] * m.post[j];
+#pragma unroll
+      for (int q = 0; q < kStreams; ++q) v = __builtin_fmaf(r4[q][e], m.comb[q * kStreams + j], v);
+      acc[e] = v;
+    }
+    const typename C::W packed = C::pack(acc);
+    C::store(out + j * H, packed);
+    C::unpack(packed, y[j]);
+  }
+  float z[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    float v = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kStreams; ++j) v = __builtin_fmaf(y[j][e], m.pre[j], v);
+    z[e] = v;
+  }
+  const typename C::W pz = C::pack(z);
+  float p[E];
+  C::unpack(pz, p);
+#pragma unroll
+  for (int e = 0; e < E; ++e) ss += (double)p[e] * (double)p[e];
+  return pz;
+}
+
+// The delayed boundary for an unsplit token whose fragment count is
+// 256 * FF + 128 (H = 5120: FF = 2), from resident partials of 8 ranks with
+// four streams and a layer input (no MXFP8).  boundary_kernel would give
+// such a token 4 FF + 2 one-fragment waves, and the SIMD that gets the
+// extra waves sets the VALU time; here four waves take FF fragments and one
+// half-fragment per thread, so each SIMD carries the same FF + 1/2
+// fragments of work.  Same arithmetic per element, same results.
+template <int FF>
+__global__ void __launch_bounds__(256) boundary_balanced_kernel(const BoundaryArgs a) {
+  constexpr int TP = 8;
+  __shared__ double red[kTokenThreadsWide / kWave + 1];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const int H = a.H;
+  const int64_t rs = a.rank_stride;
+  const uint16_t *src = a.partials + (int64_t)t * H;
+  const uint16_t *res_row = a.residual + (int64_t)t * kStreams * H;
+  uint16_t *out_row = a.residual_out + (int64_t)t * kStreams * H;
+
+  // Every load first: FF full fragments (columns 8 (tid + 256 c)), then the
+  // half fragment at column 2048 FF + 4 tid.
+  u32x4 pf[FF > 0 ? FF : 1][TP], rf[FF > 0 ? FF : 1][kStreams], gf[FF > 0 ? FF : 1];
+  u32x2 ph[TP], rh[kStreams], gh;
+#pragma unroll
+  for (int c = 0; c < FF; ++c) {
+    const int64_t col = (int64_t)(tid + 256 * c) * kFrag;
+#pragma unroll
+    for (int r = 0; r < TP; ++r) pf[c][r] = Chunk<8>::load(src + r * rs + col);
+#pragma unroll
+    for (int q = 0; q < kStreams; ++q) rf[c][q] = Chunk<8>::load(res_row + q * H + col);
+    gf[c] = Chunk<8>::load_cached(a.gamma + col);
+  }
+  const int64_t hcol = (int64_t)FF * 256 * kFrag + 4 * tid;
+#pragma unroll
+  for (int r = 0; r < TP; ++r) ph[r] = Chunk<4>::load(src + r * rs + hcol);
+#pragma unroll
+  for (int q = 0; q < kStreams; ++q) rh[q] = Chunk<4>::load(res_row + q * H + hcol);
+  gh = Chunk<4>::load_cached(a.gamma + hcol);
+  __builtin_amdgcn_sched_barrier(0);
+  Mixes<kStreams> m;
+  load_mixes<kStreams>(a, t, m);
+
+  double ss = 0.0;
+  u32x4 pzf[FF > 0 ? FF : 1];
+#pragma unroll
+  for (int c = 0; c < FF; ++c) {
+    const int64_t col = (int64_t)(tid + 256 * c) * kFrag;
+    pzf[c] = balanced_chunk<8, TP>(pf[c], rf[c], m, out_row + col, H, ss);
+  }
+  const u32x2 pzh = balanced_chunk<4, TP>(ph, rh, m, out_row + hcol, H, ss);
+
+  const float inv = token_inv(a, t, 0, ss, red, 0);
+  uint16_t *li = a.layer_input + (int64_t)t * H;
+#pragma unroll
+  for (int c = 0; c < FF; ++c) {
+    float p[8], g[8], o[8];
+    Chunk<8>::unpack(pzf[c], p);
+    Chunk<8>::unpack(gf[c], g);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (p[e] * inv) * g[e];
+    Chunk<8>::store(li + (int64_t)(tid + 256 * c) * kFrag, Chunk<8>::pack(o));
+  }
+  float p[4], g[4], o[4];
+  Chunk<4>::unpack(pzh, p);
+  Chunk<4>::unpack(gh, g);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = (p[e] * inv) * g[e];
+  Chunk<4>::store(li + hcol, Chunk<4>::pack(o));
+}
+
 template <int TRIPS, int TP, Source SRC, int HC>
 void launch_one(const BoundaryArgs &a, dim3 grid, dim3 block, hipStream_t stream) {
   hipLaunchKernelGGL((boundary_kernel<TRIPS, TP, SRC, HC>), grid, block, 0, stream, a);
@@ -478,6 +632,26 @@ hipError_t launch_tp(const BoundaryArgs &a, int threads, hipStream_t stream) {
 
 template <Source SRC, int HC>
 hipError_t launch_hc(const BoundaryArgs &a, hipStream_t stream) {
+  if constexpr (SRC == Source::kPartials && HC == kStreams) {
+    // Unsplit tokens of 256 FF + 128 fragments (FF <= 3), eight ranks, a
+    // layer input and no MXFP8, more than 128 of them: the four-wave
+    // balanced form.  Measured at H=5120 (us per call, ten-wave form in
+    // brackets): M=160 7.43 (7.49), 192 7.84 (8.23), 256 9.27 (9.82), 1024
+    // 31.3 (33.6), 4096 116.8 (120.3); at M=128, with half the compute
+    // units idle, 7.1 (7.0): four waves hide less latency than ten.
+    const int F = a.H / kFrag, FF = F / 256;
+    if (a.slices == 1 && a.M > 128 && a.tp == 8 && a.pre && !a.mx_values && F % 256 == 128 &&
+        FF <= 3) {
+      const dim3 grid(a.M), block(256);
+      switch (FF) {
+        case 0: hipLaunchKernelGGL(boundary_balanced_kernel<0>, grid, block, 0, stream, a); break;
+        case 1: hipLaunchKernelGGL(boundary_balanced_kernel<1>, grid, block, 0, stream, a); break;
+        case 2: hipLaunchKernelGGL(boundary_balanced_kernel<2>, grid, block, 0, stream, a); break;
+        default: hipLaunchKernelGGL(boundary_balanced_kernel<3>, grid, block, 0, stream, a); break;
+      }
+      return hipGetLastError();
+    }
+  }
   const Geometry g = fragment_geometry(a.slices > 1 ? a.slice_frags : a.H / kFrag,
                                        wide_threads<SRC, HC>());
   switch (g.trips) {
