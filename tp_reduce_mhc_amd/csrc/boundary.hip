@@ -165,8 +165,10 @@ __device__ __forceinline__ void stage_routes(const FinalizeView &f, int tp, int 
 // eps)) from each thread's binary64 sum of squares: wave xor sums, then one
 // wave adds the waves in index order (and, split, publishes its slice's
 // partial, adds the slices' in slice order and advances the slot's epoch:
-// the squares of BF16 values are exact in binary64, so the bits do not
-// depend on the split), one thread evaluates inv and shares it through LDS.
+// each square of a BF16 value is exact in binary64, and the sums round near
+// 2^-53 relative, far below the binary32 rounding of inv, so the split does
+// not show in the bits in practice), one thread evaluates inv and shares it
+// through LDS.
 // `callw` is the slot's epoch word (wave 0's).  Every thread calls it.
 __device__ float token_inv(const BoundaryArgs &a, int t, int s, double ss, double *red,
                            uint64_t callw) {
@@ -386,8 +388,8 @@ boundary_kernel(const BoundaryArgs a) {
   if (!norm) return;  // residual-only variant: uniform over the grid
 
   // a4 (second half): inv = 1/sqrt(sum p^2 / H + eps); out = bf16((p*inv)*gamma).
-  // The squares of BF16 values are exact in binary64 and so is their sum,
-  // whatever the order or the split.
+  // Each square of a BF16 value is exact in binary64; the binary64 sums
+  // round near 2^-53 relative, far below the binary32 rounding of inv.
   const float inv = token_inv(a, t, s, ss, red, callw);
   if (a.slices > 1 && tid < kWave)
     for (int w = tid * a.slices + s; w < kClearWords; w += kWave * a.slices)
@@ -525,7 +527,7 @@ balanced_chunk(const typename Chunk<E>::W (&part)[TP], const typename Chunk<E>::
 
 // The delayed boundary for an unsplit token whose fragment count is
 // 256 * FF + 128 (H = 5120: FF = 2), from resident partials of 8 ranks with
-// four streams and a layer input (no MXFP8).  boundary_kernel would give
+// four streams and a layer input (optionally with the MXFP8 epilogue).  boundary_kernel would give
 // such a token 4 FF + 2 one-fragment waves, and the SIMD that gets the
 // extra waves sets the VALU time; here four waves take FF fragments and one
 // half-fragment per thread, so each SIMD carries the same FF + 1/2
@@ -574,22 +576,72 @@ __global__ void __launch_bounds__(256) boundary_balanced_kernel(const BoundaryAr
   const u32x2 pzh = balanced_chunk<4, TP>(ph, rh, m, out_row + hcol, H, ss);
 
   const float inv = token_inv(a, t, 0, ss, red, 0);
+  // out = bf16((p * inv) * gamma); with MXFP8 also the E4M3 codes and the
+  // UE8M0 scale of each 32-column block, which spans lanes 4q .. 4q+3 of a
+  // full fragment and lanes 8q .. 8q+7 of a half fragment.
   uint16_t *li = a.layer_input + (int64_t)t * H;
+  const int K = H / 32;
 #pragma unroll
   for (int c = 0; c < FF; ++c) {
+    const int f = tid + 256 * c;
     float p[8], g[8], o[8];
     Chunk<8>::unpack(pzf[c], p);
     Chunk<8>::unpack(gf[c], g);
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = (p[e] * inv) * g[e];
-    Chunk<8>::store(li + (int64_t)(tid + 256 * c) * kFrag, Chunk<8>::pack(o));
+    const u32x4 out = Chunk<8>::pack(o);
+    Chunk<8>::store(li + (int64_t)f * kFrag, out);
+    if (a.mx_values) {
+      float ov[8];
+      Chunk<8>::unpack(out, ov);
+      float amax = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(ov[e]));
+      amax = __builtin_fmaxf(amax, row_xor<1>(amax));
+      amax = __builtin_fmaxf(amax, row_xor<2>(amax));
+      const uint32_t e8 = ue8m0_round_up(amax * (1.0f / 448.0f));
+      const float sc = ue8m0_inverse(e8);
+      u32x2 codes = {0, 0};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) codes[e >> 2] |= e4m3_rne_sat(ov[e] * sc) << (8 * (e & 3));
+      store8(a.mx_values + (int64_t)t * H + (int64_t)f * kFrag, codes);
+      if ((f & 3) == 0) a.mx_scales[sf_offset(t, f >> 2, K)] = (uint8_t)e8;
+    }
   }
   float p[4], g[4], o[4];
   Chunk<4>::unpack(pzh, p);
   Chunk<4>::unpack(gh, g);
 #pragma unroll
   for (int e = 0; e < 4; ++e) o[e] = (p[e] * inv) * g[e];
-  Chunk<4>::store(li + hcol, Chunk<4>::pack(o));
+  const u32x2 out = Chunk<4>::pack(o);
+  Chunk<4>::store(li + hcol, out);
+  if (a.mx_values) {
+    float ov[4];
+    Chunk<4>::unpack(out, ov);
+    float amax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(ov[e]));
+    amax = __builtin_fmaxf(amax, row_xor<1>(amax));
+    amax = __builtin_fmaxf(amax, row_xor<2>(amax));
+    amax = __builtin_fmaxf(amax, row_xor<4>(amax));
+    const uint32_t e8 = ue8m0_round_up(amax * (1.0f / 448.0f));
+    const float sc = ue8m0_inverse(e8);
+    uint32_t codes = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) codes |= e4m3_rne_sat(ov[e] * sc) << (8 * e);
+    __builtin_nontemporal_store(codes, reinterpret_cast<uint32_t *>(a.mx_values + (int64_t)t * H + hcol));
+    if ((tid & 7) == 0) a.mx_scales[sf_offset(t, (int)(hcol / 32), K)] = (uint8_t)e8;
+
+    // The scales of the padding rows M .. ceil(M/128)*128 - 1 are zero, one
+    // 4-column word per store, spread over the grid.
+    const int words_per_row = K / 4;
+    const int64_t padded = ((int64_t)a.M + 127) / 128 * 128;
+    const int64_t words = (padded - a.M) * words_per_row;
+    for (int64_t w = (int64_t)t * 256 + tid; w < words; w += (int64_t)a.M * 256) {
+      const int64_t row = a.M + w / words_per_row;
+      *reinterpret_cast<uint32_t *>(a.mx_scales + sf_offset(row, (int)(w % words_per_row) * 4, K)) = 0u;
+    }
+  }
 }
 
 template <int TRIPS, int TP, Source SRC, int HC>
@@ -633,15 +685,17 @@ hipError_t launch_tp(const BoundaryArgs &a, int threads, hipStream_t stream) {
 template <Source SRC, int HC>
 hipError_t launch_hc(const BoundaryArgs &a, hipStream_t stream) {
   if constexpr (SRC == Source::kPartials && HC == kStreams) {
-    // Unsplit tokens of 256 FF + 128 fragments (FF <= 3), eight ranks, a
-    // layer input and no MXFP8, more than 128 of them: the four-wave
-    // balanced form.  Measured at H=5120 (us per call, ten-wave form in
-    // brackets): M=160 7.43 (7.49), 192 7.84 (8.23), 256 9.27 (9.82), 1024
-    // 31.3 (33.6), 4096 116.8 (120.3); at M=128, with half the compute
-    // units idle, 7.1 (7.0): four waves hide less latency than ten.
+    // Unsplit tokens of 256 FF + 128 fragments (FF <= 3), eight ranks and a
+    // layer input: the four-wave balanced form, for more than 128 tokens
+    // (with MXFP8, 1024 or more).  Measured at H=5120 (us per call, ten-wave
+    // form in brackets): M=160 7.43 (7.49), 192 7.84 (8.23), 256 9.27
+    // (9.82), 1024 31.3 (33.6), 4096 116.8 (120.3); at M=128, with half the
+    // compute units idle, 7.1 (7.0): four waves hide less latency than ten.
+    // With MXFP8, whose epilogue lengthens each wave's serial tail: M=512
+    // 21.3 (20.6), 1024 36.9 (39.7), 2048 66.4 (69.4), 8192 246.9 (252.6).
     const int F = a.H / kFrag, FF = F / 256;
-    if (a.slices == 1 && a.M > 128 && a.tp == 8 && a.pre && !a.mx_values && F % 256 == 128 &&
-        FF <= 3) {
+    const int min_m = a.mx_values ? 1024 : 129;
+    if (a.slices == 1 && a.M >= min_m && a.tp == 8 && a.pre && F % 256 == 128 && FF <= 3) {
       const dim3 grid(a.M), block(256);
       switch (FF) {
         case 0: hipLaunchKernelGGL(boundary_balanced_kernel<0>, grid, block, 0, stream, a); break;
