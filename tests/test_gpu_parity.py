@@ -955,7 +955,8 @@ def test_mailbox_poll_gives_up_with_a_bounded_spin():
     assert torch.isnan(ro.float()).all() and torch.isnan(li.float()).all()
 
 
-def test_mailbox_consumer_polls_fragments_that_land_late():
+@pytest.mark.parametrize("M", [8, 160])
+def test_mailbox_consumer_polls_fragments_that_land_late(M):
     """The consumer's spin on fragments still landing (the DSV4.1 page's
     _LamportMHCDeviceKernel poll loop, the GLM page's _PublishDeviceKernel):
     ranks 0..tp/2-1 are published on the consumer's stream before it, ranks
@@ -965,7 +966,7 @@ def test_mailbox_consumer_polls_fragments_that_land_late():
     state, as each rank keeps on the pages).  Three calls cycle the
     generations; each is bit-equal to the direct path, no poll gives up,
     and late fragments are counted."""
-    tp, M, H = 8, 8, 5120
+    tp, H = 8, 5120
     b = synth.dsv41_delayed(M)
     ro_d, li_d, _ = run_boundary(b)
     mb = mhc.Mailbox(tp, M, H, "cuda")
