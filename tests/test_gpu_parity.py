@@ -65,12 +65,12 @@ def test_dsv41_delayed_boundary_sweep(M):
 @pytest.mark.parametrize("M,H,mxfp8", [(130, 1024, False), (129, 3072, False), (200, 5120, False),
                                        (256, 5120, False), (131, 7168, False), (1030, 1024, True),
                                        (1100, 3072, True), (1024, 5120, True), (1025, 7168, True)])
-def test_balanced_four_wave_form(M, H, mxfp8):
-    """The four-wave form (more than 128 unsplit tokens of 256 FF + 128
-    fragments, eight ranks; with MXFP8 from 1024 tokens): FF = 0, 1, 2 and
-    3, every element against the oracle (streams bit-exact, layer input
-    within 1 ulp; MXFP8 codes and scales, padding rows included,
-    bit-exact)."""
+def test_balanced_forms(M, H, mxfp8):
+    """The balanced forms for unsplit tokens of 256 FF + 128 fragments and
+    eight ranks: eight waves at H = 5120 (every M), four waves at the other
+    widths (FF = 0, 1, 3; more than 128 tokens, 1024 with MXFP8).  Every
+    element against the oracle (streams bit-exact, layer input within 1 ulp;
+    MXFP8 codes and scales, padding rows included, bit-exact)."""
     check_boundary(synth.boundary(80 + H // 1024, M, H, 8, 0.5, f"balanced-H{H}-tp8-M{M}"),
                    mxfp8=mxfp8)
 

@@ -526,42 +526,49 @@ balanced_chunk(const typename Chunk<E>::W (&part)[TP], const typename Chunk<E>::
 }
 
 // The delayed boundary for an unsplit token whose fragment count is
-// 256 * FF + 128 (H = 5120: FF = 2), from resident partials of 8 ranks with
-// four streams and a layer input (optionally with the MXFP8 epilogue).  boundary_kernel would give
-// such a token 4 FF + 2 one-fragment waves, and the SIMD that gets the
-// extra waves sets the VALU time; here four waves take FF fragments and one
-// half-fragment per thread, so each SIMD carries the same FF + 1/2
-// fragments of work.  Same arithmetic per element, same results.
-template <int FF>
-__global__ void __launch_bounds__(256) boundary_balanced_kernel(const BoundaryArgs a) {
+// NT * FF + 128 (H = 5120: FF = 2 with NT = 256 threads, FF = 1 with 512),
+// from resident partials of 8 ranks with four streams and a layer input
+// (optionally with the MXFP8 epilogue).  boundary_kernel would give such a
+// token 4 FF + 2 one-fragment waves (NT = 256), and the SIMD that gets the
+// extra waves sets the VALU time.  Here every thread takes FF fragments
+// and the first 256 threads one half-fragment each (the last 128
+// fragments), so each SIMD carries the same work: FF + 1/2 fragments in one
+// wave (NT = 256), or FF fragments in each of two waves and a half in one
+// (NT = 512).  Same arithmetic per element, same results.
+template <int FF, int NT>
+__global__ void __launch_bounds__(NT) boundary_balanced_kernel(const BoundaryArgs a) {
   constexpr int TP = 8;
+  static_assert(NT == 256 || NT == 512, "four or eight waves");
   __shared__ double red[kTokenThreadsWide / kWave + 1];
   const int t = blockIdx.x, tid = threadIdx.x;
+  const bool half = NT == 256 || tid < 256;  // uniform over each wave
   const int H = a.H;
   const int64_t rs = a.rank_stride;
   const uint16_t *src = a.partials + (int64_t)t * H;
   const uint16_t *res_row = a.residual + (int64_t)t * kStreams * H;
   uint16_t *out_row = a.residual_out + (int64_t)t * kStreams * H;
 
-  // Every load first: FF full fragments (columns 8 (tid + 256 c)), then the
-  // half fragment at column 2048 FF + 4 tid.
+  // Every load first: FF full fragments (columns 8 (tid + NT c)), then the
+  // half fragment at column 8 NT FF + 4 tid.
   u32x4 pf[FF > 0 ? FF : 1][TP], rf[FF > 0 ? FF : 1][kStreams], gf[FF > 0 ? FF : 1];
-  u32x2 ph[TP], rh[kStreams], gh;
+  u32x2 ph[TP], rh[kStreams], gh = {0, 0};
 #pragma unroll
   for (int c = 0; c < FF; ++c) {
-    const int64_t col = (int64_t)(tid + 256 * c) * kFrag;
+    const int64_t col = (int64_t)(tid + NT * c) * kFrag;
 #pragma unroll
     for (int r = 0; r < TP; ++r) pf[c][r] = Chunk<8>::load(src + r * rs + col);
 #pragma unroll
     for (int q = 0; q < kStreams; ++q) rf[c][q] = Chunk<8>::load(res_row + q * H + col);
     gf[c] = Chunk<8>::load_cached(a.gamma + col);
   }
-  const int64_t hcol = (int64_t)FF * 256 * kFrag + 4 * tid;
+  const int64_t hcol = (int64_t)FF * NT * kFrag + 4 * (tid & 255);
+  if (half) {
 #pragma unroll
-  for (int r = 0; r < TP; ++r) ph[r] = Chunk<4>::load(src + r * rs + hcol);
+    for (int r = 0; r < TP; ++r) ph[r] = Chunk<4>::load(src + r * rs + hcol);
 #pragma unroll
-  for (int q = 0; q < kStreams; ++q) rh[q] = Chunk<4>::load(res_row + q * H + hcol);
-  gh = Chunk<4>::load_cached(a.gamma + hcol);
+    for (int q = 0; q < kStreams; ++q) rh[q] = Chunk<4>::load(res_row + q * H + hcol);
+    gh = Chunk<4>::load_cached(a.gamma + hcol);
+  }
   __builtin_amdgcn_sched_barrier(0);
   Mixes<kStreams> m;
   load_mixes<kStreams>(a, t, m);
@@ -570,10 +577,11 @@ __global__ void __launch_bounds__(256) boundary_balanced_kernel(const BoundaryAr
   u32x4 pzf[FF > 0 ? FF : 1];
 #pragma unroll
   for (int c = 0; c < FF; ++c) {
-    const int64_t col = (int64_t)(tid + 256 * c) * kFrag;
+    const int64_t col = (int64_t)(tid + NT * c) * kFrag;
     pzf[c] = balanced_chunk<8, TP>(pf[c], rf[c], m, out_row + col, H, ss);
   }
-  const u32x2 pzh = balanced_chunk<4, TP>(ph, rh, m, out_row + hcol, H, ss);
+  u32x2 pzh = {0, 0};
+  if (half) pzh = balanced_chunk<4, TP>(ph, rh, m, out_row + hcol, H, ss);
 
   const float inv = token_inv(a, t, 0, ss, red, 0);
   // out = bf16((p * inv) * gamma); with MXFP8 also the E4M3 codes and the
@@ -583,7 +591,7 @@ __global__ void __launch_bounds__(256) boundary_balanced_kernel(const BoundaryAr
   const int K = H / 32;
 #pragma unroll
   for (int c = 0; c < FF; ++c) {
-    const int f = tid + 256 * c;
+    const int f = tid + NT * c;
     float p[8], g[8], o[8];
     Chunk<8>::unpack(pzf[c], p);
     Chunk<8>::unpack(gf[c], g);
@@ -608,36 +616,40 @@ __global__ void __launch_bounds__(256) boundary_balanced_kernel(const BoundaryAr
       if ((f & 3) == 0) a.mx_scales[sf_offset(t, f >> 2, K)] = (uint8_t)e8;
     }
   }
-  float p[4], g[4], o[4];
-  Chunk<4>::unpack(pzh, p);
-  Chunk<4>::unpack(gh, g);
+  if (half) {
+    float p[4], g[4], o[4];
+    Chunk<4>::unpack(pzh, p);
+    Chunk<4>::unpack(gh, g);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) o[e] = (p[e] * inv) * g[e];
-  const u32x2 out = Chunk<4>::pack(o);
-  Chunk<4>::store(li + hcol, out);
+    for (int e = 0; e < 4; ++e) o[e] = (p[e] * inv) * g[e];
+    const u32x2 out = Chunk<4>::pack(o);
+    Chunk<4>::store(li + hcol, out);
+    if (a.mx_values) {
+      float ov[4];
+      Chunk<4>::unpack(out, ov);
+      float amax = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(ov[e]));
+      amax = __builtin_fmaxf(amax, row_xor<1>(amax));
+      amax = __builtin_fmaxf(amax, row_xor<2>(amax));
+      amax = __builtin_fmaxf(amax, row_xor<4>(amax));
+      const uint32_t e8 = ue8m0_round_up(amax * (1.0f / 448.0f));
+      const float sc = ue8m0_inverse(e8);
+      uint32_t codes = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) codes |= e4m3_rne_sat(ov[e] * sc) << (8 * e);
+      __builtin_nontemporal_store(codes,
+                                  reinterpret_cast<uint32_t *>(a.mx_values + (int64_t)t * H + hcol));
+      if ((tid & 7) == 0) a.mx_scales[sf_offset(t, (int)(hcol / 32), K)] = (uint8_t)e8;
+    }
+  }
   if (a.mx_values) {
-    float ov[4];
-    Chunk<4>::unpack(out, ov);
-    float amax = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(ov[e]));
-    amax = __builtin_fmaxf(amax, row_xor<1>(amax));
-    amax = __builtin_fmaxf(amax, row_xor<2>(amax));
-    amax = __builtin_fmaxf(amax, row_xor<4>(amax));
-    const uint32_t e8 = ue8m0_round_up(amax * (1.0f / 448.0f));
-    const float sc = ue8m0_inverse(e8);
-    uint32_t codes = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) codes |= e4m3_rne_sat(ov[e] * sc) << (8 * e);
-    __builtin_nontemporal_store(codes, reinterpret_cast<uint32_t *>(a.mx_values + (int64_t)t * H + hcol));
-    if ((tid & 7) == 0) a.mx_scales[sf_offset(t, (int)(hcol / 32), K)] = (uint8_t)e8;
-
     // The scales of the padding rows M .. ceil(M/128)*128 - 1 are zero, one
     // 4-column word per store, spread over the grid.
     const int words_per_row = K / 4;
     const int64_t padded = ((int64_t)a.M + 127) / 128 * 128;
     const int64_t words = (padded - a.M) * words_per_row;
-    for (int64_t w = (int64_t)t * 256 + tid; w < words; w += (int64_t)a.M * 256) {
+    for (int64_t w = (int64_t)t * NT + tid; w < words; w += (int64_t)a.M * NT) {
       const int64_t row = a.M + w / words_per_row;
       *reinterpret_cast<uint32_t *>(a.mx_scales + sf_offset(row, (int)(w % words_per_row) * 4, K)) = 0u;
     }
@@ -685,25 +697,33 @@ hipError_t launch_tp(const BoundaryArgs &a, int threads, hipStream_t stream) {
 template <Source SRC, int HC>
 hipError_t launch_hc(const BoundaryArgs &a, hipStream_t stream) {
   if constexpr (SRC == Source::kPartials && HC == kStreams) {
-    // Unsplit tokens of 256 FF + 128 fragments (FF <= 3), eight ranks and a
-    // layer input: the four-wave balanced form, for more than 128 tokens
-    // (with MXFP8, 1024 or more).  Measured at H=5120 (us per call, ten-wave
-    // form in brackets): M=160 7.43 (7.49), 192 7.84 (8.23), 256 9.27
-    // (9.82), 1024 31.3 (33.6), 4096 116.8 (120.3); at M=128, with half the
-    // compute units idle, 7.1 (7.0): four waves hide less latency than ten.
-    // With MXFP8, whose epilogue lengthens each wave's serial tail: M=512
-    // 21.3 (20.6), 1024 36.9 (39.7), 2048 66.4 (69.4), 8192 246.9 (252.6).
+    // Unsplit tokens of NT FF + 128 fragments, eight ranks and a layer
+    // input: the balanced forms.  Measured (us per call, the ten-wave form
+    // in brackets):
+    //  - H = 5120, eight waves, at every M: M=128 6.64 (7.02), 160 6.99
+    //    (7.48), 256 9.4 (9.8), 1024 31.2 (33.6), 4096 116 (120); with
+    //    MXFP8 M=200 9.9 (10.2), 1024 34.4 (35.5), 8192 241.7 (251.2);
+    //    unsplit M = 1-64 the same within 0.05.
+    //  - other widths, four waves (FF <= 3), from 129 tokens (1024 with
+    //    MXFP8): at H=5120 four waves took 7.1 us at M=128 (7.0), 7.43 at
+    //    160, 116.8 at 4096, and with MXFP8 21.3 at M=512 (20.6) but 246.9
+    //    at 8192: one wave per SIMD hides less latency, and the MXFP8
+    //    epilogue lengthens each wave's serial tail.
     const int F = a.H / kFrag, FF = F / 256;
-    const int min_m = a.mx_values ? 1024 : 129;
-    if (a.slices == 1 && a.M >= min_m && a.tp == 8 && a.pre && F % 256 == 128 && FF <= 3) {
-      const dim3 grid(a.M), block(256);
-      switch (FF) {
-        case 0: hipLaunchKernelGGL(boundary_balanced_kernel<0>, grid, block, 0, stream, a); break;
-        case 1: hipLaunchKernelGGL(boundary_balanced_kernel<1>, grid, block, 0, stream, a); break;
-        case 2: hipLaunchKernelGGL(boundary_balanced_kernel<2>, grid, block, 0, stream, a); break;
-        default: hipLaunchKernelGGL(boundary_balanced_kernel<3>, grid, block, 0, stream, a); break;
+    if (a.slices == 1 && a.tp == 8 && a.pre && F % 256 == 128 && FF <= 3) {
+      const dim3 grid(a.M);
+      if (F == 640) {
+        hipLaunchKernelGGL((boundary_balanced_kernel<1, 512>), grid, dim3(512), 0, stream, a);
+        return hipGetLastError();
       }
-      return hipGetLastError();
+      if (a.M >= (a.mx_values ? 1024 : 129)) {
+        switch (FF) {  // FF = 2 is H = 5120, taken above
+          case 0: hipLaunchKernelGGL((boundary_balanced_kernel<0, 256>), grid, dim3(256), 0, stream, a); break;
+          case 1: hipLaunchKernelGGL((boundary_balanced_kernel<1, 256>), grid, dim3(256), 0, stream, a); break;
+          default: hipLaunchKernelGGL((boundary_balanced_kernel<3, 256>), grid, dim3(256), 0, stream, a); break;
+        }
+        return hipGetLastError();
+      }
     }
   }
   const Geometry g = fragment_geometry(a.slices > 1 ? a.slice_frags : a.H / kFrag,
