@@ -559,7 +559,7 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBS, 4),
                          "traffic": traffic,
-                         "kernel": "boundary_balanced_kernel<1, 512> (delayed mHC, tp 8, eight waves)",
+                         "kernel": "boundary_balanced_kernel<1, 512, Source 0> (delayed mHC, tp 8, eight waves)",
                          "algorithmic_bytes_per_launch": int(nbytes),
                          # The same fraction from the committed kernel trace
                          # (profiles/, mean launch duration under rocprofv3),

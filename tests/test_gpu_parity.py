@@ -955,6 +955,27 @@ def test_mailbox_poll_gives_up_with_a_bounded_spin():
     assert torch.isnan(ro.float()).all() and torch.isnan(li.float()).all()
 
 
+def test_mailbox_eight_wave_consumer_gives_up_with_a_bounded_spin():
+    """The same give-up on the eight-wave consumer (H=5120, tp=8, unsplit:
+    no workspace): every chunk's poll gives up, the kernel ends, the
+    outputs are NaN, the status counts the time-outs and late chunks, and
+    the consumed slots are back to the sentinel."""
+    M, H, tp = 3, 5120, 8
+    mb = mhc.Mailbox(tp, M, H, "cuda", spin_limit=4)
+    mb.init()
+    b = synth.dsv41_delayed(M)
+    ro = torch.zeros((M, 4, H), dtype=torch.bfloat16, device="cuda")
+    li = torch.zeros((M, H), dtype=torch.bfloat16, device="cuda")
+    mhc.mhcb_boundary(None, 0, mb, dev(b.residual), dev(b.post), dev(b.comb), dev(b.pre),
+                      dev(b.gamma), ro, li, None, None, None, 0, M, H, 4, tp, b.norm_eps)
+    torch.cuda.synchronize()
+    timeouts, late = mhc.mailbox_status(mb)
+    assert timeouts > 0 and late > 0 and not mb.status_ok()
+    assert torch.isnan(ro.float()).all() and torch.isnan(li.float()).all()
+    assert (u16(mb.slots) == 0x8000).all()
+    assert host(mb.stage_state).tolist() == [0, 1]
+
+
 @pytest.mark.parametrize("M", [8, 160])
 def test_mailbox_consumer_polls_fragments_that_land_late(M):
     """The consumer's spin on fragments still landing (the DSV4.1 page's

@@ -469,7 +469,70 @@ struct Chunk {
     for (int i = 0; i < E / 2; ++i) w[i] = pack_bf16(f[2 * i], f[2 * i + 1]);
     return w;
   }
+  static __device__ __forceinline__ W filled(uint32_t v) {
+    W w;
+#pragma unroll
+    for (int i = 0; i < E / 2; ++i) w[i] = v;
+    return w;
+  }
+  static __device__ __forceinline__ bool sentinel(W w) {
+    bool any = false;
+#pragma unroll
+    for (int i = 0; i < E / 2; ++i) any |= has_sentinel(w[i]);
+    return any;
+  }
+  // A mailbox chunk read at device scope (8-byte atomic loads).
+  static __device__ __forceinline__ W load_agent(const uint16_t *p) {
+    if constexpr (E == 8) {
+      return mhcb::load_agent(p);
+    } else {
+      const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t *>(p), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+      return W{(uint32_t)v, (uint32_t)(v >> 32)};
+    }
+  }
 };
+
+// poll() for a chunk: re-read at device scope, at most spin_limit times,
+// until no element is the sentinel; a chunk still not all there reads as
+// NaN and the time-out is counted in status[0].
+template <int E>
+__device__ __forceinline__ typename Chunk<E>::W poll_chunk(const uint16_t *p,
+                                                           typename Chunk<E>::W w,
+                                                           const MailboxView &mb) {
+  int64_t spins = 0;
+  while (Chunk<E>::sentinel(w)) {
+    if (++spins > mb.spin_limit) {
+      atomicAdd(mb.status, 1);
+      return Chunk<E>::filled(kPoisonBf16x2);
+    }
+    __builtin_amdgcn_s_sleep(1);
+    w = Chunk<E>::load_agent(p);
+  }
+  return w;
+}
+
+// The mailbox consumer's check of one chunk of every rank: a wave counts
+// its late chunks with one atomic (status[1]), and a lane with a late
+// chunk re-reads it (poll_chunk).  Called by whole waves.
+template <int E, int TP>
+__device__ __forceinline__ void settle_chunk(typename Chunk<E>::W (&part)[TP], const uint16_t *src,
+                                             int64_t rs, const MailboxView &mb) {
+  bool dirty = false;
+  int late = 0;  // ballots: uniform over the wave
+#pragma unroll
+  for (int r = 0; r < TP; ++r) {
+    const bool d = Chunk<E>::sentinel(part[r]);
+    dirty |= d;
+    late += __popcll(__ballot(d));
+  }
+  if (late) {
+    const uint64_t act = __ballot(true);
+    if ((threadIdx.x & (kWave - 1)) == __builtin_ctzll(act)) atomicAdd(mb.status + 1, late);
+    if (dirty)
+      for (int r = 0; r < TP; ++r) part[r] = poll_chunk<E>(src + r * rs, part[r], mb);
+  }
+}
 
 // One chunk of the balanced kernel below, the same steps as
 // boundary_kernel: a1 rank sum from 0 in rank order, a2 post-mix (stores
@@ -527,24 +590,35 @@ balanced_chunk(const typename Chunk<E>::W (&part)[TP], const typename Chunk<E>::
 
 // The delayed boundary for an unsplit token whose fragment count is
 // NT * FF + 128 (H = 5120: FF = 2 with NT = 256 threads, FF = 1 with 512),
-// from resident partials of 8 ranks with four streams and a layer input
-// (optionally with the MXFP8 epilogue).  boundary_kernel would give such a
+// from resident partials or the ACTIVE generation of a mailbox, 8 ranks,
+// four streams and a layer input (optionally with the MXFP8 epilogue).  boundary_kernel would give such a
 // token 4 FF + 2 one-fragment waves (NT = 256), and the SIMD that gets the
 // extra waves sets the VALU time.  Here every thread takes FF fragments
 // and the first 256 threads one half-fragment each (the last 128
 // fragments), so each SIMD carries the same work: FF + 1/2 fragments in one
 // wave (NT = 256), or FF fragments in each of two waves and a half in one
 // (NT = 512).  Same arithmetic per element, same results.
-template <int FF, int NT>
+template <int FF, int NT, Source SRC>
 __global__ void __launch_bounds__(NT) boundary_balanced_kernel(const BoundaryArgs a) {
   constexpr int TP = 8;
   static_assert(NT == 256 || NT == 512, "four or eight waves");
+  static_assert(SRC == Source::kPartials || SRC == Source::kMailbox, "partials or mailbox");
   __shared__ double red[kTokenThreadsWide / kWave + 1];
   const int t = blockIdx.x, tid = threadIdx.x;
   const bool half = NT == 256 || tid < 256;  // uniform over each wave
   const int H = a.H;
-  const int64_t rs = a.rank_stride;
-  const uint16_t *src = a.partials + (int64_t)t * H;
+  const uint16_t *src;
+  int64_t rs;
+  uint32_t gen = 0;
+  if constexpr (SRC == Source::kMailbox) {
+    gen = (uint32_t)__hip_atomic_load(a.mailbox.stage_state, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT) % 3u;  // stays inside the slots
+    rs = (int64_t)a.mailbox.capacity * H;
+    src = a.mailbox.slots + (int64_t)gen * TP * rs + (int64_t)t * H;
+  } else {
+    rs = a.rank_stride;
+    src = a.partials + (int64_t)t * H;
+  }
   const uint16_t *res_row = a.residual + (int64_t)t * kStreams * H;
   uint16_t *out_row = a.residual_out + (int64_t)t * kStreams * H;
 
@@ -572,6 +646,14 @@ __global__ void __launch_bounds__(NT) boundary_balanced_kernel(const BoundaryArg
   __builtin_amdgcn_sched_barrier(0);
   Mixes<kStreams> m;
   load_mixes<kStreams>(a, t, m);
+  if constexpr (SRC == Source::kMailbox) {
+    // A plain streaming read first (above); chunks still holding the
+    // sentinel are re-read at device scope.
+#pragma unroll
+    for (int c = 0; c < FF; ++c)
+      settle_chunk<8, TP>(pf[c], src + (int64_t)(tid + NT * c) * kFrag, rs, a.mailbox);
+    if (half) settle_chunk<4, TP>(ph, src + hcol, rs, a.mailbox);
+  }
 
   double ss = 0.0;
   u32x4 pzf[FF > 0 ? FF : 1];
@@ -582,6 +664,19 @@ __global__ void __launch_bounds__(NT) boundary_balanced_kernel(const BoundaryArg
   }
   u32x2 pzh = {0, 0};
   if (half) pzh = balanced_chunk<4, TP>(ph, rh, m, out_row + hcol, H, ss);
+  if constexpr (SRC == Source::kMailbox) {
+    // Advance the generation and return the consumed slots to the sentinel.
+    if (t == 0 && tid == 0) a.mailbox.stage_state[1] = (int32_t)((gen + 1) % 3);
+    uint16_t *slots = const_cast<uint16_t *>(src);
+#pragma unroll
+    for (int c = 0; c < FF; ++c)
+#pragma unroll
+      for (int r = 0; r < TP; ++r)
+        Chunk<8>::store(slots + r * rs + (int64_t)(tid + NT * c) * kFrag, Chunk<8>::filled(0x80008000u));
+    if (half)
+#pragma unroll
+      for (int r = 0; r < TP; ++r) Chunk<4>::store(slots + r * rs + hcol, Chunk<4>::filled(0x80008000u));
+  }
 
   const float inv = token_inv(a, t, 0, ss, red, 0);
   // out = bf16((p * inv) * gamma); with MXFP8 also the E4M3 codes and the
@@ -696,14 +791,16 @@ hipError_t launch_tp(const BoundaryArgs &a, int threads, hipStream_t stream) {
 
 template <Source SRC, int HC>
 hipError_t launch_hc(const BoundaryArgs &a, hipStream_t stream) {
-  if constexpr (SRC == Source::kPartials && HC == kStreams) {
+  if constexpr ((SRC == Source::kPartials || SRC == Source::kMailbox) && HC == kStreams) {
     // Unsplit tokens of NT FF + 128 fragments, eight ranks and a layer
     // input: the balanced forms.  Measured (us per call, the ten-wave form
     // in brackets):
     //  - H = 5120, eight waves, at every M: M=128 6.64 (7.02), 160 6.99
     //    (7.48), 256 9.4 (9.8), 1024 31.2 (33.6), 4096 116 (120); with
     //    MXFP8 M=200 9.9 (10.2), 1024 34.4 (35.5), 8192 241.7 (251.2);
-    //    unsplit M = 1-64 the same within 0.05.
+    //    unsplit M = 1-64 the same within 0.05.  Mailbox-fed (publish +
+    //    consume): M=256 20.0 (21.6), 1024 82.6 (82.7), 8192 with MXFP8
+    //    619 (623).
     //  - other widths, four waves (FF <= 3), from 129 tokens (1024 with
     //    MXFP8): at H=5120 four waves took 7.1 us at M=128 (7.0), 7.43 at
     //    160, 116.8 at 4096, and with MXFP8 21.3 at M=512 (20.6) but 246.9
@@ -713,14 +810,14 @@ hipError_t launch_hc(const BoundaryArgs &a, hipStream_t stream) {
     if (a.slices == 1 && a.tp == 8 && a.pre && F % 256 == 128 && FF <= 3) {
       const dim3 grid(a.M);
       if (F == 640) {
-        hipLaunchKernelGGL((boundary_balanced_kernel<1, 512>), grid, dim3(512), 0, stream, a);
+        hipLaunchKernelGGL((boundary_balanced_kernel<1, 512, SRC>), grid, dim3(512), 0, stream, a);
         return hipGetLastError();
       }
-      if (a.M >= (a.mx_values ? 1024 : 129)) {
+      if (SRC == Source::kPartials && a.M >= (a.mx_values ? 1024 : 129)) {
         switch (FF) {  // FF = 2 is H = 5120, taken above
-          case 0: hipLaunchKernelGGL((boundary_balanced_kernel<0, 256>), grid, dim3(256), 0, stream, a); break;
-          case 1: hipLaunchKernelGGL((boundary_balanced_kernel<1, 256>), grid, dim3(256), 0, stream, a); break;
-          default: hipLaunchKernelGGL((boundary_balanced_kernel<3, 256>), grid, dim3(256), 0, stream, a); break;
+          case 0: hipLaunchKernelGGL((boundary_balanced_kernel<0, 256, Source::kPartials>), grid, dim3(256), 0, stream, a); break;
+          case 1: hipLaunchKernelGGL((boundary_balanced_kernel<1, 256, Source::kPartials>), grid, dim3(256), 0, stream, a); break;
+          default: hipLaunchKernelGGL((boundary_balanced_kernel<3, 256, Source::kPartials>), grid, dim3(256), 0, stream, a); break;
         }
         return hipGetLastError();
       }
