@@ -637,7 +637,7 @@ def main():
             extra[f"glm_moe_tp4_k8_M{M}"] = entry(ms, nbytes, M)
             log(f"glm moe M={M}: {extra[f'glm_moe_tp4_k8_M{M}']}")
     if want("indexer") and not args.quick:
-        for M in (1, 4, 6, 8, 16, 64, 256, 1024, 4096):  # K=6144, 128 + 32 + 128 rows
+        for M in (1, 4, 6, 8, 16, 64, 256, 1024, 2048, 4096):  # K=6144, 128 + 32 + 128 rows
             ix = synth.indexer(M)
             ms, nbytes = bench_indexer(torch, mhc, ix, min(K, 100), min(W, 5))
             extra[f"indexer_projection_M{M}"] = entry(ms, nbytes, M)

@@ -256,7 +256,7 @@ def test_indexer_workspace_bytes():
     the call rejects."""
     import tp_reduce_mhc_amd as mhc
     assert mhc.mhcb_indexer_workspace_bytes(4, 6144, 128, 32, 128) == 0
-    assert mhc.mhcb_indexer_workspace_bytes(8192, 6144, 128, 32, 128) == 0
+    assert mhc.mhcb_indexer_workspace_bytes(24576, 6144, 128, 32, 128) == 0  # 1152 4x6 blocks
     small = mhc.mhcb_indexer_workspace_bytes(16, 6144, 128, 32, 128)
     large = mhc.mhcb_indexer_workspace_bytes(256, 6144, 128, 32, 128)
     assert 4096 < small < large and small % 4 == 0

@@ -1394,14 +1394,16 @@ def check_indexer(ix, got):
                           (4, 2048, 128, 32, 128, True), (9, 6144, 128, 32, 128, True),
                           (4, 6144, 128, 32, 128, True), (8, 6144, 128, 32, 128, True),
                           (6, 6144, 128, 32, 128, True), (17, 128, 4000, 64, 32, True),
-                          (2500, 1024, 128, 32, 128, True)],
+                          (2500, 1024, 128, 32, 128, True), (2048, 2048, 128, 32, 128, True),
+                          (4100, 1024, 128, 32, 128, True), (4096, 1024, 128, 32, 128, False)],
                          ids=lambda v: str(v))
 def test_indexer_projection_matches_oracle(M, K, key, heads, gate, workspace):
     """mhcb_indexer_projection against the oracle (bars in check_indexer).
     The one-workgroup-per-row form (M <= 4 and 5 .. 6) and the matrix-core
     form (M >= 7) with K split over workgroups
     (workspace) or summed by one workgroup (none, or K too short to split),
-    every output block shape (M=64, 256, 300), ragged token and row tiles,
+    every output block shape (M=64, 256, 300: 1x1, 2x2, 4x2 tiles; 2048,
+    2500: 4x3; 4100: 4x6), ragged token and row tiles,
     the largest K and the most rows (4096), an empty part; results repeat
     bit for bit."""
     ix = synth.indexer(M, K, key, heads, gate)

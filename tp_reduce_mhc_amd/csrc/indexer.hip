@@ -284,29 +284,28 @@ indexer_kernel(const IndexerArgs a, const int groups, const int blocks, const in
         for (int e = 0; e < 4; ++e) red[wave][slot(u, r, e)] = acc[u][r][e];
   __syncthreads();
 
-  // Thread tid < 256 owns elements tid * E .. tid * E + E - 1: one token, E
-  // consecutive rows of one tile (E divides 16); the other threads only
-  // take part in the barriers.
+  // Thread tid < 256 owns position tid (token m = tid / 16, row n = tid %
+  // 16) of every tile of the block: element e = u * RT + r is that position
+  // of tile (u, r).  The other threads only take part in the barriers.
   const bool owner = tid < kTile;
-  const int i0 = (owner ? tid : 0) * E, ur = i0 / kTile, m = i0 % kTile / kIdxTile,
-            n0 = i0 % kIdxTile;
-  const int64_t t = (int64_t)(group * TT + ur / RT) * kIdxTile + m;
-  const int row0 = (rgroup * RT + ur % RT) * kIdxTile + n0;
-  const bool active = owner && t < M;
+  const int pos = owner ? tid : 0, m = pos / kIdxTile, n = pos % kIdxTile;
   float v[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     v[e] = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kIdxFold; ++w) v[e] += red[w][i0 + e];
+    for (int w = 0; w < kIdxFold; ++w) v[e] += red[w][e * kTile + pos];
   }
   auto store_all = [&](const float (&o)[E]) {
 #pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (row0 + e < a.rows) store_output(a, t, row0 + e, o[e]);
+    for (int e = 0; e < E; ++e) {
+      const int64_t t = (int64_t)(group * TT + e / RT) * kIdxTile + m;
+      const int row = (rgroup * RT + e % RT) * kIdxTile + n;
+      if (t < M && row < a.rows) store_output(a, t, row, o[e]);
+    }
   };
   if (S == 1) {
-    if (active) store_all(v);
+    if (owner) store_all(v);
     return;
   }
 
@@ -314,7 +313,7 @@ indexer_kernel(const IndexerArgs a, const int groups, const int blocks, const in
   // block's last workgroup in range order.
   const int64_t plane = (int64_t)blocks * E * kTile;
   float *area = a.parts + (int64_t)block * E * kTile;
-  if (active) Words::store(area + split * plane, tid, v);
+  if (owner) Words::store(area + split * plane, tid, v);
   __builtin_amdgcn_s_waitcnt(0);  // this thread's partial stores are complete
   __syncthreads();
   uint32_t *counter = a.counters + block;
@@ -324,7 +323,7 @@ indexer_kernel(const IndexerArgs a, const int groups, const int blocks, const in
   __syncthreads();
   if (!last) return;
   if (tid == 0) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (!active) return;
+  if (!owner) return;
   // Eight ranges' words in flight at a time, added in range order.
   float sum[E];
 #pragma unroll
@@ -373,13 +372,24 @@ IndexerPlan plan_indexer(int M, int K, int rows, int cus, bool workspace) {
   // at most 96 blocks, four up to the counter area's 1024; 8 waves at
   // M <= 16, for 2x2 blocks past eight token tiles and for 4x2 blocks with
   // eight ranges, else 4.  (M=256: 15.0 us against 21.7 with the rule this
-  // replaced; M=4096: 87 against 110.)  A single range (no workspace, or
-  // more blocks than counters) takes 16 waves once a wave would have more
-  // than eight chunks, so that more of its loads are in flight.
+  // replaced; M=4096: 87 against 110.)  From 128 token tiles, 4x3 and then
+  // 4x6 blocks: a wave loads TT + RT operands a chunk for TT * RT matrix
+  // products, and with 4x2 the loads, not the matrix cores, set the time
+  // (M=2048: 40.7 us against 49.1 with 4x2; M=4096, 4x6: 72.9 against 87;
+  // 4x3 at M=1024 took 36.5 against 32.6, 4x6 at 2048 61 against 49: with
+  // few blocks their larger LDS fold and registers cost more).  A single
+  // range (no workspace, or more blocks than counters) takes 16 waves once
+  // a wave would have more than eight chunks, so that more of its loads
+  // are in flight (8 for blocks of more than 8 tiles, whose 16-wave form
+  // would spill registers).
   int64_t blocks;
   int64_t splits = 1;
   if (workspace) {
-    blocks = tiles <= 4 ? shape(1, 1) : tiles <= 16 ? shape(2, 2) : shape(4, 2);
+    blocks = tiles <= 4     ? shape(1, 1)
+             : tiles <= 16  ? shape(2, 2)
+             : tiles < 128  ? shape(4, 2)
+             : tiles < 256  ? shape(4, 3)
+                            : shape(4, 6);
     splits = blocks <= 96 ? 8 : blocks <= kIndexerCounters ? 4 : 1;
   } else {
     // Without K ranges, the largest block that still gives a workgroup per
@@ -396,7 +406,7 @@ IndexerPlan plan_indexer(int M, int K, int rows, int cus, bool workspace) {
   else if (p.tt == 2) p.waves = tiles > 8 ? 8 : 4;
   else if (p.tt == 4) p.waves = p.splits == 8 ? 8 : 4;
   else p.waves = 4;
-  if (p.splits == 1 && (int64_t)K / 32 > 8 * p.waves) p.waves = 16;
+  if (p.splits == 1 && (int64_t)K / 32 > 8 * p.waves) p.waves = p.tt * p.rt > 8 ? 8 : 16;
   p.counter_bytes = kIndexerCounters * 4;
   p.workspace_bytes =
       p.splits > 1 ? p.counter_bytes + (int64_t)p.splits * blocks * p.tt * p.rt * kIdxTile * kIdxTile * 4 : 0;
@@ -407,9 +417,10 @@ namespace {
 template <int TT, int RT>
 void launch_shape(const IndexerArgs &a, const IndexerPlan &p, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)p.blocks * p.splits));
-  if (p.waves == 16)
-    hipLaunchKernelGGL((indexer_kernel<TT, RT, 16>), grid, dim3(16 * kWave), 0, stream, a, p.groups,
-                       p.blocks, p.splits);
+  if (TT * RT <= 8 && p.waves == 16)
+    hipLaunchKernelGGL((indexer_kernel<TT, RT, TT * RT <= 8 ? 16 : 8>), grid,
+                       dim3((TT * RT <= 8 ? 16 : 8) * kWave), 0, stream, a, p.groups, p.blocks,
+                       p.splits);
   else if (p.waves == 8)
     hipLaunchKernelGGL((indexer_kernel<TT, RT, 8>), grid, dim3(8 * kWave), 0, stream, a, p.groups,
                        p.blocks, p.splits);
@@ -434,6 +445,8 @@ hipError_t launch_indexer(const IndexerArgs &a, const IndexerPlan &p, hipStream_
   if (p.tt == 1 && p.rt == 1) launch_shape<1, 1>(a, p, stream);
   else if (p.tt == 2 && p.rt == 2) launch_shape<2, 2>(a, p, stream);
   else if (p.tt == 4 && p.rt == 2) launch_shape<4, 2>(a, p, stream);
+  else if (p.tt == 4 && p.rt == 3) launch_shape<4, 3>(a, p, stream);
+  else if (p.tt == 4 && p.rt == 6) launch_shape<4, 6>(a, p, stream);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
