@@ -1224,6 +1224,35 @@ def test_finalize_random_shapes(case):
         assert_within_ulp(li, li_ref, 1, f"layer_input two_shot={two_shot} split={split}")
 
 
+@pytest.mark.parametrize("case", [(300, 4, 8, True, 0.0, True), (260, 3, 12, False, 0.2, False),
+                                  (257, 1, 1, True, 0.0, True), (290, 8, 16, False, 0.1, True),
+                                  (2048, 2, 5, False, 0.3, False), (1030, 4, 8, False, 0.125, True)],
+                         ids=lambda c: f"M{c[0]}-tp{c[1]}-k{c[2]}-mx{int(c[5])}")
+def test_finalize_balanced_form(case):
+    """MoE finalize at H=5120 on 257 to 2048 unsplit tokens (eight balanced
+    waves, ranks computed one at a time, routes in blocks of eight): the
+    range's ends, mixed rank counts, top_k up to 16, per-rank routing with
+    dropped routes, and the MXFP8 epilogue, against the oracle (codes and
+    scales too)."""
+    M, tp, k, replicated, drop, mxfp8 = case
+    f = synth.moe_finalize(M, H=5120, tp=tp, top_k=k, replicated_routing=replicated,
+                           drop_fraction=drop)
+    print(f"[gpu] {f.name} M={M} tp={tp} top_k={k} mxfp8={mxfp8}", flush=True)
+    ro, li, mx = run_finalize(f, mxfp8=mxfp8, split=False)
+    ro_ref, li_ref, _ = oracle.finalize(f.gemm2, f.weights, f.idx, f.shared, f.residual, f.post,
+                                        f.comb, f.pre, f.gamma, f.norm_eps,
+                                        replicated_routing=replicated, threads=8)
+    assert_bits_equal(ro, ro_ref, "residual_out")
+    assert_within_ulp(li, li_ref, 1, "layer_input")
+    if mxfp8:
+        v_q, s_q = oracle.quant_mxfp8(li)          # the oracle quantizes the GPU's BF16 output
+        assert_bits_equal(mx[0], v_q, "mxfp8 values")
+        assert_bits_equal(mx[1], s_q, "mxfp8 scales")
+    ro2, li2, _ = run_finalize(f, two_shot=True)
+    assert_bits_equal(ro2, ro, "two-shot residual_out")
+    assert_bits_equal(li2, li, "two-shot layer_input")
+
+
 # ---------------------------------------------------------------------------
 # GLM boundary of an MoE sublayer
 # ---------------------------------------------------------------------------

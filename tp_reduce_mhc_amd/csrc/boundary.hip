@@ -534,25 +534,29 @@ __device__ __forceinline__ void settle_chunk(typename Chunk<E>::W (&part)[TP], c
   }
 }
 
-// One chunk of the balanced kernel below, the same steps as
-// boundary_kernel: a1 rank sum from 0 in rank order, a2 post-mix (stores
-// residual_out), a4 collapse; returns the BF16 collapse and adds its
-// squares to ss.
+// a1 for one chunk: the ranks' BF16 contributions added from 0 in rank
+// order.
 template <int E, int TP>
-__device__ __forceinline__ typename Chunk<E>::W
-balanced_chunk(const typename Chunk<E>::W (&part)[TP], const typename Chunk<E>::W (&res)[kStreams],
-               const Mixes<kStreams> &m, uint16_t *out, int64_t H, double &ss) {
-  using C = Chunk<E>;
-  float sum[E];
+__device__ __forceinline__ void rank_sum_chunk(const typename Chunk<E>::W (&part)[TP], float (&sum)[E]) {
 #pragma unroll
   for (int e = 0; e < E; ++e) sum[e] = 0.0f;
 #pragma unroll
   for (int r = 0; r < TP; ++r) {
     float v[E];
-    C::unpack(part[r], v);
+    Chunk<E>::unpack(part[r], v);
 #pragma unroll
     for (int e = 0; e < E; ++e) sum[e] = sum[e] + v[e];
   }
+}
+
+// The rest of one chunk of the balanced kernel below, the same steps as
+// boundary_kernel: xr = bf16(rank sum), a2 post-mix (stores residual_out),
+// a4 collapse; returns the BF16 collapse and adds its squares to ss.
+template <int E>
+__device__ __forceinline__ typename Chunk<E>::W
+balanced_chunk(const float (&sum)[E], const typename Chunk<E>::W (&res)[kStreams],
+               const Mixes<kStreams> &m, uint16_t *out, int64_t H, double &ss) {
+  using C = Chunk<E>;
   float x[E];
   C::unpack(C::pack(sum), x);
   float r4[kStreams][E], y[kStreams][E];
@@ -588,10 +592,95 @@ balanced_chunk(const typename Chunk<E>::W (&part)[TP], const typename Chunk<E>::
   return pz;
 }
 
+// One rank's MoE finalize contributions (as finalize_fragment: acc = 0,
+// fma(row_k, w_k, acc) for the valid routes k ascending, + shared, BF16,
+// negative zero -> +0) to a thread's FF full fragments (columns
+// 8 (tid + NT c)) and, with `half`, its half fragment at column hcol, each
+// added to its rank sum.  Every gather of a block of eight routes is
+// issued before the first product.
+template <int FF, int NT>
+__device__ __forceinline__ void finalize_rank(const FinalizeView &f, const int32_t *srow,
+                                              const float *sw, int r, int64_t t, int64_t H,
+                                              int tid, int64_t hcol, bool half,
+                                              float (&sf)[FF > 0 ? FF : 1][8], float (&sh)[4]) {
+  const uint16_t *g = f.gemm2 + r * f.g_stride;
+  const uint16_t *shared = f.shared + r * f.s_stride + t * H;
+  float af[FF > 0 ? FF : 1][8], ah[4];
+  u32x4 shf[FF > 0 ? FF : 1];
+  u32x2 shh = {0, 0};
+#pragma unroll
+  for (int c = 0; c < FF; ++c) {
+    shf[c] = Chunk<8>::load(shared + (int64_t)(tid + NT * c) * kFrag);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) af[c][e] = 0.0f;
+  }
+  if (half) shh = Chunk<4>::load(shared + hcol);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) ah[e] = 0.0f;
+  for (int k0 = 0; k0 < f.top_k; k0 += 8) {
+    u32x4 rf[FF > 0 ? FF : 1][8];
+    u32x2 rh[8];
+    bool ok[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int k = k0 + i;
+      const int32_t row = k < f.top_k ? srow[r * f.top_k + k] : -1;
+      ok[i] = row >= 0 && row < f.rows;
+      const uint16_t *rp = g + (int64_t)(ok[i] ? row : 0) * H;
+#pragma unroll
+      for (int c = 0; c < FF; ++c)
+        rf[c][i] = ok[i] ? Chunk<8>::load(rp + (int64_t)(tid + NT * c) * kFrag) : u32x4{0, 0, 0, 0};
+      rh[i] = ok[i] && half ? Chunk<4>::load(rp + hcol) : u32x2{0, 0};
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (!ok[i]) continue;
+      const float w = sw[r * f.top_k + k0 + i];
+#pragma unroll
+      for (int c = 0; c < FF; ++c) {
+        float v[8];
+        Chunk<8>::unpack(rf[c][i], v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) af[c][e] = __builtin_fmaf(v[e], w, af[c][e]);
+      }
+      float v[4];
+      Chunk<4>::unpack(rh[i], v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ah[e] = __builtin_fmaf(v[e], w, ah[e]);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < FF; ++c) {
+    float s[8];
+    Chunk<8>::unpack(shf[c], s);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) af[c][e] = af[c][e] + s[e];
+    float v[8];
+    Chunk<8>::unpack(sanitize4(Chunk<8>::pack(af[c])), v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sf[c][e] = sf[c][e] + v[e];
+  }
+  if (half) {
+    float s[4];
+    Chunk<4>::unpack(shh, s);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ah[e] = ah[e] + s[e];
+    u32x2 w = Chunk<4>::pack(ah);
+    w[0] = sanitize_word(w[0]);
+    w[1] = sanitize_word(w[1]);
+    float v[4];
+    Chunk<4>::unpack(w, v);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sh[e] = sh[e] + v[e];
+  }
+}
+
 // The delayed boundary for an unsplit token whose fragment count is
 // NT * FF + 128 (H = 5120: FF = 2 with NT = 256 threads, FF = 1 with 512),
-// from resident partials or the ACTIVE generation of a mailbox, 8 ranks,
-// four streams and a layer input (optionally with the MXFP8 epilogue).  boundary_kernel would give such a
+// from 8 ranks' resident partials or the ACTIVE generation of a mailbox,
+// or from the MoE finalize contributions of any rank count (computed a
+// rank at a time), four streams and a layer input (optionally with the
+// MXFP8 epilogue).  boundary_kernel would give such a
 // token 4 FF + 2 one-fragment waves (NT = 256), and the SIMD that gets the
 // extra waves sets the VALU time.  Here every thread takes FF fragments
 // and the first 256 threads one half-fragment each (the last 128
@@ -600,22 +689,24 @@ balanced_chunk(const typename Chunk<E>::W (&part)[TP], const typename Chunk<E>::
 // (NT = 512).  Same arithmetic per element, same results.
 template <int FF, int NT, Source SRC>
 __global__ void __launch_bounds__(NT) boundary_balanced_kernel(const BoundaryArgs a) {
-  constexpr int TP = 8;
+  constexpr bool kFin = SRC == Source::kFinalize;
+  constexpr int TP = kFin ? 1 : 8;  // ranks held in registers
   static_assert(NT == 256 || NT == 512, "four or eight waves");
-  static_assert(SRC == Source::kPartials || SRC == Source::kMailbox, "partials or mailbox");
   __shared__ double red[kTokenThreadsWide / kWave + 1];
+  __shared__ int32_t srow[kFin ? kMaxRoutes : 1];
+  __shared__ float sw[kFin ? kMaxRoutes : 1];
   const int t = blockIdx.x, tid = threadIdx.x;
   const bool half = NT == 256 || tid < 256;  // uniform over each wave
   const int H = a.H;
-  const uint16_t *src;
-  int64_t rs;
+  const uint16_t *src = nullptr;
+  int64_t rs = 0;
   uint32_t gen = 0;
   if constexpr (SRC == Source::kMailbox) {
     gen = (uint32_t)__hip_atomic_load(a.mailbox.stage_state, __ATOMIC_RELAXED,
                                       __HIP_MEMORY_SCOPE_AGENT) % 3u;  // stays inside the slots
     rs = (int64_t)a.mailbox.capacity * H;
     src = a.mailbox.slots + (int64_t)gen * TP * rs + (int64_t)t * H;
-  } else {
+  } else if constexpr (SRC == Source::kPartials) {
     rs = a.rank_stride;
     src = a.partials + (int64_t)t * H;
   }
@@ -629,20 +720,26 @@ __global__ void __launch_bounds__(NT) boundary_balanced_kernel(const BoundaryArg
 #pragma unroll
   for (int c = 0; c < FF; ++c) {
     const int64_t col = (int64_t)(tid + NT * c) * kFrag;
+    if constexpr (!kFin) {
 #pragma unroll
-    for (int r = 0; r < TP; ++r) pf[c][r] = Chunk<8>::load(src + r * rs + col);
+      for (int r = 0; r < TP; ++r) pf[c][r] = Chunk<8>::load(src + r * rs + col);
+    }
 #pragma unroll
     for (int q = 0; q < kStreams; ++q) rf[c][q] = Chunk<8>::load(res_row + q * H + col);
     gf[c] = Chunk<8>::load_cached(a.gamma + col);
   }
   const int64_t hcol = (int64_t)FF * NT * kFrag + 4 * (tid & 255);
   if (half) {
+    if constexpr (!kFin) {
 #pragma unroll
-    for (int r = 0; r < TP; ++r) ph[r] = Chunk<4>::load(src + r * rs + hcol);
+      for (int r = 0; r < TP; ++r) ph[r] = Chunk<4>::load(src + r * rs + hcol);
+    }
 #pragma unroll
     for (int q = 0; q < kStreams; ++q) rh[q] = Chunk<4>::load(res_row + q * H + hcol);
     gh = Chunk<4>::load_cached(a.gamma + hcol);
   }
+  // Finalize: the routes are staged while those loads are in flight.
+  if constexpr (kFin) stage_routes(a.fin, a.tp, t, srow, sw);
   __builtin_amdgcn_sched_barrier(0);
   Mixes<kStreams> m;
   load_mixes<kStreams>(a, t, m);
@@ -655,15 +752,30 @@ __global__ void __launch_bounds__(NT) boundary_balanced_kernel(const BoundaryArg
     if (half) settle_chunk<4, TP>(ph, src + hcol, rs, a.mailbox);
   }
 
+  float sumf[FF > 0 ? FF : 1][8], sumh[4];
+  if constexpr (kFin) {
+#pragma unroll
+    for (int c = 0; c < FF; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sumf[c][e] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sumh[e] = 0.0f;
+    for (int r = 0; r < a.tp; ++r)
+      finalize_rank<FF, NT>(a.fin, srow, sw, r, t, H, tid, hcol, half, sumf, sumh);
+  }
   double ss = 0.0;
   u32x4 pzf[FF > 0 ? FF : 1];
 #pragma unroll
   for (int c = 0; c < FF; ++c) {
     const int64_t col = (int64_t)(tid + NT * c) * kFrag;
-    pzf[c] = balanced_chunk<8, TP>(pf[c], rf[c], m, out_row + col, H, ss);
+    if constexpr (!kFin) rank_sum_chunk<8, TP>(pf[c], sumf[c]);
+    pzf[c] = balanced_chunk<8>(sumf[c], rf[c], m, out_row + col, H, ss);
   }
   u32x2 pzh = {0, 0};
-  if (half) pzh = balanced_chunk<4, TP>(ph, rh, m, out_row + hcol, H, ss);
+  if (half) {
+    if constexpr (!kFin) rank_sum_chunk<4, TP>(ph, sumh);
+    pzh = balanced_chunk<4>(sumh, rh, m, out_row + hcol, H, ss);
+  }
   if constexpr (SRC == Source::kMailbox) {
     // Advance the generation and return the consumed slots to the sentinel.
     if (t == 0 && tid == 0) a.mailbox.stage_state[1] = (int32_t)((gen + 1) % 3);
@@ -791,6 +903,20 @@ hipError_t launch_tp(const BoundaryArgs &a, int threads, hipStream_t stream) {
 
 template <Source SRC, int HC>
 hipError_t launch_hc(const BoundaryArgs &a, hipStream_t stream) {
+  if constexpr (SRC == Source::kFinalize && HC == kStreams) {
+    // Unsplit H = 5120 tokens with a layer input, 257 to 2048 of them: eight
+    // balanced waves.  Measured (tp=4, top_k=8, us per call, ten waves in
+    // brackets): M=192 20.5 (19.4), 256 24.1 (23.9), 320 31.1 (36.1), 384
+    // 33.3 (39.0), 512 40.4-41.0 (44.3-45.5), 768 60.8 (64.0), 1024 77.0
+    // (82.1), 1536 116.2 (120.3), 2048 158.4 (159.5), 3072 243.5 (241.2),
+    // 4096 331.7 (321.5).  Past that, ten waves (five a SIMD against
+    // four) are faster again.
+    if (a.slices == 1 && a.pre && a.H / kFrag == 640 && a.M > 256 && a.M <= 2048) {
+      hipLaunchKernelGGL((boundary_balanced_kernel<1, 512, Source::kFinalize>), dim3(a.M), dim3(512), 0,
+                         stream, a);
+      return hipGetLastError();
+    }
+  }
   if constexpr ((SRC == Source::kPartials || SRC == Source::kMailbox) && HC == kStreams) {
     // Unsplit tokens of NT FF + 128 fragments, eight ranks and a layer
     // input: the balanced forms.  Measured (us per call, the ten-wave form
