@@ -643,10 +643,17 @@ __device__ __forceinline__ void finalize_rank(const FinalizeView &f, const int32
 #pragma unroll
         for (int e = 0; e < 8; ++e) af[c][e] = __builtin_fmaf(v[e], w, af[c][e]);
       }
-      float v[4];
-      Chunk<4>::unpack(rh[i], v);
+    }
+    if (half) {  // (uniform over each wave: the waves without one skip it)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ah[e] = __builtin_fmaf(v[e], w, ah[e]);
+      for (int i = 0; i < 8; ++i) {
+        if (!ok[i]) continue;
+        const float w = sw[r * f.top_k + k0 + i];
+        float v[4];
+        Chunk<4>::unpack(rh[i], v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ah[e] = __builtin_fmaf(v[e], w, ah[e]);
+      }
     }
   }
 #pragma unroll
