@@ -75,6 +75,26 @@ def test_balanced_forms(M, H, mxfp8):
                    mxfp8=mxfp8)
 
 
+@pytest.mark.parametrize("M,mxfp8", [(1, True), (3, False), (26, True), (51, False), (52, True),
+                                     (64, False)])
+def test_split_half_form(M, mxfp8):
+    """H = 5120 tokens split with a workspace, as chosen on 256 compute
+    units: five slices of 128 fragments (four columns a thread) up to
+    M = 51, four one-fragment slices beyond.  Every element against the
+    oracle, MXFP8 codes and scales with the padding rows included; the
+    unsplit call gives the same bits."""
+    b = synth.boundary(90, M, 5120, 8, 0.5, f"split-half-H5120-tp8-M{M}")
+    ro, li, mx = check_boundary(b, mxfp8=mxfp8)
+    out = mhc.boundary(dev(b.partials), dev(b.residual), dev(b.post), dev(b.comb), dev(b.pre),
+                       dev(b.gamma), b.norm_eps, mxfp8=mxfp8, split=False)
+    torch.cuda.synchronize()
+    assert_bits_equal(u16(out[0]), ro, "unsplit residual_out")
+    assert_bits_equal(u16(out[1]), li, "unsplit layer_input")
+    if mxfp8:
+        assert_bits_equal(host(out[2][0]), mx[0], "unsplit mxfp8 values")
+        assert_bits_equal(host(out[2][1]), mx[1], "unsplit mxfp8 scales")
+
+
 def test_bf16_sum_is_bit_exact_through_the_probe():
     """post = 1, comb = 0 expose the BF16 rank sum in every output stream."""
     b = synth.dsv41_delayed(32)
@@ -1020,22 +1040,26 @@ def test_mailbox_consumer_polls_fragments_that_land_late(M):
     assert late_total > 0
 
 
-def test_split_wait_gives_up_with_a_tiny_spin_limit():
+@pytest.mark.parametrize("S", [16, 5])
+def test_split_wait_gives_up_with_a_tiny_spin_limit(S):
     """A workspace spin limit of one re-read on token-split delayed calls
-    (M = 1024, 16 slices): slices that find a partner's value missing give
-    up.  Every kernel exits; the streams stay exact; each slice's block of
-    the layer input is either the oracle's bits or all NaN; the status
-    counts the time-outs."""
+    (M = 1024; 16 slices of 40 fragments, or 5 of 128 in the form with
+    four columns a thread): slices that find a partner's value missing
+    give up.  Every
+    kernel exits; the streams stay exact; each slice's block of the layer
+    input is either the oracle's bits or all NaN; the status counts the
+    time-outs."""
     M, H = 1024, 5120
     b = synth.boundary(32, M, H, 8, 0.5, "split-timeout-H5120-tp8-M1024")
+    print(f"[gpu] {b.name} slices={S}", flush=True)
     ro_ref, li_ref, _ = oracle.boundary(b.partials, b.residual, b.post, b.comb, b.pre, b.gamma,
                                         b.norm_eps, threads=oracle.default_threads())
     ws = mhc.new_workspace(mhc.mhcb_workspace_bytes(0, 0, 1, 0), "cuda")
-    block = -(-(H // 8) // 16)
-    block = (block + 3) // 4 * 4 * 8          # columns per slice (16 slices of 40 fragments)
+    block = -(-(H // 8) // S)
+    block = (block + 3) // 4 * 4 * 8          # columns per slice
     args = [dev(b.partials), M * H, None, dev(b.residual), dev(b.post), dev(b.comb), dev(b.pre),
             dev(b.gamma)]
-    prev = mhc.mhcb_set_token_slices(16)
+    prev = mhc.mhcb_set_token_slices(S)
     gave_up = 0
     try:
         mhc.mhcb_workspace_set_spin_limit(ws, 1)

@@ -870,6 +870,105 @@ __global__ void __launch_bounds__(NT) boundary_balanced_kernel(const BoundaryArg
   }
 }
 
+// The delayed boundary for a token split over slices of 128 fragments
+// (H = 5120: five slices), from 8 ranks' resident partials or the ACTIVE
+// generation of a mailbox, four streams and a layer input (optionally with
+// the MXFP8 epilogue).  Each of the 256 threads takes a half fragment (4
+// columns): one wave per SIMD, each with half a fragment's chain.  Slices
+// of 160 one-fragment lanes (192 threads) ran a whole fragment's chain on
+// three SIMDs and left the fourth idle.  Same arithmetic per element, same
+// results; the slices' sums of squares meet in token_inv.
+template <Source SRC>
+__global__ void __launch_bounds__(256) boundary_split_half_kernel(const BoundaryArgs a) {
+  constexpr int TP = 8;
+  static_assert(SRC == Source::kPartials || SRC == Source::kMailbox, "partials or mailbox");
+  __shared__ double red[kTokenThreadsWide / kWave + 1];
+  const int s = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
+  const int H = a.H;
+  const int64_t col = (int64_t)s * a.slice_frags * kFrag + 4 * tid;
+  const uint16_t *src;
+  int64_t rs;
+  uint32_t gen = 0;
+  if constexpr (SRC == Source::kMailbox) {
+    gen = (uint32_t)__hip_atomic_load(a.mailbox.stage_state, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT) % 3u;  // stays inside the slots
+    rs = (int64_t)a.mailbox.capacity * H;
+    src = a.mailbox.slots + (int64_t)gen * TP * rs + (int64_t)t * H;
+  } else {
+    rs = a.rank_stride;
+    src = a.partials + (int64_t)t * H;
+  }
+  const uint16_t *res_row = a.residual + (int64_t)t * kStreams * H;
+  u32x2 ph[TP], rh[kStreams];
+#pragma unroll
+  for (int r = 0; r < TP; ++r) ph[r] = Chunk<4>::load(src + r * rs + col);
+#pragma unroll
+  for (int q = 0; q < kStreams; ++q) rh[q] = Chunk<4>::load(res_row + q * H + col);
+  const u32x2 gh = Chunk<4>::load_cached(a.gamma + col);
+  __builtin_amdgcn_sched_barrier(0);
+  Mixes<kStreams> m;
+  load_mixes<kStreams>(a, t, m);
+  // The token slot's epoch word, read by wave 0 behind the loads above.
+  uint64_t callw = 0;
+  if (tid < kWave) callw = slot_call_word(token_slot(a.sync, t));
+  if constexpr (SRC == Source::kMailbox) settle_chunk<4, TP>(ph, src + col, rs, a.mailbox);
+
+  float sum[4];
+  rank_sum_chunk<4, TP>(ph, sum);
+  double ss = 0.0;
+  const u32x2 pz = balanced_chunk<4>(sum, rh, m, a.residual_out + (int64_t)t * kStreams * H + col, H, ss);
+  if constexpr (SRC == Source::kMailbox) {
+    // Advance the generation and return the consumed slots to the sentinel.
+    if (t == 0 && s == 0 && tid == 0) a.mailbox.stage_state[1] = (int32_t)((gen + 1) % 3);
+    uint16_t *slots = const_cast<uint16_t *>(src);
+#pragma unroll
+    for (int r = 0; r < TP; ++r) Chunk<4>::store(slots + r * rs + col, Chunk<4>::filled(0x80008000u));
+  }
+
+  const float inv = token_inv(a, t, s, ss, red, callw);
+  if (tid < kWave)
+    for (int w = tid * a.slices + s; w < kClearWords; w += kWave * a.slices)
+      clear_previous_word(token_slot(a.sync, t), unpack_call(callw), w);
+
+  // out = bf16((p * inv) * gamma); with MXFP8 also the E4M3 codes and the
+  // UE8M0 scale of each 32-column block (lanes 8q .. 8q+7).
+  float p[4], g[4], o[4];
+  Chunk<4>::unpack(pz, p);
+  Chunk<4>::unpack(gh, g);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = (p[e] * inv) * g[e];
+  const u32x2 out = Chunk<4>::pack(o);
+  Chunk<4>::store(a.layer_input + (int64_t)t * H + col, out);
+  if (a.mx_values) {
+    const int K = H / 32;
+    float ov[4];
+    Chunk<4>::unpack(out, ov);
+    float amax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(ov[e]));
+    amax = __builtin_fmaxf(amax, row_xor<1>(amax));
+    amax = __builtin_fmaxf(amax, row_xor<2>(amax));
+    amax = __builtin_fmaxf(amax, row_xor<4>(amax));
+    const uint32_t e8 = ue8m0_round_up(amax * (1.0f / 448.0f));
+    const float sc = ue8m0_inverse(e8);
+    uint32_t codes = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) codes |= e4m3_rne_sat(ov[e] * sc) << (8 * e);
+    __builtin_nontemporal_store(codes, reinterpret_cast<uint32_t *>(a.mx_values + (int64_t)t * H + col));
+    if ((tid & 7) == 0) a.mx_scales[sf_offset(t, (int)(col / 32), K)] = (uint8_t)e8;
+    // The scales of the padding rows M .. ceil(M/128)*128 - 1 are zero, one
+    // 4-column word per store, spread over the grid.
+    const int words_per_row = K / 4;
+    const int64_t padded = ((int64_t)a.M + 127) / 128 * 128;
+    const int64_t words = (padded - a.M) * words_per_row;
+    const int64_t wg = (int64_t)t * a.slices + s, wgs = (int64_t)a.M * a.slices;
+    for (int64_t w = wg * 256 + tid; w < words; w += wgs * 256) {
+      const int64_t row = a.M + w / words_per_row;
+      *reinterpret_cast<uint32_t *>(a.mx_scales + sf_offset(row, (int)(w % words_per_row) * 4, K)) = 0u;
+    }
+  }
+}
+
 template <int TRIPS, int TP, Source SRC, int HC>
 void launch_one(const BoundaryArgs &a, dim3 grid, dim3 block, hipStream_t stream) {
   hipLaunchKernelGGL((boundary_kernel<TRIPS, TP, SRC, HC>), grid, block, 0, stream, a);
@@ -925,6 +1024,10 @@ hipError_t launch_hc(const BoundaryArgs &a, hipStream_t stream) {
     }
   }
   if constexpr ((SRC == Source::kPartials || SRC == Source::kMailbox) && HC == kStreams) {
+    if (a.slices > 1 && a.slice_frags == 128 && a.tp == 8 && a.pre && a.H / kFrag == 640) {
+      hipLaunchKernelGGL((boundary_split_half_kernel<SRC>), dim3(a.slices, a.M), dim3(256), 0, stream, a);
+      return hipGetLastError();
+    }
     // Unsplit tokens of NT FF + 128 fragments, eight ranks and a layer
     // input: the balanced forms.  Measured (us per call, the ten-wave form
     // in brackets):
