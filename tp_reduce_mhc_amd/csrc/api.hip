@@ -404,17 +404,27 @@ int mhcb_boundary(const uint16_t *partials, int64_t rank_stride, const mhcb_mail
   a.H = hidden_size;
   a.norm_eps = norm_eps;
   choose_slices(a, workspace, device_cus(), 4);
-  // H = 5120 with eight ranks, four streams and a layer input, where four
-  // slices were chosen: five slices of 128 fragments (four columns a
-  // thread) while every slice of the call has a compute unit of its own.
-  // Measured per call (us, four slices in brackets): M=1 4.16-4.33
-  // (4.72-4.75), 8 4.63 (5.28), 16 4.75 (5.33), 32 4.93-5.03 (5.53-5.55),
-  // 51 5.48 (5.87); at M=64, 320 workgroups, 6.21 (6.08).  Ten slices of
-  // 64 fragments (two columns a thread) were no faster up to M=25.
-  if (a.slices == 4 && g_slices_override <= 0 && a.tp == 8 && a.hc == kStreams && a.pre &&
-      a.H / kFrag == 640 && 5 * a.M <= device_cus()) {
-    a.slices = 5;
-    a.slice_frags = 128;
+  // H = 5120 with eight ranks, four streams and a layer input:
+  //  - where four slices were chosen: five slices of 128 fragments (four
+  //    columns a thread) while every slice of the call has a compute unit
+  //    of its own.  Per call (us, four slices in brackets): M=1 4.16-4.33
+  //    (4.72-4.75), 8 4.63 (5.28), 16 4.75 (5.33), 32 4.93-5.03
+  //    (5.53-5.55), 51 5.43-5.48 (5.84-5.87); at M=64, 320 workgroups, 6.21
+  //    (6.08).  Ten slices of 64 fragments (two columns a thread) were no
+  //    faster up to M=25;
+  //  - where two were chosen (86-127 tokens): none, the eight-wave form.
+  //    Per call (us, two slices in brackets): M=90 6.36-6.39 (6.70-6.73),
+  //    100 6.39-6.45 (6.80-6.82), 127 6.55-6.58 (7.21-7.28); with three
+  //    slices (65-85 tokens) the split still wins or ties: M=72 6.15-6.17
+  //    against 6.24-6.35 unsplit, M=80 6.24 against 6.26-6.27.
+  if (g_slices_override <= 0 && a.tp == 8 && a.hc == kStreams && a.pre && a.H / kFrag == 640) {
+    if (a.slices == 4 && 5 * a.M <= device_cus()) {
+      a.slices = 5;
+      a.slice_frags = 128;
+    } else if (a.slices == 2) {
+      a.slices = 1;
+      a.slice_frags = a.H / kFrag;
+    }
   }
   return launched(launch_boundary(a, stream), fn);
 }
