@@ -662,9 +662,11 @@ static int finalize_impl(const char *fn, const uint16_t *gemm2_permuted, int64_t
     if ((rc = check_workspace(fn, workspace, workspace_bytes, kSyncBytes))) return rc;
     a.source = Source::kFinalize;
     a.fin = f;
-    // One workgroup per compute unit: measured on MI355X (H=5120, tp=4,
-    // top_k=8, M=64), 4 slices take 13.1 us, 2 take 14.1, 8 take 15.5.
-    choose_slices(a, workspace, device_cus(), kMaxSlices);
+    // About one workgroup per compute unit, at most five a token.  Measured
+    // on MI355X (H=5120, tp=4, top_k=8; us per call): M=64 4 slices 11.6, 2
+    // 12.6, 8 13.7; M=32 5 slices 10.85, 4 11.0, 8 11.8; M=8 5 slices 10.4,
+    // 10 slices 10.5, 8 11.5.
+    choose_slices(a, workspace, device_cus(), 5);
     return launched(launch_boundary(a, stream), fn);
   }
   const int64_t need = mhcb_workspace_bytes(M, hidden_size, tp, 1);
