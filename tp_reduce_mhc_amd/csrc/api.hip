@@ -138,15 +138,16 @@ SyncView sync_view(void *ws) {
 // Workgroups per token: with a workspace and few tokens, the token's
 // fragments are spread over up to `max_slices` workgroups (at least one
 // wave of fragments each; slices cover whole 32-column blocks) until there
-// are about `target` workgroups in flight.  Measured on MI355X (H=5120,
-// tp=8): 4 slices save 0.5-0.8 us per call for M <= 64 (M=1: 4.9 vs 5.7 us,
-// M=64: 6.0 vs 6.5); at M=128, 2 slices cost 0.3 us more than none.
-void choose_slices(BoundaryArgs &a, void *ws, int target, int max_slices) {
+// are about `target` workgroups in flight, for fewer than `split_below`
+// tokens.  Measured on MI355X (H=5120, tp=8): 4 slices save 0.5-0.8 us per
+// call for M <= 64 (M=1: 4.9 vs 5.7 us, M=64: 6.0 vs 6.5); at M=128, 2
+// slices cost 0.3 us more than none.
+void choose_slices(BoundaryArgs &a, void *ws, int target, int max_slices, int split_below = 128) {
   a.slices = 1;
   a.slice_frags = a.H / kFrag;
   if (!ws || a.M > kSyncTokens) return;
   const int F = a.H / kFrag;
-  int S = g_slices_override > 0 ? g_slices_override : (a.M < 128 ? target / a.M : 1);
+  int S = g_slices_override > 0 ? g_slices_override : (a.M < split_below ? target / a.M : 1);
   if (g_slices_override <= 0 && S > max_slices) S = max_slices;
   const int cap = g_slices_override > 0 ? F / 4 : F / kWave;
   S = S < 1 ? 1 : S;
@@ -662,11 +663,14 @@ static int finalize_impl(const char *fn, const uint16_t *gemm2_permuted, int64_t
     if ((rc = check_workspace(fn, workspace, workspace_bytes, kSyncBytes))) return rc;
     a.source = Source::kFinalize;
     a.fin = f;
-    // About one workgroup per compute unit, at most five a token.  Measured
-    // on MI355X (H=5120, tp=4, top_k=8; us per call): M=64 4 slices 11.6, 2
-    // 12.6, 8 13.7; M=32 5 slices 10.85, 4 11.0, 8 11.8; M=8 5 slices 10.4,
-    // 10 slices 10.5, 8 11.5.
-    choose_slices(a, workspace, device_cus(), 5);
+    // About one workgroup per compute unit, at most five a token, up to
+    // half as many tokens as compute units.  Measured on MI355X (H=5120,
+    // tp=4, top_k=8; us per call): M=64 4 slices 11.6, 2 12.6, 8 13.7;
+    // M=32 5 slices 10.85, 4 11.0, 8 11.8; M=8 5 slices 10.4, 10 slices
+    // 10.5, 8 11.5; M=128 2 slices 15.6, none 17.4; M=160 3 slices 18.1,
+    // none 18.0, 2 26.4.
+    const int cus = device_cus();
+    choose_slices(a, workspace, cus, 5, cus / 2 + 1);
     return launched(launch_boundary(a, stream), fn);
   }
   const int64_t need = mhcb_workspace_bytes(M, hidden_size, tp, 1);
